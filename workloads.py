@@ -1,0 +1,199 @@
+"""Seeded synthetic inputs for MLA paged-KV decode.
+
+This module only draws random numbers and lays them out in the paged-cache
+format; it performs none of the attention arithmetic.  Both the fp64 oracle
+(``oracle/``) and the HIP path consume exactly the bytes produced here.
+
+Workload shapes follow the paged-KV decode setting of the page
+"深度剖析DeepSeek Infra开源全貌" (jingzhunhuoke.net/55333.html), DAY1 FlashMLA,
+feature ② (KV cache paged in 64-token blocks); head sizes (576-wide latent+rope
+key, value = its first 512 dims, one shared KV head) are the MLA decode shape.
+
+Recipe (per workload, generator ``torch.Generator('cpu').manual_seed(seed)``,
+drawn in this order):
+  1. seqlens (distribution per workload, below),
+  2. a random permutation of the KV pool assigned, in order, to every
+     request's logical blocks,
+  3. Q ~ N(0,1) fp32 [B, s_q, h_q, 576] rounded to bf16 (round-to-nearest-even),
+  4. KV pool ~ N(0,1) fp32 [pool, 64, 1, 576] rounded to bf16.
+Then: one extra NaN-filled "sentinel" block is appended at index ``pool`` and
+every unused block-table slot points at it; the rows of each request's last
+block that lie beyond its length are overwritten with NaN.  Neither may ever
+influence a result.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+BLOCK_SIZE = 64
+D_K = 576
+D_V = 512
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    name: str
+    batch: int
+    s_q: int
+    h_q: int
+    seqlen_kind: str
+    seed: int
+    h_kv: int = 1
+    extra_pool: int = 64
+    fixed_pool: int | None = None
+    desc: str = field(default="", compare=False)
+
+    @property
+    def rows(self) -> int:
+        return self.s_q * self.h_q
+
+
+WORKLOADS: dict[str, Workload] = {
+    "tiny": Workload("tiny", "tiny MLA decode", batch=2, s_q=1, h_q=16,
+                     seqlen_kind="tiny", seed=1000, fixed_pool=8,
+                     desc="B=2, s_q=1, h_q=16, seqlens {65,130}, pool of 8 blocks"),
+    "membound": Workload("membound", "memory-bound decode", batch=64, s_q=1, h_q=16,
+                         seqlen_kind="const4096", seed=1001, extra_pool=64,
+                         desc="B=64, s_q=1, h_q=16, every seqlen 4096, pool 4096+64"),
+    "ridge": Workload("ridge", "compute-near-ridge decode", batch=128, s_q=1, h_q=128,
+                      seqlen_kind="uniform1024_8192", seed=1002, extra_pool=64,
+                      desc="B=128, s_q=1, h_q=128, seqlens U[1024,8192]"),
+    "ragged": Workload("ragged", "ragged 2-token speculative decode", batch=132, s_q=2,
+                       h_q=128, seqlen_kind="lognormal", seed=1003, extra_pool=64,
+                       desc="B=132, s_q=2 causal, h_q=128, seqlens "
+                            "clamp(round(lognormal(7.5,1)),1,32768)"),
+    "long": Workload("long", "long-context decode", batch=16, s_q=1, h_q=128,
+                     seqlen_kind="alt16k_64k", seed=1004, fixed_pool=10496,
+                     desc="B=16, s_q=1, h_q=128, seqlens alternating 16384/65536, "
+                          "pool 10496 blocks"),
+}
+
+# The order the workloads are listed in (index 0 is the small case).
+WORKLOAD_ORDER = ["tiny", "membound", "ridge", "ragged", "long"]
+
+
+def draw_seqlens(kind: str, batch: int, gen: torch.Generator) -> torch.Tensor:
+    if kind == "tiny":
+        return torch.tensor([65, 130], dtype=torch.int32)
+    if kind == "const4096":
+        return torch.full((batch,), 4096, dtype=torch.int32)
+    if kind == "uniform1024_8192":
+        return torch.randint(1024, 8193, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
+    if kind == "lognormal":
+        z = torch.randn((batch,), generator=gen, dtype=torch.float64)
+        lens = torch.round(torch.exp(7.5 + 1.0 * z)).clamp(1, 32768)
+        return lens.to(torch.int32)
+    if kind == "alt16k_64k":
+        return torch.tensor([16384 if b % 2 == 0 else 65536 for b in range(batch)],
+                            dtype=torch.int32)
+    raise ValueError(f"unknown seqlen kind {kind}")
+
+
+def blocks_for(seqlen: int) -> int:
+    """Number of 64-token pages a request of ``seqlen`` tokens occupies."""
+    return (int(seqlen) + BLOCK_SIZE - 1) // BLOCK_SIZE
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor            # bf16 [B, s_q, h_q, 576]
+    kcache: torch.Tensor       # bf16 [num_blocks, 64, 1, 576]  (last block = NaN sentinel)
+    block_table: torch.Tensor  # int32 [B, bt_stride]
+    seqlens: torch.Tensor      # int32 [B]
+    scale: float
+    causal: bool
+    s_q: int
+    h_q: int
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    def to(self, device) -> "DecodeInputs":
+        return DecodeInputs(self.q.to(device), self.kcache.to(device),
+                            self.block_table.to(device), self.seqlens.to(device),
+                            self.scale, self.causal, self.s_q, self.h_q)
+
+
+def build_inputs(seqlens, s_q: int, h_q: int, seed: int, pool: int | None = None,
+                 extra_pool: int = 64, nan_tails: bool = True,
+                 q_scale: float = 1.0, gen: torch.Generator | None = None) -> DecodeInputs:
+    """Paged-cache inputs for explicit per-request lengths.
+
+    ``pool`` defaults to (total pages + extra_pool).  Draw order: permutation,
+    Q, KV pool (the seqlens are given).
+    """
+    seqlens = torch.as_tensor(seqlens, dtype=torch.int32).reshape(-1)
+    if gen is None:
+        gen = torch.Generator().manual_seed(seed)
+    batch = int(seqlens.shape[0])
+    nblk = [blocks_for(int(x)) for x in seqlens]
+    total = sum(nblk)
+    if pool is None:
+        pool = total + extra_pool
+    if pool < total:
+        raise ValueError(f"pool {pool} smaller than the {total} pages needed")
+    perm = torch.randperm(pool, generator=gen).to(torch.int32)
+    bt_stride = max(1, max(nblk) if nblk else 1)
+    sentinel = pool
+    block_table = torch.full((batch, bt_stride), sentinel, dtype=torch.int32)
+    pos = 0
+    for b, n in enumerate(nblk):
+        block_table[b, :n] = perm[pos:pos + n]
+        pos += n
+    q = torch.randn((batch, s_q, h_q, D_K), generator=gen, dtype=torch.float32)
+    if q_scale != 1.0:
+        q = q * q_scale
+    q = q.to(torch.bfloat16)
+    kv = torch.empty((pool + 1, BLOCK_SIZE, 1, D_K), dtype=torch.bfloat16)
+    # Draw the pool in slabs to bound the fp32 temporary.
+    slab = 1024
+    for s in range(0, pool, slab):
+        e = min(pool, s + slab)
+        kv[s:e] = torch.randn((e - s, BLOCK_SIZE, 1, D_K), generator=gen,
+                              dtype=torch.float32).to(torch.bfloat16)
+    kv[pool] = float("nan")
+    if nan_tails:
+        for b, n in enumerate(nblk):
+            L = int(seqlens[b])
+            tail = n * BLOCK_SIZE - L
+            if n > 0 and tail > 0:
+                kv[int(block_table[b, n - 1]), BLOCK_SIZE - tail:] = float("nan")
+    return DecodeInputs(q=q, kcache=kv, block_table=block_table, seqlens=seqlens,
+                        scale=D_K ** -0.5, causal=s_q > 1, s_q=s_q, h_q=h_q)
+
+
+def make_inputs(key: str, nan_tails: bool = True) -> DecodeInputs:
+    """The seeded inputs of one named workload (see WORKLOADS)."""
+    w = WORKLOADS[key]
+    gen = torch.Generator().manual_seed(w.seed)
+    seqlens = draw_seqlens(w.seqlen_kind, w.batch, gen)
+    total = sum(blocks_for(int(x)) for x in seqlens)
+    pool = w.fixed_pool if w.fixed_pool is not None else total + w.extra_pool
+    return build_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
+                        nan_tails=nan_tails, gen=gen)
+
+
+def algorithmic_counts(seqlens, s_q: int, h_q: int) -> dict:
+    """Bytes and flops the method must move/compute (no padding, no partials).
+
+    bytes = sum_b L_b*576*2 (each KV row once per request)
+            + B*M*(576*2 + 512*2 + 4) (Q in, O and LSE out)
+            + sum_b ceil(L_b/64)*4 (block table) + B*4 (seqlens)
+    flops = 2*(576+512) per visible (query row, key) pair; with s_q query
+            tokens under the causal rule token t sees L-s_q+1+t keys.
+    """
+    seqlens = [int(x) for x in seqlens]
+    M = s_q * h_q
+    kv = sum(L * D_K * 2 for L in seqlens)
+    io = len(seqlens) * M * (D_K * 2 + D_V * 2 + 4)
+    meta = sum(blocks_for(L) * 4 for L in seqlens) + len(seqlens) * 4
+    pairs = 0
+    for L in seqlens:
+        for t in range(s_q):
+            pairs += h_q * max(0, L - s_q + 1 + t)
+    return {"bytes": kv + io + meta, "kv_bytes": kv, "flops": 2 * (D_K + D_V) * pairs}
