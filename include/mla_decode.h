@@ -1,0 +1,182 @@
+/*
+ * mla_decode.h — C ABI of the MI355X (gfx950) paged-KV MLA decode library.
+ *
+ * The operation (page "深度剖析DeepSeek Infra开源全貌", jingzhunhuoke.net/55333.html,
+ * section DAY1 FlashMLA):
+ *   - MLA: all query heads of a request attend over ONE shared latent KV head
+ *     (terminology paragraph on MLA).  A key row is 576 wide (512 latent + 64
+ *     rope); the value row is the first 512 dims of the same cache row.
+ *   - The KV cache is paged in blocks of 64 tokens (feature ②): token j of
+ *     request b is row j % 64 of page block_table[b][j / 64].
+ *   - The result is exact softmax attention computed tile by tile, as two
+ *     products, scores then probabilities times values (FlashMLA terminology
+ *     paragraph; feature ④).
+ *   - Variable per-request lengths are balanced across compute units by
+ *     splitting long requests' keys over several workers and merging the
+ *     partial results (feature ⑤, dynamic load for variable-length input).
+ *
+ *   For query row r = t*h_q + h of request b (t < s_q, h < h_q):
+ *     visible keys  J = { j < L_b - s_q + 1 + t }  if causal, else { j < L_b }
+ *     s_j  = scale * dot(q[b,t,h,0:576], K_b[j,0:576])
+ *     LSE  = ln( sum_{j in J} exp(s_j) )                (natural log, fp32)
+ *     O    = sum_{j in J} exp(s_j - LSE) * K_b[j,0:512]  (bf16, RNE)
+ *   An empty J gives O = 0 and LSE = -inf.
+ *
+ * Conventions for every entry point:
+ *   - All pointers named *_d are DEVICE pointers; the caller allocates and owns
+ *     every buffer (inputs, outputs, metadata, workspace).  The library never
+ *     allocates or frees and keeps no mutable global state, so calls on
+ *     different streams may run concurrently.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Enqueueing entry points are asynchronous: results are valid once the
+ *     stream has been synchronised.  They never synchronise the host.
+ *   - All arguments are validated on the host BEFORE anything is enqueued; an
+ *     invalid call returns a negative status and enqueues nothing.
+ *   - Tensors are dense, row-major ("contiguous") with the stated shapes.
+ *     q, kcache and out must be 16-byte aligned; int32 and fp32 buffers
+ *     4-byte aligned; workspace 256-byte aligned.
+ *   - Device data (seqlens, block_table) is not visible to host validation.
+ *     Page ids outside [0, num_blocks) and table slots at or beyond bt_stride
+ *     are read as all-zero key rows (never out of bounds); seqlens must lie in
+ *     [0, bt_stride*64] for the result to be the attention defined above.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MLA_OK               0
+#define MLA_ERR_INVALID_ARG (-1) /* null/misaligned pointer, bad size or enum */
+#define MLA_ERR_UNSUPPORTED (-2) /* valid but not implemented shape (h_q) */
+#define MLA_ERR_WORKSPACE   (-3) /* workspace smaller than mla_decode_workspace_bytes */
+#define MLA_ERR_HIP         (-4) /* a HIP runtime call or launch failed */
+
+/* Fixed shape constants. */
+#define MLA_BLOCK_SIZE 64        /* tokens per KV page (feature ②) */
+#define MLA_D_K 576              /* key width: 512 latent + 64 rope */
+#define MLA_D_V 512              /* value width: first 512 dims of the key row */
+#define MLA_TILE_META_INTS 8     /* int32 words per part in tile_meta */
+
+/*
+ * mla_decode_num_parts — host only, no HIP call.
+ * Recommended number of split-KV parts (workers) for a launch: one workgroup
+ * per compute unit.  A workgroup carries one row tile of query rows (up to 64
+ * rows; s_q*h_q <= 32 fits one tile, larger counts use s_q*h_q/64 tiles), and
+ * each part runs once per row tile, so parts = num_cus / row_tiles.
+ *   h_q in {16,32,64,128}, s_q in {1,2}, h_kv == 1, num_cus >= 1.
+ * Returns MLA_OK and *num_parts_out >= 1, or an error status.
+ */
+int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int num_cus,
+                         int* num_parts_out);
+
+/*
+ * mla_decode_workspace_bytes — host only, no HIP call.
+ * Size of the fp32 split-partial workspace that mla_decode_fwd /
+ * mla_decode_splitkv / mla_decode_combine need for `num_parts` parts:
+ *   slots = 2*(num_parts-1) (an upper bound of the pieces of split requests),
+ *   bytes = slots * s_q*h_q * (512 + 1) * 4, rounded up to 256.
+ * May be 0 (num_parts == 1); then the workspace pointer may be NULL.
+ * Layout (M = s_q*h_q, slots as above): fp32 partial outputs
+ * O_part[slots][M][512], each normalised over its own keys, followed by fp32
+ * LSE_part[slots][M] in BASE-2 (log2 of the sum of exp(scale*q.k)), -inf for a
+ * piece with no visible key.  Request b's pieces occupy slots
+ * [split_offsets[b], split_offsets[b+1]) in key order.
+ */
+int mla_decode_workspace_bytes(int batch, int s_q, int h_q, int num_parts,
+                               size_t* bytes_out);
+
+/*
+ * mla_decode_metadata — enqueue the split-KV scheduler (one workgroup).
+ * Reads seqlens_d on the device (no host sync) and writes the partition of
+ * all requests' pages over num_parts parts:
+ *   tile_meta_d     int32 [num_parts][8] = {begin_req, begin_page, end_req,
+ *                   end_page, first_split, 0, 0, 0}; part p covers the
+ *                   (request, page) range [begin, end) in lexicographic order.
+ *   split_offsets_d int32 [batch+1]: partial-slot prefix; request b owns slots
+ *                   [split_offsets[b], split_offsets[b+1]) (empty when the
+ *                   request is handled by one part and written directly).
+ * Balancing rule (all integers): cost_b = ceil(L_b/64) + c for L_b > 0 and 0
+ * otherwise, with the per-request overhead c = max(1, min(s_q*h_q, 128)/32)
+ * pages; the total cost C is cut into num_parts quotas of q = ceil(C/num_parts)
+ * units (a request's first c units are its overhead, then one unit per page).
+ * Deterministic.
+ *   seqlens_d int32 [batch]; block_size must be 64; h_kv must be 1.
+ */
+int mla_decode_metadata(const int32_t* seqlens_d, int batch, int s_q, int h_q,
+                        int h_kv, int block_size, int num_parts,
+                        int32_t* tile_meta_d, int32_t* split_offsets_d,
+                        void* stream);
+
+/*
+ * mla_decode_splitkv — enqueue the main decode kernel only.
+ * For every part and row tile: gathers the part's pages through the block
+ * table into LDS, computes scores (bf16 MFMA, fp32 accumulate), the online
+ * softmax in fp32, and probabilities times values (bf16 MFMA).  A request
+ * covered by one part is written to out_d / lse_d directly; pieces of split
+ * requests are written as fp32 partials into the workspace, to be merged by
+ * mla_decode_combine.
+ *   q_d           bf16 [batch, s_q, h_q, 576]
+ *   kcache_d      bf16 [num_blocks, 64, h_kv=1, 576]
+ *   block_table_d int32 [batch, bt_stride]
+ *   seqlens_d     int32 [batch]  (tokens in the cache, incl. the s_q new ones)
+ *   scale         softmax scale multiplying q.k (finite)
+ *   causal        0/1: with causal, query token t sees L - s_q + 1 + t keys
+ *   tile_meta_d, split_offsets_d, num_parts: output of mla_decode_metadata
+ *                 for the same seqlens/s_q/h_q/num_parts
+ *   workspace_d   >= mla_decode_workspace_bytes(batch, s_q, h_q, num_parts)
+ *   out_d         bf16 [batch, s_q, h_q, 512]
+ *   lse_d         fp32 [batch, s_q, h_q]
+ */
+int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                       const int32_t* block_table_d, int bt_stride,
+                       const int32_t* seqlens_d, int batch, int s_q, int h_q,
+                       int h_kv, float scale, int causal,
+                       const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                       int num_parts, void* workspace_d, size_t workspace_bytes,
+                       void* out_d, float* lse_d, void* stream);
+
+/*
+ * mla_decode_combine — enqueue the log-sum-exp merge of split partials.
+ * For every request with split_offsets[b+1] > split_offsets[b]:
+ *   LSE = ln sum_i exp(LSE_i),  O = sum_i exp(LSE_i - LSE) * O_i  (exact merge),
+ * written to out_d (bf16) / lse_d.  Requests with seqlens[b] <= 0 get O = 0,
+ * LSE = -inf.  Other rows are left untouched.  Arguments as in
+ * mla_decode_splitkv.
+ */
+int mla_decode_combine(const int32_t* seqlens_d, int batch, int s_q, int h_q,
+                       const int32_t* split_offsets_d, int num_parts,
+                       const void* workspace_d, size_t workspace_bytes,
+                       void* out_d, float* lse_d, void* stream);
+
+/*
+ * mla_decode_fwd — mla_decode_splitkv followed by mla_decode_combine on the
+ * same stream: the whole decode attention for one batch.
+ */
+int mla_decode_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                   const int32_t* block_table_d, int bt_stride,
+                   const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                   float scale, int causal,
+                   const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                   int num_parts, void* workspace_d, size_t workspace_bytes,
+                   void* out_d, float* lse_d, void* stream);
+
+/* Static text for a status code. */
+const char* mla_status_string(int status);
+
+/* Text of the last HIP error seen by this thread in the library ("" if none). */
+const char* mla_last_hip_error(void);
+
+/* Number of compute units of `device` (a HIP call). */
+int mla_device_num_cus(int device, int* num_cus_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

@@ -1,0 +1,9 @@
+"""MI355X (gfx950) paged-KV MLA decode attention.
+
+The computation runs entirely in the HIP library libmla_decode.so (C ABI in
+include/mla_decode.h); this package only marshals torch tensors into it.
+"""
+from .binding import (  # noqa: F401
+    MLAError, combine, device_num_cus, fwd, lib, metadata, num_parts, splitkv,
+    status_string, workspace_bytes,
+)

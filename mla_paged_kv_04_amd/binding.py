@@ -1,0 +1,224 @@
+"""ctypes binding of libmla_decode.so (include/mla_decode.h).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels.
+torch supplies device memory (outputs, metadata, workspace) and the current
+HIP stream.  If the library is missing this module raises; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmla_decode.so")
+
+MLA_OK = 0
+BLOCK_SIZE = 64
+D_K = 576
+D_V = 512
+TILE_META_INTS = 8
+
+_c_int = ctypes.c_int
+_c_ptr = ctypes.c_void_p
+_c_i64 = ctypes.c_int64
+_c_size = ctypes.c_size_t
+_c_float = ctypes.c_float
+
+_SIGNATURES = {
+    "mla_decode_num_parts": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
+                                      ctypes.POINTER(_c_int)]),
+    "mla_decode_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int, _c_int,
+                                            ctypes.POINTER(_c_size)]),
+    "mla_decode_metadata": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_ptr, _c_ptr, _c_ptr]),
+    "mla_decode_splitkv": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr,
+                                    _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                    _c_ptr, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr,
+                                    _c_ptr]),
+    "mla_decode_combine": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_ptr, _c_int, _c_ptr,
+                                    _c_size, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int,
+                                _c_int, _c_int, _c_int, _c_float, _c_int, _c_ptr, _c_ptr,
+                                _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_status_string": (ctypes.c_char_p, [_c_int]),
+    "mla_last_hip_error": (ctypes.c_char_p, []),
+    "mla_device_num_cus": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
+}
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        text = lib().mla_status_string(status).decode()
+        hip = lib().mla_last_hip_error().decode() if status == -4 else ""
+        super().__init__(f"{where}: {text}" + (f" ({hip})" if hip else ""))
+        self.status = status
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mla_paged_kv_04_amd.build_lib` (there is no fallback path)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != MLA_OK:
+        raise MLAError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def device_num_cus(device=None) -> int:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    out = _c_int(0)
+    _check(lib().mla_device_num_cus(dev.index or 0, ctypes.byref(out)), "mla_device_num_cus")
+    return out.value
+
+
+def num_parts(batch: int, s_q: int, h_q: int, h_kv: int = 1, num_cus: int = 256) -> int:
+    out = _c_int(0)
+    _check(lib().mla_decode_num_parts(batch, s_q, h_q, h_kv, num_cus, ctypes.byref(out)),
+           "mla_decode_num_parts")
+    return out.value
+
+
+def workspace_bytes(batch: int, s_q: int, h_q: int, parts: int) -> int:
+    out = _c_size(0)
+    _check(lib().mla_decode_workspace_bytes(batch, s_q, h_q, parts, ctypes.byref(out)),
+           "mla_decode_workspace_bytes")
+    return out.value
+
+
+@dataclass
+class Metadata:
+    tile_meta: torch.Tensor       # int32 [num_parts, 8]
+    split_offsets: torch.Tensor   # int32 [batch + 1]
+    num_parts: int
+    s_q: int
+    h_q: int
+
+
+def _require(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def metadata(seqlens: torch.Tensor, s_q: int, h_q: int, h_kv: int = 1,
+             parts: int | None = None) -> Metadata:
+    """Enqueue the split-KV scheduler for these lengths (no host sync)."""
+    _require(seqlens, torch.int32, "seqlens", 1)
+    batch = seqlens.shape[0]
+    if parts is None:
+        parts = num_parts(batch, s_q, h_q, h_kv, device_num_cus(seqlens.device))
+    tm = torch.empty((parts, TILE_META_INTS), dtype=torch.int32, device=seqlens.device)
+    so = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
+    _check(lib().mla_decode_metadata(_ptr(seqlens), batch, s_q, h_q, h_kv, BLOCK_SIZE, parts,
+                                     _ptr(tm), _ptr(so), _stream(seqlens.device)),
+           "mla_decode_metadata")
+    return Metadata(tm, so, parts, s_q, h_q)
+
+
+def _alloc_workspace(batch, s_q, h_q, parts, device, workspace):
+    need = workspace_bytes(batch, s_q, h_q, parts)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def _decode_args(q, kcache, block_table, seqlens):
+    _require(q, torch.bfloat16, "q", 4)
+    _require(kcache, torch.bfloat16, "kcache", 4)
+    _require(block_table, torch.int32, "block_table", 2)
+    _require(seqlens, torch.int32, "seqlens", 1)
+    batch, s_q, h_q, dk = q.shape
+    if dk != D_K or kcache.shape[1] != BLOCK_SIZE or kcache.shape[3] != D_K:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kcache {tuple(kcache.shape)}")
+    h_kv = kcache.shape[2]
+    return batch, s_q, h_q, h_kv
+
+
+def _outputs(q, out, lse):
+    batch, s_q, h_q, _ = q.shape
+    if out is None:
+        out = torch.empty((batch, s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device=q.device)
+    _require(out, torch.bfloat16, "out", 4)
+    _require(lse, torch.float32, "lse", 3)
+    return out, lse
+
+
+def splitkv(q, kcache, block_table, seqlens, scale: float, causal: bool, meta: Metadata,
+            workspace: torch.Tensor, out=None, lse=None):
+    """Enqueue only the split-KV decode kernel (partials left in workspace)."""
+    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens)
+    out, lse = _outputs(q, out, lse)
+    _check(lib().mla_decode_splitkv(
+        _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
+        _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)),
+        "mla_decode_splitkv")
+    return out, lse
+
+
+def combine(seqlens, s_q: int, h_q: int, meta: Metadata, workspace: torch.Tensor, out, lse):
+    """Enqueue only the log-sum-exp merge of the split partials."""
+    batch = seqlens.shape[0]
+    _check(lib().mla_decode_combine(
+        _ptr(seqlens), batch, s_q, h_q, _ptr(meta.split_offsets), meta.num_parts,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _stream(seqlens.device)), "mla_decode_combine")
+    return out, lse
+
+
+def fwd(q, kcache, block_table, seqlens, scale: float, causal: bool | None = None,
+        meta: Metadata | None = None, parts: int | None = None, workspace=None,
+        out=None, lse=None):
+    """Paged MLA decode: returns (O bf16 [B, s_q, h_q, 512], LSE fp32 [B, s_q, h_q])."""
+    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens)
+    if causal is None:
+        causal = s_q > 1
+    if meta is None:
+        meta = metadata(seqlens, s_q, h_q, h_kv, parts)
+    workspace = _alloc_workspace(batch, s_q, h_q, meta.num_parts, q.device, workspace)
+    out, lse = _outputs(q, out, lse)
+    _check(lib().mla_decode_fwd(
+        _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
+        _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)),
+        "mla_decode_fwd")
+    return out, lse

@@ -1,0 +1,216 @@
+// Host side of the C ABI declared in include/mla_decode.h: argument
+// validation, workspace sizing and kernel launches.  No allocation, no host
+// synchronisation, no global mutable state except a thread-local error text.
+#include "../../include/mla_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mla_kernels.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int hip_fail(hipError_t e, const char* where) {
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s: %s", where, hipGetErrorString(e));
+  return MLA_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_h_q(int h_q) { return h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128; }
+
+int check_shape(int batch, int s_q, int h_q, int h_kv) {
+  if (batch < 1 || s_q < 1 || s_q > 2 || h_kv != 1 || h_q < 1) return MLA_ERR_INVALID_ARG;
+  if (!supported_h_q(h_q)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+constexpr int kMaxParts = 1 << 16;
+
+int row_tiles(int s_q, int h_q) {
+  const int M = s_q * h_q;
+  const int t = mla::tile_rows_for(M);
+  return (M + t - 1) / t;
+}
+
+size_t workspace_need(int s_q, int h_q, int num_parts) {
+  const size_t slots = num_parts > 1 ? 2 * (size_t)(num_parts - 1) : 0;
+  const size_t M = (size_t)s_q * h_q;
+  size_t bytes = slots * M * (mla::kDV + 1) * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+// Partial O lives first, partial LSE after it.
+void split_workspace(void* ws, int s_q, int h_q, int num_parts, float** po, float** plse) {
+  const size_t slots = num_parts > 1 ? 2 * (size_t)(num_parts - 1) : 0;
+  const size_t M = (size_t)s_q * h_q;
+  *po = static_cast<float*>(ws);
+  *plse = ws ? static_cast<float*>(ws) + slots * M * mla::kDV : nullptr;
+}
+
+int check_common(const void* seqlens, const void* split_offsets, int batch, int s_q, int h_q,
+                 int h_kv, int num_parts, const void* workspace, size_t workspace_bytes,
+                 const void* out, const float* lse) {
+  int st = check_shape(batch, s_q, h_q, h_kv);
+  if (st != MLA_OK) return st;
+  if (num_parts < 1 || num_parts > kMaxParts) return MLA_ERR_INVALID_ARG;
+  if (!seqlens || !split_offsets || !out || !lse) return MLA_ERR_INVALID_ARG;
+  if (!aligned(seqlens, 4) || !aligned(split_offsets, 4) || !aligned(lse, 4) ||
+      !aligned(out, 16))
+    return MLA_ERR_INVALID_ARG;
+  const size_t need = workspace_need(s_q, h_q, num_parts);
+  if (need > 0) {
+    if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+    if (!workspace || !aligned(workspace, 256)) return MLA_ERR_INVALID_ARG;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int num_cus,
+                         int* num_parts_out) {
+  if (!num_parts_out || num_cus < 1) return MLA_ERR_INVALID_ARG;
+  int st = check_shape(batch, s_q, h_q, h_kv);
+  if (st != MLA_OK) return st;
+  int p = num_cus / row_tiles(s_q, h_q);
+  if (p < 1) p = 1;
+  if (p > kMaxParts) p = kMaxParts;
+  *num_parts_out = p;
+  return MLA_OK;
+}
+
+int mla_decode_workspace_bytes(int batch, int s_q, int h_q, int num_parts, size_t* bytes_out) {
+  if (!bytes_out) return MLA_ERR_INVALID_ARG;
+  int st = check_shape(batch, s_q, h_q, 1);
+  if (st != MLA_OK) return st;
+  if (num_parts < 1 || num_parts > kMaxParts) return MLA_ERR_INVALID_ARG;
+  *bytes_out = workspace_need(s_q, h_q, num_parts);
+  return MLA_OK;
+}
+
+int mla_decode_metadata(const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                        int block_size, int num_parts, int32_t* tile_meta_d,
+                        int32_t* split_offsets_d, void* stream) {
+  int st = check_shape(batch, s_q, h_q, h_kv);
+  if (st != MLA_OK) return st;
+  if (block_size != MLA_BLOCK_SIZE) return MLA_ERR_INVALID_ARG;
+  if (num_parts < 1 || num_parts > kMaxParts) return MLA_ERR_INVALID_ARG;
+  if (!seqlens_d || !tile_meta_d || !split_offsets_d) return MLA_ERR_INVALID_ARG;
+  if (!aligned(seqlens_d, 4) || !aligned(tile_meta_d, 4) || !aligned(split_offsets_d, 4))
+    return MLA_ERR_INVALID_ARG;
+  const int c = mla::fixed_cost_pages(mla::rows_per_tile(s_q, h_q));
+  hipError_t e = mla::launch_metadata(seqlens_d, batch, c, num_parts, tile_meta_d,
+                                      split_offsets_d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_metadata launch");
+  return MLA_OK;
+}
+
+int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                       const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                       int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                       const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                       int num_parts, void* workspace_d, size_t workspace_bytes, void* out_d,
+                       float* lse_d, void* stream) {
+  int st = check_common(seqlens_d, split_offsets_d, batch, s_q, h_q, h_kv, num_parts,
+                        workspace_d, workspace_bytes, out_d, lse_d);
+  if (st != MLA_OK) return st;
+  if (!q_d || !kcache_d || !block_table_d || !tile_meta_d) return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_d, 16) || !aligned(kcache_d, 16) || !aligned(block_table_d, 4) ||
+      !aligned(tile_meta_d, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (num_blocks < 1 || bt_stride < 1 || !isfinite(scale) || (causal != 0 && causal != 1))
+    return MLA_ERR_INVALID_ARG;
+  mla::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q_d);
+  a.kcache = static_cast<const uint16_t*>(kcache_d);
+  a.num_blocks = num_blocks;
+  a.block_table = block_table_d;
+  a.seqlens = seqlens_d;
+  a.tile_meta = tile_meta_d;
+  a.split_offsets = split_offsets_d;
+  split_workspace(workspace_d, s_q, h_q, num_parts, &a.part_o, &a.part_lse);
+  a.out = static_cast<uint16_t*>(out_d);
+  a.lse = lse_d;
+  a.bt_stride = bt_stride;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.h_q = h_q;
+  a.M = s_q * h_q;
+  a.causal = causal;
+  a.num_parts = num_parts;
+  a.row_tiles = row_tiles(s_q, h_q);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_splitkv launch");
+  return MLA_OK;
+}
+
+int mla_decode_combine(const int32_t* seqlens_d, int batch, int s_q, int h_q,
+                       const int32_t* split_offsets_d, int num_parts, const void* workspace_d,
+                       size_t workspace_bytes, void* out_d, float* lse_d, void* stream) {
+  int st = check_common(seqlens_d, split_offsets_d, batch, s_q, h_q, 1, num_parts, workspace_d,
+                        workspace_bytes, out_d, lse_d);
+  if (st != MLA_OK) return st;
+  mla::CombineArgs a;
+  float *po, *plse;
+  split_workspace(const_cast<void*>(workspace_d), s_q, h_q, num_parts, &po, &plse);
+  a.seqlens = seqlens_d;
+  a.split_offsets = split_offsets_d;
+  a.part_o = po;
+  a.part_lse = plse;
+  a.out = static_cast<uint16_t*>(out_d);
+  a.lse = lse_d;
+  a.batch = batch;
+  a.M = s_q * h_q;
+  hipError_t e = mla::launch_combine(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_combine launch");
+  return MLA_OK;
+}
+
+int mla_decode_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                   const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                   int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                   const int32_t* tile_meta_d, const int32_t* split_offsets_d, int num_parts,
+                   void* workspace_d, size_t workspace_bytes, void* out_d, float* lse_d,
+                   void* stream) {
+  int st = mla_decode_splitkv(q_d, kcache_d, num_blocks, block_table_d, bt_stride, seqlens_d,
+                              batch, s_q, h_q, h_kv, scale, causal, tile_meta_d,
+                              split_offsets_d, num_parts, workspace_d, workspace_bytes, out_d,
+                              lse_d, stream);
+  if (st != MLA_OK) return st;
+  return mla_decode_combine(seqlens_d, batch, s_q, h_q, split_offsets_d, num_parts,
+                            workspace_d, workspace_bytes, out_d, lse_d, stream);
+}
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: unsupported shape (h_q must be 16, 32, 64 or 128)";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_last_hip_error(void) { return g_last_hip_error; }
+
+int mla_device_num_cus(int device, int* num_cus_out) {
+  if (!num_cus_out || device < 0) return MLA_ERR_INVALID_ARG;
+  int v = 0;
+  hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  *num_cus_out = v;
+  return MLA_OK;
+}
+
+}  // extern "C"

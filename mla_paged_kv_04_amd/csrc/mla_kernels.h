@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI host layer (mla_api.cpp) and the
+// gfx950 kernels (mla_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kBlock = 64;                 // tokens per KV page
+constexpr int kDK = 576;                   // key width (512 latent + 64 rope)
+constexpr int kDV = 512;                   // value width (first 512 key dims)
+constexpr int kRowBytes = kDK * 2;         // 1152 bytes per bf16 cache row
+constexpr int kPageBytes = kBlock * kRowBytes;  // 73728 bytes per page
+constexpr int kMaxRowsPerTile = 128;       // query rows one workgroup carries
+constexpr int kMetaInts = 8;
+
+// Fixed per-request overhead of the balancing rule, in page units.
+inline int fixed_cost_pages(int rows_per_tile) {
+  int c = rows_per_tile / 32;
+  return c < 1 ? 1 : c;
+}
+
+inline int rows_per_tile(int s_q, int h_q) {
+  int m = s_q * h_q;
+  return m < kMaxRowsPerTile ? m : kMaxRowsPerTile;
+}
+
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [B, s_q, h_q, 576]
+  const uint16_t* kcache;     // bf16 [num_blocks, 64, 1, 576]
+  long long num_blocks;
+  const int32_t* block_table; // [B, bt_stride]
+  const int32_t* seqlens;     // [B]
+  const int32_t* tile_meta;   // [P, 8]
+  const int32_t* split_offsets;  // [B+1]
+  float* part_o;              // [slots, M, 512]
+  float* part_lse;            // [slots, M]   (log2 domain)
+  uint16_t* out;              // bf16 [B, s_q, h_q, 512]
+  float* lse;                 // [B, s_q, h_q] (natural log)
+  int bt_stride;
+  int batch;
+  int s_q;
+  int h_q;
+  int M;                      // s_q * h_q
+  int causal;
+  int num_parts;
+  int row_tiles;
+  float scale_log2;           // scale * log2(e)
+};
+
+struct CombineArgs {
+  const int32_t* seqlens;
+  const int32_t* split_offsets;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  float* lse;
+  int batch;
+  int M;
+};
+
+// Launchers (return hipGetLastError() of the launch).
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int c_fix, int num_parts,
+                           int32_t* tile_meta, int32_t* split_offsets, hipStream_t stream);
+hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// Row-tile geometry chosen for M query rows (rows per workgroup tile).
+int tile_rows_for(int M);
+
+}  // namespace mla

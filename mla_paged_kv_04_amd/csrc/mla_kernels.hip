@@ -1,0 +1,634 @@
+// gfx950 (MI355X) kernels of paged-KV MLA decode attention.
+//
+// Sources for what is computed: page "深度剖析DeepSeek Infra开源全貌"
+// (jingzhunhuoke.net/55333.html), section DAY1 FlashMLA:
+//   * MLA — every query head of a request attends over one shared latent KV
+//     head (terminology paragraph on MLA);
+//   * the KV cache is paged in 64-token blocks (feature ②);
+//   * the kernel keeps a page on chip while it is used (feature ③, shared
+//     memory; here LDS) and computes two products per page, scores and then
+//     probabilities times values (feature ④, "Gemm1"/"Gemm2");
+//   * variable lengths are balanced dynamically with double buffering
+//     (feature ⑤) — here a split-KV partition plus a log-sum-exp merge.
+//
+// gfx950 design (not the page's Hopper design):
+//   * one 256-thread workgroup (4 wave64) per CU; a page (64 x 576 bf16 =
+//     72 KB) is streamed HBM -> LDS with 16-byte direct-to-LDS buffer loads
+//     (no VGPR staging), two pages double-buffered = 144 KB of the 160 KB LDS;
+//   * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_16x16x32_bf16
+//     with the page rows as the A operand (ds_read_b128) and Q held in VGPRs as
+//     the B operand.  The MFMA output then holds, per lane, one query row and
+//     four consecutive keys — so the online softmax needs only 2 cross-lane
+//     steps per row, and the bf16 probabilities are already in the B-operand
+//     layout of the second product;
+//   * O^T += V^T . P^T on the same MFMA: V is the first 512 columns of the
+//     same LDS page, read with ds_read_b64_tr_b16 (hardware 4x16 transpose),
+//     so the key axis becomes the reduction axis without a second copy;
+//   * LDS rows are XOR-swizzled in 16-byte units (see lds_swizzle) so the
+//     row-wise A reads and the transposed V reads are bank-conflict free;
+//   * the page's tail rows beyond the sequence length are zero-filled by the
+//     buffer unit's range check (num_records), never read from memory.
+#include "mla_kernels.h"
+
+#include <math.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;
+constexpr int kChunksPerRow = kRowBytes / 16;   // 72 16-byte units per row
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit format
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;           // lazy-rescale threshold (log2)
+
+// 16-byte unit swizzle of LDS row r: unit c is stored at c ^ lds_swizzle(r).
+// A bijection on r mod 8 (conflict-free 8-row column reads) whose upper two
+// bits also differ over any 4 consecutive rows (conflict-free transposed
+// reads of 4 rows x 32 bytes).  XOR stays inside an aligned group of 8 units,
+// and 72 units per row is a multiple of 8.
+__device__ __forceinline__ int lds_swizzle(int r) {
+  return ((r & 3) << 1) | ((r >> 2) & 1);
+}
+
+__device__ __forceinline__ float wave_max_4lanes(float x) {
+  // max over lanes {i, i^16, i^32, i^48}: the four lanes holding one query row
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_4lanes(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ int n_pages(int L) {
+  return L > 0 ? (L + kBlock - 1) / kBlock : 0;
+}
+
+// --------------------------------------------------------------------------
+// Split-KV scheduler: one workgroup.  Implements the integer balancing rule
+// documented with mla_decode_metadata (cost_b = pages + c, equal quotas).
+// Every tile_meta word is written by exactly one thread.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void mla_metadata_kernel(
+    const int32_t* __restrict__ seqlens, int batch, int c_fix, int num_parts,
+    int32_t* __restrict__ tile_meta, int32_t* __restrict__ split_offsets) {
+  __shared__ long long s_red[kThreads];
+  __shared__ long long s_scan_cost[kThreads];
+  __shared__ int s_scan_slots[kThreads];
+  const int tid = threadIdx.x;
+
+  // total cost C
+  long long local = 0;
+  for (int b = tid; b < batch; b += kThreads) {
+    int n = n_pages(seqlens[b]);
+    local += n > 0 ? (long long)(n + c_fix) : 0;
+  }
+  s_red[tid] = local;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) s_red[tid] += s_red[tid + s];
+    __syncthreads();
+  }
+  const long long C = s_red[0];
+  const long long P = num_parts;
+  const long long q = C > 0 ? (C + P - 1) / P : 1;
+
+  long long carry_cost = 0;
+  int carry_slots = 0;
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    int n = 0;
+    if (b < batch) n = n_pages(seqlens[b]);
+    const long long cost = n > 0 ? (long long)(n + c_fix) : 0;
+    // inclusive scans (Hillis-Steele) of cost and slots within the chunk
+    s_scan_cost[tid] = cost;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      long long v = tid >= off ? s_scan_cost[tid - off] : 0;
+      __syncthreads();
+      s_scan_cost[tid] += v;
+      __syncthreads();
+    }
+    const long long start = carry_cost + s_scan_cost[tid] - cost;
+    int nsplit = 1;
+    if (n > 0) {
+      const long long lo = start + c_fix;
+      const long long hi = lo + n;
+      nsplit = 1 + (int)((hi - 1) / q - lo / q);
+    }
+    const int slots = nsplit >= 2 ? nsplit : 0;
+    s_scan_slots[tid] = slots;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      int v = tid >= off ? s_scan_slots[tid - off] : 0;
+      __syncthreads();
+      s_scan_slots[tid] += v;
+      __syncthreads();
+    }
+    if (b < batch) {
+      split_offsets[b] = carry_slots + s_scan_slots[tid] - slots;
+      if (cost > 0) {
+        // boundaries p*q that fall inside [start, start + cost)
+        const long long p_lo = (start + q - 1) / q;
+        const long long p_hi = (start + cost + q - 1) / q;
+        const long long p0 = (start + c_fix) / q + 1;
+        for (long long p = p_lo; p < p_hi && p < P; ++p) {
+          long long k = p * q - start - c_fix;
+          k = k < 0 ? 0 : (k > n ? n : k);
+          const int first = (k > 0 && k < n) ? (int)(p - p0 + 1) : 0;
+          int32_t* tm = tile_meta + p * kMetaInts;
+          tm[0] = b;
+          tm[1] = (int)k;
+          tm[4] = first;
+          if (p > 0) {
+            tile_meta[(p - 1) * kMetaInts + 2] = b;
+            tile_meta[(p - 1) * kMetaInts + 3] = (int)k;
+          }
+        }
+      }
+    }
+    carry_cost += s_scan_cost[kThreads - 1];
+    carry_slots += s_scan_slots[kThreads - 1];
+    __syncthreads();
+  }
+  if (tid == 0) split_offsets[batch] = carry_slots;
+  // parts whose boundary lies at or beyond C begin (and the last part ends) at (B, 0)
+  const long long p_tail = (C + q - 1) / q;
+  for (long long p = tid; p < P; p += kThreads) {
+    int32_t* tm = tile_meta + p * kMetaInts;
+    tm[5] = 0;
+    tm[6] = 0;
+    tm[7] = 0;
+    if (p >= p_tail) {
+      tm[0] = batch;
+      tm[1] = 0;
+      tm[4] = 0;
+      if (p > 0) {
+        tile_meta[(p - 1) * kMetaInts + 2] = batch;
+        tile_meta[(p - 1) * kMetaInts + 3] = 0;
+      }
+    }
+    if (p == P - 1) {
+      tm[2] = batch;
+      tm[3] = 0;
+    }
+  }
+}
+
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int c_fix, int num_parts,
+                           int32_t* tile_meta, int32_t* split_offsets, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_metadata_kernel, dim3(1), dim3(kThreads), 0, stream, seqlens, batch,
+                     c_fix, num_parts, tile_meta, split_offsets);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Split-KV decode kernel.
+//   RT: 16-row query tiles per wave (1 or 2);  KG: waves sharing one row
+//   group, each taking 64/KG keys of every page (1 or 2).
+//   Rows per workgroup tile = (4/KG) * RT * 16.
+// --------------------------------------------------------------------------
+struct Cursor {
+  int b;   // request
+  int k;   // page within the request
+  bool valid;
+};
+
+// Values the hardware needs in SGPRs (buffer resources, M0) are read from
+// global memory with vector loads (the kernel also stores, so loads are not
+// provably invariant); readfirstlane tells the compiler they are wave-uniform
+// so no waterfall loop is emitted.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ void issue_page_load(char* lds_tile, const DecodeArgs& a, int b,
+                                                int k, const int (&off)[9], int w) {
+  const int L = uni(a.seqlens[b]);
+  int rows = L - k * kBlock;
+  rows = rows > kBlock ? kBlock : rows;
+  int page = -1;
+  if (k < a.bt_stride) page = uni(a.block_table[(long long)b * a.bt_stride + k]);
+  const bool ok = page >= 0 && (long long)page < a.num_blocks && rows > 0;
+  const char* base = reinterpret_cast<const char*>(a.kcache) +
+                     (ok ? (long long)page * kPageBytes : 0);
+  const int nrec = ok ? rows * kRowBytes : 0;
+  // The buffer unit's range check ignores the SGPR offset, so rows 32..63 get a
+  // resource of their own (based 32 rows further on) instead of an soffset:
+  // each half then zero-fills exactly the rows at or beyond the sequence end.
+  constexpr int kHalf = 32 * kRowBytes;
+  const int nrec_lo = uni(nrec < kHalf ? nrec : kHalf);
+  const int nrec_hi = uni(nrec > kHalf ? nrec - kHalf : 0);
+  __amdgpu_buffer_rsrc_t r_lo =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec_lo, kRsrcWord3);
+  __amdgpu_buffer_rsrc_t r_hi =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + kHalf, 0, nrec_hi, kRsrcWord3);
+#pragma unroll
+  for (int j = 0; j < 18; ++j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 9 ? r_lo : r_hi,
+                                             (MLA_LDS void*)(lds_tile + j * 4096 + w * 1024), 16,
+                                             off[j % 9], 0, 0, 0);
+  }
+}
+
+// First valid (request, page) position at or after (b, k) inside [.., (b1, k1)).
+__device__ __forceinline__ Cursor seek(const DecodeArgs& a, int b, int k, int b1, int k1) {
+  while (b < a.batch && (b < b1 || (b == b1 && k < k1))) {
+    const int end = (b == b1) ? k1 : n_pages(uni(a.seqlens[b]));
+    if (k < end) return Cursor{b, k, true};
+    ++b;
+    k = 0;
+  }
+  return Cursor{b, k, false};
+}
+
+template <int RT, int KG>
+__global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeArgs a) {
+  constexpr int KW = 64 / KG;     // keys per wave per page
+  constexpr int KT = KW / 16;     // 16-key score tiles per wave
+  constexpr int KP = KT / 2;      // 32-key reduction steps of the value product
+  constexpr int RG = 4 / KG;      // row groups per workgroup
+  constexpr int MT = RG * RT * 16;
+  static_assert(KP >= 1, "at least 32 keys per wave");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes];
+
+  const int tid = threadIdx.x;
+  // wave index made provably uniform (the LDS destination of direct loads
+  // lives in M0 and must not be treated as divergent)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int i = lane & 15;
+  const int kg = w % KG;
+  const int rg = w / KG;
+
+  // workgroup -> (part, row tile); the two row tiles of a part share an XCD
+  // (workgroups are dealt to the 8 XCDs round-robin) so the second read of a
+  // page hits that XCD's L2.
+  int part, rtile;
+  const int x = blockIdx.x;
+  if (a.row_tiles == 2 && (a.num_parts % 8) == 0) {
+    part = (x >> 4) * 8 + (x & 7);
+    rtile = (x >> 3) & 1;
+  } else {
+    part = x / a.row_tiles;
+    rtile = x % a.row_tiles;
+  }
+  const int32_t* tm = a.tile_meta + part * kMetaInts;
+  const int b0 = uni(tm[0]), k0 = uni(tm[1]), b1 = uni(tm[2]), k1 = uni(tm[3]);
+  const int first_split = uni(tm[4]);
+
+  Cursor cur = seek(a, b0, k0, b1, k1);
+  if (!cur.valid) return;  // uniform: empty part
+
+  const int row0 = rtile * MT + rg * RT * 16;
+  const bool active = row0 < a.M;
+
+  // per-lane global byte offsets of the 9 distinct direct-load slots
+  int off[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int u = j * kThreads + tid;
+    const int r = u / kChunksPerRow;
+    const int pc = u - r * kChunksPerRow;
+    off[j] = r * kRowBytes + ((pc ^ lds_swizzle(r)) << 4);
+  }
+  // LDS read offsets (bytes, relative to the page buffer)
+  const int kgoff = kg * KW * kRowBytes;
+  const int fi = lds_swizzle(i & 7);
+  const int a_off0 = kgoff + i * kRowBytes + (((0 + g) ^ fi) << 4);
+  const int a_off1 = kgoff + i * kRowBytes + (((4 + g) ^ fi) << 4);
+  const int tr_row = 4 * g + (i >> 2);
+  const int ft = lds_swizzle(tr_row & 7);
+  const int hh = (i & 3) >> 1;
+  int t_off[4];
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4)
+    t_off[d4] = kgoff + tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
+
+  issue_page_load(smem, a, cur.b, cur.k, off, w);
+  int buf = 0;
+  Cursor nxt;
+
+  // ---------------- one iteration per piece (request slice) ----------------
+  while (true) {
+    const int b = uni(cur.b);
+    const int L = uni(a.seqlens[b]);
+    const int n = n_pages(L);
+    const int pbeg = cur.k;
+    const int pend = (b == b1) ? k1 : n;     // exclusive
+    const int lim_min = a.causal ? L - a.s_q + 1 : L;
+
+    bf16x8 qreg[RT][18];
+    f32x4 o[RT][32];
+    float m_run[RT], l_run[RT];
+    int lim[RT];
+
+    for (int k = pbeg;; ++k) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+
+      // The piece's query rows are loaded BEFORE the next page's prefetch so
+      // the compiler's vmcnt wait for Q never waits for the prefetch (vmcnt
+      // retires in issue order).
+      if (k == pbeg && active) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int row = row0 + rt * 16 + i;
+          const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+              a.q + ((long long)b * a.M + row) * kDK + 8 * g);
+#pragma unroll
+          for (int ks = 0; ks < 18; ++ks) qreg[rt][ks] = qp[ks * 4];
+          const int t = row / a.h_q;
+          lim[rt] = a.causal ? L - a.s_q + 1 + t : L;
+          m_run[rt] = -INFINITY;
+          l_run[rt] = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < 32; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+
+      // prefetch the part's next page (possibly of the next piece)
+      nxt = seek(a, b, k + 1, b1, k1);
+      if (nxt.valid) issue_page_load(smem + (buf ^ 1) * kPageBytes, a, nxt.b, nxt.k, off, w);
+
+      const char* page = smem + buf * kPageBytes;
+      if (active) {
+        // ---- scores S^T[key][row] = K . Q^T over 576 dims ----
+        // Software pipeline: operand reads for step ks+D1 are in flight while
+        // the MFMAs of step ks run; sched_barrier stops the compiler from
+        // hoisting every read of the unrolled loop (register blow-up).
+        constexpr int D1 = (RT * KT >= 8) ? 1 : 2;
+        f32x4 s[RT][KT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 ka[D1 + 1][KT];
+#pragma unroll
+        for (int ks = 0; ks < 18 + D1; ++ks) {
+          if (ks < 18) {
+            const char* ab = page + ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+              ka[ks % (D1 + 1)][kt] = *reinterpret_cast<const bf16x8*>(ab + kt * 16 * kRowBytes);
+          }
+          const int cs = ks - D1;
+          if (cs >= 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+              for (int kt = 0; kt < KT; ++kt)
+                s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    ka[cs % (D1 + 1)][kt], qreg[rt][cs], s[rt][kt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- online softmax (fp32, base 2, lazy rescale) ----
+        const int key0 = k * kBlock + kg * KW + 4 * g;
+        const bool need_mask = (k + 1) * kBlock > lim_min;
+        bf16x8 pb[RT][KP];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float xv = s[rt][kt][v] * a.scale_log2;
+              if (need_mask && key0 + kt * 16 + v >= lim[rt]) xv = -INFINITY;
+              s[rt][kt][v] = xv;
+              mx = fmaxf(mx, xv);
+            }
+          mx = wave_max_4lanes(mx);
+          const float m_new = fmaxf(m_run[rt], mx);
+          // Keep the running max unless it grew by more than kRescaleSlack:
+          // probabilities stay <= 2^kRescaleSlack and the result is exact
+          // either way (numerator and denominator share the reference max).
+          const bool grow = m_new > m_run[rt] + kRescaleSlack;
+          if (__any(grow)) {
+            const float alpha = grow ? exp2f(m_run[rt] - m_new) : 1.f;
+            if (grow) m_run[rt] = m_new;
+            l_run[rt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 32; ++dt) o[rt][dt] *= alpha;
+          }
+          const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
+          float lsum = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float p = exp2f(s[rt][kt][v] - m_use);
+              lsum += p;
+              pb[rt][kt >> 1][(kt & 1) * 4 + v] = (__bf16)p;
+            }
+          l_run[rt] += lsum;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- O^T[dim][row] += V^T . P^T over this wave's keys ----
+        constexpr int D2 = (RT * KP >= 4) ? 1 : 2;
+        bf16x8 va[D2 + 1][KP];
+#pragma unroll
+        for (int dt = 0; dt < 32 + D2; ++dt) {
+          if (dt < 32) {
+            const char* tb = page + t_off[dt & 3] + 128 * (dt >> 2);
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp) {
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (MLA_LDS bf16x4*)(tb + (kp * 32) * kRowBytes));
+              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (MLA_LDS bf16x4*)(tb + (kp * 32 + 16) * kRowBytes));
+              va[dt % (D2 + 1)][kp] =
+                  bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+          }
+          const int cd = dt - D2;
+          if (cd >= 0) {
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt)
+                o[rt][cd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    va[cd % (D2 + 1)][kp], pb[rt][kp], o[rt][cd], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      if (k + 1 >= pend) break;
+      buf ^= 1;
+    }
+
+    // ---- merge the KG key groups of each row group, then write ----
+    // With KG == 2 the partner wave's (m, l, O) go through the LDS buffer of
+    // the last page; the merge is folded into the store loop so the
+    // accumulators are only read here.
+    float a_self[RT], a_other[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      a_self[rt] = 1.f;
+      a_other[rt] = 0.f;
+    }
+    const f32x4* mo = nullptr;
+    if constexpr (KG == 2) {
+      __syncthreads();  // every wave is done reading the last page buffer
+      char* mb = smem + buf * kPageBytes;
+      f32x4* mw = reinterpret_cast<f32x4*>(mb) + (rg * RT * 32) * 64;
+      float* mm = reinterpret_cast<float*>(mb + RG * RT * 32 * 1024) + rg * RT * 128;
+      if (active && kg == 1) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+          for (int dt = 0; dt < 32; ++dt) mw[(rt * 32 + dt) * 64 + lane] = o[rt][dt];
+          mm[rt * 128 + lane] = m_run[rt];
+          mm[rt * 128 + 64 + lane] = l_run[rt];
+        }
+      }
+      __syncthreads();
+      if (active && kg == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float m1 = mm[rt * 128 + lane];
+          const float l1 = mm[rt * 128 + 64 + lane];
+          const float m0 = m_run[rt];
+          const float mn = fmaxf(m0, m1);
+          a_self[rt] = m0 == -INFINITY ? 0.f : exp2f(m0 - mn);
+          a_other[rt] = m1 == -INFINITY ? 0.f : exp2f(m1 - mn);
+          l_run[rt] = l_run[rt] * a_self[rt] + l1 * a_other[rt];
+          m_run[rt] = mn;
+        }
+      }
+      mo = mw;
+    }
+
+    // ---- epilogue: normalise; write O/LSE, or the split partials ----
+    if (active && kg == 0) {
+      const bool whole = pbeg == 0 && pend == n;
+      const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
+      const long long slot = whole ? 0 : (long long)uni(a.split_offsets[b]) + sidx;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float lt = wave_sum_4lanes(l_run[rt]);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float lse2 = lt > 0.f ? m_run[rt] + log2f(lt) : -INFINITY;
+        const float cs = a_self[rt] * inv;
+        const float co = a_other[rt] * inv;
+        const int row = row0 + rt * 16 + i;
+        if (whole) {
+          uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + 4 * g;
+#pragma unroll
+          for (int d8 = 0; d8 < 32; d8 += 8) {
+#pragma unroll
+            for (int dt = d8; dt < d8 + 8; ++dt) {
+              f32x4 v = o[rt][dt] * cs;
+              if constexpr (KG == 2) v += mo[(rt * 32 + dt) * 64 + lane] * co;
+              const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+              *reinterpret_cast<bf16x4*>(op + dt * 16) = bv;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (g == 0) a.lse[(long long)b * a.M + row] = lse2 * kLn2;
+        } else {
+          float* op = a.part_o + (slot * a.M + row) * kDV + 4 * g;
+#pragma unroll
+          for (int d8 = 0; d8 < 32; d8 += 8) {
+#pragma unroll
+            for (int dt = d8; dt < d8 + 8; ++dt) {
+              f32x4 v = o[rt][dt] * cs;
+              if constexpr (KG == 2) v += mo[(rt * 32 + dt) * 64 + lane] * co;
+              *reinterpret_cast<f32x4*>(op + dt * 16) = v;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (g == 0) a.part_lse[slot * a.M + row] = lse2;
+        }
+      }
+    }
+
+    if (!nxt.valid) break;
+    cur = nxt;
+    buf ^= 1;
+  }
+}
+
+int tile_rows_for(int M) {
+  if (M <= 32) return 32;    // RT=1, KG=2
+  return 64;                 // RT=1, KG=1 (M = 128, 256 use 2 or 4 row tiles)
+}
+
+hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_parts * a.row_tiles), block(kThreads);
+  if (a.M <= 32)
+    hipLaunchKernelGGL((mla_splitkv_kernel<1, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((mla_splitkv_kernel<1, 1>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// LSE combine: exact merge of the split partials of each split request.
+// One workgroup per (request, 16 query rows); 16 threads per row, 32 dims
+// each (8 x float4, interleaved so a row's 16 threads read 256 contiguous
+// bytes per step).
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void mla_combine_kernel(const CombineArgs a) {
+  const int b = blockIdx.x;
+  const int r = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  if (r >= a.M) return;
+  const int s0 = a.split_offsets[b];
+  const int ns = a.split_offsets[b + 1] - s0;
+  uint16_t* op = a.out + ((long long)b * a.M + r) * kDV;
+  if (ns == 0) {
+    if (a.seqlens[b] <= 0) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<uint2*>(op + (j + 16 * c) * 4) = make_uint2(0u, 0u);
+      if (j == 0) a.lse[(long long)b * a.M + r] = -INFINITY;
+    }
+    return;
+  }
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_lse[(long long)(s0 + s) * a.M + r]);
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < ns; ++s) {
+      const long long rowi = (long long)(s0 + s) * a.M + r;
+      const float ls = a.part_lse[rowi];
+      const float wgt = ls == -INFINITY ? 0.f : exp2f(ls - mx);
+      tot += wgt;
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + rowi * kDV);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] += wgt * src[j + 16 * c];
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const f32x4 v = acc[c] * inv;
+    const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(op + (j + 16 * c) * 4) = bv;
+  }
+  if (j == 0) a.lse[(long long)b * a.M + r] = tot > 0.f ? (mx + log2f(tot)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  const dim3 grid(a.batch, (a.M + 15) / 16), block(kThreads);
+  hipLaunchKernelGGL(mla_combine_kernel, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,288 @@
+"""GPU parity of the HIP path against the fp64 oracle (MI355X only).
+
+Bar (per case): max|O_gpu - O_ref| <= 1e-2 * max|O_ref| and
+|LSE_gpu - LSE_ref| <= 1e-3 on rows with a visible key; rows with no visible
+key must give exactly O = 0 and LSE = -inf.  Integer work (the split plan) is
+compared bit for bit.  Full-size workloads are compared on sampled requests
+(the oracle computes those requests one by one), in the launch configuration
+the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attend_rows, decode, gather_request_kv, lse_merge, split_plan
+from workloads import WORKLOAD_ORDER, WORKLOADS, build_inputs, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 1e-2
+TOL_LSE = 1e-3
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_kv_04_amd as m
+    m.lib()
+    return m
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run(mla, inp, parts=None, dev="cuda"):
+    g = inp.to(dev)
+    meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
+    out, lse = mla.fwd(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta=meta)
+    torch.cuda.synchronize()
+    return out, lse, meta
+
+
+def _assert_parity(out, lse, O_ref, L_ref, reqs=None, tag=""):
+    O = out.float().cpu().numpy().astype(np.float64)
+    L = lse.cpu().numpy().astype(np.float64)
+    if reqs is not None:
+        O, L, O_ref, L_ref = O[reqs], L[reqs], O_ref[reqs], L_ref[reqs]
+    assert not np.any(np.isnan(O)), f"{tag}: NaN in O"
+    fin = np.isfinite(L_ref)
+    assert np.array_equal(np.isfinite(L), fin), f"{tag}: -inf rows differ"
+    if np.any(~fin):
+        assert np.all(L[~fin] == -np.inf) and np.all(O[~fin] == 0.0), f"{tag}: empty rows"
+    tol_o = TOL_O * float(np.max(np.abs(O_ref[fin]))) if np.any(fin) else 0.0
+    err_o = float(np.max(np.abs(O - O_ref))) if O.size else 0.0
+    err_l = float(np.max(np.abs(L[fin] - L_ref[fin]))) if np.any(fin) else 0.0
+    _say(f"  {tag}: max|dO|={err_o:.3e} (tol {tol_o:.3e}) max|dLSE|={err_l:.3e}")
+    assert err_o <= tol_o, f"{tag}: O error {err_o} > {tol_o}"
+    assert err_l <= TOL_LSE, f"{tag}: LSE error {err_l}"
+
+
+@pytest.mark.parametrize("parts", [None, 1, 2, 3])
+def test_tiny_workload(mla, parts):
+    _say(f"case tiny parts={parts}")
+    inp = make_inputs("tiny")
+    out, lse, _ = _run(mla, inp, parts)
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal)
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"tiny P={parts}")
+
+
+SMALL_LENS = [1, 63, 64, 65, 127, 128, 129, 300, 1000, 2, 0, 191]
+
+
+@pytest.mark.parametrize("h_q", [16, 32, 64, 128])
+@pytest.mark.parametrize("s_q", [1, 2])
+@pytest.mark.parametrize("parts", [None, 1, 5])
+def test_small_shapes(mla, h_q, s_q, parts):
+    _say(f"case small h_q={h_q} s_q={s_q} parts={parts}")
+    inp = build_inputs(SMALL_LENS, s_q, h_q, seed=100 + h_q + s_q, extra_pool=7)
+    out, lse, _ = _run(mla, inp, parts)
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal)
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"small h{h_q} s{s_q} P={parts}")
+
+
+def test_non_causal_two_tokens(mla):
+    _say("case non-causal s_q=2")
+    inp = build_inputs([5, 70, 130], 2, 16, seed=5, extra_pool=2)
+    g = inp.to("cuda")
+    out, lse = mla.fwd(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, causal=False)
+    torch.cuda.synchronize()
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, False)
+    _assert_parity(out, lse, O_ref, L_ref, tag="non-causal")
+
+
+def _sample_requests(seqlens, k=6, seed=0):
+    sl = seqlens.tolist()
+    B = len(sl)
+    pick = {0, B - 1, int(np.argmax(sl)), int(np.argmin(sl))}
+    rng = np.random.default_rng(seed)
+    while len(pick) < min(k, B):
+        pick.add(int(rng.integers(0, B)))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("key", ["membound", "ridge", "ragged", "long"])
+def test_full_workload_sampled(mla, key):
+    """Full-size workload in the benchmark's launch configuration; the oracle
+    recomputes a sample of requests (incl. the longest and the shortest)."""
+    _say(f"case full {key}: generating inputs")
+    inp = make_inputs(key)
+    _say(f"case full {key}: decode on GPU")
+    out, lse, meta = _run(mla, inp)
+    reqs = _sample_requests(inp.seqlens, k=6, seed=WORKLOADS[key].seed)
+    _say(f"case full {key}: oracle on requests {reqs}")
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale,
+                          inp.causal, requests=reqs)
+    _assert_parity(out, lse, O_ref, L_ref, reqs=reqs, tag=f"full {key}")
+    # properties over every request: no NaN, finite LSE wherever a key is visible
+    O = out.float()
+    assert not torch.isnan(O).any().item()
+    L = lse.cpu()
+    sl = inp.seqlens.tolist()
+    for b, Lb in enumerate(sl):
+        for t in range(inp.s_q):
+            vis = Lb - inp.s_q + 1 + t if inp.causal else Lb
+            row = L[b, t]
+            if vis > 0:
+                assert torch.isfinite(row).all(), (key, b, t)
+            else:
+                assert (row == -math.inf).all(), (key, b, t)
+
+
+@pytest.mark.parametrize("key", WORKLOAD_ORDER)
+@pytest.mark.parametrize("parts", [1, 7, 64, 128, 256, 1000])
+def test_metadata_matches_model(mla, key, parts):
+    _say(f"case metadata {key} P={parts}")
+    w = WORKLOADS[key]
+    from workloads import draw_seqlens
+    sl = draw_seqlens(w.seqlen_kind, w.batch, torch.Generator().manual_seed(w.seed))
+    meta = mla.metadata(sl.cuda(), w.s_q, w.h_q, parts=parts)
+    torch.cuda.synchronize()
+    tm_ref, so_ref = split_plan(sl, w.s_q, w.h_q, parts)
+    assert np.array_equal(meta.tile_meta.cpu().numpy(), tm_ref)
+    assert np.array_equal(meta.split_offsets.cpu().numpy(), so_ref)
+
+
+def test_metadata_edge_lengths(mla):
+    for sl in ([0, 0, 0], [0, 5, 0, 64, 65], [1] * 300, [100000, 1, 0]):
+        for parts in (1, 3, 256):
+            t = torch.tensor(sl, dtype=torch.int32)
+            meta = mla.metadata(t.cuda(), 1, 16, parts=parts)
+            torch.cuda.synchronize()
+            tm_ref, so_ref = split_plan(t, 1, 16, parts)
+            assert np.array_equal(meta.tile_meta.cpu().numpy(), tm_ref), (sl, parts)
+            assert np.array_equal(meta.split_offsets.cpu().numpy(), so_ref), (sl, parts)
+
+
+@pytest.mark.parametrize("s_q,h_q", [(1, 16), (2, 128)])
+def test_combine_standalone(mla, s_q, h_q):
+    """The combine kernel alone on partials made by the oracle."""
+    _say(f"case combine s_q={s_q} h_q={h_q}")
+    lens = [300, 1, 700, 0]
+    inp = build_inputs(lens, s_q, h_q, seed=77, extra_pool=1)
+    M = s_q * h_q
+    cuts = {0: [0, 64, 128, 300], 1: [0, 1], 2: [0, 64, 320, 640, 700], 3: [0]}
+    split_offsets = [0]
+    for b in range(4):
+        n = len(cuts[b]) - 1
+        split_offsets.append(split_offsets[-1] + (n if n >= 2 else 0))
+    slots = split_offsets[-1]
+    parts = 64
+    nbytes = mla.workspace_bytes(4, s_q, h_q, parts)
+    max_slots = 2 * (parts - 1)
+    assert slots <= max_slots
+    ws = torch.zeros(nbytes // 4, dtype=torch.float32)
+    po = ws[: max_slots * M * 512].view(max_slots, M, 512)
+    pl = ws[max_slots * M * 512: max_slots * M * 513].view(max_slots, M)
+    expect_O = np.zeros((4, M, 512))
+    expect_L = np.full((4, M), -np.inf)
+    for b in range(4):
+        K = gather_request_kv(inp.kcache, inp.block_table, inp.seqlens, b)
+        qrows = inp.q[b].double().numpy().reshape(M, 576)
+        c = cuts[b]
+        parts_b = []
+        for i, (lo, hi) in enumerate(zip(c[:-1], c[1:])):
+            nvis = np.array([max(0, min(hi, lens[b] - s_q + 1 + r // h_q) - lo) if s_q > 1
+                             else hi - lo for r in range(M)])
+            Ob, Lb = attend_rows(qrows, K[lo:hi], inp.scale, nvis)
+            parts_b.append((Ob, Lb))
+            if len(c) - 1 >= 2:
+                po[split_offsets[b] + i] = torch.from_numpy(Ob).float()
+                pl[split_offsets[b] + i] = torch.from_numpy(Lb / math.log(2)).float()
+        if len(c) - 1 >= 2:
+            expect_O[b], expect_L[b] = lse_merge(parts_b)
+    so = torch.tensor(split_offsets, dtype=torch.int32).cuda()
+    meta = type("M", (), {"split_offsets": so, "num_parts": parts})()
+    out = torch.full((4, s_q, h_q, 512), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((4, s_q, h_q), 7.0, dtype=torch.float32, device="cuda")
+    mla.combine(inp.seqlens.cuda(), s_q, h_q, meta, ws.cuda(), out, lse)
+    torch.cuda.synchronize()
+    O = out.float().cpu().numpy().reshape(4, M, 512)
+    L = lse.cpu().numpy().reshape(4, M)
+    # split requests 0 and 2 are merged; request 3 (L = 0) is written empty;
+    # request 1 (one piece) is left untouched
+    for b in (0, 2):
+        assert np.max(np.abs(O[b] - expect_O[b])) <= TOL_O * np.max(np.abs(expect_O[b]))
+        assert np.max(np.abs(L[b] - expect_L[b])) <= TOL_LSE
+    assert np.all(O[3] == 0) and np.all(L[3] == -np.inf)
+    assert np.all(O[1] == 7.0) and np.all(L[1] == 7.0)
+
+
+def test_run_to_run_bitwise(mla):
+    _say("case determinism")
+    inp = build_inputs([5000, 333, 64, 7000], 2, 128, seed=3, extra_pool=5)
+    a = _run(mla, inp)
+    b = _run(mla, inp)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+
+
+def test_page_permutation_bitwise(mla):
+    _say("case page permutation")
+    inp = build_inputs([1000, 129, 64, 4000], 1, 64, seed=9, extra_pool=11)
+    a = _run(mla, inp)
+    npg = inp.kcache.shape[0]
+    perm = torch.randperm(npg, generator=torch.Generator().manual_seed(1))
+    newk = torch.empty_like(inp.kcache)
+    newk[perm] = inp.kcache
+    inp2 = type(inp)(inp.q, newk, perm[inp.block_table.long()].to(torch.int32), inp.seqlens,
+                     inp.scale, inp.causal, inp.s_q, inp.h_q)
+    b = _run(mla, inp2)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+
+
+def test_spiky_scores(mla):
+    """Sharp softmax: Q x 8 and a planted key equal to 4*q mid-sequence, so the
+    running max moves across pages."""
+    _say("case spiky")
+    inp = build_inputs([3000, 5000], 1, 16, seed=21, extra_pool=3, q_scale=8.0)
+    for b, pos in ((0, 1500), (1, 4100)):
+        page = int(inp.block_table[b, pos // 64])
+        inp.kcache[page, pos % 64, 0] = (4.0 * inp.q[b, 0, 0].float()).to(torch.bfloat16)
+    out, lse, _ = _run(mla, inp)
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, False)
+    _assert_parity(out, lse, O_ref, L_ref, tag="spiky")
+
+
+def test_growing_scores(mla):
+    """Scores rising by ~10 (log2 units) every page: the running max is
+    rescaled on every page."""
+    _say("case growing")
+    lens = [1000, 777]
+    inp = build_inputs(lens, 1, 32, seed=23, extra_pool=2, nan_tails=False)
+    q = torch.zeros_like(inp.q)
+    q[..., 512] = 1.0
+    inp.q = q
+    # per-key increment so that scale*k*log2(e) rises by 10 every 64 keys
+    beta = 10.0 / (64 * inp.scale * 1.4426950408889634)
+    for b, L in enumerate(lens):
+        for j in range(L):
+            page = int(inp.block_table[b, j // 64])
+            inp.kcache[page, j % 64, 0, 512] = float(beta * j)
+    out, lse, _ = _run(mla, inp)
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, False)
+    _assert_parity(out, lse, O_ref, L_ref, tag="growing")
+
+
+def test_zero_scale_mean(mla):
+    _say("case zero scale")
+    inp = build_inputs([700, 64, 1], 1, 16, seed=31, extra_pool=2)
+    g = inp.to("cuda")
+    out, lse = mla.fwd(g.q, g.kcache, g.block_table, g.seqlens, 0.0, False)
+    torch.cuda.synchronize()
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, 0.0, False)
+    _assert_parity(out, lse, O_ref, L_ref, tag="zero scale")
+
+
+def test_single_token_exact(mla):
+    """L = 1: O equals the stored bf16 value row exactly."""
+    inp = build_inputs([1, 1, 1], 1, 128, seed=41, extra_pool=2)
+    out, lse, _ = _run(mla, inp)
+    for b in range(3):
+        v = inp.kcache[int(inp.block_table[b, 0]), 0, 0, :512]
+        assert torch.equal(out[b, 0].cpu().view(torch.int16),
+                           v.expand(128, 512).contiguous().view(torch.int16))
