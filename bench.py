@@ -1,0 +1,218 @@
+"""Benchmark of paged MLA decode attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the split-KV
+scheduler, the split-KV decode kernel (page gather -> LDS, scores and values
+on bf16 MFMA, fp32 online softmax) and the LSE combine.  Inputs are resident
+in HBM before timing starts.  Between timed steps a separate 1 GiB buffer is
+read (outside the timed events) so that L2 and the 256 MB Infinity Cache hold
+no KV pages and no dirty lines: every step reads its KV from HBM.
+
+Prints one JSON line (rank 0).  `value` is algorithmic HBM GB/s of the whole
+step; `roofline` reports the dominant kernel (mla_decode_splitkv) measured
+with HIP events on the stream it is launched on.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload membound]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode attention TFLOPS + HBM GB/s (% of roofline), 1 MI355X"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    whole requests in order until about `budget_s` seconds have elapsed."""
+    import numpy as np
+    from oracle import decode
+    from workloads import algorithmic_counts
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    done = []
+    t0 = time.perf_counter()
+    for b in range(inp.batch):
+        decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal,
+               requests=[b])
+        done.append(b)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    sl = [int(inp.seqlens[b]) for b in done]
+    c = algorithmic_counts(sl, inp.s_q, inp.h_q)
+    return {
+        "value": round(c["bytes"] / dt / 1e9, 4),
+        "unit": "GB/s",
+        "tflops": round(c["flops"] / dt / 1e12, 6),
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {inp.batch} requests ({sum(sl)} keys) in {dt:.1f} s, "
+                  f"fp64 numpy on {_cpu_model()}, {os.cpu_count()} logical CPUs",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="membound",
+                    help="tiny | membound | ridge | ragged | long")
+    ap.add_argument("--parts", type=int, default=None, help="override split-KV part count")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="cache flush between timed steps (outside the timed events)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not "
+              "part of it (see DESIGN.md for how the path would shard).", file=sys.stderr)
+        return 2
+
+    import torch
+    import mla_paged_kv_04_amd as mla
+    from workloads import WORKLOADS, algorithmic_counts, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = make_inputs(args.workload)
+    g = inp.to(dev)
+    counts = algorithmic_counts(inp.seqlens.tolist(), inp.s_q, inp.h_q)
+
+    parts = args.parts or mla.num_parts(inp.batch, inp.s_q, inp.h_q, 1, mla.device_num_cus(dev))
+    ws = torch.empty((max(256, mla.workspace_bytes(inp.batch, inp.s_q, inp.h_q, parts)),),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((inp.batch, inp.s_q, inp.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.batch, inp.s_q, inp.h_q), dtype=torch.float32, device=dev)
+    flush_buf = torch.ones((1 << 28,), dtype=torch.int32, device=dev)   # 1 GiB
+    flush_sink = torch.empty((), dtype=torch.int32, device=dev)
+
+    def flush():
+        if args.flush == "read":
+            torch.amax(flush_buf, dim=0, out=flush_sink)
+        elif args.flush == "write":
+            flush_buf.fill_(1)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
+        if evs is not None:
+            evs[1].record()
+        mla.splitkv(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
+                    out, lse)
+        if evs is not None:
+            evs[2].record()
+        mla.combine(g.seqlens, inp.s_q, inp.h_q, meta, ws, out, lse)
+        if evs is not None:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        flush()
+        step()
+    torch.cuda.synchronize(dev)
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize(dev)
+    t_wall0 = time.perf_counter()
+    for k in range(K):
+        flush()
+        step(evs[k])
+    torch.cuda.synchronize(dev)
+    t_wall = time.perf_counter() - t_wall0
+
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    meta_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    mean = lambda xs: sum(xs) / len(xs)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    ms = mean(step_ms)
+    gbs = counts["bytes"] / (ms * 1e-3) / 1e9
+    tfl = counts["flops"] / (ms * 1e-3) / 1e12
+    dec = mean(dec_ms)
+    dec_gbs = counts["bytes"] / (dec * 1e-3) / 1e9
+    dec_tfl = counts["flops"] / (dec * 1e-3) / 1e12
+
+    # warm back-to-back rate (no flush), for reference only
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    warm_ms = e0.elapsed_time(e1) / K
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "desc": w.desc, "batch": inp.batch,
+                   "s_q": inp.s_q, "h_q": inp.h_q, "h_kv": 1, "d_k": 576, "d_v": 512,
+                   "block_size": 64, "total_keys": int(inp.seqlens.sum()),
+                   "num_parts": parts, "cache_flush_between_steps": args.flush},
+        "tflops": round(tfl, 2),
+        "algorithmic_bytes": counts["bytes"],
+        "algorithmic_flops": counts["flops"],
+        "kernels_ms": {"metadata": round(mean(meta_ms), 5), "splitkv": round(dec, 5),
+                       "combine": round(mean(comb_ms), 5),
+                       "splitkv_median": round(med(dec_ms), 5)},
+        "warm_ms_per_step": round(warm_ms, 5),
+        "wall_s_timed_region": round(t_wall, 4),
+        "roofline": {
+            "kernel": "mla_splitkv_kernel",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "mfma_tflops": round(dec_tfl, 2),
+            "mfma_frac": round(dec_tfl / PEAK_BF16_TFLOPS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

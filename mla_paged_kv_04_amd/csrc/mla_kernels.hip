@@ -68,6 +68,18 @@ __device__ __forceinline__ float wave_sum_4lanes(float x) {
   return x;
 }
 
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// makes the compiler wait for ALL outstanding vector memory ops (vmcnt(0)),
+// including the page prefetches that must stay in flight.  Callers wait
+// explicitly for what the barrier publishes (vmcnt for direct-to-LDS page
+// loads, lgkmcnt for ds_write); the empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ int n_pages(int L) {
   return L > 0 ? (L + kBlock - 1) / kBlock : 0;
 }
@@ -196,25 +208,29 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int c_fix, int num
 //   group, each taking 64/KG keys of every page (1 or 2).
 //   Rows per workgroup tile = (4/KG) * RT * 16.
 // --------------------------------------------------------------------------
-struct Cursor {
-  int b;   // request
-  int k;   // page within the request
-  bool valid;
-};
-
 // Values the hardware needs in SGPRs (buffer resources, M0) are read from
 // global memory with vector loads (the kernel also stores, so loads are not
 // provably invariant); readfirstlane tells the compiler they are wave-uniform
 // so no waterfall loop is emitted.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Scalar (SMEM) load of read-only metadata: through the constant address
+// space a wave-uniform address becomes s_load, tracked by lgkmcnt.  Vector
+// loads would be tracked by vmcnt, which retires in issue order, so waiting
+// for such a value would also wait for every page load issued before it.
+// seqlens, block_table, tile_meta and split_offsets are never written while
+// the kernel runs.
+__device__ __forceinline__ int ldc(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(p);
+}
+
 __device__ __forceinline__ void issue_page_load(char* lds_tile, const DecodeArgs& a, int b,
                                                 int k, const int (&off)[9], int w) {
-  const int L = uni(a.seqlens[b]);
+  const int L = ldc(a.seqlens + b);
   int rows = L - k * kBlock;
   rows = rows > kBlock ? kBlock : rows;
   int page = -1;
-  if (k < a.bt_stride) page = uni(a.block_table[(long long)b * a.bt_stride + k]);
+  if (k < a.bt_stride) page = ldc(a.block_table + (long long)b * a.bt_stride + k);
   const bool ok = page >= 0 && (long long)page < a.num_blocks && rows > 0;
   const char* base = reinterpret_cast<const char*>(a.kcache) +
                      (ok ? (long long)page * kPageBytes : 0);
@@ -237,15 +253,57 @@ __device__ __forceinline__ void issue_page_load(char* lds_tile, const DecodeArgs
   }
 }
 
-// First valid (request, page) position at or after (b, k) inside [.., (b1, k1)).
-__device__ __forceinline__ Cursor seek(const DecodeArgs& a, int b, int k, int b1, int k1) {
-  while (b < a.batch && (b < b1 || (b == b1 && k < k1))) {
-    const int end = (b == b1) ? k1 : n_pages(uni(a.seqlens[b]));
-    if (k < end) return Cursor{b, k, true};
+// L2 prefetch of a page: one 4-byte direct-to-LDS load per kPrefetchGran
+// bytes of the page, written to a per-wave junk LDS slot.  It costs no VGPRs
+// and nothing reads the result; it only pulls the page into L2 / Infinity
+// Cache a few iterations before its real (16-byte) load into LDS.  Rows at or
+// beyond the sequence end are outside num_records and are not fetched.
+constexpr int kPrefetchGran = 64;
+constexpr int kPrefetchLanes = kPageBytes / kPrefetchGran;                 // 1152
+constexpr int kPrefetchPerWave = (kPrefetchLanes + kThreads - 1) / kThreads;  // 5
+
+// Always issues exactly kPrefetchPerWave loads per wave (with valid == false
+// they are all out of range and touch no memory): the main loop's vmcnt wait
+// counts on that number.
+__device__ __forceinline__ void issue_page_prefetch(char* junk, const DecodeArgs& a, bool valid,
+                                                    int b, int k, int tid, int w) {
+  int rows = 0;
+  int page = -1;
+  if (valid) {
+    const int L = ldc(a.seqlens + b);
+    rows = L - k * kBlock;
+    rows = rows > kBlock ? kBlock : rows;
+    if (k < a.bt_stride) page = ldc(a.block_table + (long long)b * a.bt_stride + k);
+  }
+  const bool ok = page >= 0 && (long long)page < a.num_blocks && rows > 0;
+  const char* base = reinterpret_cast<const char*>(a.kcache) +
+                     (ok ? (long long)page * kPageBytes : 0);
+  const int nrec = uni(ok ? rows * kRowBytes : 0);
+  __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, kRsrcWord3);
+#pragma unroll
+  for (int j = 0; j < kPrefetchPerWave; ++j) {
+    const int idx = j * kThreads + tid;
+    const int off = idx < kPrefetchLanes ? idx * kPrefetchGran : 0x7ffffff0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(junk + w * 256), 4, off, 0, 0,
+                                             0);
+  }
+}
+
+// A position in a part's page sequence is a (request b, page k) pair of
+// wave-uniform ints; it is valid while (b, k) < (b1, k1) lexicographically.
+__device__ __forceinline__ bool before_end(const DecodeArgs& a, int b, int k, int b1, int k1) {
+  return b < a.batch && (b < b1 || (b == b1 && k < k1));
+}
+
+// Move (b, k) to the first page at or after it that belongs to the part.
+__device__ __forceinline__ void seek(const DecodeArgs& a, int& b, int& k, int b1, int k1) {
+  while (before_end(a, b, k, b1, k1)) {
+    const int end = (b == b1) ? k1 : n_pages(ldc(a.seqlens + b));
+    if (k < end) return;
     ++b;
     k = 0;
   }
-  return Cursor{b, k, false};
 }
 
 template <int RT, int KG>
@@ -257,7 +315,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
   constexpr int MT = RG * RT * 16;
   static_assert(KP >= 1, "at least 32 keys per wave");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes + 1024];
+  char* const junk = smem + 2 * kPageBytes;
 
   const int tid = threadIdx.x;
   // wave index made provably uniform (the LDS destination of direct loads
@@ -282,11 +341,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
     rtile = x % a.row_tiles;
   }
   const int32_t* tm = a.tile_meta + part * kMetaInts;
-  const int b0 = uni(tm[0]), k0 = uni(tm[1]), b1 = uni(tm[2]), k1 = uni(tm[3]);
-  const int first_split = uni(tm[4]);
+  const int b0 = ldc(tm + 0), k0 = ldc(tm + 1), b1 = ldc(tm + 2), k1 = ldc(tm + 3);
+  const int first_split = ldc(tm + 4);
 
-  Cursor cur = seek(a, b0, k0, b1, k1);
-  if (!cur.valid) return;  // uniform: empty part
+  int cur_b = b0, cur_k = k0;
+  seek(a, cur_b, cur_k, b1, k1);
+  if (!before_end(a, cur_b, cur_k, b1, k1)) return;  // uniform: empty part
 
   const int row0 = rtile * MT + rg * RT * 16;
   const bool active = row0 < a.M;
@@ -313,16 +373,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
   for (int d4 = 0; d4 < 4; ++d4)
     t_off[d4] = kgoff + tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
 
-  issue_page_load(smem, a, cur.b, cur.k, off, w);
+  issue_page_load(smem, a, cur_b, cur_k, off, w);
+  // prefetch position: runs a.pf_dist pages ahead of the next LDS load
+  int pf_b = cur_b, pf_k = cur_k;
+  __builtin_amdgcn_sched_barrier(0);
+  for (int d = 0; d < a.pf_dist; ++d) {
+    ++pf_k;
+    seek(a, pf_b, pf_k, b1, k1);
+    issue_page_prefetch(junk, a, before_end(a, pf_b, pf_k, b1, k1), pf_b, pf_k, tid, w);
+  }
   int buf = 0;
-  Cursor nxt;
+  int nxt_b = cur_b, nxt_k = cur_k;
 
   // ---------------- one iteration per piece (request slice) ----------------
   while (true) {
-    const int b = uni(cur.b);
-    const int L = uni(a.seqlens[b]);
+    const int b = cur_b;
+    const int L = ldc(a.seqlens + b);
     const int n = n_pages(L);
-    const int pbeg = cur.k;
+    const int pbeg = cur_k;
     const int pend = (b == b1) ? k1 : n;     // exclusive
     const int lim_min = a.causal ? L - a.s_q + 1 : L;
 
@@ -332,8 +400,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
     int lim[RT];
 
     for (int k = pbeg;; ++k) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      // This wave's loads of the current page have landed once at most the
+      // prefetch loads issued after them are outstanding (vmcnt retires in
+      // issue order); the barrier then makes every wave's part visible.
+      if (a.pf_dist > 0)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrefetchPerWave) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wg_barrier();
 
       // The piece's query rows are loaded BEFORE the next page's prefetch so
       // the compiler's vmcnt wait for Q never waits for the prefetch (vmcnt
@@ -356,8 +430,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
       }
 
       // prefetch the part's next page (possibly of the next piece)
-      nxt = seek(a, b, k + 1, b1, k1);
-      if (nxt.valid) issue_page_load(smem + (buf ^ 1) * kPageBytes, a, nxt.b, nxt.k, off, w);
+      nxt_b = b;
+      nxt_k = k + 1;
+      seek(a, nxt_b, nxt_k, b1, k1);
+      const bool nxt_valid = before_end(a, nxt_b, nxt_k, b1, k1);
+      if (nxt_valid) issue_page_load(smem + (buf ^ 1) * kPageBytes, a, nxt_b, nxt_k, off, w);
+      if (a.pf_dist > 0) {
+        // the prefetch loads must be the youngest VMEM ops of the iteration
+        __builtin_amdgcn_sched_barrier(0);
+        ++pf_k;
+        seek(a, pf_b, pf_k, b1, k1);
+        issue_page_prefetch(junk, a, before_end(a, pf_b, pf_k, b1, k1), pf_b, pf_k, tid, w);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 
       const char* page = smem + buf * kPageBytes;
       if (active) {
@@ -418,8 +503,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
             const float alpha = grow ? exp2f(m_run[rt] - m_new) : 1.f;
             if (grow) m_run[rt] = m_new;
             l_run[rt] *= alpha;
+            // chunked so only a few accumulator tiles are in VGPRs at once
 #pragma unroll
-            for (int dt = 0; dt < 32; ++dt) o[rt][dt] *= alpha;
+            for (int d8 = 0; d8 < 32; d8 += 8) {
+#pragma unroll
+              for (int dt = d8; dt < d8 + 8; ++dt) o[rt][dt] *= alpha;
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
           const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
           float lsum = 0.f;
@@ -481,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
     }
     const f32x4* mo = nullptr;
     if constexpr (KG == 2) {
-      __syncthreads();  // every wave is done reading the last page buffer
+      wg_barrier();  // every wave is done reading the last page buffer (reads consumed)
       char* mb = smem + buf * kPageBytes;
       f32x4* mw = reinterpret_cast<f32x4*>(mb) + (rg * RT * 32) * 64;
       float* mm = reinterpret_cast<float*>(mb + RG * RT * 32 * 1024) + rg * RT * 128;
@@ -494,7 +584,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
           mm[rt * 128 + 64 + lane] = l_run[rt];
         }
       }
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // partner's ds_writes done
+      wg_barrier();
       if (active && kg == 0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -515,7 +606,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
     if (active && kg == 0) {
       const bool whole = pbeg == 0 && pend == n;
       const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
-      const long long slot = whole ? 0 : (long long)uni(a.split_offsets[b]) + sidx;
+      const long long slot = whole ? 0 : (long long)ldc(a.split_offsets + b) + sidx;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const float lt = wave_sum_4lanes(l_run[rt]);
@@ -555,8 +646,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
       }
     }
 
-    if (!nxt.valid) break;
-    cur = nxt;
+    if (!before_end(a, nxt_b, nxt_k, b1, k1)) break;
+    cur_b = nxt_b;
+    cur_k = nxt_k;
     buf ^= 1;
   }
 }
