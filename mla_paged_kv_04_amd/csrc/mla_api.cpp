@@ -8,7 +8,6 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include "mla_kernels.h"
@@ -33,18 +32,6 @@ int check_shape(int batch, int s_q, int h_q, int h_kv) {
 }
 
 constexpr int kMaxParts = 1 << 16;
-
-// Pages the L2 prefetch runs ahead of the LDS loads.  Tuning knob:
-// MLA_DECODE_PREFETCH_PAGES (0..8) overrides the default.
-int prefetch_pages() {
-  static const int v = [] {
-    const char* e = getenv("MLA_DECODE_PREFETCH_PAGES");
-    int d = 2;
-    if (e && *e) d = atoi(e);
-    return d < 0 ? 0 : (d > 8 ? 8 : d);
-  }();
-  return v;
-}
 
 int row_tiles(int s_q, int h_q) {
   const int M = s_q * h_q;
@@ -162,7 +149,6 @@ int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks
   a.num_parts = num_parts;
   a.row_tiles = row_tiles(s_q, h_q);
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.pf_dist = prefetch_pages();
   hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mla_decode_splitkv launch");
   return MLA_OK;

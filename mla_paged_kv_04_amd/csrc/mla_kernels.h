@@ -47,7 +47,6 @@ struct DecodeArgs {
   int num_parts;
   int row_tiles;
   float scale_log2;           // scale * log2(e)
-  int pf_dist;                // pages the L2 prefetch runs ahead (0 = off)
 };
 
 struct CombineArgs {

@@ -224,6 +224,17 @@ __device__ __forceinline__ int ldc(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)(p);
 }
 
+// Issue the 18 direct-to-LDS 16-byte loads of one page for this wave.
+//
+// Written as inline asm on purpose: the compiler then does not track these
+// loads.  Tracked, every LDS read that it cannot prove disjoint from an
+// in-flight direct load (the transposed V reads, for one) gets an
+// "s_waitcnt vmcnt(0)", which would wait for the NEXT page's loads and
+// serialise the pipeline.  All waits for these loads are therefore explicit
+// (see the main loop), and the asm clobbers "memory" so the compiler keeps LDS
+// accesses on the right side of it.  M0 holds the LDS destination; nothing
+// else in this kernel uses M0 (gfx9 LDS instructions do not), and one wait
+// state separates each M0 write from the load that reads it.
 __device__ __forceinline__ void issue_page_load(char* lds_tile, const DecodeArgs& a, int b,
                                                 int k, const int (&off)[9], int w) {
   const int L = ldc(a.seqlens + b);
@@ -241,53 +252,67 @@ __device__ __forceinline__ void issue_page_load(char* lds_tile, const DecodeArgs
   constexpr int kHalf = 32 * kRowBytes;
   const int nrec_lo = uni(nrec < kHalf ? nrec : kHalf);
   const int nrec_hi = uni(nrec > kHalf ? nrec - kHalf : 0);
-  __amdgpu_buffer_rsrc_t r_lo =
+  const __amdgpu_buffer_rsrc_t r_lo =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec_lo, kRsrcWord3);
-  __amdgpu_buffer_rsrc_t r_hi =
+  const __amdgpu_buffer_rsrc_t r_hi =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + kHalf, 0, nrec_hi, kRsrcWord3);
-#pragma unroll
-  for (int j = 0; j < 18; ++j) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 9 ? r_lo : r_hi,
-                                             (MLA_LDS void*)(lds_tile + j * 4096 + w * 1024), 16,
-                                             off[j % 9], 0, 0, 0);
-  }
+  // LDS byte address of this wave's first 1 KB slot: tile + w * 1024; slot j
+  // of the wave is 4096 bytes further on per j.
+  const uint32_t m0 = uni(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_tile)) + w * 1024));
+#define MLA_DMA(R, O) "s_nop 0\n\tbuffer_load_dwordx4 %[" #O "], %[" #R "], 0 offen lds\n\t"
+#define MLA_M0_NEXT "s_add_u32 m0, m0, 0x1000\n\t"
+  asm volatile(
+      "s_mov_b32 m0, %[m]\n\t"
+      MLA_DMA(rl, o0) MLA_M0_NEXT MLA_DMA(rl, o1) MLA_M0_NEXT MLA_DMA(rl, o2) MLA_M0_NEXT
+      MLA_DMA(rl, o3) MLA_M0_NEXT MLA_DMA(rl, o4) MLA_M0_NEXT MLA_DMA(rl, o5) MLA_M0_NEXT
+      MLA_DMA(rl, o6) MLA_M0_NEXT MLA_DMA(rl, o7) MLA_M0_NEXT MLA_DMA(rl, o8) MLA_M0_NEXT
+      MLA_DMA(rh, o0) MLA_M0_NEXT MLA_DMA(rh, o1) MLA_M0_NEXT MLA_DMA(rh, o2) MLA_M0_NEXT
+      MLA_DMA(rh, o3) MLA_M0_NEXT MLA_DMA(rh, o4) MLA_M0_NEXT MLA_DMA(rh, o5) MLA_M0_NEXT
+      MLA_DMA(rh, o6) MLA_M0_NEXT MLA_DMA(rh, o7) MLA_M0_NEXT MLA_DMA(rh, o8)
+      :
+      : [m] "s"(m0), [rl] "s"(r_lo), [rh] "s"(r_hi), [o0] "v"(off[0]), [o1] "v"(off[1]),
+        [o2] "v"(off[2]), [o3] "v"(off[3]), [o4] "v"(off[4]), [o5] "v"(off[5]),
+        [o6] "v"(off[6]), [o7] "v"(off[7]), [o8] "v"(off[8])
+      : "memory", "m0");
+#undef MLA_DMA
+#undef MLA_M0_NEXT
 }
 
-// L2 prefetch of a page: one 4-byte direct-to-LDS load per kPrefetchGran
-// bytes of the page, written to a per-wave junk LDS slot.  It costs no VGPRs
-// and nothing reads the result; it only pulls the page into L2 / Infinity
-// Cache a few iterations before its real (16-byte) load into LDS.  Rows at or
-// beyond the sequence end are outside num_records and are not fetched.
-constexpr int kPrefetchGran = 64;
-constexpr int kPrefetchLanes = kPageBytes / kPrefetchGran;                 // 1152
-constexpr int kPrefetchPerWave = (kPrefetchLanes + kThreads - 1) / kThreads;  // 5
+// Number of vector-memory instructions issue_page_load issues per wave.
+constexpr int kPageLoadsPerWave = 18;
 
-// Always issues exactly kPrefetchPerWave loads per wave (with valid == false
-// they are all out of range and touch no memory): the main loop's vmcnt wait
-// counts on that number.
-__device__ __forceinline__ void issue_page_prefetch(char* junk, const DecodeArgs& a, bool valid,
-                                                    int b, int k, int tid, int w) {
-  int rows = 0;
-  int page = -1;
-  if (valid) {
-    const int L = ldc(a.seqlens + b);
-    rows = L - k * kBlock;
-    rows = rows > kBlock ? kBlock : rows;
-    if (k < a.bt_stride) page = ldc(a.block_table + (long long)b * a.bt_stride + k);
-  }
-  const bool ok = page >= 0 && (long long)page < a.num_blocks && rows > 0;
-  const char* base = reinterpret_cast<const char*>(a.kcache) +
-                     (ok ? (long long)page * kPageBytes : 0);
-  const int nrec = uni(ok ? rows * kRowBytes : 0);
-  __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, kRsrcWord3);
-#pragma unroll
-  for (int j = 0; j < kPrefetchPerWave; ++j) {
-    const int idx = j * kThreads + tid;
-    const int off = idx < kPrefetchLanes ? idx * kPrefetchGran : 0x7ffffff0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MLA_LDS void*)(junk + w * 256), 4, off, 0, 0,
-                                             0);
-  }
+// Load 16 rows x 576 bf16 of Q (the B operand of the score product) for one
+// lane: 18 x 16 bytes at a 64-byte stride.  Inline asm so the compiler does
+// not place its own (in-order, hence pipeline-draining) vmcnt wait for it;
+// the block waits for its own loads before it ends (its outputs are
+// early-clobber so no load can overwrite the address of a later one).
+__device__ __forceinline__ void load_q_rows(bf16x8 (&q)[18], const bf16x8* qp) {
+  asm volatile(
+      "global_load_dwordx4 %0, %18, off\n\t"
+      "global_load_dwordx4 %1, %18, off offset:64\n\t"
+      "global_load_dwordx4 %2, %18, off offset:128\n\t"
+      "global_load_dwordx4 %3, %18, off offset:192\n\t"
+      "global_load_dwordx4 %4, %18, off offset:256\n\t"
+      "global_load_dwordx4 %5, %18, off offset:320\n\t"
+      "global_load_dwordx4 %6, %18, off offset:384\n\t"
+      "global_load_dwordx4 %7, %18, off offset:448\n\t"
+      "global_load_dwordx4 %8, %18, off offset:512\n\t"
+      "global_load_dwordx4 %9, %18, off offset:576\n\t"
+      "global_load_dwordx4 %10, %18, off offset:640\n\t"
+      "global_load_dwordx4 %11, %18, off offset:704\n\t"
+      "global_load_dwordx4 %12, %18, off offset:768\n\t"
+      "global_load_dwordx4 %13, %18, off offset:832\n\t"
+      "global_load_dwordx4 %14, %18, off offset:896\n\t"
+      "global_load_dwordx4 %15, %18, off offset:960\n\t"
+      "global_load_dwordx4 %16, %18, off offset:1024\n\t"
+      "global_load_dwordx4 %17, %18, off offset:1088\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]),
+        "=&v"(q[6]), "=&v"(q[7]), "=&v"(q[8]), "=&v"(q[9]), "=&v"(q[10]), "=&v"(q[11]),
+        "=&v"(q[12]), "=&v"(q[13]), "=&v"(q[14]), "=&v"(q[15]), "=&v"(q[16]), "=&v"(q[17])
+      : "v"(qp)
+      : "memory");
 }
 
 // A position in a part's page sequence is a (request b, page k) pair of
@@ -315,8 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
   constexpr int MT = RG * RT * 16;
   static_assert(KP >= 1, "at least 32 keys per wave");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes + 1024];
-  char* const junk = smem + 2 * kPageBytes;
+  // Two page buffers (double buffering), 2 x 72 KB of the 160 KB LDS.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes];
 
   const int tid = threadIdx.x;
   // wave index made provably uniform (the LDS destination of direct loads
@@ -328,17 +353,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
   const int kg = w % KG;
   const int rg = w / KG;
 
-  // workgroup -> (part, row tile); the two row tiles of a part share an XCD
-  // (workgroups are dealt to the 8 XCDs round-robin) so the second read of a
-  // page hits that XCD's L2.
+  // workgroup -> (part, row tile).  Workgroups are dealt to the 8 XCDs
+  // round-robin; all row tiles of a part get ids x, x+8, x+16, ... and so
+  // share an XCD, whose L2 then serves the repeated reads of each page.
   int part, rtile;
   const int x = blockIdx.x;
-  if (a.row_tiles == 2 && (a.num_parts % 8) == 0) {
-    part = (x >> 4) * 8 + (x & 7);
-    rtile = (x >> 3) & 1;
+  const int R = a.row_tiles;
+  if (R > 1 && (a.num_parts % 8) == 0) {
+    part = (x / (8 * R)) * 8 + (x & 7);
+    rtile = (x >> 3) % R;
   } else {
-    part = x / a.row_tiles;
-    rtile = x % a.row_tiles;
+    part = x / R;
+    rtile = x % R;
   }
   const int32_t* tm = a.tile_meta + part * kMetaInts;
   const int b0 = ldc(tm + 0), k0 = ldc(tm + 1), b1 = ldc(tm + 2), k1 = ldc(tm + 3);
@@ -373,78 +399,71 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
   for (int d4 = 0; d4 < 4; ++d4)
     t_off[d4] = kgoff + tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
 
+  bf16x8 qreg[RT][18];
+  f32x4 o[RT][32];
+  float m_run[RT], l_run[RT];
+  int lim[RT];
+  int L = 0, n = 0, pbeg = 0, pend = 0, lim_min = 0;
+
+  auto load_q = [&](int b) {
+    if (active) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int row = row0 + rt * 16 + i;
+        load_q_rows(qreg[rt], reinterpret_cast<const bf16x8*>(
+                                  a.q + ((long long)b * a.M + row) * kDK + 8 * g));
+      }
+    }
+  };
+  auto start_piece = [&](int b, int k) {
+    L = ldc(a.seqlens + b);
+    n = n_pages(L);
+    pbeg = k;
+    pend = (b == b1) ? k1 : n;     // exclusive
+    lim_min = a.causal ? L - a.s_q + 1 : L;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int t = (row0 + rt * 16 + i) / a.h_q;
+      lim[rt] = a.causal ? L - a.s_q + 1 + t : L;
+      m_run[rt] = -INFINITY;
+      l_run[rt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  // Pipeline (two page buffers).  A buffer is refilled with page p+2 as soon
+  // as every wave has finished computing page p in it, so while a wave waits
+  // for page p+1, pages p+1 and p+2 are both in flight.  The only vector
+  // memory ops in flight at a loop top are page loads (Q loads wait for
+  // themselves), so the wait for page p is vmcnt(18) when page p+1's 18 loads
+  // were issued after it (vmcnt retires in issue order), else vmcnt(0).
   issue_page_load(smem, a, cur_b, cur_k, off, w);
-  // prefetch position: runs a.pf_dist pages ahead of the next LDS load
-  int pf_b = cur_b, pf_k = cur_k;
-  __builtin_amdgcn_sched_barrier(0);
-  for (int d = 0; d < a.pf_dist; ++d) {
-    ++pf_k;
-    seek(a, pf_b, pf_k, b1, k1);
-    issue_page_prefetch(junk, a, before_end(a, pf_b, pf_k, b1, k1), pf_b, pf_k, tid, w);
-  }
+  load_q(cur_b);
+  int nxt_b = cur_b, nxt_k = cur_k + 1;
+  seek(a, nxt_b, nxt_k, b1, k1);
+  bool nxt_valid = before_end(a, nxt_b, nxt_k, b1, k1);
+  if (nxt_valid) issue_page_load(smem + kPageBytes, a, nxt_b, nxt_k, off, w);
+  start_piece(cur_b, cur_k);
   int buf = 0;
-  int nxt_b = cur_b, nxt_k = cur_k;
 
   // ---------------- one iteration per piece (request slice) ----------------
   while (true) {
     const int b = cur_b;
-    const int L = ldc(a.seqlens + b);
-    const int n = n_pages(L);
-    const int pbeg = cur_k;
-    const int pend = (b == b1) ? k1 : n;     // exclusive
-    const int lim_min = a.causal ? L - a.s_q + 1 : L;
-
-    bf16x8 qreg[RT][18];
-    f32x4 o[RT][32];
-    float m_run[RT], l_run[RT];
-    int lim[RT];
-
-    for (int k = pbeg;; ++k) {
-      // This wave's loads of the current page have landed once at most the
-      // prefetch loads issued after them are outstanding (vmcnt retires in
-      // issue order); the barrier then makes every wave's part visible.
-      if (a.pf_dist > 0)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrefetchPerWave) : "memory");
+    int k = cur_k;
+    int nn_b = 0, nn_k = 0;
+    bool nn_valid = false;
+    char* page;
+    // -------- pages of the piece --------
+    while (true) {
+      static_assert(kPageLoadsPerWave == 18, "wait count below");
+      if (nxt_valid)
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       wg_barrier();
+      page = smem + buf * kPageBytes;
 
-      // The piece's query rows are loaded BEFORE the next page's prefetch so
-      // the compiler's vmcnt wait for Q never waits for the prefetch (vmcnt
-      // retires in issue order).
-      if (k == pbeg && active) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int row = row0 + rt * 16 + i;
-          const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-              a.q + ((long long)b * a.M + row) * kDK + 8 * g);
-#pragma unroll
-          for (int ks = 0; ks < 18; ++ks) qreg[rt][ks] = qp[ks * 4];
-          const int t = row / a.h_q;
-          lim[rt] = a.causal ? L - a.s_q + 1 + t : L;
-          m_run[rt] = -INFINITY;
-          l_run[rt] = 0.f;
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-
-      // prefetch the part's next page (possibly of the next piece)
-      nxt_b = b;
-      nxt_k = k + 1;
-      seek(a, nxt_b, nxt_k, b1, k1);
-      const bool nxt_valid = before_end(a, nxt_b, nxt_k, b1, k1);
-      if (nxt_valid) issue_page_load(smem + (buf ^ 1) * kPageBytes, a, nxt_b, nxt_k, off, w);
-      if (a.pf_dist > 0) {
-        // the prefetch loads must be the youngest VMEM ops of the iteration
-        __builtin_amdgcn_sched_barrier(0);
-        ++pf_k;
-        seek(a, pf_b, pf_k, b1, k1);
-        issue_page_prefetch(junk, a, before_end(a, pf_b, pf_k, b1, k1), pf_b, pf_k, tid, w);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      const char* page = smem + buf * kPageBytes;
       if (active) {
         // ---- scores S^T[key][row] = K . Q^T over 576 dims ----
         // Software pipeline: operand reads for step ks+D1 are in flight while
@@ -452,24 +471,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
         // hoisting every read of the unrolled loop (register blow-up).
         constexpr int D1 = (RT * KT >= 8) ? 1 : 2;
         f32x4 s[RT][KT];
-#pragma unroll
+  #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
+  #pragma unroll
           for (int kt = 0; kt < KT; ++kt) s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         bf16x8 ka[D1 + 1][KT];
-#pragma unroll
+  #pragma unroll
         for (int ks = 0; ks < 18 + D1; ++ks) {
           if (ks < 18) {
             const char* ab = page + ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
-#pragma unroll
+  #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
               ka[ks % (D1 + 1)][kt] = *reinterpret_cast<const bf16x8*>(ab + kt * 16 * kRowBytes);
           }
           const int cs = ks - D1;
           if (cs >= 0) {
-#pragma unroll
+  #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
+  #pragma unroll
               for (int kt = 0; kt < KT; ++kt)
                 s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     ka[cs % (D1 + 1)][kt], qreg[rt][cs], s[rt][kt], 0, 0, 0);
@@ -481,12 +500,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
         const int key0 = k * kBlock + kg * KW + 4 * g;
         const bool need_mask = (k + 1) * kBlock > lim_min;
         bf16x8 pb[RT][KP];
-#pragma unroll
+  #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           float mx = -INFINITY;
-#pragma unroll
+  #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
+  #pragma unroll
             for (int v = 0; v < 4; ++v) {
               float xv = s[rt][kt][v] * a.scale_log2;
               if (need_mask && key0 + kt * 16 + v >= lim[rt]) xv = -INFINITY;
@@ -500,24 +519,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
           // either way (numerator and denominator share the reference max).
           const bool grow = m_new > m_run[rt] + kRescaleSlack;
           if (__any(grow)) {
-            const float alpha = grow ? exp2f(m_run[rt] - m_new) : 1.f;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[rt] - m_new) : 1.f;
             if (grow) m_run[rt] = m_new;
             l_run[rt] *= alpha;
             // chunked so only a few accumulator tiles are in VGPRs at once
-#pragma unroll
+  #pragma unroll
             for (int d8 = 0; d8 < 32; d8 += 8) {
-#pragma unroll
+  #pragma unroll
               for (int dt = d8; dt < d8 + 8; ++dt) o[rt][dt] *= alpha;
               __builtin_amdgcn_sched_barrier(0);
             }
           }
           const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
           float lsum = 0.f;
-#pragma unroll
+  #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
+  #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const float p = exp2f(s[rt][kt][v] - m_use);
+              const float p = __builtin_amdgcn_exp2f(s[rt][kt][v] - m_use);
               lsum += p;
               pb[rt][kt >> 1][(kt & 1) * 4 + v] = (__bf16)p;
             }
@@ -528,11 +547,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
         // ---- O^T[dim][row] += V^T . P^T over this wave's keys ----
         constexpr int D2 = (RT * KP >= 4) ? 1 : 2;
         bf16x8 va[D2 + 1][KP];
-#pragma unroll
+  #pragma unroll
         for (int dt = 0; dt < 32 + D2; ++dt) {
           if (dt < 32) {
             const char* tb = page + t_off[dt & 3] + 128 * (dt >> 2);
-#pragma unroll
+  #pragma unroll
             for (int kp = 0; kp < KP; ++kp) {
               const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                   (MLA_LDS bf16x4*)(tb + (kp * 32) * kRowBytes));
@@ -544,9 +563,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
           }
           const int cd = dt - D2;
           if (cd >= 0) {
-#pragma unroll
+  #pragma unroll
             for (int kp = 0; kp < KP; ++kp)
-#pragma unroll
+  #pragma unroll
               for (int rt = 0; rt < RT; ++rt)
                 o[rt][cd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     va[cd % (D2 + 1)][kp], pb[rt][kp], o[rt][cd], 0, 0, 0);
@@ -555,14 +574,27 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
         }
       }
 
+
+      // position of page k+2 (the refill of this buffer)
+      nn_b = nxt_b;
+      nn_k = nxt_k + 1;
+      if (nxt_valid) seek(a, nn_b, nn_k, b1, k1);
+      nn_valid = nxt_valid && before_end(a, nn_b, nn_k, b1, k1);
       if (k + 1 >= pend) break;
+      // same piece continues with page k+1 (= nxt): refill this buffer
+      wg_barrier();  // every wave is done reading this buffer (reads consumed)
+      if (nn_valid) issue_page_load(page, a, nn_b, nn_k, off, w);
+      nxt_b = nn_b;
+      nxt_k = nn_k;
+      nxt_valid = nn_valid;
       buf ^= 1;
+      ++k;
     }
 
-    // ---- merge the KG key groups of each row group, then write ----
-    // With KG == 2 the partner wave's (m, l, O) go through the LDS buffer of
-    // the last page; the merge is folded into the store loop so the
-    // accumulators are only read here.
+    // ---- piece end: merge the KG key groups, then write ----
+    // With KG == 2 the partner wave's (m, l, O) go through this page
+    // buffer; the merge is folded into the store loop so the accumulators
+    // are only read here.
     float a_self[RT], a_other[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -571,10 +603,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
     }
     const f32x4* mo = nullptr;
     if constexpr (KG == 2) {
-      wg_barrier();  // every wave is done reading the last page buffer (reads consumed)
-      char* mb = smem + buf * kPageBytes;
-      f32x4* mw = reinterpret_cast<f32x4*>(mb) + (rg * RT * 32) * 64;
-      float* mm = reinterpret_cast<float*>(mb + RG * RT * 32 * 1024) + rg * RT * 128;
+      wg_barrier();  // every wave is done reading this buffer (reads consumed)
+      f32x4* mw = reinterpret_cast<f32x4*>(page) + (rg * RT * 32) * 64;
+      float* mm = reinterpret_cast<float*>(page + RG * RT * 32 * 1024) + rg * RT * 128;
       if (active && kg == 1) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -593,8 +624,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
           const float l1 = mm[rt * 128 + 64 + lane];
           const float m0 = m_run[rt];
           const float mn = fmaxf(m0, m1);
-          a_self[rt] = m0 == -INFINITY ? 0.f : exp2f(m0 - mn);
-          a_other[rt] = m1 == -INFINITY ? 0.f : exp2f(m1 - mn);
+          a_self[rt] = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mn);
+          a_other[rt] = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
           l_run[rt] = l_run[rt] * a_self[rt] + l1 * a_other[rt];
           m_run[rt] = mn;
         }
@@ -602,7 +633,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
       mo = mw;
     }
 
-    // ---- epilogue: normalise; write O/LSE, or the split partials ----
     if (active && kg == 0) {
       const bool whole = pbeg == 0 && pend == n;
       const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
@@ -646,9 +676,321 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
       }
     }
 
-    if (!before_end(a, nxt_b, nxt_k, b1, k1)) break;
+    if (!nxt_valid) break;
+    // The next piece starts at page k+1 (already in flight): load its Q rows
+    // (the load waits for everything issued before it, page k+1 included),
+    // then refill this buffer with page k+2.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // merge-area reads done
+    wg_barrier();  // every wave is done with this buffer (incl. merge reads)
+    load_q(nxt_b);
+    if (nn_valid) issue_page_load(page, a, nn_b, nn_k, off, w);
+    start_piece(nxt_b, nxt_k);
     cur_b = nxt_b;
     cur_k = nxt_k;
+    nxt_b = nn_b;
+    nxt_k = nn_k;
+    nxt_valid = nn_valid;
+    buf ^= 1;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Column-split variant for row tiles of 64 query rows (s_q*h_q >= 64).
+//   scores:  row split    — wave w owns query rows 16w..16w+15, all 64 keys;
+//   values:  column split — wave w owns output dims 128w..128w+127 for all 64
+//            rows, so it reads only its quarter of V from LDS (the transposed
+//            reads run at half the LDS rate of 16-byte reads; reading all of
+//            V in every wave made the row-split kernel LDS-bound).
+// The bf16 probabilities (64 rows x 64 keys) go through LDS in exactly the
+// B-operand order of the value MFMA, so they are written and read as
+// contiguous 16-byte per-lane accesses.  Row statistics (running max m, sum
+// l) stay with the row-owning wave; the per-row rescale factors and the
+// final 1/l are published through LDS.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void mla_splitkv_cs_kernel(const DecodeArgs a) {
+  constexpr int KT = 4;   // 16-key score tiles (all 64 keys)
+  constexpr int KP = 2;   // 32-key reduction steps of the value product
+  constexpr int DL = 8;   // 16-dim output tiles per wave (128 dims)
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes];
+  __shared__ bf16x8 p_lds[4][KP][64];      // P^T operands, [row tile][kp][lane]
+  __shared__ float alpha_lds[64];          // per-row rescale factor of this page
+  __shared__ int grow_lds[4];              // per row tile: any row rescaled
+  __shared__ float stat_l[64];             // per-row sum at piece end
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int i = lane & 15;
+
+  int part, rtile;
+  const int x = blockIdx.x;
+  const int R = a.row_tiles;
+  if (R > 1 && (a.num_parts % 8) == 0) {
+    part = (x / (8 * R)) * 8 + (x & 7);
+    rtile = (x >> 3) % R;
+  } else {
+    part = x / R;
+    rtile = x % R;
+  }
+  const int32_t* tm = a.tile_meta + part * kMetaInts;
+  const int b0 = ldc(tm + 0), k0 = ldc(tm + 1), b1 = ldc(tm + 2), k1 = ldc(tm + 3);
+  const int first_split = ldc(tm + 4);
+
+  int cur_b = b0, cur_k = k0;
+  seek(a, cur_b, cur_k, b1, k1);
+  if (!before_end(a, cur_b, cur_k, b1, k1)) return;  // uniform: empty part
+
+  const int tile_row0 = rtile * 64;       // first query row of the tile
+  const int row_own = tile_row0 + w * 16 + i;  // score/softmax row of this lane
+
+  int off[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int u = j * kThreads + tid;
+    const int r = u / kChunksPerRow;
+    const int pc = u - r * kChunksPerRow;
+    off[j] = r * kRowBytes + ((pc ^ lds_swizzle(r)) << 4);
+  }
+  const int fi = lds_swizzle(i & 7);
+  const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
+  const int a_off1 = i * kRowBytes + (((4 + g) ^ fi) << 4);
+  const int tr_row = 4 * g + (i >> 2);
+  const int ft = lds_swizzle(tr_row & 7);
+  const int hh = (i & 3) >> 1;
+  int t_off[4];
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4)
+    t_off[d4] = tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
+  // this wave's dims start at dim tile 8w: byte offset 128 * (8w >> 2) = 256 w
+  const int t_base = 256 * w;
+
+  bf16x8 qreg[18];
+  f32x4 o[DL][4];          // O^T tiles: [dim tile of this wave][row tile]
+  float m_run, l_run;      // statistics of row_own
+  int lim;
+  int L = 0, n = 0, pend = 0, lim_min = 0, pbeg = 0;
+
+  auto load_q = [&](int b) {
+    load_q_rows(qreg, reinterpret_cast<const bf16x8*>(
+                          a.q + ((long long)b * a.M + row_own) * kDK + 8 * g));
+  };
+  auto start_piece = [&](int b, int k) {
+    L = ldc(a.seqlens + b);
+    n = n_pages(L);
+    pbeg = k;
+    pend = (b == b1) ? k1 : n;
+    lim_min = a.causal ? L - a.s_q + 1 : L;
+    const int t = row_own / a.h_q;
+    lim = a.causal ? L - a.s_q + 1 + t : L;
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int dl = 0; dl < DL; ++dl)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) o[dl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  issue_page_load(smem, a, cur_b, cur_k, off, w);
+  load_q(cur_b);
+  int nxt_b = cur_b, nxt_k = cur_k + 1;
+  seek(a, nxt_b, nxt_k, b1, k1);
+  bool nxt_valid = before_end(a, nxt_b, nxt_k, b1, k1);
+  if (nxt_valid) issue_page_load(smem + kPageBytes, a, nxt_b, nxt_k, off, w);
+  start_piece(cur_b, cur_k);
+  int buf = 0;
+
+  while (true) {
+    const int b = cur_b;
+    int k = cur_k;
+    int nn_b = 0, nn_k = 0;
+    bool nn_valid = false;
+    char* page;
+    while (true) {
+      static_assert(kPageLoadsPerWave == 18, "wait count below");
+      if (nxt_valid)
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wg_barrier();
+      page = smem + buf * kPageBytes;
+
+      // ---- scores S^T[key][row] = K . Q^T for this wave's 16 rows ----
+      f32x4 s[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        constexpr int D1 = 2;
+        bf16x8 ka[D1 + 1][KT];
+#pragma unroll
+        for (int ks = 0; ks < 18 + D1; ++ks) {
+          if (ks < 18) {
+            const char* ab = page + ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+              ka[ks % (D1 + 1)][kt] = *reinterpret_cast<const bf16x8*>(ab + kt * 16 * kRowBytes);
+          }
+          const int cs = ks - D1;
+          if (cs >= 0) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+              s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[cs % (D1 + 1)][kt], qreg[cs],
+                                                             s[kt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- online softmax of row_own (fp32, base 2, lazy rescale) ----
+      {
+        const int key0 = k * kBlock + 4 * g;
+        const bool need_mask = (k + 1) * kBlock > lim_min;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float xv = s[kt][v] * a.scale_log2;
+            if (need_mask && key0 + kt * 16 + v >= lim) xv = -INFINITY;
+            s[kt][v] = xv;
+            mx = fmaxf(mx, xv);
+          }
+        mx = wave_max_4lanes(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const bool grow = m_new > m_run + kRescaleSlack;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        if (grow) m_run = m_new;
+        l_run *= alpha;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float lsum = 0.f;
+        bf16x8 pb[KP];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float p = __builtin_amdgcn_exp2f(s[kt][v] - m_use);
+            lsum += p;
+            pb[kt >> 1][(kt & 1) * 4 + v] = (__bf16)p;
+          }
+        l_run += lsum;
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp) p_lds[w][kp][lane] = pb[kp];
+        if (g == 0) alpha_lds[w * 16 + i] = alpha;
+        const int any = __any(grow) ? 1 : 0;
+        if (lane == 0) grow_lds[w] = any;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P, alpha, flags written
+      wg_barrier();
+
+      // ---- O^T[dim][row] += V^T . P^T, this wave's 128 dims, all 64 rows ----
+      {
+        if (grow_lds[0] | grow_lds[1] | grow_lds[2] | grow_lds[3]) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const float al = alpha_lds[rt * 16 + i];
+#pragma unroll
+            for (int dl = 0; dl < DL; ++dl) o[dl][rt] *= al;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        bf16x8 pB[4][KP];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int kp = 0; kp < KP; ++kp) pB[rt][kp] = p_lds[rt][kp][lane];
+        constexpr int D2 = 1;
+        bf16x8 va[D2 + 1][KP];
+#pragma unroll
+        for (int dl = 0; dl < DL + D2; ++dl) {
+          if (dl < DL) {
+            const char* tb = page + t_base + t_off[dl & 3] + 128 * (dl >> 2);
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp) {
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (MLA_LDS bf16x4*)(tb + (kp * 32) * kRowBytes));
+              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (MLA_LDS bf16x4*)(tb + (kp * 32 + 16) * kRowBytes));
+              va[dl % (D2 + 1)][kp] =
+                  bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+          }
+          const int cd = dl - D2;
+          if (cd >= 0) {
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+              for (int rt = 0; rt < 4; ++rt)
+                o[cd][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    va[cd % (D2 + 1)][kp], pB[rt][kp], o[cd][rt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      nn_b = nxt_b;
+      nn_k = nxt_k + 1;
+      if (nxt_valid) seek(a, nn_b, nn_k, b1, k1);
+      nn_valid = nxt_valid && before_end(a, nn_b, nn_k, b1, k1);
+      if (k + 1 >= pend) break;
+      wg_barrier();  // every wave is done reading this buffer and P (reads consumed)
+      if (nn_valid) issue_page_load(page, a, nn_b, nn_k, off, w);
+      nxt_b = nn_b;
+      nxt_k = nn_k;
+      nxt_valid = nn_valid;
+      buf ^= 1;
+      ++k;
+    }
+
+    // ---- piece end: publish 1/l per row, write O (by columns) and LSE ----
+    const bool whole = pbeg == 0 && pend == n;
+    const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
+    const long long slot = whole ? 0 : (long long)ldc(a.split_offsets + b) + sidx;
+    {
+      const float lt = wave_sum_4lanes(l_run);
+      const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
+      if (g == 0) {
+        stat_l[w * 16 + i] = lt;
+        if (whole)
+          a.lse[(long long)b * a.M + row_own] = lse2 * kLn2;
+        else
+          a.part_lse[slot * a.M + row_own] = lse2;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float lt = stat_l[rt * 16 + i];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int row = tile_row0 + rt * 16 + i;
+      if (whole) {
+        uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + w * 128 + 4 * g;
+#pragma unroll
+        for (int dl = 0; dl < DL; ++dl) {
+          const f32x4 v = o[dl][rt] * inv;
+          const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+          *reinterpret_cast<bf16x4*>(op + dl * 16) = bv;
+        }
+      } else {
+        float* op = a.part_o + (slot * a.M + row) * kDV + w * 128 + 4 * g;
+#pragma unroll
+        for (int dl = 0; dl < DL; ++dl) *reinterpret_cast<f32x4*>(op + dl * 16) = o[dl][rt] * inv;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (!nxt_valid) break;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();  // every wave is done with this buffer, P and the statistics
+    load_q(nxt_b);
+    if (nn_valid) issue_page_load(page, a, nn_b, nn_k, off, w);
+    start_piece(nxt_b, nxt_k);
+    cur_b = nxt_b;
+    cur_k = nxt_k;
+    nxt_b = nn_b;
+    nxt_k = nn_k;
+    nxt_valid = nn_valid;
     buf ^= 1;
   }
 }
@@ -663,7 +1005,7 @@ hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream) {
   if (a.M <= 32)
     hipLaunchKernelGGL((mla_splitkv_kernel<1, 2>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((mla_splitkv_kernel<1, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(mla_splitkv_cs_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -700,7 +1042,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const CombineArgs
     for (int s = 0; s < ns; ++s) {
       const long long rowi = (long long)(s0 + s) * a.M + r;
       const float ls = a.part_lse[rowi];
-      const float wgt = ls == -INFINITY ? 0.f : exp2f(ls - mx);
+      const float wgt = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
       tot += wgt;
       const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + rowi * kDV);
 #pragma unroll
