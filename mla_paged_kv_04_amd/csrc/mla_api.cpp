@@ -148,6 +148,7 @@ int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks
   a.causal = causal;
   a.num_parts = num_parts;
   a.row_tiles = row_tiles(s_q, h_q);
+  a.row_tile_rows = mla::tile_rows_for(s_q * h_q);
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mla_decode_splitkv launch");

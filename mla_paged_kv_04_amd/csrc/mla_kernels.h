@@ -46,6 +46,7 @@ struct DecodeArgs {
   int causal;
   int num_parts;
   int row_tiles;
+  int row_tile_rows;          // query rows per workgroup tile (32, 64 or 128)
   float scale_log2;           // scale * log2(e)
 };
 

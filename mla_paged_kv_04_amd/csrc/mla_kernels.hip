@@ -234,7 +234,8 @@ __device__ __forceinline__ int ldc(const int32_t* p) {
 // (see the main loop), and the asm clobbers "memory" so the compiler keeps LDS
 // accesses on the right side of it.  M0 holds the LDS destination; nothing
 // else in this kernel uses M0 (gfx9 LDS instructions do not), and one wait
-// state separates each M0 write from the load that reads it.
+// state separates each M0 write from the load that reads it.  The M0
+// increments are SALU adds, which write SCC: SCC is declared clobbered.
 __device__ __forceinline__ void issue_page_load(char* lds_tile, const DecodeArgs& a, int b,
                                                 int k, const int (&off)[9], int w) {
   const int L = ldc(a.seqlens + b);
@@ -274,7 +275,7 @@ __device__ __forceinline__ void issue_page_load(char* lds_tile, const DecodeArgs
       : [m] "s"(m0), [rl] "s"(r_lo), [rh] "s"(r_hi), [o0] "v"(off[0]), [o1] "v"(off[1]),
         [o2] "v"(off[2]), [o3] "v"(off[3]), [o4] "v"(off[4]), [o5] "v"(off[5]),
         [o6] "v"(off[6]), [o7] "v"(off[7]), [o8] "v"(off[8])
-      : "memory", "m0");
+      : "memory", "m0", "scc");
 #undef MLA_DMA
 #undef MLA_M0_NEXT
 }
@@ -995,15 +996,433 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_cs_kernel(const Decod
   }
 }
 
+// --------------------------------------------------------------------------
+// 128-row tile kernel (s_q*h_q >= 128): one workgroup carries 128 query rows,
+// so every page is read once per part.  Work unit = half a page (32 keys,
+// 36 KB); four half-page LDS buffers keep three units in flight.
+//   scores:  wave w owns query rows 32w..32w+31 (two 16-row tiles), all 32
+//            keys of the unit; each 16-byte K read from LDS feeds 2 MFMAs;
+//   values:  wave w owns output dims 128w..128w+127 for all 128 rows
+//            (8 x 8 tiles of 16x16 = 256 accumulator registers), reading
+//            only its quarter of V.
+// Probabilities (128 rows x 32 keys, bf16), per-row rescale factors and row
+// sums are exchanged through LDS.
+// --------------------------------------------------------------------------
+constexpr int kHalfRows = 32;
+constexpr int kHalfBytes = kHalfRows * kRowBytes;   // 36864
+constexpr int kHalfLoadsPerWave = 9;
+
+// Issue the 9 direct-to-LDS loads of half `h` of page k of request b.  Same
+// contract as issue_page_load (asm, untracked by the compiler, M0 holds the
+// LDS destination; rows at or beyond the sequence end are zero-filled).
+__device__ __forceinline__ void issue_half_load(char* lds_buf, const DecodeArgs& a, int b, int k,
+                                                int h, const int (&off)[9], int w) {
+  const int L = ldc(a.seqlens + b);
+  int rows = L - k * kBlock - h * kHalfRows;
+  rows = rows > kHalfRows ? kHalfRows : rows;
+  int page = -1;
+  if (k < a.bt_stride) page = ldc(a.block_table + (long long)b * a.bt_stride + k);
+  const bool ok = page >= 0 && (long long)page < a.num_blocks && rows > 0;
+  const char* base = reinterpret_cast<const char*>(a.kcache) +
+                     (ok ? (long long)page * kPageBytes + h * kHalfBytes : 0);
+  const int nrec = uni(ok ? rows * kRowBytes : 0);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, kRsrcWord3);
+  const uint32_t m0 = uni(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_buf)) + w * 1024));
+#define MLA_DMA(O) "s_nop 0\n\tbuffer_load_dwordx4 %[" #O "], %[r], 0 offen lds\n\t"
+#define MLA_M0_NEXT "s_add_u32 m0, m0, 0x1000\n\t"
+  asm volatile(
+      "s_mov_b32 m0, %[m]\n\t"
+      MLA_DMA(o0) MLA_M0_NEXT MLA_DMA(o1) MLA_M0_NEXT MLA_DMA(o2) MLA_M0_NEXT
+      MLA_DMA(o3) MLA_M0_NEXT MLA_DMA(o4) MLA_M0_NEXT MLA_DMA(o5) MLA_M0_NEXT
+      MLA_DMA(o6) MLA_M0_NEXT MLA_DMA(o7) MLA_M0_NEXT MLA_DMA(o8)
+      :
+      : [m] "s"(m0), [r] "s"(r), [o0] "v"(off[0]), [o1] "v"(off[1]), [o2] "v"(off[2]),
+        [o3] "v"(off[3]), [o4] "v"(off[4]), [o5] "v"(off[5]), [o6] "v"(off[6]),
+        [o7] "v"(off[7]), [o8] "v"(off[8])
+      : "memory", "m0", "scc");
+#undef MLA_DMA
+#undef MLA_M0_NEXT
+}
+
+// Q for 32 rows (two 16-row tiles): 36 x 16 bytes, waits for its own loads.
+__device__ __forceinline__ void load_q_rows32(bf16x8 (&q)[2][18], const bf16x8* qp0,
+                                              const bf16x8* qp1) {
+#define MLA_QL(D, P, OFF) "global_load_dwordx4 %" #D ", %" #P ", off offset:" #OFF "\n\t"
+  asm volatile(
+      MLA_QL(0, 36, 0) MLA_QL(1, 36, 64) MLA_QL(2, 36, 128) MLA_QL(3, 36, 192)
+      MLA_QL(4, 36, 256) MLA_QL(5, 36, 320) MLA_QL(6, 36, 384) MLA_QL(7, 36, 448)
+      MLA_QL(8, 36, 512) MLA_QL(9, 36, 576) MLA_QL(10, 36, 640) MLA_QL(11, 36, 704)
+      MLA_QL(12, 36, 768) MLA_QL(13, 36, 832) MLA_QL(14, 36, 896) MLA_QL(15, 36, 960)
+      MLA_QL(16, 36, 1024) MLA_QL(17, 36, 1088)
+      MLA_QL(18, 37, 0) MLA_QL(19, 37, 64) MLA_QL(20, 37, 128) MLA_QL(21, 37, 192)
+      MLA_QL(22, 37, 256) MLA_QL(23, 37, 320) MLA_QL(24, 37, 384) MLA_QL(25, 37, 448)
+      MLA_QL(26, 37, 512) MLA_QL(27, 37, 576) MLA_QL(28, 37, 640) MLA_QL(29, 37, 704)
+      MLA_QL(30, 37, 768) MLA_QL(31, 37, 832) MLA_QL(32, 37, 896) MLA_QL(33, 37, 960)
+      MLA_QL(34, 37, 1024) MLA_QL(35, 37, 1088)
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(q[0][0]), "=&v"(q[0][1]), "=&v"(q[0][2]), "=&v"(q[0][3]), "=&v"(q[0][4]),
+        "=&v"(q[0][5]), "=&v"(q[0][6]), "=&v"(q[0][7]), "=&v"(q[0][8]), "=&v"(q[0][9]),
+        "=&v"(q[0][10]), "=&v"(q[0][11]), "=&v"(q[0][12]), "=&v"(q[0][13]), "=&v"(q[0][14]),
+        "=&v"(q[0][15]), "=&v"(q[0][16]), "=&v"(q[0][17]), "=&v"(q[1][0]), "=&v"(q[1][1]),
+        "=&v"(q[1][2]), "=&v"(q[1][3]), "=&v"(q[1][4]), "=&v"(q[1][5]), "=&v"(q[1][6]),
+        "=&v"(q[1][7]), "=&v"(q[1][8]), "=&v"(q[1][9]), "=&v"(q[1][10]), "=&v"(q[1][11]),
+        "=&v"(q[1][12]), "=&v"(q[1][13]), "=&v"(q[1][14]), "=&v"(q[1][15]), "=&v"(q[1][16]),
+        "=&v"(q[1][17])
+      : "v"(qp0), "v"(qp1)
+      : "memory");
+#undef MLA_QL
+}
+
+// Wait until at most 9*ahead direct loads of this wave are outstanding.
+__device__ __forceinline__ void wait_units_ahead(int ahead) {
+  static_assert(kHalfLoadsPerWave == 9, "wait counts below");
+  if (ahead >= 3)
+    asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+  else if (ahead == 2)
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if (ahead == 1)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Unit positions: (request b, page k, half h); the second half of a page is a
+// unit only if the page has keys in it.
+__device__ __forceinline__ void next_unit(const DecodeArgs& a, int& b, int& k, int& h, int b1,
+                                          int k1) {
+  if (h == 0 && ldc(a.seqlens + b) - k * kBlock > kHalfRows) {
+    h = 1;
+    return;
+  }
+  h = 0;
+  ++k;
+  seek(a, b, k, b1, k1);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mla_splitkv_t128_kernel(const DecodeArgs a) {
+  constexpr int NBUF = 4;
+  constexpr int DL = 8;   // output dim tiles per wave (128 dims)
+  constexpr int RTG = 8;  // 16-row tiles in the workgroup tile
+
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kHalfBytes];
+  __shared__ bf16x8 p_lds[RTG][64];   // P^T operands per 16-row tile
+  __shared__ float alpha_lds[128];
+  __shared__ int grow_lds[4];
+  __shared__ float stat_l[128];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int i = lane & 15;
+
+  int part, rtile;
+  const int x = blockIdx.x;
+  const int R = a.row_tiles;
+  if (R > 1 && (a.num_parts % 8) == 0) {
+    part = (x / (8 * R)) * 8 + (x & 7);
+    rtile = (x >> 3) % R;
+  } else {
+    part = x / R;
+    rtile = x % R;
+  }
+  const int32_t* tm = a.tile_meta + part * kMetaInts;
+  const int b0 = ldc(tm + 0), k0 = ldc(tm + 1), b1 = ldc(tm + 2), k1 = ldc(tm + 3);
+  const int first_split = ldc(tm + 4);
+
+  // compute position (unit being computed) and issue position (next to load)
+  int cb = b0, ck = k0, ch = 0;
+  seek(a, cb, ck, b1, k1);
+  if (!before_end(a, cb, ck, b1, k1)) return;  // uniform: empty part
+  int ib = cb, ik = ck, ih = 0;
+
+  const int tile_row0 = rtile * 128;
+  const int own_row0 = tile_row0 + w * 32;   // rows of this wave: own_row0 + 16 rt + i
+
+  int off[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int u = j * kThreads + tid;
+    const int r = u / kChunksPerRow;
+    const int pc = u - r * kChunksPerRow;
+    off[j] = r * kRowBytes + ((pc ^ lds_swizzle(r)) << 4);
+  }
+  const int fi = lds_swizzle(i & 7);
+  const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
+  const int a_off1 = i * kRowBytes + (((4 + g) ^ fi) << 4);
+  const int tr_row = 4 * g + (i >> 2);
+  const int ft = lds_swizzle(tr_row & 7);
+  const int hh = (i & 3) >> 1;
+  int t_off[4];
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4)
+    t_off[d4] = 256 * w + tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
+
+  bf16x8 qreg[2][18];
+  f32x4 o[DL][RTG];
+  float m_run[2], l_run[2];
+  int lim[2];
+  int L = 0, n = 0, pbeg = 0, pend = 0, lim_min = 0;
+
+  auto load_q = [&](int b) {
+    const bf16x8* q0 = reinterpret_cast<const bf16x8*>(
+        a.q + ((long long)b * a.M + own_row0 + i) * kDK + 8 * g);
+    load_q_rows32(qreg, q0, q0 + 16 * kDK / 8);
+  };
+  auto start_piece = [&](int b, int k) {
+    L = ldc(a.seqlens + b);
+    n = n_pages(L);
+    pbeg = k;
+    pend = (b == b1) ? k1 : n;
+    lim_min = a.causal ? L - a.s_q + 1 : L;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int t = (own_row0 + 16 * rt + i) / a.h_q;
+      lim[rt] = a.causal ? L - a.s_q + 1 + t : L;
+      m_run[rt] = -INFINITY;
+      l_run[rt] = 0.f;
+    }
+#pragma unroll
+    for (int dl = 0; dl < DL; ++dl)
+#pragma unroll
+      for (int rt = 0; rt < RTG; ++rt) o[dl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // prologue: unit 0, Q of its piece, then units 1..3
+  int issued = 0;  // units issued so far
+  int u = 0;       // index of the unit being computed
+  issue_half_load(smem, a, ib, ik, ih, off, w);
+  ++issued;
+  next_unit(a, ib, ik, ih, b1, k1);
+  load_q(cb);
+#pragma unroll
+  for (int j = 1; j < NBUF; ++j) {
+    if (before_end(a, ib, ik, b1, k1)) {
+      issue_half_load(smem + j * kHalfBytes, a, ib, ik, ih, off, w);
+      ++issued;
+      next_unit(a, ib, ik, ih, b1, k1);
+    }
+  }
+  start_piece(cb, ck);
+
+  while (true) {
+    const int b = cb;
+    char* ubuf;
+    bool more;     // another unit follows in the part
+    bool same;     // ... and it belongs to this piece
+    while (true) {
+      wait_units_ahead(issued - u - 1);
+      wg_barrier();
+      ubuf = smem + (u % NBUF) * kHalfBytes;
+      const int k = ck, h = ch;
+
+      // ---- scores S^T[key][row], 32 keys x this wave's 32 rows ----
+      f32x4 s[2][2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        constexpr int D1 = 2;
+        bf16x8 ka[D1 + 1][2];
+#pragma unroll
+        for (int ks = 0; ks < 18 + D1; ++ks) {
+          if (ks < 18) {
+            const char* ab = ubuf + ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+              ka[ks % (D1 + 1)][kt] = *reinterpret_cast<const bf16x8*>(ab + kt * 16 * kRowBytes);
+          }
+          const int cs = ks - D1;
+          if (cs >= 0) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt)
+                s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    ka[cs % (D1 + 1)][kt], qreg[rt][cs], s[rt][kt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- online softmax of this wave's rows ----
+      {
+        const int key0 = k * kBlock + h * kHalfRows + 4 * g;
+        const bool need_mask = k * kBlock + (h + 1) * kHalfRows > lim_min;
+        int any = 0;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float xv = s[rt][kt][v] * a.scale_log2;
+              if (need_mask && key0 + kt * 16 + v >= lim[rt]) xv = -INFINITY;
+              s[rt][kt][v] = xv;
+              mx = fmaxf(mx, xv);
+            }
+          mx = wave_max_4lanes(mx);
+          const float m_new = fmaxf(m_run[rt], mx);
+          // Keep the running max unless it grew by more than kRescaleSlack
+          // (exact either way: numerator and denominator share it).
+          const bool grow = m_new > m_run[rt] + kRescaleSlack;
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[rt] - m_new) : 1.f;
+          if (grow) m_run[rt] = m_new;
+          l_run[rt] *= alpha;
+          any |= __any(grow) ? 1 : 0;
+          const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
+          float lsum = 0.f;
+          bf16x8 pb;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float p = __builtin_amdgcn_exp2f(s[rt][kt][v] - m_use);
+              lsum += p;
+              pb[kt * 4 + v] = (__bf16)p;
+            }
+          l_run[rt] += lsum;
+          p_lds[2 * w + rt][lane] = pb;
+          if (g == 0) alpha_lds[32 * w + 16 * rt + i] = alpha;
+        }
+        if (lane == 0) grow_lds[w] = any;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P, alpha, flags written
+      wg_barrier();
+
+      // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all 128 rows ----
+      {
+        if (grow_lds[0] | grow_lds[1] | grow_lds[2] | grow_lds[3]) {
+#pragma unroll
+          for (int rt = 0; rt < RTG; ++rt) {
+            const float al = alpha_lds[16 * rt + i];
+#pragma unroll
+            for (int dl = 0; dl < DL; ++dl) o[dl][rt] *= al;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        bf16x8 va[DL];
+#pragma unroll
+        for (int dl = 0; dl < DL; ++dl) {
+          const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
+          const bf16x4 lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
+          const bf16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
+          va[dl] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 pB[2];
+        pB[0] = p_lds[0][lane];
+#pragma unroll
+        for (int rt = 0; rt < RTG; ++rt) {
+          if (rt + 1 < RTG) pB[(rt + 1) & 1] = p_lds[rt + 1][lane];
+#pragma unroll
+          for (int dl = 0; dl < DL; ++dl)
+            o[dl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pB[rt & 1], o[dl][rt],
+                                                               0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // next unit to compute
+      int nb = cb, nk = ck, nh = ch;
+      next_unit(a, nb, nk, nh, b1, k1);
+      more = before_end(a, nb, nk, b1, k1);
+      same = more && nb == cb;
+      if (!same) break;
+      // release this buffer and refill it with the unit NBUF ahead
+      wg_barrier();  // every wave is done reading this buffer and P
+      if (before_end(a, ib, ik, b1, k1)) {
+        issue_half_load(ubuf, a, ib, ik, ih, off, w);
+        ++issued;
+        next_unit(a, ib, ik, ih, b1, k1);
+      }
+      cb = nb;
+      ck = nk;
+      ch = nh;
+      ++u;
+    }
+
+    // ---- piece end: publish row sums, write LSE (row owners) and O (columns) ----
+    const bool whole = pbeg == 0 && pend == n;
+    const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
+    const long long slot = whole ? 0 : (long long)ldc(a.split_offsets + b) + sidx;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const float lt = wave_sum_4lanes(l_run[rt]);
+      const float lse2 = lt > 0.f ? m_run[rt] + log2f(lt) : -INFINITY;
+      const int row = own_row0 + 16 * rt + i;
+      if (g == 0) {
+        stat_l[32 * w + 16 * rt + i] = lt;
+        if (whole)
+          a.lse[(long long)b * a.M + row] = lse2 * kLn2;
+        else
+          a.part_lse[slot * a.M + row] = lse2;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();
+#pragma unroll
+    for (int rt = 0; rt < RTG; ++rt) {
+      const float lt = stat_l[16 * rt + i];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int row = tile_row0 + 16 * rt + i;
+      if (whole) {
+        uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + w * 128 + 4 * g;
+#pragma unroll
+        for (int dl = 0; dl < DL; ++dl) {
+          const f32x4 v = o[dl][rt] * inv;
+          const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+          *reinterpret_cast<bf16x4*>(op + dl * 16) = bv;
+        }
+      } else {
+        float* op = a.part_o + (slot * a.M + row) * kDV + w * 128 + 4 * g;
+#pragma unroll
+        for (int dl = 0; dl < DL; ++dl) *reinterpret_cast<f32x4*>(op + dl * 16) = o[dl][rt] * inv;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (!more) break;
+    // Next piece: Q rows (the load waits for everything in flight), then the
+    // refill of the buffer just computed.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();  // every wave is done with the buffer, P and the statistics
+    int nb = cb, nk = ck, nh = ch;
+    next_unit(a, nb, nk, nh, b1, k1);
+    load_q(nb);
+    if (before_end(a, ib, ik, b1, k1)) {
+      issue_half_load(ubuf, a, ib, ik, ih, off, w);
+      ++issued;
+      next_unit(a, ib, ik, ih, b1, k1);
+    }
+    start_piece(nb, nk);
+    cb = nb;
+    ck = nk;
+    ch = nh;
+    ++u;
+  }
+}
+
+// Rows per workgroup tile.  The 128-row kernel reads each page once per
+// part but does not fit the register file without spilling yet, so the
+// 64-row column-split kernel serves s_q*h_q >= 64.
 int tile_rows_for(int M) {
-  if (M <= 32) return 32;    // RT=1, KG=2
-  return 64;                 // RT=1, KG=1 (M = 128, 256 use 2 or 4 row tiles)
+  if (M <= 32) return 32;    // mla_splitkv_kernel<1, 2>
+  return 64;                 // mla_splitkv_cs_kernel (M = 128, 256: 2 or 4 row tiles)
 }
 
 hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_parts * a.row_tiles), block(kThreads);
   if (a.M <= 32)
     hipLaunchKernelGGL((mla_splitkv_kernel<1, 2>), grid, block, 0, stream, a);
+  else if (a.row_tile_rows == 128)
+    hipLaunchKernelGGL(mla_splitkv_t128_kernel, grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL(mla_splitkv_cs_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
