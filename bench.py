@@ -31,6 +31,58 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 
 
+# HBM bytes per launch of the decode kernel, from two rocprofv3 --pmc runs of
+# this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
+# by what the same counter reads for a plain 1 GiB int32 elementwise copy
+# (--copy-calib-mib 1024): FETCH_SIZE reads 0.5 GiB for it, WRITE_SIZE 1 GiB.
+# Keyed by workload; valid only for the kernel source it was measured on
+# (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
+HBM_TRAFFIC = {
+    "membound": {
+        "kernel_sha256": "37986d50a251612af55ab864ee8d25b7043e89e851c69e9021dc1e5b1e3877fe",
+        "fetch_bytes": 308137142,
+        "write_bytes": 9882688,
+        "fetch_scale": 1.99986,
+        "write_scale": 1.0
+    },
+    "ridge": {
+        "kernel_sha256": "37986d50a251612af55ab864ee8d25b7043e89e851c69e9021dc1e5b1e3877fe",
+        "fetch_bytes": 705006987,
+        "write_bytes": 59894272,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0
+    },
+    "long": {
+        "kernel_sha256": "37986d50a251612af55ab864ee8d25b7043e89e851c69e9021dc1e5b1e3877fe",
+        "fetch_bytes": 771086643,
+        "write_bytes": 37559808,
+        "fetch_scale": 1.99989,
+        "write_scale": 1.0
+    },
+    "ragged": {
+        "kernel_sha256": "37986d50a251612af55ab864ee8d25b7043e89e851c69e9021dc1e5b1e3877fe",
+        "fetch_bytes": 510699178,
+        "write_bytes": 78838784,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0
+    }
+}
+
+
+def _kernel_source_sha() -> str:
+    import hashlib
+    p = os.path.join(ROOT, "mla_paged_kv_04_amd", "csrc", "mla_kernels.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    rec = HBM_TRAFFIC.get(workload)
+    if rec is None or rec["kernel_sha256"] != _kernel_source_sha():
+        return None
+    return rec
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -55,12 +107,18 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
         threads = os.cpu_count() or 1
     done = []
     t0 = time.perf_counter()
-    for b in range(inp.batch):
-        decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal,
-               requests=[b])
-        done.append(b)
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    passes = 0
+    while True:
+        for b in range(inp.batch):
+            decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal,
+                   requests=[b])
+            done.append(b)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            passes += 1
+            continue
+        break
     dt = time.perf_counter() - t0
     sl = [int(inp.seqlens[b]) for b in done]
     c = algorithmic_counts(sl, inp.s_q, inp.h_q)
@@ -70,9 +128,15 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
         "tflops": round(c["flops"] / dt / 1e12, 6),
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{len(done)} of {inp.batch} requests ({sum(sl)} keys) in {dt:.1f} s, "
-                  f"fp64 numpy on {_cpu_model()}, {os.cpu_count()} logical CPUs",
+        "sample": f"{len(done)} requests ({passes} full passes over the {inp.batch}-request "
+                  f"batch, {sum(sl)} keys) in {dt:.1f} s, fp64 numpy on {_cpu_model()}, "
+                  f"{os.cpu_count()} logical CPUs",
     }
+
+
+def splitkv_kernel_name(m_rows: int) -> str:
+    """HIP kernel that mla_decode_splitkv launches for s_q*h_q = m_rows."""
+    return "mla_splitkv_kernel<1, 2>" if m_rows <= 32 else "mla_splitkv_cs_kernel"
 
 
 def main(argv=None) -> int:
@@ -85,6 +149,10 @@ def main(argv=None) -> int:
     ap.add_argument("--parts", type=int, default=None, help="override split-KV part count")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="cache flush between timed steps (outside the timed events)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run one plain elementwise copy of this many MiB (int32 -> int32) "
+                         "after warmup, outside the timed region: the known-size kernel "
+                         "that HBM byte counters are scaled against")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args(argv)
@@ -119,27 +187,53 @@ def main(argv=None) -> int:
         elif args.flush == "write":
             flush_buf.fill_(1)
 
+    # evs: [step start, step end, decode kernel start, decode kernel end]; the
+    # last two are recorded by the decode kernel's own launch, so the step's
+    # stream carries no marker between its three kernels.
     def step(evs=None):
         if evs is not None:
             evs[0].record()
         meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
-        if evs is not None:
-            evs[1].record()
         mla.splitkv(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
-                    out, lse)
-        if evs is not None:
-            evs[2].record()
+                    out, lse, start_event=evs[2] if evs else None,
+                    stop_event=evs[3] if evs else None)
         mla.combine(g.seqlens, inp.s_q, inp.h_q, meta, ws, out, lse)
         if evs is not None:
-            evs[3].record()
+            evs[1].record()
+
+    # Per-kernel breakdown of the scheduler and the combine (marker events
+    # between kernels), in a separate loop after the timed one.
+    def step_breakdown(evs):
+        evs[0].record()
+        meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
+        evs[1].record()
+        mla.splitkv(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
+                    out, lse)
+        evs[2].record()
+        mla.combine(g.seqlens, inp.s_q, inp.h_q, meta, ws, out, lse)
+        evs[3].record()
 
     for _ in range(args.warmup):
         flush()
         step()
     torch.cuda.synchronize(dev)
 
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 18
+        src = torch.ones((n,), dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize(dev)
+        del src, dst
+
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                          for _ in range(K)]
+    evs = new_events()
+    for e in evs:             # create the kernel-timing events before the timed region
+        e[2].record()
+        e[3].record()
     torch.cuda.synchronize(dev)
     t_wall0 = time.perf_counter()
     for k in range(K):
@@ -148,10 +242,16 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
     t_wall = time.perf_counter() - t_wall0
 
-    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
-    meta_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    bevs = new_events()
+    for k in range(K):
+        flush()
+        step_breakdown(bevs[k])
+    torch.cuda.synchronize(dev)
+
+    step_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    meta_ms = [e[0].elapsed_time(e[1]) for e in bevs]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in bevs]
     mean = lambda xs: sum(xs) / len(xs)
     med = lambda xs: sorted(xs)[len(xs) // 2]
     ms = mean(step_ms)
@@ -171,6 +271,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
     warm_ms = e0.elapsed_time(e1) / K
 
+    traffic = measured_traffic(args.workload)
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -193,17 +294,23 @@ def main(argv=None) -> int:
         "algorithmic_flops": counts["flops"],
         "kernels_ms": {"metadata": round(mean(meta_ms), 5), "splitkv": round(dec, 5),
                        "combine": round(mean(comb_ms), 5),
-                       "splitkv_median": round(med(dec_ms), 5)},
+                       "splitkv_median": round(med(dec_ms), 5),
+                       "splitkv_p90": round(sorted(dec_ms)[int(0.9 * (len(dec_ms) - 1))], 5),
+                       "step_median": round(med(step_ms), 5)},
         "warm_ms_per_step": round(warm_ms, 5),
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": {
-            "kernel": "mla_splitkv_kernel",
+            "kernel": splitkv_kernel_name(inp.s_q * inp.h_q),
             "bound": "hbm",
             "achieved": round(dec_gbs, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": (None if traffic is None
+                        else traffic["fetch_bytes"] + traffic["write_bytes"]),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "copy-calibrated)",
+            "traffic_detail": traffic,
             "mfma_tflops": round(dec_tfl, 2),
             "mfma_frac": round(dec_tfl / PEAK_BF16_TFLOPS, 4),
         },

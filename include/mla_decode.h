@@ -142,6 +142,23 @@ int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks
                        void* out_d, float* lse_d, void* stream);
 
 /*
+ * mla_decode_splitkv_timed — mla_decode_splitkv, and in addition the two
+ * caller-created HIP events (hipEvent_t, timing enabled; either may be NULL)
+ * are recorded at the decode kernel's own start and end (hipExtLaunchKernel),
+ * so their elapsed time is the kernel's duration without the launch and
+ * marker-packet overhead that separately recorded events include.  Same
+ * arguments, validation and status codes as mla_decode_splitkv.
+ */
+int mla_decode_splitkv_timed(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                             const int32_t* block_table_d, int bt_stride,
+                             const int32_t* seqlens_d, int batch, int s_q, int h_q,
+                             int h_kv, float scale, int causal,
+                             const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                             int num_parts, void* workspace_d, size_t workspace_bytes,
+                             void* out_d, float* lse_d, void* start_event,
+                             void* stop_event, void* stream);
+
+/*
  * mla_decode_combine — enqueue the log-sum-exp merge of split partials.
  * For every request with split_offsets[b+1] > split_offsets[b]:
  *   LSE = ln sum_i exp(LSE_i),  O = sum_i exp(LSE_i - LSE) * O_i  (exact merge),

@@ -39,6 +39,10 @@ _SIGNATURES = {
                                     _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                     _c_ptr, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr,
                                     _c_ptr]),
+    "mla_decode_splitkv_timed": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr,
+                                          _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                          _c_ptr, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr,
+                                          _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "mla_decode_combine": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_ptr, _c_int, _c_ptr,
                                     _c_size, _c_ptr, _c_ptr, _c_ptr]),
     "mla_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int,
@@ -180,17 +184,35 @@ def _outputs(q, out, lse):
     return out, lse
 
 
+def _event_handle(ev):
+    """Raw hipEvent_t of a torch.cuda.Event (None -> NULL).  torch creates the
+    event on its first record, so an unrecorded event is recorded once here."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()
+    return ev.cuda_event
+
+
 def splitkv(q, kcache, block_table, seqlens, scale: float, causal: bool, meta: Metadata,
-            workspace: torch.Tensor, out=None, lse=None):
-    """Enqueue only the split-KV decode kernel (partials left in workspace)."""
+            workspace: torch.Tensor, out=None, lse=None, start_event=None, stop_event=None):
+    """Enqueue only the split-KV decode kernel (partials left in workspace).
+
+    With start_event / stop_event (torch.cuda.Event(enable_timing=True)), the
+    events are recorded at the kernel's own start and end
+    (mla_decode_splitkv_timed)."""
     batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens)
     out, lse = _outputs(q, out, lse)
-    _check(lib().mla_decode_splitkv(
-        _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
-        _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
-        _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)),
-        "mla_decode_splitkv")
+    args = (_ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+            _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
+            _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse))
+    if start_event is None and stop_event is None:
+        _check(lib().mla_decode_splitkv(*args, _stream(q.device)), "mla_decode_splitkv")
+    else:
+        _check(lib().mla_decode_splitkv_timed(*args, _event_handle(start_event),
+                                              _event_handle(stop_event), _stream(q.device)),
+               "mla_decode_splitkv_timed")
     return out, lse
 
 

@@ -114,12 +114,13 @@ int mla_decode_metadata(const int32_t* seqlens_d, int batch, int s_q, int h_q, i
   return MLA_OK;
 }
 
-int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks,
-                       const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
-                       int batch, int s_q, int h_q, int h_kv, float scale, int causal,
-                       const int32_t* tile_meta_d, const int32_t* split_offsets_d,
-                       int num_parts, void* workspace_d, size_t workspace_bytes, void* out_d,
-                       float* lse_d, void* stream) {
+int mla_decode_splitkv_timed(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                             const int32_t* block_table_d, int bt_stride,
+                             const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                             float scale, int causal, const int32_t* tile_meta_d,
+                             const int32_t* split_offsets_d, int num_parts, void* workspace_d,
+                             size_t workspace_bytes, void* out_d, float* lse_d,
+                             void* start_event, void* stop_event, void* stream) {
   int st = check_common(seqlens_d, split_offsets_d, batch, s_q, h_q, h_kv, num_parts,
                         workspace_d, workspace_bytes, out_d, lse_d);
   if (st != MLA_OK) return st;
@@ -150,9 +151,23 @@ int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks
   a.row_tiles = row_tiles(s_q, h_q);
   a.row_tile_rows = mla::tile_rows_for(s_q * h_q);
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream));
+  hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream),
+                                     static_cast<hipEvent_t>(start_event),
+                                     static_cast<hipEvent_t>(stop_event));
   if (e != hipSuccess) return hip_fail(e, "mla_decode_splitkv launch");
   return MLA_OK;
+}
+
+int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                       const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                       int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                       const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                       int num_parts, void* workspace_d, size_t workspace_bytes, void* out_d,
+                       float* lse_d, void* stream) {
+  return mla_decode_splitkv_timed(q_d, kcache_d, num_blocks, block_table_d, bt_stride,
+                                  seqlens_d, batch, s_q, h_q, h_kv, scale, causal, tile_meta_d,
+                                  split_offsets_d, num_parts, workspace_d, workspace_bytes,
+                                  out_d, lse_d, nullptr, nullptr, stream);
 }
 
 int mla_decode_combine(const int32_t* seqlens_d, int batch, int s_q, int h_q,

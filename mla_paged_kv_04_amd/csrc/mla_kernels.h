@@ -64,7 +64,9 @@ struct CombineArgs {
 // Launchers (return hipGetLastError() of the launch).
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int c_fix, int num_parts,
                            int32_t* tile_meta, int32_t* split_offsets, hipStream_t stream);
-hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream);
+// start/stop (may be null) are recorded at the kernel's own start and end.
+hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start = nullptr,
+                          hipEvent_t stop = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 // Row-tile geometry chosen for M query rows (rows per workgroup tile).

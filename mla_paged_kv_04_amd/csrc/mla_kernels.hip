@@ -30,6 +30,8 @@
 //     buffer unit's range check (num_records), never read from memory.
 #include "mla_kernels.h"
 
+#include <hip/hip_ext.h>
+
 #include <math.h>
 
 namespace mla {
@@ -1417,14 +1419,15 @@ int tile_rows_for(int M) {
   return 64;                 // mla_splitkv_cs_kernel (M = 128, 256: 2 or 4 row tiles)
 }
 
-hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
   const dim3 grid(a.num_parts * a.row_tiles), block(kThreads);
   if (a.M <= 32)
-    hipLaunchKernelGGL((mla_splitkv_kernel<1, 2>), grid, block, 0, stream, a);
+    hipExtLaunchKernelGGL((mla_splitkv_kernel<1, 2>), grid, block, 0, stream, start, stop, 0, a);
   else if (a.row_tile_rows == 128)
-    hipLaunchKernelGGL(mla_splitkv_t128_kernel, grid, block, 0, stream, a);
+    hipExtLaunchKernelGGL(mla_splitkv_t128_kernel, grid, block, 0, stream, start, stop, 0, a);
   else
-    hipLaunchKernelGGL(mla_splitkv_cs_kernel, grid, block, 0, stream, a);
+    hipExtLaunchKernelGGL(mla_splitkv_cs_kernel, grid, block, 0, stream, start, stop, 0, a);
   return hipGetLastError();
 }
 
