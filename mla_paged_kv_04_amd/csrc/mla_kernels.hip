@@ -49,13 +49,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;           // lazy-rescale threshold (log2)
 
 // 16-byte unit swizzle of LDS row r: unit c is stored at c ^ lds_swizzle(r).
-// A bijection on r mod 8 (conflict-free 8-row column reads) whose upper two
-// bits also differ over any 4 consecutive rows (conflict-free transposed
-// reads of 4 rows x 32 bytes).  XOR stays inside an aligned group of 8 units,
-// and 72 units per row is a multiple of 8.
-__device__ __forceinline__ int lds_swizzle(int r) {
-  return ((r & 3) << 1) | ((r >> 2) & 1);
-}
+// Chosen by measurement on gfx950 among XOR and rotation swizzles of the low
+// three unit bits: with r & 7 both read patterns of the kernels run at the
+// conflict-free rate — 16 consecutive rows at one unit (ds_read_b128, score
+// operand: 4.9 clk per wave instruction per CU, against 8.1-8.6 for the other
+// 8-row bijections tried and 16.1 unswizzled) and 4 rows x 32 bytes per
+// 16-lane group (ds_read_b64_tr_b16, value operand: 3.3 clk, against 4.6-8.1).
+// XOR stays inside an aligned group of 8 units; 72 units per row is a
+// multiple of 8.
+__device__ __forceinline__ int lds_swizzle(int r) { return r & 7; }
 
 __device__ __forceinline__ float wave_max_4lanes(float x) {
   // max over lanes {i, i^16, i^32, i^48}: the four lanes holding one query row
