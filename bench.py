@@ -136,7 +136,7 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
 
 def splitkv_kernel_name(m_rows: int) -> str:
     """HIP kernel that mla_decode_splitkv launches for s_q*h_q = m_rows."""
-    return "mla_splitkv_kernel<1, 2>" if m_rows <= 32 else "mla_splitkv_cs_kernel"
+    return "mla_splitkv_kernel<1, 2>" if m_rows <= 32 else "mla_splitkv_ws_kernel"
 
 
 def main(argv=None) -> int:

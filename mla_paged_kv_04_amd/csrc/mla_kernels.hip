@@ -700,327 +700,35 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
 }
 
 // --------------------------------------------------------------------------
-// Column-split variant for row tiles of 64 query rows (s_q*h_q >= 64).
-//   scores:  row split    — wave w owns query rows 16w..16w+15, all 64 keys;
-//   values:  column split — wave w owns output dims 128w..128w+127 for all 64
-//            rows, so it reads only its quarter of V from LDS (the transposed
-//            reads run at half the LDS rate of 16-byte reads; reading all of
-//            V in every wave made the row-split kernel LDS-bound).
-// The bf16 probabilities (64 rows x 64 keys) go through LDS in exactly the
-// B-operand order of the value MFMA, so they are written and read as
-// contiguous 16-byte per-lane accesses.  Row statistics (running max m, sum
-// l) stay with the row-owning wave; the per-row rescale factors and the
-// final 1/l are published through LDS.
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 1) void mla_splitkv_cs_kernel(const DecodeArgs a) {
-  constexpr int KT = 4;   // 16-key score tiles (all 64 keys)
-  constexpr int KP = 2;   // 32-key reduction steps of the value product
-  constexpr int DL = 8;   // 16-dim output tiles per wave (128 dims)
-
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes];
-  __shared__ bf16x8 p_lds[4][KP][64];      // P^T operands, [row tile][kp][lane]
-  __shared__ float alpha_lds[64];          // per-row rescale factor of this page
-  __shared__ int grow_lds[4];              // per row tile: any row rescaled
-  __shared__ float stat_l[64];             // per-row sum at piece end
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int g = lane >> 4;
-  const int i = lane & 15;
-
-  int part, rtile;
-  const int x = blockIdx.x;
-  const int R = a.row_tiles;
-  if (R > 1 && (a.num_parts % 8) == 0) {
-    part = (x / (8 * R)) * 8 + (x & 7);
-    rtile = (x >> 3) % R;
-  } else {
-    part = x / R;
-    rtile = x % R;
-  }
-  const int32_t* tm = a.tile_meta + part * kMetaInts;
-  const int b0 = ldc(tm + 0), k0 = ldc(tm + 1), b1 = ldc(tm + 2), k1 = ldc(tm + 3);
-  const int first_split = ldc(tm + 4);
-
-  int cur_b = b0, cur_k = k0;
-  seek(a, cur_b, cur_k, b1, k1);
-  if (!before_end(a, cur_b, cur_k, b1, k1)) return;  // uniform: empty part
-
-  const int tile_row0 = rtile * 64;       // first query row of the tile
-  const int row_own = tile_row0 + w * 16 + i;  // score/softmax row of this lane
-
-  int off[9];
-#pragma unroll
-  for (int j = 0; j < 9; ++j) {
-    const int u = j * kThreads + tid;
-    const int r = u / kChunksPerRow;
-    const int pc = u - r * kChunksPerRow;
-    off[j] = r * kRowBytes + ((pc ^ lds_swizzle(r)) << 4);
-  }
-  const int fi = lds_swizzle(i & 7);
-  const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
-  const int a_off1 = i * kRowBytes + (((4 + g) ^ fi) << 4);
-  const int tr_row = 4 * g + (i >> 2);
-  const int ft = lds_swizzle(tr_row & 7);
-  const int hh = (i & 3) >> 1;
-  int t_off[4];
-#pragma unroll
-  for (int d4 = 0; d4 < 4; ++d4)
-    t_off[d4] = tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
-  // this wave's dims start at dim tile 8w: byte offset 128 * (8w >> 2) = 256 w
-  const int t_base = 256 * w;
-
-  bf16x8 qreg[18];
-  f32x4 o[DL][4];          // O^T tiles: [dim tile of this wave][row tile]
-  float m_run, l_run;      // statistics of row_own
-  int lim;
-  int L = 0, n = 0, pend = 0, lim_min = 0, pbeg = 0;
-
-  auto load_q = [&](int b) {
-    load_q_rows(qreg, reinterpret_cast<const bf16x8*>(
-                          a.q + ((long long)b * a.M + row_own) * kDK + 8 * g));
-  };
-  auto start_piece = [&](int b, int k) {
-    L = ldc(a.seqlens + b);
-    n = n_pages(L);
-    pbeg = k;
-    pend = (b == b1) ? k1 : n;
-    lim_min = a.causal ? L - a.s_q + 1 : L;
-    const int t = row_own / a.h_q;
-    lim = a.causal ? L - a.s_q + 1 + t : L;
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int dl = 0; dl < DL; ++dl)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) o[dl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-
-  issue_page_load(smem, a, cur_b, cur_k, off, w);
-  load_q(cur_b);
-  int nxt_b = cur_b, nxt_k = cur_k + 1;
-  seek(a, nxt_b, nxt_k, b1, k1);
-  bool nxt_valid = before_end(a, nxt_b, nxt_k, b1, k1);
-  if (nxt_valid) issue_page_load(smem + kPageBytes, a, nxt_b, nxt_k, off, w);
-  start_piece(cur_b, cur_k);
-  int buf = 0;
-
-  while (true) {
-    const int b = cur_b;
-    int k = cur_k;
-    int nn_b = 0, nn_k = 0;
-    bool nn_valid = false;
-    char* page;
-    while (true) {
-      static_assert(kPageLoadsPerWave == 18, "wait count below");
-      if (nxt_valid)
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      wg_barrier();
-      page = smem + buf * kPageBytes;
-
-      // ---- scores S^T[key][row] = K . Q^T for this wave's 16 rows ----
-      f32x4 s[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      {
-        constexpr int D1 = 2;
-        bf16x8 ka[D1 + 1][KT];
-#pragma unroll
-        for (int ks = 0; ks < 18 + D1; ++ks) {
-          if (ks < 18) {
-            const char* ab = page + ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-              ka[ks % (D1 + 1)][kt] = *reinterpret_cast<const bf16x8*>(ab + kt * 16 * kRowBytes);
-          }
-          const int cs = ks - D1;
-          if (cs >= 0) {
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-              s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[cs % (D1 + 1)][kt], qreg[cs],
-                                                             s[kt], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      // ---- online softmax of row_own (fp32, base 2, lazy rescale) ----
-      {
-        const int key0 = k * kBlock + 4 * g;
-        const bool need_mask = (k + 1) * kBlock > lim_min;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float xv = s[kt][v] * a.scale_log2;
-            if (need_mask && key0 + kt * 16 + v >= lim) xv = -INFINITY;
-            s[kt][v] = xv;
-            mx = fmaxf(mx, xv);
-          }
-        mx = wave_max_4lanes(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const bool grow = m_new > m_run + kRescaleSlack;
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        if (grow) m_run = m_new;
-        l_run *= alpha;
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float lsum = 0.f;
-        bf16x8 pb[KP];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float p = __builtin_amdgcn_exp2f(s[kt][v] - m_use);
-            lsum += p;
-            pb[kt >> 1][(kt & 1) * 4 + v] = (__bf16)p;
-          }
-        l_run += lsum;
-#pragma unroll
-        for (int kp = 0; kp < KP; ++kp) p_lds[w][kp][lane] = pb[kp];
-        if (g == 0) alpha_lds[w * 16 + i] = alpha;
-        const int any = __any(grow) ? 1 : 0;
-        if (lane == 0) grow_lds[w] = any;
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P, alpha, flags written
-      wg_barrier();
-
-      // ---- O^T[dim][row] += V^T . P^T, this wave's 128 dims, all 64 rows ----
-      {
-        if (grow_lds[0] | grow_lds[1] | grow_lds[2] | grow_lds[3]) {
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            const float al = alpha_lds[rt * 16 + i];
-#pragma unroll
-            for (int dl = 0; dl < DL; ++dl) o[dl][rt] *= al;
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        bf16x8 pB[4][KP];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int kp = 0; kp < KP; ++kp) pB[rt][kp] = p_lds[rt][kp][lane];
-        constexpr int D2 = 1;
-        bf16x8 va[D2 + 1][KP];
-#pragma unroll
-        for (int dl = 0; dl < DL + D2; ++dl) {
-          if (dl < DL) {
-            const char* tb = page + t_base + t_off[dl & 3] + 128 * (dl >> 2);
-#pragma unroll
-            for (int kp = 0; kp < KP; ++kp) {
-              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                  (MLA_LDS bf16x4*)(tb + (kp * 32) * kRowBytes));
-              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                  (MLA_LDS bf16x4*)(tb + (kp * 32 + 16) * kRowBytes));
-              va[dl % (D2 + 1)][kp] =
-                  bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-          }
-          const int cd = dl - D2;
-          if (cd >= 0) {
-#pragma unroll
-            for (int kp = 0; kp < KP; ++kp)
-#pragma unroll
-              for (int rt = 0; rt < 4; ++rt)
-                o[cd][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    va[cd % (D2 + 1)][kp], pB[rt][kp], o[cd][rt], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      nn_b = nxt_b;
-      nn_k = nxt_k + 1;
-      if (nxt_valid) seek(a, nn_b, nn_k, b1, k1);
-      nn_valid = nxt_valid && before_end(a, nn_b, nn_k, b1, k1);
-      if (k + 1 >= pend) break;
-      wg_barrier();  // every wave is done reading this buffer and P (reads consumed)
-      if (nn_valid) issue_page_load(page, a, nn_b, nn_k, off, w);
-      nxt_b = nn_b;
-      nxt_k = nn_k;
-      nxt_valid = nn_valid;
-      buf ^= 1;
-      ++k;
-    }
-
-    // ---- piece end: publish 1/l per row, write O (by columns) and LSE ----
-    const bool whole = pbeg == 0 && pend == n;
-    const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
-    const long long slot = whole ? 0 : (long long)ldc(a.split_offsets + b) + sidx;
-    {
-      const float lt = wave_sum_4lanes(l_run);
-      const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
-      if (g == 0) {
-        stat_l[w * 16 + i] = lt;
-        if (whole)
-          a.lse[(long long)b * a.M + row_own] = lse2 * kLn2;
-        else
-          a.part_lse[slot * a.M + row_own] = lse2;
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wg_barrier();
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float lt = stat_l[rt * 16 + i];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int row = tile_row0 + rt * 16 + i;
-      if (whole) {
-        uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + w * 128 + 4 * g;
-#pragma unroll
-        for (int dl = 0; dl < DL; ++dl) {
-          const f32x4 v = o[dl][rt] * inv;
-          const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-          *reinterpret_cast<bf16x4*>(op + dl * 16) = bv;
-        }
-      } else {
-        float* op = a.part_o + (slot * a.M + row) * kDV + w * 128 + 4 * g;
-#pragma unroll
-        for (int dl = 0; dl < DL; ++dl) *reinterpret_cast<f32x4*>(op + dl * 16) = o[dl][rt] * inv;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    if (!nxt_valid) break;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wg_barrier();  // every wave is done with this buffer, P and the statistics
-    load_q(nxt_b);
-    if (nn_valid) issue_page_load(page, a, nn_b, nn_k, off, w);
-    start_piece(nxt_b, nxt_k);
-    cur_b = nxt_b;
-    cur_k = nxt_k;
-    nxt_b = nn_b;
-    nxt_k = nn_k;
-    nxt_valid = nn_valid;
-    buf ^= 1;
-  }
-}
-
-// --------------------------------------------------------------------------
-// 128-row tile kernel (s_q*h_q >= 128): one workgroup carries 128 query rows,
-// so every page is read once per part.  Work unit = half a page (32 keys,
-// 36 KB); four half-page LDS buffers keep three units in flight.
-//   scores:  wave w owns query rows 32w..32w+31 (two 16-row tiles), all 32
-//            keys of the unit; each 16-byte K read from LDS feeds 2 MFMAs;
-//   values:  wave w owns output dims 128w..128w+127 for all 128 rows
-//            (8 x 8 tiles of 16x16 = 256 accumulator registers), reading
-//            only its quarter of V.
-// Probabilities (128 rows x 32 keys, bf16), per-row rescale factors and row
-// sums are exchanged through LDS.
+// Warp-specialised kernel for row tiles of 64 query rows (s_q*h_q >= 64).
+// Eight waves, two per SIMD, in two roles that work one unit apart so that
+// each SIMD always holds one wave of each and their matrix products, LDS
+// reads and softmax interleave:
+//   score waves 0..3:  rows 16q .. 16q+15 of the tile (q = w), all 32 keys
+//                      of unit t: S^T = K . Q^T, online softmax (exact row
+//                      max over the unit, lazy rescale), bf16 P to LDS;
+//   value waves 4..7:  output dims 128j .. 128j+127 (j = w - 4) for all 64
+//                      rows: O^T += V^T . P^T of unit t-1, and every direct
+//                      page load, so no score wave ever waits on a load
+//                      queue it did not fill.
+// Work unit = half a page (32 keys, 36 KB) in a ring of four LDS buffers:
+// while unit t is scored and unit t-1 multiplied, unit t+1 lands and unit
+// t+2 is loading.  One workgroup barrier per unit.  Probabilities, rescale
+// factors and final row sums are double-buffered by unit parity.
 // --------------------------------------------------------------------------
 constexpr int kHalfRows = 32;
 constexpr int kHalfBytes = kHalfRows * kRowBytes;   // 36864
-constexpr int kHalfLoadsPerWave = 9;
+constexpr int kThreadsWS = 512;
+constexpr int kWSBufs = 4;
+constexpr int kHalfLoadsPerWave = 9;                // 36 1 KB slots over 4 value waves
 
-// Issue the 9 direct-to-LDS loads of half `h` of page k of request b.  Same
-// contract as issue_page_load (asm, untracked by the compiler, M0 holds the
-// LDS destination; rows at or beyond the sequence end are zero-filled).
+// Issue the 9 direct-to-LDS loads of half `h` of page k of request b for
+// value wave j: 1 KB slots j, j+4, ..., j+32 of the unit.  Same contract as
+// issue_page_load (asm, untracked by the compiler, M0 holds the LDS
+// destination, SCC clobbered; rows at or beyond the sequence end are
+// zero-filled by the range check).
 __device__ __forceinline__ void issue_half_load(char* lds_buf, const DecodeArgs& a, int b, int k,
-                                                int h, const int (&off)[9], int w) {
+                                                int h, const int (&off)[9], int j) {
   const int L = ldc(a.seqlens + b);
   int rows = L - k * kBlock - h * kHalfRows;
   rows = rows > kHalfRows ? kHalfRows : rows;
@@ -1033,7 +741,7 @@ __device__ __forceinline__ void issue_half_load(char* lds_buf, const DecodeArgs&
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, kRsrcWord3);
   const uint32_t m0 = uni(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_buf)) + w * 1024));
+      reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_buf)) + j * 1024));
 #define MLA_DMA(O) "s_nop 0\n\tbuffer_load_dwordx4 %[" #O "], %[r], 0 offen lds\n\t"
 #define MLA_M0_NEXT "s_add_u32 m0, m0, 0x1000\n\t"
   asm volatile(
@@ -1050,48 +758,6 @@ __device__ __forceinline__ void issue_half_load(char* lds_buf, const DecodeArgs&
 #undef MLA_M0_NEXT
 }
 
-// Q for 32 rows (two 16-row tiles): 36 x 16 bytes, waits for its own loads.
-__device__ __forceinline__ void load_q_rows32(bf16x8 (&q)[2][18], const bf16x8* qp0,
-                                              const bf16x8* qp1) {
-#define MLA_QL(D, P, OFF) "global_load_dwordx4 %" #D ", %" #P ", off offset:" #OFF "\n\t"
-  asm volatile(
-      MLA_QL(0, 36, 0) MLA_QL(1, 36, 64) MLA_QL(2, 36, 128) MLA_QL(3, 36, 192)
-      MLA_QL(4, 36, 256) MLA_QL(5, 36, 320) MLA_QL(6, 36, 384) MLA_QL(7, 36, 448)
-      MLA_QL(8, 36, 512) MLA_QL(9, 36, 576) MLA_QL(10, 36, 640) MLA_QL(11, 36, 704)
-      MLA_QL(12, 36, 768) MLA_QL(13, 36, 832) MLA_QL(14, 36, 896) MLA_QL(15, 36, 960)
-      MLA_QL(16, 36, 1024) MLA_QL(17, 36, 1088)
-      MLA_QL(18, 37, 0) MLA_QL(19, 37, 64) MLA_QL(20, 37, 128) MLA_QL(21, 37, 192)
-      MLA_QL(22, 37, 256) MLA_QL(23, 37, 320) MLA_QL(24, 37, 384) MLA_QL(25, 37, 448)
-      MLA_QL(26, 37, 512) MLA_QL(27, 37, 576) MLA_QL(28, 37, 640) MLA_QL(29, 37, 704)
-      MLA_QL(30, 37, 768) MLA_QL(31, 37, 832) MLA_QL(32, 37, 896) MLA_QL(33, 37, 960)
-      MLA_QL(34, 37, 1024) MLA_QL(35, 37, 1088)
-      "s_waitcnt vmcnt(0)"
-      : "=&v"(q[0][0]), "=&v"(q[0][1]), "=&v"(q[0][2]), "=&v"(q[0][3]), "=&v"(q[0][4]),
-        "=&v"(q[0][5]), "=&v"(q[0][6]), "=&v"(q[0][7]), "=&v"(q[0][8]), "=&v"(q[0][9]),
-        "=&v"(q[0][10]), "=&v"(q[0][11]), "=&v"(q[0][12]), "=&v"(q[0][13]), "=&v"(q[0][14]),
-        "=&v"(q[0][15]), "=&v"(q[0][16]), "=&v"(q[0][17]), "=&v"(q[1][0]), "=&v"(q[1][1]),
-        "=&v"(q[1][2]), "=&v"(q[1][3]), "=&v"(q[1][4]), "=&v"(q[1][5]), "=&v"(q[1][6]),
-        "=&v"(q[1][7]), "=&v"(q[1][8]), "=&v"(q[1][9]), "=&v"(q[1][10]), "=&v"(q[1][11]),
-        "=&v"(q[1][12]), "=&v"(q[1][13]), "=&v"(q[1][14]), "=&v"(q[1][15]), "=&v"(q[1][16]),
-        "=&v"(q[1][17])
-      : "v"(qp0), "v"(qp1)
-      : "memory");
-#undef MLA_QL
-}
-
-// Wait until at most 9*ahead direct loads of this wave are outstanding.
-__device__ __forceinline__ void wait_units_ahead(int ahead) {
-  static_assert(kHalfLoadsPerWave == 9, "wait counts below");
-  if (ahead >= 3)
-    asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
-  else if (ahead == 2)
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else if (ahead == 1)
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Unit positions: (request b, page k, half h); the second half of a page is a
 // unit only if the page has keys in it.
 __device__ __forceinline__ void next_unit(const DecodeArgs& a, int& b, int& k, int& h, int b1,
@@ -1105,16 +771,16 @@ __device__ __forceinline__ void next_unit(const DecodeArgs& a, int& b, int& k, i
   seek(a, b, k, b1, k1);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void mla_splitkv_t128_kernel(const DecodeArgs a) {
-  constexpr int NBUF = 4;
-  constexpr int DL = 8;   // output dim tiles per wave (128 dims)
-  constexpr int RTG = 8;  // 16-row tiles in the workgroup tile
+__global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const DecodeArgs a) {
+  constexpr int NBUF = kWSBufs;
+  constexpr int DL = 8;   // 16-dim output tiles per value wave (128 dims)
+  constexpr int RT = 4;   // 16-row tiles of the workgroup tile
 
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * kHalfBytes];
-  __shared__ bf16x8 p_lds[RTG][64];   // P^T operands per 16-row tile
-  __shared__ float alpha_lds[128];
-  __shared__ int grow_lds[4];
-  __shared__ float stat_l[128];
+  __shared__ bf16x8 p_lds[2][RT][64];   // P^T operands: [unit parity][row tile][lane]
+  __shared__ float alpha_lds[2][64];    // per-row rescale factor of the unit
+  __shared__ int grow_lds[2][RT];       // per row tile: any row rescaled
+  __shared__ float lfin_lds[2][64];     // per-row sum of a piece ending at the unit
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1136,98 +802,52 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_t128_kernel(const Dec
   const int b0 = ldc(tm + 0), k0 = ldc(tm + 1), b1 = ldc(tm + 2), k1 = ldc(tm + 3);
   const int first_split = ldc(tm + 4);
 
-  // compute position (unit being computed) and issue position (next to load)
   int cb = b0, ck = k0, ch = 0;
   seek(a, cb, ck, b1, k1);
   if (!before_end(a, cb, ck, b1, k1)) return;  // uniform: empty part
-  int ib = cb, ik = ck, ih = 0;
+  const int tile_row0 = rtile * 64;
 
-  const int tile_row0 = rtile * 128;
-  const int own_row0 = tile_row0 + w * 32;   // rows of this wave: own_row0 + 16 rt + i
-
-  int off[9];
-#pragma unroll
-  for (int j = 0; j < 9; ++j) {
-    const int u = j * kThreads + tid;
-    const int r = u / kChunksPerRow;
-    const int pc = u - r * kChunksPerRow;
-    off[j] = r * kRowBytes + ((pc ^ lds_swizzle(r)) << 4);
-  }
-  const int fi = lds_swizzle(i & 7);
-  const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
-  const int a_off1 = i * kRowBytes + (((4 + g) ^ fi) << 4);
-  const int tr_row = 4 * g + (i >> 2);
-  const int ft = lds_swizzle(tr_row & 7);
-  const int hh = (i & 3) >> 1;
-  int t_off[4];
-#pragma unroll
-  for (int d4 = 0; d4 < 4; ++d4)
-    t_off[d4] = 256 * w + tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
-
-  bf16x8 qreg[2][18];
-  f32x4 o[DL][RTG];
-  float m_run[2], l_run[2];
-  int lim[2];
-  int L = 0, n = 0, pbeg = 0, pend = 0, lim_min = 0;
-
-  auto load_q = [&](int b) {
-    const bf16x8* q0 = reinterpret_cast<const bf16x8*>(
-        a.q + ((long long)b * a.M + own_row0 + i) * kDK + 8 * g);
-    load_q_rows32(qreg, q0, q0 + 16 * kDK / 8);
-  };
-  auto start_piece = [&](int b, int k) {
-    L = ldc(a.seqlens + b);
-    n = n_pages(L);
-    pbeg = k;
-    pend = (b == b1) ? k1 : n;
-    lim_min = a.causal ? L - a.s_q + 1 : L;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int t = (own_row0 + 16 * rt + i) / a.h_q;
-      lim[rt] = a.causal ? L - a.s_q + 1 + t : L;
-      m_run[rt] = -INFINITY;
-      l_run[rt] = 0.f;
-    }
-#pragma unroll
-    for (int dl = 0; dl < DL; ++dl)
-#pragma unroll
-      for (int rt = 0; rt < RTG; ++rt) o[dl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Piece bookkeeping shared by both roles: a piece is the run of units of
+  // one request inside the part.
+  auto piece_slot = [&](int b, int pbeg, int pend, int n, bool& whole) {
+    whole = pbeg == 0 && pend == n;
+    const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
+    return whole ? 0LL : (long long)ldc(a.split_offsets + b) + sidx;
   };
 
-  // prologue: unit 0, Q of its piece, then units 1..3
-  int issued = 0;  // units issued so far
-  int u = 0;       // index of the unit being computed
-  issue_half_load(smem, a, ib, ik, ih, off, w);
-  ++issued;
-  next_unit(a, ib, ik, ih, b1, k1);
-  load_q(cb);
-#pragma unroll
-  for (int j = 1; j < NBUF; ++j) {
-    if (before_end(a, ib, ik, b1, k1)) {
-      issue_half_load(smem + j * kHalfBytes, a, ib, ik, ih, off, w);
-      ++issued;
-      next_unit(a, ib, ik, ih, b1, k1);
-    }
-  }
-  start_piece(cb, ck);
+  if (w < 4) {
+    // ======================= score waves =======================
+    const int q = w;
+    const int row_own = tile_row0 + 16 * q + i;
+    const int fi = lds_swizzle(i & 7);
+    const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
+    const int a_off1 = a_off0 ^ 64;   // unit 4+g instead of g (row bases are multiples of 128)
 
-  while (true) {
-    const int b = cb;
-    char* ubuf;
-    bool more;     // another unit follows in the part
-    bool same;     // ... and it belongs to this piece
+    bf16x8 qreg[18];
+    float m_run = -INFINITY, l_run = 0.f;
+    int lim = 0, lim_min = 0, L = 0, n = 0, pbeg = 0;
+    bool new_piece = true;
+    int t = 0;
     while (true) {
-      wait_units_ahead(issued - u - 1);
-      wg_barrier();
-      ubuf = smem + (u % NBUF) * kHalfBytes;
-      const int k = ck, h = ch;
+      wg_barrier();   // unit t landed; P of unit t-2 consumed
+      const int b = cb, k = ck, h = ch;
+      if (new_piece) {
+        L = ldc(a.seqlens + b);
+        n = n_pages(L);
+        pbeg = k;
+        lim_min = a.causal ? L - a.s_q + 1 : L;
+        lim = a.causal ? L - a.s_q + 1 + row_own / a.h_q : L;
+        m_run = -INFINITY;
+        l_run = 0.f;
+        load_q_rows(qreg, reinterpret_cast<const bf16x8*>(
+                              a.q + ((long long)b * a.M + row_own) * kDK + 8 * g));
+      }
+      const char* ubuf = smem + (t % NBUF) * kHalfBytes;
 
-      // ---- scores S^T[key][row], 32 keys x this wave's 32 rows ----
-      f32x4 s[2][2];
+      // ---- S^T[key][row] = K . Q^T: 32 keys x this wave's 16 rows ----
+      f32x4 s[2];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < 2; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       {
         constexpr int D1 = 2;
         bf16x8 ka[D1 + 1][2];
@@ -1242,194 +862,241 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_t128_kernel(const Dec
           const int cs = ks - D1;
           if (cs >= 0) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-              for (int kt = 0; kt < 2; ++kt)
-                s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    ka[cs % (D1 + 1)][kt], qreg[rt][cs], s[rt][kt], 0, 0, 0);
+            for (int kt = 0; kt < 2; ++kt)
+              s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[cs % (D1 + 1)][kt], qreg[cs],
+                                                             s[kt], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 
-      // ---- online softmax of this wave's rows ----
+      // ---- online softmax of row_own (fp32, base 2, lazy rescale) ----
       {
         const int key0 = k * kBlock + h * kHalfRows + 4 * g;
         const bool need_mask = k * kBlock + (h + 1) * kHalfRows > lim_min;
-        int any = 0;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          float mx = -INFINITY;
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              float xv = s[rt][kt][v] * a.scale_log2;
-              if (need_mask && key0 + kt * 16 + v >= lim[rt]) xv = -INFINITY;
-              s[rt][kt][v] = xv;
-              mx = fmaxf(mx, xv);
-            }
-          mx = wave_max_4lanes(mx);
-          const float m_new = fmaxf(m_run[rt], mx);
-          // Keep the running max unless it grew by more than kRescaleSlack
-          // (exact either way: numerator and denominator share it).
-          const bool grow = m_new > m_run[rt] + kRescaleSlack;
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[rt] - m_new) : 1.f;
-          if (grow) m_run[rt] = m_new;
-          l_run[rt] *= alpha;
-          any |= __any(grow) ? 1 : 0;
-          const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
-          float lsum = 0.f;
-          bf16x8 pb;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float p = __builtin_amdgcn_exp2f(s[rt][kt][v] - m_use);
-              lsum += p;
-              pb[kt * 4 + v] = (__bf16)p;
-            }
-          l_run[rt] += lsum;
-          p_lds[2 * w + rt][lane] = pb;
-          if (g == 0) alpha_lds[32 * w + 16 * rt + i] = alpha;
-        }
-        if (lane == 0) grow_lds[w] = any;
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P, alpha, flags written
-      wg_barrier();
-
-      // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all 128 rows ----
-      {
-        if (grow_lds[0] | grow_lds[1] | grow_lds[2] | grow_lds[3]) {
-#pragma unroll
-          for (int rt = 0; rt < RTG; ++rt) {
-            const float al = alpha_lds[16 * rt + i];
-#pragma unroll
-            for (int dl = 0; dl < DL; ++dl) o[dl][rt] *= al;
-            __builtin_amdgcn_sched_barrier(0);
+          for (int v = 0; v < 4; ++v) {
+            float xv = s[kt][v] * a.scale_log2;
+            if (need_mask && key0 + kt * 16 + v >= lim) xv = -INFINITY;
+            s[kt][v] = xv;
+            mx = fmaxf(mx, xv);
           }
+        mx = wave_max_4lanes(mx);
+        const float m_new = fmaxf(m_run, mx);
+        // Keep the running max unless it grew by more than kRescaleSlack
+        // (exact either way: numerator and denominator share it).
+        const bool grow = m_new > m_run + kRescaleSlack;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        if (grow) m_run = m_new;
+        l_run *= alpha;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float lsum = 0.f;
+        bf16x8 pb;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float p = __builtin_amdgcn_exp2f(s[kt][v] - m_use);
+            lsum += p;
+            pb[kt * 4 + v] = (__bf16)p;
+          }
+        l_run += lsum;
+        p_lds[t & 1][q][lane] = pb;
+        if (g == 0) alpha_lds[t & 1][16 * q + i] = alpha;
+        const int any = __any(grow) ? 1 : 0;
+        if (lane == 0) grow_lds[t & 1][q] = any;
+      }
+
+      // ---- next unit; at a piece end publish the row sum and write the LSE ----
+      int nb = cb, nk = ck, nh = ch;
+      next_unit(a, nb, nk, nh, b1, k1);
+      const bool more = before_end(a, nb, nk, b1, k1);
+      new_piece = !(more && nb == b);
+      if (new_piece) {
+        const float lt = wave_sum_4lanes(l_run);
+        const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
+        bool whole;
+        const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : n, n, whole);
+        if (g == 0) {
+          lfin_lds[t & 1][16 * q + i] = lt;
+          if (whole)
+            a.lse[(long long)b * a.M + row_own] = lse2 * kLn2;
+          else
+            a.part_lse[slot * a.M + row_own] = lse2;
         }
-        bf16x8 va[DL];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P, alpha, flags, sums written
+      ++t;
+      if (!more) break;
+      cb = nb;
+      ck = nk;
+      ch = nh;
+    }
+    wg_barrier();   // the value waves' last product may start
+  } else {
+    // ======================= value waves =======================
+    const int j = w - 4;
+    const int tj = tid - 256;   // 0..255 within the value waves
+    int off[9];
 #pragma unroll
-        for (int dl = 0; dl < DL; ++dl) {
-          const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
-          const bf16x4 lo =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
-          const bf16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
-          va[dl] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int m = 0; m < 9; ++m) {
+      const int p = 256 * m + tj;   // LDS 16-byte unit of the 36 KB unit buffer
+      const int r = p / kChunksPerRow;
+      const int pc = p - r * kChunksPerRow;
+      off[m] = r * kRowBytes + ((pc ^ lds_swizzle(r)) << 4);
+    }
+    const int tr_row = 4 * g + (i >> 2);
+    const int ft = lds_swizzle(tr_row & 7);
+    const int hh = (i & 3) >> 1;
+    int t_off[4];
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+      t_off[d4] = 256 * j + tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
+
+    f32x4 o[DL][RT];
+#pragma unroll
+    for (int dl = 0; dl < DL; ++dl)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) o[dl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // issue cursor (ib, ik, ih); compute cursor (cb, ck, ch) is one unit behind
+    // the score waves
+    int ib = cb, ik = ck, ih = 0;
+    int issued = 0;
+    auto issue_next = [&]() {
+      if (before_end(a, ib, ik, b1, k1)) {
+        issue_half_load(smem + (issued % NBUF) * kHalfBytes, a, ib, ik, ih, off, j);
+        ++issued;
+        next_unit(a, ib, ik, ih, b1, k1);
+      }
+    };
+    // wait until unit u has landed (units issued after it stay in flight)
+    auto wait_unit = [&](int u) {
+      static_assert(kHalfLoadsPerWave == 9, "wait counts below");
+      if (issued - u - 1 >= 1)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    issue_next();   // unit 0
+    issue_next();   // unit 1
+    wait_unit(0);
+    wg_barrier();   // b_0: unit 0 landed
+    issue_next();   // unit 2 (buffer 2)
+    wait_unit(1);
+    wg_barrier();   // b_1: unit 1 landed, P of unit 0 written
+
+    int L = ldc(a.seqlens + cb), n = n_pages(L), pbeg = ck;
+    int t = 0;   // unit multiplied in this phase
+    while (true) {
+      const int b = cb;
+      const char* ubuf = smem + (t % NBUF) * kHalfBytes;
+      const int par = t & 1;
+
+      // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all 64 rows ----
+      if (grow_lds[par][0] | grow_lds[par][1] | grow_lds[par][2] | grow_lds[par][3]) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float al = alpha_lds[par][16 * rt + i];
+#pragma unroll
+          for (int dl = 0; dl < DL; ++dl) o[dl][rt] *= al;
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 pB[2];
-        pB[0] = p_lds[0][lane];
+      }
+      {
+        bf16x8 pB[RT];
 #pragma unroll
-        for (int rt = 0; rt < RTG; ++rt) {
-          if (rt + 1 < RTG) pB[(rt + 1) & 1] = p_lds[rt + 1][lane];
+        for (int rt = 0; rt < RT; ++rt) pB[rt] = p_lds[par][rt][lane];
+        constexpr int D2 = 1;
+        bf16x8 va[D2 + 1];
 #pragma unroll
-          for (int dl = 0; dl < DL; ++dl)
-            o[dl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pB[rt & 1], o[dl][rt],
-                                                               0, 0, 0);
+        for (int dl = 0; dl < DL + D2; ++dl) {
+          if (dl < DL) {
+            const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
+            va[dl % (D2 + 1)] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+          const int cd = dl - D2;
+          if (cd >= 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              o[cd][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[cd % (D2 + 1)], pB[rt],
+                                                                 o[cd][rt], 0, 0, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 
-      // next unit to compute
+      // ---- next unit; at a piece end write O (by columns) and restart ----
       int nb = cb, nk = ck, nh = ch;
       next_unit(a, nb, nk, nh, b1, k1);
-      more = before_end(a, nb, nk, b1, k1);
-      same = more && nb == cb;
-      if (!same) break;
-      // release this buffer and refill it with the unit NBUF ahead
-      wg_barrier();  // every wave is done reading this buffer and P
-      if (before_end(a, ib, ik, b1, k1)) {
-        issue_half_load(ubuf, a, ib, ik, ih, off, w);
-        ++issued;
-        next_unit(a, ib, ik, ih, b1, k1);
+      const bool more = before_end(a, nb, nk, b1, k1);
+      if (!(more && nb == b)) {
+        bool whole;
+        const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : n, n, whole);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float lt = lfin_lds[par][16 * rt + i];
+          const float inv = lt > 0.f ? 1.f / lt : 0.f;
+          const int row = tile_row0 + 16 * rt + i;
+          if (whole) {
+            uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + j * 128 + 4 * g;
+#pragma unroll
+            for (int dl = 0; dl < DL; ++dl) {
+              const f32x4 v = o[dl][rt] * inv;
+              const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+              *reinterpret_cast<bf16x4*>(op + dl * 16) = bv;
+            }
+          } else {
+            float* op = a.part_o + (slot * a.M + row) * kDV + j * 128 + 4 * g;
+#pragma unroll
+            for (int dl = 0; dl < DL; ++dl)
+              *reinterpret_cast<f32x4*>(op + dl * 16) = o[dl][rt] * inv;
+          }
+#pragma unroll
+          for (int dl = 0; dl < DL; ++dl) o[dl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (more) {
+          L = ldc(a.seqlens + nb);
+          n = n_pages(L);
+          pbeg = nk;
+        }
       }
+      if (!more) break;
+      // unit t+3 goes into the buffer of unit t-1 (multiplied in the previous
+      // phase); unit t+2 must land before the next barrier
+      issue_next();
+      wait_unit(t + 2);
+      wg_barrier();   // b_{t+2}: unit t+2 landed, P of unit t+1 written
       cb = nb;
       ck = nk;
       ch = nh;
-      ++u;
+      ++t;
     }
-
-    // ---- piece end: publish row sums, write LSE (row owners) and O (columns) ----
-    const bool whole = pbeg == 0 && pend == n;
-    const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
-    const long long slot = whole ? 0 : (long long)ldc(a.split_offsets + b) + sidx;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const float lt = wave_sum_4lanes(l_run[rt]);
-      const float lse2 = lt > 0.f ? m_run[rt] + log2f(lt) : -INFINITY;
-      const int row = own_row0 + 16 * rt + i;
-      if (g == 0) {
-        stat_l[32 * w + 16 * rt + i] = lt;
-        if (whole)
-          a.lse[(long long)b * a.M + row] = lse2 * kLn2;
-        else
-          a.part_lse[slot * a.M + row] = lse2;
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wg_barrier();
-#pragma unroll
-    for (int rt = 0; rt < RTG; ++rt) {
-      const float lt = stat_l[16 * rt + i];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int row = tile_row0 + 16 * rt + i;
-      if (whole) {
-        uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + w * 128 + 4 * g;
-#pragma unroll
-        for (int dl = 0; dl < DL; ++dl) {
-          const f32x4 v = o[dl][rt] * inv;
-          const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-          *reinterpret_cast<bf16x4*>(op + dl * 16) = bv;
-        }
-      } else {
-        float* op = a.part_o + (slot * a.M + row) * kDV + w * 128 + 4 * g;
-#pragma unroll
-        for (int dl = 0; dl < DL; ++dl) *reinterpret_cast<f32x4*>(op + dl * 16) = o[dl][rt] * inv;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    if (!more) break;
-    // Next piece: Q rows (the load waits for everything in flight), then the
-    // refill of the buffer just computed.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wg_barrier();  // every wave is done with the buffer, P and the statistics
-    int nb = cb, nk = ck, nh = ch;
-    next_unit(a, nb, nk, nh, b1, k1);
-    load_q(nb);
-    if (before_end(a, ib, ik, b1, k1)) {
-      issue_half_load(ubuf, a, ib, ik, ih, off, w);
-      ++issued;
-      next_unit(a, ib, ik, ih, b1, k1);
-    }
-    start_piece(nb, nk);
-    cb = nb;
-    ck = nk;
-    ch = nh;
-    ++u;
   }
 }
 
-// Rows per workgroup tile.  The 128-row kernel reads each page once per
-// part but does not fit the register file without spilling yet, so the
-// 64-row column-split kernel serves s_q*h_q >= 64.
+// Rows per workgroup tile.
 int tile_rows_for(int M) {
   if (M <= 32) return 32;    // mla_splitkv_kernel<1, 2>
-  return 64;                 // mla_splitkv_cs_kernel (M = 128, 256: 2 or 4 row tiles)
+  return 64;                 // mla_splitkv_ws_kernel (M = 128, 256: 2 or 4 row tiles)
 }
 
 hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
   const dim3 grid(a.num_parts * a.row_tiles), block(kThreads);
-  if (a.M <= 32)
+  if (a.row_tile_rows == 32)
     hipExtLaunchKernelGGL((mla_splitkv_kernel<1, 2>), grid, block, 0, stream, start, stop, 0, a);
-  else if (a.row_tile_rows == 128)
-    hipExtLaunchKernelGGL(mla_splitkv_t128_kernel, grid, block, 0, stream, start, stop, 0, a);
   else
-    hipExtLaunchKernelGGL(mla_splitkv_cs_kernel, grid, block, 0, stream, start, stop, 0, a);
+    hipExtLaunchKernelGGL(mla_splitkv_ws_kernel, grid, dim3(kThreadsWS), 0, stream, start, stop,
+                          0, a);
   return hipGetLastError();
 }
 
