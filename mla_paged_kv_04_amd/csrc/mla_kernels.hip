@@ -712,8 +712,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeAr
 //                      page load, so no score wave ever waits on a load
 //                      queue it did not fill.
 // Work unit = half a page (32 keys, 36 KB) in a ring of four LDS buffers:
-// while unit t is scored and unit t-1 multiplied, unit t+1 lands and unit
-// t+2 is loading.  One workgroup barrier per unit.  Probabilities, rescale
+// while unit t is scored and unit t-1 multiplied, units t+1 and t+2 are in
+// flight (each has two phases to land).  One workgroup barrier per unit.  Probabilities, rescale
 // factors and final row sums are double-buffered by unit parity.
 // --------------------------------------------------------------------------
 constexpr int kHalfRows = 32;
@@ -817,6 +817,10 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
 
   if (w < 4) {
     // ======================= score waves =======================
+    // The score waves carry the critical path of every phase (scores, then
+    // the softmax chain); at a higher issue priority they take the SIMD first
+    // and the value wave's products fill the gaps.
+    __builtin_amdgcn_s_setprio(1);
     const int q = w;
     const int row_own = tile_row0 + 16 * q + i;
     const int fi = lds_swizzle(i & 7);
@@ -976,7 +980,10 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     // wait until unit u has landed (units issued after it stay in flight)
     auto wait_unit = [&](int u) {
       static_assert(kHalfLoadsPerWave == 9, "wait counts below");
-      if (issued - u - 1 >= 1)
+      const int ahead = issued - u - 1;
+      if (ahead >= 2)
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      else if (ahead == 1)
         asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -984,15 +991,20 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
 
     issue_next();   // unit 0
     issue_next();   // unit 1
+    issue_next();   // unit 2
     wait_unit(0);
     wg_barrier();   // b_0: unit 0 landed
-    issue_next();   // unit 2 (buffer 2)
+    issue_next();   // unit 3 (buffer 3)
     wait_unit(1);
     wg_barrier();   // b_1: unit 1 landed, P of unit 0 written
 
     int L = ldc(a.seqlens + cb), n = n_pages(L), pbeg = ck;
     int t = 0;   // unit multiplied in this phase
     while (true) {
+      // Unit t+3 goes into the buffer of unit t-1, free since the last
+      // barrier (its product ended in the previous phase); issued first so
+      // that it has two phases to land.
+      if (t >= 1) issue_next();
       const int b = cb;
       const char* ubuf = smem + (t % NBUF) * kHalfBytes;
       const int par = t & 1;
@@ -1070,9 +1082,6 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         }
       }
       if (!more) break;
-      // unit t+3 goes into the buffer of unit t-1 (multiplied in the previous
-      // phase); unit t+2 must land before the next barrier
-      issue_next();
       wait_unit(t + 2);
       wg_barrier();   // b_{t+2}: unit t+2 landed, P of unit t+1 written
       cb = nb;
