@@ -59,17 +59,28 @@ constexpr float kRescaleSlack = 8.0f;           // lazy-rescale threshold (log2)
 // multiple of 8.
 __device__ __forceinline__ int lds_swizzle(int r) { return r & 7; }
 
+// Reductions over lanes {i, i^16, i^32, i^48}, the four lanes holding one
+// query row, with the gfx950 row-swap permutes (VALU; a __shfl_xor would be a
+// round trip through the LDS crossbar).  permlane16_swap(x, x) hands every
+// lane x of lane i^16 in one of its two results and its own x in the other,
+// permlane32_swap likewise for lane i^32, so combining the pair is the
+// reduction step whichever way round the two come back.
 __device__ __forceinline__ float wave_max_4lanes(float x) {
-  // max over lanes {i, i^16, i^32, i^48}: the four lanes holding one query row
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const unsigned xi = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const unsigned yi = __float_as_uint(x);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
 __device__ __forceinline__ float wave_sum_4lanes(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const unsigned xi = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const unsigned yi = __float_as_uint(x);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence
