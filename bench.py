@@ -136,7 +136,8 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
 
 def splitkv_kernel_name(m_rows: int) -> str:
     """HIP kernel that mla_decode_splitkv launches for s_q*h_q = m_rows."""
-    return "mla_splitkv_kernel<1, 2>" if m_rows <= 32 else "mla_splitkv_ws_kernel"
+    rt = 1 if m_rows <= 16 else 2 if m_rows <= 32 else 4
+    return f"mla_splitkv_ws_kernel<{rt}>"
 
 
 def main(argv=None) -> int:
@@ -153,6 +154,9 @@ def main(argv=None) -> int:
                     help="run one plain elementwise copy of this many MiB (int32 -> int32) "
                          "after warmup, outside the timed region: the known-size kernel "
                          "that HBM byte counters are scaled against")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the step instead of eager launches "
+                         "(slower on this stack: replays add ~4-14 us per step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args(argv)
@@ -218,6 +222,24 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize(dev)
 
+    # The step captured once as a HIP graph (metadata, decode, combine), as a
+    # serving loop would launch it; replays reuse the same buffers.
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            flush()
+            graph.replay()
+        torch.cuda.synchronize(dev)
+
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 18
         src = torch.ones((n,), dtype=torch.int32, device=dev)
@@ -235,12 +257,25 @@ def main(argv=None) -> int:
         e[2].record()
         e[3].record()
     torch.cuda.synchronize(dev)
+    gevs = new_events()
     t_wall0 = time.perf_counter()
-    for k in range(K):
-        flush()
-        step(evs[k])
+    if graph is not None:
+        for k in range(K):
+            flush()
+            gevs[k][0].record()
+            graph.replay()
+            gevs[k][1].record()
+    else:
+        for k in range(K):
+            flush()
+            step(evs[k])
     torch.cuda.synchronize(dev)
     t_wall = time.perf_counter() - t_wall0
+    if graph is not None:   # eager steps: the decode kernel's own duration
+        for k in range(K):
+            flush()
+            step(evs[k])
+        torch.cuda.synchronize(dev)
 
     bevs = new_events()
     for k in range(K):
@@ -248,7 +283,8 @@ def main(argv=None) -> int:
         step_breakdown(bevs[k])
     torch.cuda.synchronize(dev)
 
-    step_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    eager_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[1]) for e in gevs] if graph is not None else eager_ms
     dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
     meta_ms = [e[0].elapsed_time(e[1]) for e in bevs]
     comb_ms = [e[2].elapsed_time(e[3]) for e in bevs]
@@ -266,7 +302,10 @@ def main(argv=None) -> int:
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(K):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     e1.record()
     torch.cuda.synchronize(dev)
     warm_ms = e0.elapsed_time(e1) / K
@@ -288,7 +327,8 @@ def main(argv=None) -> int:
         "config": {"workload": args.workload, "desc": w.desc, "batch": inp.batch,
                    "s_q": inp.s_q, "h_q": inp.h_q, "h_kv": 1, "d_k": 576, "d_v": 512,
                    "block_size": 64, "total_keys": int(inp.seqlens.sum()),
-                   "num_parts": parts, "cache_flush_between_steps": args.flush},
+                   "num_parts": parts, "cache_flush_between_steps": args.flush,
+                   "step_launch": "hip_graph" if graph is not None else "eager"},
         "tflops": round(tfl, 2),
         "algorithmic_bytes": counts["bytes"],
         "algorithmic_flops": counts["flops"],
@@ -296,7 +336,8 @@ def main(argv=None) -> int:
                        "combine": round(mean(comb_ms), 5),
                        "splitkv_median": round(med(dec_ms), 5),
                        "splitkv_p90": round(sorted(dec_ms)[int(0.9 * (len(dec_ms) - 1))], 5),
-                       "step_median": round(med(step_ms), 5)},
+                       "step_median": round(med(step_ms), 5),
+                       "eager_step": round(mean(eager_ms), 5)},
         "warm_ms_per_step": round(warm_ms, 5),
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": {

@@ -12,9 +12,12 @@
 //     (feature ⑤) — here a split-KV partition plus a log-sum-exp merge.
 //
 // gfx950 design (not the page's Hopper design):
-//   * one 256-thread workgroup (4 wave64) per CU; a page (64 x 576 bf16 =
-//     72 KB) is streamed HBM -> LDS with 16-byte direct-to-LDS buffer loads
-//     (no VGPR staging), two pages double-buffered = 144 KB of the 160 KB LDS;
+//   * one 512-thread workgroup (8 wave64, two per SIMD) per CU, in two roles:
+//     four score waves (scores + softmax) and four value waves (values +
+//     page loads), one half-page unit apart (see mla_splitkv_ws_kernel);
+//   * half pages (32 x 576 bf16 = 36 KB) are streamed HBM -> LDS with 16-byte
+//     direct-to-LDS buffer loads (no VGPR staging) into a ring of four unit
+//     buffers (144 KB of the 160 KB LDS), two units in flight;
 //   * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_16x16x32_bf16
 //     with the page rows as the A operand (ds_read_b128) and Q held in VGPRs as
 //     the B operand.  The MFMA output then holds, per lane, one query row and
@@ -104,69 +107,59 @@ __device__ __forceinline__ int n_pages(int L) {
 // documented with mla_decode_metadata (cost_b = pages + c, equal quotas).
 // Every tile_meta word is written by exactly one thread.
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void mla_metadata_kernel(
+// One wave64: requests are taken 64 at a time; the cost scan inside a chunk
+// fits 32 bits (a request has fewer than 2^25 pages), the running offsets are
+// 64-bit.  No workgroup barriers.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(64) void mla_metadata_kernel(
     const int32_t* __restrict__ seqlens, int batch, int c_fix, int num_parts,
     int32_t* __restrict__ tile_meta, int32_t* __restrict__ split_offsets) {
-  __shared__ long long s_red[kThreads];
-  __shared__ long long s_scan_cost[kThreads];
-  __shared__ int s_scan_slots[kThreads];
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x;
 
   // total cost C
   long long local = 0;
-  for (int b = tid; b < batch; b += kThreads) {
-    int n = n_pages(seqlens[b]);
+  for (int b = lane; b < batch; b += 64) {
+    const int n = n_pages(seqlens[b]);
     local += n > 0 ? (long long)(n + c_fix) : 0;
   }
-  s_red[tid] = local;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) s_red[tid] += s_red[tid + s];
-    __syncthreads();
-  }
-  const long long C = s_red[0];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
+  const long long C = local;
   const long long P = num_parts;
   const long long q = C > 0 ? (C + P - 1) / P : 1;
 
   long long carry_cost = 0;
   int carry_slots = 0;
-  for (int base = 0; base < batch; base += kThreads) {
-    const int b = base + tid;
-    int n = 0;
-    if (b < batch) n = n_pages(seqlens[b]);
-    const long long cost = n > 0 ? (long long)(n + c_fix) : 0;
-    // inclusive scans (Hillis-Steele) of cost and slots within the chunk
-    s_scan_cost[tid] = cost;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      long long v = tid >= off ? s_scan_cost[tid - off] : 0;
-      __syncthreads();
-      s_scan_cost[tid] += v;
-      __syncthreads();
-    }
-    const long long start = carry_cost + s_scan_cost[tid] - cost;
+  for (int base = 0; base < batch; base += 64) {
+    const int b = base + lane;
+    const int n = b < batch ? n_pages(seqlens[b]) : 0;
+    const int cost = n > 0 ? n + c_fix : 0;
+    const int incl = wave_incl_scan(cost);
+    const long long start = carry_cost + (incl - cost);
+    long long p0 = 0;   // first boundary index after the request's overhead units
     int nsplit = 1;
     if (n > 0) {
       const long long lo = start + c_fix;
-      const long long hi = lo + n;
-      nsplit = 1 + (int)((hi - 1) / q - lo / q);
+      p0 = lo / q + 1;
+      nsplit = 1 + (int)((lo + n - 1) / q - (p0 - 1));
     }
     const int slots = nsplit >= 2 ? nsplit : 0;
-    s_scan_slots[tid] = slots;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      int v = tid >= off ? s_scan_slots[tid - off] : 0;
-      __syncthreads();
-      s_scan_slots[tid] += v;
-      __syncthreads();
-    }
+    const int slots_incl = wave_incl_scan(slots);
     if (b < batch) {
-      split_offsets[b] = carry_slots + s_scan_slots[tid] - slots;
+      split_offsets[b] = carry_slots + slots_incl - slots;
       if (cost > 0) {
         // boundaries p*q that fall inside [start, start + cost)
         const long long p_lo = (start + q - 1) / q;
         const long long p_hi = (start + cost + q - 1) / q;
-        const long long p0 = (start + c_fix) / q + 1;
         for (long long p = p_lo; p < p_hi && p < P; ++p) {
           long long k = p * q - start - c_fix;
           k = k < 0 ? 0 : (k > n ? n : k);
@@ -182,14 +175,13 @@ __global__ __launch_bounds__(kThreads) void mla_metadata_kernel(
         }
       }
     }
-    carry_cost += s_scan_cost[kThreads - 1];
-    carry_slots += s_scan_slots[kThreads - 1];
-    __syncthreads();
+    carry_cost += __shfl(incl, 63);
+    carry_slots += __shfl(slots_incl, 63);
   }
-  if (tid == 0) split_offsets[batch] = carry_slots;
+  if (lane == 0) split_offsets[batch] = carry_slots;
   // parts whose boundary lies at or beyond C begin (and the last part ends) at (B, 0)
   const long long p_tail = (C + q - 1) / q;
-  for (long long p = tid; p < P; p += kThreads) {
+  for (long long p = lane; p < P; p += 64) {
     int32_t* tm = tile_meta + p * kMetaInts;
     tm[5] = 0;
     tm[6] = 0;
@@ -212,17 +204,11 @@ __global__ __launch_bounds__(kThreads) void mla_metadata_kernel(
 
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int c_fix, int num_parts,
                            int32_t* tile_meta, int32_t* split_offsets, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_metadata_kernel, dim3(1), dim3(kThreads), 0, stream, seqlens, batch,
-                     c_fix, num_parts, tile_meta, split_offsets);
+  hipLaunchKernelGGL(mla_metadata_kernel, dim3(1), dim3(64), 0, stream, seqlens, batch, c_fix,
+                     num_parts, tile_meta, split_offsets);
   return hipGetLastError();
 }
 
-// --------------------------------------------------------------------------
-// Split-KV decode kernel.
-//   RT: 16-row query tiles per wave (1 or 2);  KG: waves sharing one row
-//   group, each taking 64/KG keys of every page (1 or 2).
-//   Rows per workgroup tile = (4/KG) * RT * 16.
-// --------------------------------------------------------------------------
 // Values the hardware needs in SGPRs (buffer resources, M0) are read from
 // global memory with vector loads (the kernel also stores, so loads are not
 // provably invariant); readfirstlane tells the compiler they are wave-uniform
@@ -238,65 +224,6 @@ __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ int ldc(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)(p);
 }
-
-// Issue the 18 direct-to-LDS 16-byte loads of one page for this wave.
-//
-// Written as inline asm on purpose: the compiler then does not track these
-// loads.  Tracked, every LDS read that it cannot prove disjoint from an
-// in-flight direct load (the transposed V reads, for one) gets an
-// "s_waitcnt vmcnt(0)", which would wait for the NEXT page's loads and
-// serialise the pipeline.  All waits for these loads are therefore explicit
-// (see the main loop), and the asm clobbers "memory" so the compiler keeps LDS
-// accesses on the right side of it.  M0 holds the LDS destination; nothing
-// else in this kernel uses M0 (gfx9 LDS instructions do not), and one wait
-// state separates each M0 write from the load that reads it.  The M0
-// increments are SALU adds, which write SCC: SCC is declared clobbered.
-__device__ __forceinline__ void issue_page_load(char* lds_tile, const DecodeArgs& a, int b,
-                                                int k, const int (&off)[9], int w) {
-  const int L = ldc(a.seqlens + b);
-  int rows = L - k * kBlock;
-  rows = rows > kBlock ? kBlock : rows;
-  int page = -1;
-  if (k < a.bt_stride) page = ldc(a.block_table + (long long)b * a.bt_stride + k);
-  const bool ok = page >= 0 && (long long)page < a.num_blocks && rows > 0;
-  const char* base = reinterpret_cast<const char*>(a.kcache) +
-                     (ok ? (long long)page * kPageBytes : 0);
-  const int nrec = ok ? rows * kRowBytes : 0;
-  // The buffer unit's range check ignores the SGPR offset, so rows 32..63 get a
-  // resource of their own (based 32 rows further on) instead of an soffset:
-  // each half then zero-fills exactly the rows at or beyond the sequence end.
-  constexpr int kHalf = 32 * kRowBytes;
-  const int nrec_lo = uni(nrec < kHalf ? nrec : kHalf);
-  const int nrec_hi = uni(nrec > kHalf ? nrec - kHalf : 0);
-  const __amdgpu_buffer_rsrc_t r_lo =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec_lo, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t r_hi =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + kHalf, 0, nrec_hi, kRsrcWord3);
-  // LDS byte address of this wave's first 1 KB slot: tile + w * 1024; slot j
-  // of the wave is 4096 bytes further on per j.
-  const uint32_t m0 = uni(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_tile)) + w * 1024));
-#define MLA_DMA(R, O) "s_nop 0\n\tbuffer_load_dwordx4 %[" #O "], %[" #R "], 0 offen lds\n\t"
-#define MLA_M0_NEXT "s_add_u32 m0, m0, 0x1000\n\t"
-  asm volatile(
-      "s_mov_b32 m0, %[m]\n\t"
-      MLA_DMA(rl, o0) MLA_M0_NEXT MLA_DMA(rl, o1) MLA_M0_NEXT MLA_DMA(rl, o2) MLA_M0_NEXT
-      MLA_DMA(rl, o3) MLA_M0_NEXT MLA_DMA(rl, o4) MLA_M0_NEXT MLA_DMA(rl, o5) MLA_M0_NEXT
-      MLA_DMA(rl, o6) MLA_M0_NEXT MLA_DMA(rl, o7) MLA_M0_NEXT MLA_DMA(rl, o8) MLA_M0_NEXT
-      MLA_DMA(rh, o0) MLA_M0_NEXT MLA_DMA(rh, o1) MLA_M0_NEXT MLA_DMA(rh, o2) MLA_M0_NEXT
-      MLA_DMA(rh, o3) MLA_M0_NEXT MLA_DMA(rh, o4) MLA_M0_NEXT MLA_DMA(rh, o5) MLA_M0_NEXT
-      MLA_DMA(rh, o6) MLA_M0_NEXT MLA_DMA(rh, o7) MLA_M0_NEXT MLA_DMA(rh, o8)
-      :
-      : [m] "s"(m0), [rl] "s"(r_lo), [rh] "s"(r_hi), [o0] "v"(off[0]), [o1] "v"(off[1]),
-        [o2] "v"(off[2]), [o3] "v"(off[3]), [o4] "v"(off[4]), [o5] "v"(off[5]),
-        [o6] "v"(off[6]), [o7] "v"(off[7]), [o8] "v"(off[8])
-      : "memory", "m0", "scc");
-#undef MLA_DMA
-#undef MLA_M0_NEXT
-}
-
-// Number of vector-memory instructions issue_page_load issues per wave.
-constexpr int kPageLoadsPerWave = 18;
 
 // Load 16 rows x 576 bf16 of Q (the B operand of the score product) for one
 // lane: 18 x 16 bytes at a 64-byte stride.  Inline asm so the compiler does
@@ -347,369 +274,6 @@ __device__ __forceinline__ void seek(const DecodeArgs& a, int& b, int& k, int b1
   }
 }
 
-template <int RT, int KG>
-__global__ __launch_bounds__(kThreads, 1) void mla_splitkv_kernel(const DecodeArgs a) {
-  constexpr int KW = 64 / KG;     // keys per wave per page
-  constexpr int KT = KW / 16;     // 16-key score tiles per wave
-  constexpr int KP = KT / 2;      // 32-key reduction steps of the value product
-  constexpr int RG = 4 / KG;      // row groups per workgroup
-  constexpr int MT = RG * RT * 16;
-  static_assert(KP >= 1, "at least 32 keys per wave");
-
-  // Two page buffers (double buffering), 2 x 72 KB of the 160 KB LDS.
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kPageBytes];
-
-  const int tid = threadIdx.x;
-  // wave index made provably uniform (the LDS destination of direct loads
-  // lives in M0 and must not be treated as divergent)
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int g = lane >> 4;
-  const int i = lane & 15;
-  const int kg = w % KG;
-  const int rg = w / KG;
-
-  // workgroup -> (part, row tile).  Workgroups are dealt to the 8 XCDs
-  // round-robin; all row tiles of a part get ids x, x+8, x+16, ... and so
-  // share an XCD, whose L2 then serves the repeated reads of each page.
-  int part, rtile;
-  const int x = blockIdx.x;
-  const int R = a.row_tiles;
-  if (R > 1 && (a.num_parts % 8) == 0) {
-    part = (x / (8 * R)) * 8 + (x & 7);
-    rtile = (x >> 3) % R;
-  } else {
-    part = x / R;
-    rtile = x % R;
-  }
-  const int32_t* tm = a.tile_meta + part * kMetaInts;
-  const int b0 = ldc(tm + 0), k0 = ldc(tm + 1), b1 = ldc(tm + 2), k1 = ldc(tm + 3);
-  const int first_split = ldc(tm + 4);
-
-  int cur_b = b0, cur_k = k0;
-  seek(a, cur_b, cur_k, b1, k1);
-  if (!before_end(a, cur_b, cur_k, b1, k1)) return;  // uniform: empty part
-
-  const int row0 = rtile * MT + rg * RT * 16;
-  const bool active = row0 < a.M;
-
-  // per-lane global byte offsets of the 9 distinct direct-load slots
-  int off[9];
-#pragma unroll
-  for (int j = 0; j < 9; ++j) {
-    const int u = j * kThreads + tid;
-    const int r = u / kChunksPerRow;
-    const int pc = u - r * kChunksPerRow;
-    off[j] = r * kRowBytes + ((pc ^ lds_swizzle(r)) << 4);
-  }
-  // LDS read offsets (bytes, relative to the page buffer)
-  const int kgoff = kg * KW * kRowBytes;
-  const int fi = lds_swizzle(i & 7);
-  const int a_off0 = kgoff + i * kRowBytes + (((0 + g) ^ fi) << 4);
-  const int a_off1 = kgoff + i * kRowBytes + (((4 + g) ^ fi) << 4);
-  const int tr_row = 4 * g + (i >> 2);
-  const int ft = lds_swizzle(tr_row & 7);
-  const int hh = (i & 3) >> 1;
-  int t_off[4];
-#pragma unroll
-  for (int d4 = 0; d4 < 4; ++d4)
-    t_off[d4] = kgoff + tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
-
-  bf16x8 qreg[RT][18];
-  f32x4 o[RT][32];
-  float m_run[RT], l_run[RT];
-  int lim[RT];
-  int L = 0, n = 0, pbeg = 0, pend = 0, lim_min = 0;
-
-  auto load_q = [&](int b) {
-    if (active) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int row = row0 + rt * 16 + i;
-        load_q_rows(qreg[rt], reinterpret_cast<const bf16x8*>(
-                                  a.q + ((long long)b * a.M + row) * kDK + 8 * g));
-      }
-    }
-  };
-  auto start_piece = [&](int b, int k) {
-    L = ldc(a.seqlens + b);
-    n = n_pages(L);
-    pbeg = k;
-    pend = (b == b1) ? k1 : n;     // exclusive
-    lim_min = a.causal ? L - a.s_q + 1 : L;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int t = (row0 + rt * 16 + i) / a.h_q;
-      lim[rt] = a.causal ? L - a.s_q + 1 + t : L;
-      m_run[rt] = -INFINITY;
-      l_run[rt] = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-
-  // Pipeline (two page buffers).  A buffer is refilled with page p+2 as soon
-  // as every wave has finished computing page p in it, so while a wave waits
-  // for page p+1, pages p+1 and p+2 are both in flight.  The only vector
-  // memory ops in flight at a loop top are page loads (Q loads wait for
-  // themselves), so the wait for page p is vmcnt(18) when page p+1's 18 loads
-  // were issued after it (vmcnt retires in issue order), else vmcnt(0).
-  issue_page_load(smem, a, cur_b, cur_k, off, w);
-  load_q(cur_b);
-  int nxt_b = cur_b, nxt_k = cur_k + 1;
-  seek(a, nxt_b, nxt_k, b1, k1);
-  bool nxt_valid = before_end(a, nxt_b, nxt_k, b1, k1);
-  if (nxt_valid) issue_page_load(smem + kPageBytes, a, nxt_b, nxt_k, off, w);
-  start_piece(cur_b, cur_k);
-  int buf = 0;
-
-  // ---------------- one iteration per piece (request slice) ----------------
-  while (true) {
-    const int b = cur_b;
-    int k = cur_k;
-    int nn_b = 0, nn_k = 0;
-    bool nn_valid = false;
-    char* page;
-    // -------- pages of the piece --------
-    while (true) {
-      static_assert(kPageLoadsPerWave == 18, "wait count below");
-      if (nxt_valid)
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      wg_barrier();
-      page = smem + buf * kPageBytes;
-
-      if (active) {
-        // ---- scores S^T[key][row] = K . Q^T over 576 dims ----
-        // Software pipeline: operand reads for step ks+D1 are in flight while
-        // the MFMAs of step ks run; sched_barrier stops the compiler from
-        // hoisting every read of the unrolled loop (register blow-up).
-        constexpr int D1 = (RT * KT >= 8) ? 1 : 2;
-        f32x4 s[RT][KT];
-  #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-  #pragma unroll
-          for (int kt = 0; kt < KT; ++kt) s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 ka[D1 + 1][KT];
-  #pragma unroll
-        for (int ks = 0; ks < 18 + D1; ++ks) {
-          if (ks < 18) {
-            const char* ab = page + ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1);
-  #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-              ka[ks % (D1 + 1)][kt] = *reinterpret_cast<const bf16x8*>(ab + kt * 16 * kRowBytes);
-          }
-          const int cs = ks - D1;
-          if (cs >= 0) {
-  #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-  #pragma unroll
-              for (int kt = 0; kt < KT; ++kt)
-                s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    ka[cs % (D1 + 1)][kt], qreg[rt][cs], s[rt][kt], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // ---- online softmax (fp32, base 2, lazy rescale) ----
-        const int key0 = k * kBlock + kg * KW + 4 * g;
-        const bool need_mask = (k + 1) * kBlock > lim_min;
-        bf16x8 pb[RT][KP];
-  #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          float mx = -INFINITY;
-  #pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-  #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              float xv = s[rt][kt][v] * a.scale_log2;
-              if (need_mask && key0 + kt * 16 + v >= lim[rt]) xv = -INFINITY;
-              s[rt][kt][v] = xv;
-              mx = fmaxf(mx, xv);
-            }
-          mx = wave_max_4lanes(mx);
-          const float m_new = fmaxf(m_run[rt], mx);
-          // Keep the running max unless it grew by more than kRescaleSlack:
-          // probabilities stay <= 2^kRescaleSlack and the result is exact
-          // either way (numerator and denominator share the reference max).
-          const bool grow = m_new > m_run[rt] + kRescaleSlack;
-          if (__any(grow)) {
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[rt] - m_new) : 1.f;
-            if (grow) m_run[rt] = m_new;
-            l_run[rt] *= alpha;
-            // chunked so only a few accumulator tiles are in VGPRs at once
-  #pragma unroll
-            for (int d8 = 0; d8 < 32; d8 += 8) {
-  #pragma unroll
-              for (int dt = d8; dt < d8 + 8; ++dt) o[rt][dt] *= alpha;
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-          const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
-          float lsum = 0.f;
-  #pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-  #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float p = __builtin_amdgcn_exp2f(s[rt][kt][v] - m_use);
-              lsum += p;
-              pb[rt][kt >> 1][(kt & 1) * 4 + v] = (__bf16)p;
-            }
-          l_run[rt] += lsum;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // ---- O^T[dim][row] += V^T . P^T over this wave's keys ----
-        constexpr int D2 = (RT * KP >= 4) ? 1 : 2;
-        bf16x8 va[D2 + 1][KP];
-  #pragma unroll
-        for (int dt = 0; dt < 32 + D2; ++dt) {
-          if (dt < 32) {
-            const char* tb = page + t_off[dt & 3] + 128 * (dt >> 2);
-  #pragma unroll
-            for (int kp = 0; kp < KP; ++kp) {
-              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                  (MLA_LDS bf16x4*)(tb + (kp * 32) * kRowBytes));
-              const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                  (MLA_LDS bf16x4*)(tb + (kp * 32 + 16) * kRowBytes));
-              va[dt % (D2 + 1)][kp] =
-                  bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-          }
-          const int cd = dt - D2;
-          if (cd >= 0) {
-  #pragma unroll
-            for (int kp = 0; kp < KP; ++kp)
-  #pragma unroll
-              for (int rt = 0; rt < RT; ++rt)
-                o[rt][cd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    va[cd % (D2 + 1)][kp], pb[rt][kp], o[rt][cd], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-
-      // position of page k+2 (the refill of this buffer)
-      nn_b = nxt_b;
-      nn_k = nxt_k + 1;
-      if (nxt_valid) seek(a, nn_b, nn_k, b1, k1);
-      nn_valid = nxt_valid && before_end(a, nn_b, nn_k, b1, k1);
-      if (k + 1 >= pend) break;
-      // same piece continues with page k+1 (= nxt): refill this buffer
-      wg_barrier();  // every wave is done reading this buffer (reads consumed)
-      if (nn_valid) issue_page_load(page, a, nn_b, nn_k, off, w);
-      nxt_b = nn_b;
-      nxt_k = nn_k;
-      nxt_valid = nn_valid;
-      buf ^= 1;
-      ++k;
-    }
-
-    // ---- piece end: merge the KG key groups, then write ----
-    // With KG == 2 the partner wave's (m, l, O) go through this page
-    // buffer; the merge is folded into the store loop so the accumulators
-    // are only read here.
-    float a_self[RT], a_other[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      a_self[rt] = 1.f;
-      a_other[rt] = 0.f;
-    }
-    const f32x4* mo = nullptr;
-    if constexpr (KG == 2) {
-      wg_barrier();  // every wave is done reading this buffer (reads consumed)
-      f32x4* mw = reinterpret_cast<f32x4*>(page) + (rg * RT * 32) * 64;
-      float* mm = reinterpret_cast<float*>(page + RG * RT * 32 * 1024) + rg * RT * 128;
-      if (active && kg == 1) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-          for (int dt = 0; dt < 32; ++dt) mw[(rt * 32 + dt) * 64 + lane] = o[rt][dt];
-          mm[rt * 128 + lane] = m_run[rt];
-          mm[rt * 128 + 64 + lane] = l_run[rt];
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // partner's ds_writes done
-      wg_barrier();
-      if (active && kg == 0) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const float m1 = mm[rt * 128 + lane];
-          const float l1 = mm[rt * 128 + 64 + lane];
-          const float m0 = m_run[rt];
-          const float mn = fmaxf(m0, m1);
-          a_self[rt] = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mn);
-          a_other[rt] = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
-          l_run[rt] = l_run[rt] * a_self[rt] + l1 * a_other[rt];
-          m_run[rt] = mn;
-        }
-      }
-      mo = mw;
-    }
-
-    if (active && kg == 0) {
-      const bool whole = pbeg == 0 && pend == n;
-      const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
-      const long long slot = whole ? 0 : (long long)ldc(a.split_offsets + b) + sidx;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const float lt = wave_sum_4lanes(l_run[rt]);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const float lse2 = lt > 0.f ? m_run[rt] + log2f(lt) : -INFINITY;
-        const float cs = a_self[rt] * inv;
-        const float co = a_other[rt] * inv;
-        const int row = row0 + rt * 16 + i;
-        if (whole) {
-          uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + 4 * g;
-#pragma unroll
-          for (int d8 = 0; d8 < 32; d8 += 8) {
-#pragma unroll
-            for (int dt = d8; dt < d8 + 8; ++dt) {
-              f32x4 v = o[rt][dt] * cs;
-              if constexpr (KG == 2) v += mo[(rt * 32 + dt) * 64 + lane] * co;
-              const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-              *reinterpret_cast<bf16x4*>(op + dt * 16) = bv;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if (g == 0) a.lse[(long long)b * a.M + row] = lse2 * kLn2;
-        } else {
-          float* op = a.part_o + (slot * a.M + row) * kDV + 4 * g;
-#pragma unroll
-          for (int d8 = 0; d8 < 32; d8 += 8) {
-#pragma unroll
-            for (int dt = d8; dt < d8 + 8; ++dt) {
-              f32x4 v = o[rt][dt] * cs;
-              if constexpr (KG == 2) v += mo[(rt * 32 + dt) * 64 + lane] * co;
-              *reinterpret_cast<f32x4*>(op + dt * 16) = v;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if (g == 0) a.part_lse[slot * a.M + row] = lse2;
-        }
-      }
-    }
-
-    if (!nxt_valid) break;
-    // The next piece starts at page k+1 (already in flight): load its Q rows
-    // (the load waits for everything issued before it, page k+1 included),
-    // then refill this buffer with page k+2.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // merge-area reads done
-    wg_barrier();  // every wave is done with this buffer (incl. merge reads)
-    load_q(nxt_b);
-    if (nn_valid) issue_page_load(page, a, nn_b, nn_k, off, w);
-    start_piece(nxt_b, nxt_k);
-    cur_b = nxt_b;
-    cur_k = nxt_k;
-    nxt_b = nn_b;
-    nxt_k = nn_k;
-    nxt_valid = nn_valid;
-    buf ^= 1;
-  }
-}
-
 // --------------------------------------------------------------------------
 // Warp-specialised kernel for row tiles of 64 query rows (s_q*h_q >= 64).
 // Eight waves, two per SIMD, in two roles that work one unit apart so that
@@ -734,10 +298,19 @@ constexpr int kWSBufs = 4;
 constexpr int kHalfLoadsPerWave = 9;                // 36 1 KB slots over 4 value waves
 
 // Issue the 9 direct-to-LDS loads of half `h` of page k of request b for
-// value wave j: 1 KB slots j, j+4, ..., j+32 of the unit.  Same contract as
-// issue_page_load (asm, untracked by the compiler, M0 holds the LDS
-// destination, SCC clobbered; rows at or beyond the sequence end are
-// zero-filled by the range check).
+// value wave j: 1 KB slots j, j+4, ..., j+32 of the unit.  Rows at or beyond
+// the sequence end are zero-filled by the buffer range check.
+//
+// Written as inline asm on purpose: the compiler then does not track these
+// loads.  Tracked, every LDS read that it cannot prove disjoint from an
+// in-flight direct load (the transposed V reads, for one) gets an
+// "s_waitcnt vmcnt(0)", which would wait for the NEXT units' loads and
+// serialise the pipeline.  All waits for these loads are therefore explicit
+// (wait_unit in the kernel), and the asm clobbers "memory" so the compiler
+// keeps LDS accesses on the right side of it.  M0 holds the LDS destination;
+// nothing else in the kernels uses M0 (gfx9 LDS instructions do not), and one
+// wait state separates each M0 write from the load that reads it.  The M0
+// increments are SALU adds, which write SCC: SCC is declared clobbered.
 __device__ __forceinline__ void issue_half_load(char* lds_buf, const DecodeArgs& a, int b, int k,
                                                 int h, const int (&off)[9], int j) {
   const int L = ldc(a.seqlens + b);
@@ -782,16 +355,18 @@ __device__ __forceinline__ void next_unit(const DecodeArgs& a, int& b, int& k, i
   seek(a, b, k, b1, k1);
 }
 
+// RT: 16-row tiles in the workgroup tile (1, 2 or 4: 16, 32 or 64 query
+// rows); score waves q >= RT have no rows and only keep step with the others.
+template <int RT>
 __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const DecodeArgs a) {
   constexpr int NBUF = kWSBufs;
   constexpr int DL = 8;   // 16-dim output tiles per value wave (128 dims)
-  constexpr int RT = 4;   // 16-row tiles of the workgroup tile
 
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * kHalfBytes];
   __shared__ bf16x8 p_lds[2][RT][64];   // P^T operands: [unit parity][row tile][lane]
-  __shared__ float alpha_lds[2][64];    // per-row rescale factor of the unit
+  __shared__ float alpha_lds[2][16 * RT];   // per-row rescale factor of the unit
   __shared__ int grow_lds[2][RT];       // per row tile: any row rescaled
-  __shared__ float lfin_lds[2][64];     // per-row sum of a piece ending at the unit
+  __shared__ float lfin_lds[2][16 * RT];    // per-row sum of a piece ending at the unit
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -816,7 +391,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
   int cb = b0, ck = k0, ch = 0;
   seek(a, cb, ck, b1, k1);
   if (!before_end(a, cb, ck, b1, k1)) return;  // uniform: empty part
-  const int tile_row0 = rtile * 64;
+  const int tile_row0 = rtile * 16 * RT;
 
   // Piece bookkeeping shared by both roles: a piece is the run of units of
   // one request inside the part.
@@ -833,6 +408,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     // and the value wave's products fill the gaps.
     __builtin_amdgcn_s_setprio(1);
     const int q = w;
+    const bool active = q < RT;   // uniform: this wave has query rows
     const int row_own = tile_row0 + 16 * q + i;
     const int fi = lds_swizzle(i & 7);
     const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
@@ -854,10 +430,12 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         lim = a.causal ? L - a.s_q + 1 + row_own / a.h_q : L;
         m_run = -INFINITY;
         l_run = 0.f;
-        load_q_rows(qreg, reinterpret_cast<const bf16x8*>(
-                              a.q + ((long long)b * a.M + row_own) * kDK + 8 * g));
+        if (active)
+          load_q_rows(qreg, reinterpret_cast<const bf16x8*>(
+                                a.q + ((long long)b * a.M + row_own) * kDK + 8 * g));
       }
       const char* ubuf = smem + (t % NBUF) * kHalfBytes;
+      if (active) {
 
       // ---- S^T[key][row] = K . Q^T: 32 keys x this wave's 16 rows ----
       f32x4 s[2];
@@ -924,13 +502,14 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         const int any = __any(grow) ? 1 : 0;
         if (lane == 0) grow_lds[t & 1][q] = any;
       }
+      }   // active
 
       // ---- next unit; at a piece end publish the row sum and write the LSE ----
       int nb = cb, nk = ck, nh = ch;
       next_unit(a, nb, nk, nh, b1, k1);
       const bool more = before_end(a, nb, nk, b1, k1);
       new_piece = !(more && nb == b);
-      if (new_piece) {
+      if (new_piece && active) {
         const float lt = wave_sum_4lanes(l_run);
         const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
         bool whole;
@@ -1020,8 +599,11 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       const char* ubuf = smem + (t % NBUF) * kHalfBytes;
       const int par = t & 1;
 
-      // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all 64 rows ----
-      if (grow_lds[par][0] | grow_lds[par][1] | grow_lds[par][2] | grow_lds[par][3]) {
+      // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all rows ----
+      int grown = 0;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) grown |= grow_lds[par][rt];
+      if (grown) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const float al = alpha_lds[par][16 * rt + i];
@@ -1105,73 +687,110 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
 
 // Rows per workgroup tile.
 int tile_rows_for(int M) {
-  if (M <= 32) return 32;    // mla_splitkv_kernel<1, 2>
-  return 64;                 // mla_splitkv_ws_kernel (M = 128, 256: 2 or 4 row tiles)
+  if (M <= 16) return 16;    // mla_splitkv_ws_kernel<1>
+  if (M <= 32) return 32;    // mla_splitkv_ws_kernel<2>
+  return 64;                 // mla_splitkv_ws_kernel<4> (M = 128, 256: 2 or 4 row tiles)
 }
 
 hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
-  const dim3 grid(a.num_parts * a.row_tiles), block(kThreads);
-  if (a.row_tile_rows == 32)
-    hipExtLaunchKernelGGL((mla_splitkv_kernel<1, 2>), grid, block, 0, stream, start, stop, 0, a);
-  else
-    hipExtLaunchKernelGGL(mla_splitkv_ws_kernel, grid, dim3(kThreadsWS), 0, stream, start, stop,
-                          0, a);
+  const dim3 grid(a.num_parts * a.row_tiles);
+  const dim3 block(kThreadsWS);
+  const void* fn = a.row_tile_rows == 16   ? reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<1>)
+                   : a.row_tile_rows == 32 ? reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<2>)
+                                           : reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<4>);
+  if (start == nullptr && stop == nullptr) {
+    // plain launch (also what a HIP graph capture records)
+    if (a.row_tile_rows == 16)
+      hipLaunchKernelGGL(mla_splitkv_ws_kernel<1>, grid, block, 0, stream, a);
+    else if (a.row_tile_rows == 32)
+      hipLaunchKernelGGL(mla_splitkv_ws_kernel<2>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(mla_splitkv_ws_kernel<4>, grid, block, 0, stream, a);
+  } else {
+    // events recorded at the kernel's own start and end
+    void* args[] = {const_cast<DecodeArgs*>(&a)};
+    hipError_t e = hipExtLaunchKernel(fn, grid, block, args, 0, stream, start, stop, 0);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
 // LSE combine: exact merge of the split partials of each split request.
-// One workgroup per (request, 16 query rows); 16 threads per row, 32 dims
-// each (8 x float4, interleaved so a row's 16 threads read 256 contiguous
-// bytes per step).
+// One workgroup per (request, 16 query rows, quarter of the 512 output dims):
+// 16 threads per row, 8 dims each (2 x float4, interleaved so that a row's
+// 16 threads read 256 contiguous bytes per step).  Splitting the dims keeps
+// a few hundred workgroups in flight even for small batches.
 // --------------------------------------------------------------------------
+constexpr int kCombineQuarters = 4;
+
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const CombineArgs a) {
   const int b = blockIdx.x;
   const int r = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int dq = blockIdx.z * (kDV / kCombineQuarters);   // first dim of this quarter
   const int j = threadIdx.x & 15;
   if (r >= a.M) return;
   const int s0 = a.split_offsets[b];
   const int ns = a.split_offsets[b + 1] - s0;
-  uint16_t* op = a.out + ((long long)b * a.M + r) * kDV;
+  uint16_t* op = a.out + ((long long)b * a.M + r) * kDV + dq;
   if (ns == 0) {
     if (a.seqlens[b] <= 0) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < 2; ++c)
         *reinterpret_cast<uint2*>(op + (j + 16 * c) * 4) = make_uint2(0u, 0u);
-      if (j == 0) a.lse[(long long)b * a.M + r] = -INFINITY;
+      if (j == 0 && blockIdx.z == 0) a.lse[(long long)b * a.M + r] = -INFINITY;
     }
     return;
   }
-  float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_lse[(long long)(s0 + s) * a.M + r]);
-  f32x4 acc[8];
+  // Merge in groups of four partials: each group's loads (LSEs and rows) go
+  // out together, then fold into a running (max, weight sum, weighted row),
+  // the same exact log-sum-exp merge in a streaming order.
+  constexpr int G = 4;
+  float mx = -INFINITY, tot = 0.f;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int s = 0; s < ns; s += G) {
+    float ls[G];
+    f32x4 po[G][2];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const long long rowi = (long long)(s0 + s) * a.M + r;
-      const float ls = a.part_lse[rowi];
-      const float wgt = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
-      tot += wgt;
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + rowi * kDV);
+    for (int u = 0; u < G; ++u) {
+      const bool ok = s + u < ns;
+      const long long rowi = (long long)(s0 + (ok ? s + u : 0)) * a.M + r;
+      ls[u] = ok ? a.part_lse[rowi] : -INFINITY;
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + rowi * kDV + dq);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] += wgt * src[j + 16 * c];
+      for (int c = 0; c < 2; ++c) po[u][c] = src[j + 16 * c];
     }
+    float gm = mx;
+#pragma unroll
+    for (int u = 0; u < G; ++u) gm = fmaxf(gm, ls[u]);
+    if (gm == -INFINITY) continue;   // every partial so far is empty
+    const float al = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - gm);
+    tot *= al;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[c] *= al;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const float wgt = ls[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[u] - gm);
+      tot += wgt;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[c] += wgt * po[u][c];
+    }
+    mx = gm;
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < 2; ++c) {
     const f32x4 v = acc[c] * inv;
     const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     *reinterpret_cast<bf16x4*>(op + (j + 16 * c) * 4) = bv;
   }
-  if (j == 0) a.lse[(long long)b * a.M + r] = tot > 0.f ? (mx + log2f(tot)) * kLn2 : -INFINITY;
+  if (j == 0 && blockIdx.z == 0)
+    a.lse[(long long)b * a.M + r] = tot > 0.f ? (mx + log2f(tot)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  const dim3 grid(a.batch, (a.M + 15) / 16), block(kThreads);
+  const dim3 grid(a.batch, (a.M + 15) / 16, kCombineQuarters), block(kThreads);
   hipLaunchKernelGGL(mla_combine_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
