@@ -344,6 +344,29 @@ __device__ __forceinline__ void issue_half_load(char* lds_buf, const DecodeArgs&
 
 // Unit positions: (request b, page k, half h); the second half of a page is a
 // unit only if the page has keys in it.
+__device__ __forceinline__ int seqlen_of(const DecodeArgs& a, int b) {
+  return b < a.batch ? ldc(a.seqlens + b) : 0;
+}
+
+// Same walk as next_unit with the request length L cached: re-read only when
+// the position moves to another request.
+__device__ __forceinline__ void unit_next(const DecodeArgs& a, int& b, int& k, int& h, int& L,
+                                          int b1, int k1) {
+  if (h == 0 && L - k * kBlock > kHalfRows) {
+    h = 1;
+    return;
+  }
+  h = 0;
+  ++k;
+  while (before_end(a, b, k, b1, k1)) {
+    const int end = (b == b1) ? k1 : n_pages(L);
+    if (k < end) return;
+    ++b;
+    k = 0;
+    L = seqlen_of(a, b);
+  }
+}
+
 __device__ __forceinline__ void next_unit(const DecodeArgs& a, int& b, int& k, int& h, int b1,
                                           int k1) {
   if (h == 0 && ldc(a.seqlens + b) - k * kBlock > kHalfRows) {
@@ -391,6 +414,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
   int cb = b0, ck = k0, ch = 0;
   seek(a, cb, ck, b1, k1);
   if (!before_end(a, cb, ck, b1, k1)) return;  // uniform: empty part
+  int cL = seqlen_of(a, cb);
   const int tile_row0 = rtile * 16 * RT;
 
   // Piece bookkeeping shared by both roles: a piece is the run of units of
@@ -416,18 +440,17 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
 
     bf16x8 qreg[18];
     float m_run = -INFINITY, l_run = 0.f;
-    int lim = 0, lim_min = 0, L = 0, n = 0, pbeg = 0;
+    int lim = 0, lim_min = 0, n = 0, pbeg = 0;
     bool new_piece = true;
     int t = 0;
     while (true) {
       wg_barrier();   // unit t landed; P of unit t-2 consumed
       const int b = cb, k = ck, h = ch;
       if (new_piece) {
-        L = ldc(a.seqlens + b);
-        n = n_pages(L);
+        n = n_pages(cL);
         pbeg = k;
-        lim_min = a.causal ? L - a.s_q + 1 : L;
-        lim = a.causal ? L - a.s_q + 1 + row_own / a.h_q : L;
+        lim_min = a.causal ? cL - a.s_q + 1 : cL;
+        lim = a.causal ? cL - a.s_q + 1 + row_own / a.h_q : cL;
         m_run = -INFINITY;
         l_run = 0.f;
         if (active)
@@ -438,10 +461,15 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       if (active) {
 
       // ---- S^T[key][row] = K . Q^T: 32 keys x this wave's 16 rows ----
+      // Two accumulators per 16-key tile (even and odd 32-dim steps), so four
+      // independent MFMA chains hide the accumulate latency.
       f32x4 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       {
+        f32x4 sp[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) sp[kt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
         constexpr int D1 = 2;
         bf16x8 ka[D1 + 1][2];
 #pragma unroll
@@ -456,11 +484,13 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           if (cs >= 0) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
-              s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[cs % (D1 + 1)][kt], qreg[cs],
-                                                             s[kt], 0, 0, 0);
+              sp[kt][cs & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  ka[cs % (D1 + 1)][kt], qreg[cs], sp[kt][cs & 1], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) s[kt] = sp[kt][0] + sp[kt][1];
       }
 
       // ---- online softmax of row_own (fp32, base 2, lazy rescale) ----
@@ -505,10 +535,9 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       }   // active
 
       // ---- next unit; at a piece end publish the row sum and write the LSE ----
-      int nb = cb, nk = ck, nh = ch;
-      next_unit(a, nb, nk, nh, b1, k1);
-      const bool more = before_end(a, nb, nk, b1, k1);
-      new_piece = !(more && nb == b);
+      unit_next(a, cb, ck, ch, cL, b1, k1);
+      const bool more = before_end(a, cb, ck, b1, k1);
+      new_piece = !(more && cb == b);
       if (new_piece && active) {
         const float lt = wave_sum_4lanes(l_run);
         const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
@@ -525,9 +554,6 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P, alpha, flags, sums written
       ++t;
       if (!more) break;
-      cb = nb;
-      ck = nk;
-      ch = nh;
     }
     wg_barrier();   // the value waves' last product may start
   } else {
@@ -558,13 +584,13 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
 
     // issue cursor (ib, ik, ih); compute cursor (cb, ck, ch) is one unit behind
     // the score waves
-    int ib = cb, ik = ck, ih = 0;
+    int ib = cb, ik = ck, ih = 0, iL = cL;
     int issued = 0;
     auto issue_next = [&]() {
       if (before_end(a, ib, ik, b1, k1)) {
         issue_half_load(smem + (issued % NBUF) * kHalfBytes, a, ib, ik, ih, off, j);
         ++issued;
-        next_unit(a, ib, ik, ih, b1, k1);
+        unit_next(a, ib, ik, ih, iL, b1, k1);
       }
     };
     // wait until unit u has landed (units issued after it stay in flight)
@@ -588,7 +614,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     wait_unit(1);
     wg_barrier();   // b_1: unit 1 landed, P of unit 0 written
 
-    int L = ldc(a.seqlens + cb), n = n_pages(L), pbeg = ck;
+    int n = n_pages(cL), pbeg = ck;
     int t = 0;   // unit multiplied in this phase
     while (true) {
       // Unit t+3 goes into the buffer of unit t-1, free since the last
@@ -616,33 +642,28 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         bf16x8 pB[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) pB[rt] = p_lds[par][rt][lane];
-        constexpr int D2 = 1;
-        bf16x8 va[D2 + 1];
+        bf16x8 va[DL];
 #pragma unroll
-        for (int dl = 0; dl < DL + D2; ++dl) {
-          if (dl < DL) {
-            const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
-            const bf16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
-            va[dl % (D2 + 1)] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-          const int cd = dl - D2;
-          if (cd >= 0) {
+        for (int dl = 0; dl < DL; ++dl) {
+          const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
+          const bf16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
+          va[dl] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-              o[cd][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[cd % (D2 + 1)], pB[rt],
-                                                                 o[cd][rt], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int dl = 0; dl < DL; ++dl) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            o[dl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pB[rt], o[dl][rt], 0, 0, 0);
         }
       }
 
       // ---- next unit; at a piece end write O (by columns) and restart ----
-      int nb = cb, nk = ck, nh = ch;
-      next_unit(a, nb, nk, nh, b1, k1);
-      const bool more = before_end(a, nb, nk, b1, k1);
-      if (!(more && nb == b)) {
+      unit_next(a, cb, ck, ch, cL, b1, k1);
+      const bool more = before_end(a, cb, ck, b1, k1);
+      if (!(more && cb == b)) {
         bool whole;
         const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : n, n, whole);
 #pragma unroll
@@ -669,17 +690,13 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           __builtin_amdgcn_sched_barrier(0);
         }
         if (more) {
-          L = ldc(a.seqlens + nb);
-          n = n_pages(L);
-          pbeg = nk;
+          n = n_pages(cL);
+          pbeg = ck;
         }
       }
       if (!more) break;
       wait_unit(t + 2);
       wg_barrier();   // b_{t+2}: unit t+2 landed, P of unit t+1 written
-      cb = nb;
-      ck = nk;
-      ch = nh;
       ++t;
     }
   }
