@@ -39,29 +39,29 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "37986d50a251612af55ab864ee8d25b7043e89e851c69e9021dc1e5b1e3877fe",
-        "fetch_bytes": 308137142,
-        "write_bytes": 9882688,
-        "fetch_scale": 1.99986,
+        "kernel_sha256": "88e1c09cbed3f7605e73d16795edef7b6e057509ea7e9d20041a8f678000cacd",
+        "fetch_bytes": 307841000,
+        "write_bytes": 9882592,
+        "fetch_scale": 1.99987,
         "write_scale": 1.0
     },
     "ridge": {
-        "kernel_sha256": "37986d50a251612af55ab864ee8d25b7043e89e851c69e9021dc1e5b1e3877fe",
-        "fetch_bytes": 705006987,
+        "kernel_sha256": "88e1c09cbed3f7605e73d16795edef7b6e057509ea7e9d20041a8f678000cacd",
+        "fetch_bytes": 704687645,
         "write_bytes": 59894272,
-        "fetch_scale": 1.99992,
-        "write_scale": 1.0
-    },
-    "long": {
-        "kernel_sha256": "37986d50a251612af55ab864ee8d25b7043e89e851c69e9021dc1e5b1e3877fe",
-        "fetch_bytes": 771086643,
-        "write_bytes": 37559808,
         "fetch_scale": 1.99989,
         "write_scale": 1.0
     },
+    "long": {
+        "kernel_sha256": "88e1c09cbed3f7605e73d16795edef7b6e057509ea7e9d20041a8f678000cacd",
+        "fetch_bytes": 770863098,
+        "write_bytes": 37559808,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0
+    },
     "ragged": {
-        "kernel_sha256": "37986d50a251612af55ab864ee8d25b7043e89e851c69e9021dc1e5b1e3877fe",
-        "fetch_bytes": 510699178,
+        "kernel_sha256": "88e1c09cbed3f7605e73d16795edef7b6e057509ea7e9d20041a8f678000cacd",
+        "fetch_bytes": 510510339,
         "write_bytes": 78838784,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
