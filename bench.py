@@ -146,7 +146,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="membound",
-                    help="tiny | membound | ridge | ragged | long")
+                    help="tiny | membound | ridge | ragged | long | draft")
     ap.add_argument("--parts", type=int, default=None, help="override split-KV part count")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="cache flush between timed steps (outside the timed events)")

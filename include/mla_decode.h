@@ -62,6 +62,7 @@ extern "C" {
 #define MLA_D_K 576              /* key width: 512 latent + 64 rope */
 #define MLA_D_V 512              /* value width: first 512 dims of the key row */
 #define MLA_TILE_META_INTS 8     /* int32 words per part in tile_meta */
+#define MLA_MAX_S_Q 8            /* query tokens per request: 1 (decode) .. 8 (draft tokens) */
 
 /*
  * mla_decode_num_parts — host only, no HIP call.
@@ -69,7 +70,7 @@ extern "C" {
  * per compute unit.  A workgroup carries one row tile of query rows (up to 64
  * rows; s_q*h_q <= 32 fits one tile, larger counts use s_q*h_q/64 tiles), and
  * each part runs once per row tile, so parts = num_cus / row_tiles.
- *   h_q in {16,32,64,128}, s_q in {1,2}, h_kv == 1, num_cus >= 1.
+ *   h_q in {16,32,64,128}, 1 <= s_q <= MLA_MAX_S_Q, h_kv == 1, num_cus >= 1.
  * Returns MLA_OK and *num_parts_out >= 1, or an error status.
  */
 int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int num_cus,

@@ -26,7 +26,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool supported_h_q(int h_q) { return h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128; }
 
 int check_shape(int batch, int s_q, int h_q, int h_kv) {
-  if (batch < 1 || s_q < 1 || s_q > 2 || h_kv != 1 || h_q < 1) return MLA_ERR_INVALID_ARG;
+  if (batch < 1 || s_q < 1 || s_q > MLA_MAX_S_Q || h_kv != 1 || h_q < 1) return MLA_ERR_INVALID_ARG;
   if (!supported_h_q(h_q)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }

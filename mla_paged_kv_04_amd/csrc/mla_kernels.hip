@@ -432,7 +432,9 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     // and the value wave's products fill the gaps.
     __builtin_amdgcn_s_setprio(1);
     const int q = w;
-    const bool active = q < RT;   // uniform: this wave has query rows
+    // uniform: this wave's 16-row block exists (s_q*h_q is a multiple of 16,
+    // so a block is either all real rows or all beyond the last one)
+    const bool active = q < RT && tile_row0 + 16 * q < a.M;
     const int row_own = tile_row0 + 16 * q + i;
     const int fi = lds_swizzle(i & 7);
     const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
@@ -628,7 +630,8 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all rows ----
       int grown = 0;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) grown |= grow_lds[par][rt];
+      for (int rt = 0; rt < RT; ++rt)
+        if (tile_row0 + 16 * rt < a.M) grown |= grow_lds[par][rt];
       if (grown) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -671,7 +674,8 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           const float lt = lfin_lds[par][16 * rt + i];
           const float inv = lt > 0.f ? 1.f / lt : 0.f;
           const int row = tile_row0 + 16 * rt + i;
-          if (whole) {
+          if (tile_row0 + 16 * rt >= a.M) {   // rows past the last query row
+          } else if (whole) {
             uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + j * 128 + 4 * g;
 #pragma unroll
             for (int dl = 0; dl < DL; ++dl) {

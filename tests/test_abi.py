@@ -46,7 +46,10 @@ def test_num_parts():
     out = ctypes.c_int(0)
     L = mla.lib()
     assert L.mla_decode_num_parts(2, 1, 48, 1, 256, ctypes.byref(out)) == UNSUPPORTED
-    assert L.mla_decode_num_parts(2, 3, 16, 1, 256, ctypes.byref(out)) == INVALID
+    assert L.mla_decode_num_parts(2, 9, 16, 1, 256, ctypes.byref(out)) == INVALID
+    assert L.mla_decode_num_parts(2, 0, 16, 1, 256, ctypes.byref(out)) == INVALID
+    assert mla.num_parts(2, 3, 16, 1, 256) == 256          # 48 rows: one 64-row tile
+    assert mla.num_parts(2, 8, 128, 1, 256) == 16          # 1024 rows: sixteen tiles
     assert L.mla_decode_num_parts(2, 1, 16, 2, 256, ctypes.byref(out)) == INVALID
     assert L.mla_decode_num_parts(0, 1, 16, 1, 256, ctypes.byref(out)) == INVALID
     assert L.mla_decode_num_parts(2, 1, 16, 1, 0, ctypes.byref(out)) == INVALID
@@ -84,7 +87,7 @@ def _fwd_raw(**kw):
     (dict(tm=0), INVALID), (dict(so=0), INVALID), (dict(out=0), INVALID), (dict(lse=0), INVALID),
     (dict(q=8), INVALID), (dict(kc=4), INVALID), (dict(out=8), INVALID), (dict(lse=2), INVALID),
     (dict(ws=128), INVALID), (dict(ws=0), INVALID),
-    (dict(batch=0), INVALID), (dict(s_q=3), INVALID), (dict(h_kv=2), INVALID),
+    (dict(batch=0), INVALID), (dict(s_q=9), INVALID), (dict(s_q=0), INVALID), (dict(h_kv=2), INVALID),
     (dict(h_q=48), UNSUPPORTED), (dict(h_q=8), UNSUPPORTED),
     (dict(parts=0), INVALID), (dict(nblk=0), INVALID), (dict(bt_stride=0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),

@@ -84,6 +84,21 @@ def test_small_shapes(mla, h_q, s_q, parts):
     _assert_parity(out, lse, O_ref, L_ref, tag=f"small h{h_q} s{s_q} P={parts}")
 
 
+# Draft-token decode (speculative decoding): up to eight query tokens per
+# request, causal among themselves.  s_q*h_q = 48, 80, 112 ... leave the last
+# 64-row tile partly empty; lengths below s_q leave leading rows with no key.
+@pytest.mark.parametrize("h_q", [16, 64, 128])
+@pytest.mark.parametrize("s_q", [3, 4, 5, 8])
+@pytest.mark.parametrize("parts", [None, 5])
+def test_draft_tokens(mla, h_q, s_q, parts):
+    _say(f"case draft h_q={h_q} s_q={s_q} parts={parts}")
+    lens = [1, 3, 4, 63, 64, 65, 129, 300, 0, 7]
+    inp = build_inputs(lens, s_q, h_q, seed=300 + h_q + s_q, extra_pool=5)
+    out, lse, _ = _run(mla, inp, parts)
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal)
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"draft h{h_q} s{s_q} P={parts}")
+
+
 def test_non_causal_two_tokens(mla):
     _say("case non-causal s_q=2")
     inp = build_inputs([5, 70, 130], 2, 16, seed=5, extra_pool=2)
@@ -104,7 +119,7 @@ def _sample_requests(seqlens, k=6, seed=0):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("key", ["membound", "ridge", "ragged", "long"])
+@pytest.mark.parametrize("key", ["membound", "ridge", "ragged", "long", "draft"])
 def test_full_workload_sampled(mla, key):
     """Full-size workload in the benchmark's launch configuration; the oracle
     recomputes a sample of requests (incl. the longest and the shortest)."""

@@ -72,7 +72,7 @@ def test_plan_invariants(seqlens, P, s_q, h_q):
     _check_plan(seqlens, s_q, h_q, P)
 
 
-@pytest.mark.parametrize("key", ["tiny", "membound", "ridge", "ragged", "long"])
+@pytest.mark.parametrize("key", ["tiny", "membound", "ridge", "ragged", "long", "draft"])
 def test_plan_invariants_workloads(key):
     w = WORKLOADS[key]
     gen = torch.Generator().manual_seed(w.seed)

@@ -70,6 +70,11 @@ WORKLOADS: dict[str, Workload] = {
                      seqlen_kind="alt16k_64k", seed=1004, fixed_pool=10496,
                      desc="B=16, s_q=1, h_q=128, seqlens alternating 16384/65536, "
                           "pool 10496 blocks"),
+    # Beyond the five configurations above: decode of four draft tokens per
+    # request (speculative decoding), causal among themselves.
+    "draft": Workload("draft", "4-token draft decode", batch=32, s_q=4, h_q=128,
+                      seqlen_kind="uniform2048_8192", seed=1005, extra_pool=64,
+                      desc="B=32, s_q=4 causal, h_q=128, seqlens U[2048,8192]"),
 }
 
 # The order the workloads are listed in (index 0 is the small case).
@@ -83,6 +88,8 @@ def draw_seqlens(kind: str, batch: int, gen: torch.Generator) -> torch.Tensor:
         return torch.full((batch,), 4096, dtype=torch.int32)
     if kind == "uniform1024_8192":
         return torch.randint(1024, 8193, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
+    if kind == "uniform2048_8192":
+        return torch.randint(2048, 8193, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
     if kind == "lognormal":
         z = torch.randn((batch,), generator=gen, dtype=torch.float64)
         lens = torch.round(torch.exp(7.5 + 1.0 * z)).clamp(1, 32768)
