@@ -154,6 +154,9 @@ def main(argv=None) -> int:
                     help="run one plain elementwise copy of this many MiB (int32 -> int32) "
                          "after warmup, outside the timed region: the known-size kernel "
                          "that HBM byte counters are scaled against")
+    ap.add_argument("--with-append", action="store_true",
+                    help="include the paged-KV append of the step's new tokens "
+                         "(mla_kv_append) in every step")
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the step instead of eager launches "
                          "(slower on this stack: replays add ~4-14 us per step)")
@@ -182,6 +185,8 @@ def main(argv=None) -> int:
                      dtype=torch.uint8, device=dev)
     out = torch.empty((inp.batch, inp.s_q, inp.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((inp.batch, inp.s_q, inp.h_q), dtype=torch.float32, device=dev)
+    new_kv = (torch.randn((inp.batch, inp.s_q, 576), generator=torch.Generator().manual_seed(5))
+              .to(torch.bfloat16).to(dev)) if args.with_append else None
     flush_buf = torch.ones((1 << 28,), dtype=torch.int32, device=dev)   # 1 GiB
     flush_sink = torch.empty((), dtype=torch.int32, device=dev)
 
@@ -197,6 +202,8 @@ def main(argv=None) -> int:
     def step(evs=None):
         if evs is not None:
             evs[0].record()
+        if new_kv is not None:
+            mla.kv_append(new_kv, g.kcache, g.block_table, g.seqlens)
         meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
         mla.splitkv(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
                     out, lse, start_event=evs[2] if evs else None,
@@ -208,6 +215,8 @@ def main(argv=None) -> int:
     # Per-kernel breakdown of the scheduler and the combine (marker events
     # between kernels), in a separate loop after the timed one.
     def step_breakdown(evs):
+        if new_kv is not None:
+            mla.kv_append(new_kv, g.kcache, g.block_table, g.seqlens)
         evs[0].record()
         meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
         evs[1].record()
@@ -284,6 +293,16 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
 
     eager_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    append_ms = None
+    if new_kv is not None:
+        aevs = new_events()
+        for k in range(K):
+            flush()
+            aevs[k][0].record()
+            mla.kv_append(new_kv, g.kcache, g.block_table, g.seqlens)
+            aevs[k][1].record()
+        torch.cuda.synchronize(dev)
+        append_ms = [e[0].elapsed_time(e[1]) for e in aevs]
     step_ms = [e[0].elapsed_time(e[1]) for e in gevs] if graph is not None else eager_ms
     dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
     meta_ms = [e[0].elapsed_time(e[1]) for e in bevs]
@@ -328,7 +347,8 @@ def main(argv=None) -> int:
                    "s_q": inp.s_q, "h_q": inp.h_q, "h_kv": 1, "d_k": 576, "d_v": 512,
                    "block_size": 64, "total_keys": int(inp.seqlens.sum()),
                    "num_parts": parts, "cache_flush_between_steps": args.flush,
-                   "step_launch": "hip_graph" if graph is not None else "eager"},
+                   "step_launch": "hip_graph" if graph is not None else "eager",
+                   "kv_append_in_step": new_kv is not None},
         "tflops": round(tfl, 2),
         "algorithmic_bytes": counts["bytes"],
         "algorithmic_flops": counts["flops"],
@@ -337,7 +357,8 @@ def main(argv=None) -> int:
                        "splitkv_median": round(med(dec_ms), 5),
                        "splitkv_p90": round(sorted(dec_ms)[int(0.9 * (len(dec_ms) - 1))], 5),
                        "step_median": round(med(step_ms), 5),
-                       "eager_step": round(mean(eager_ms), 5)},
+                       "eager_step": round(mean(eager_ms), 5),
+                       "append": round(mean(append_ms), 5) if append_ms else None},
         "warm_ms_per_step": round(warm_ms, 5),
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": {

@@ -184,6 +184,25 @@ int mla_decode_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
                    int num_parts, void* workspace_d, size_t workspace_bytes,
                    void* out_d, float* lse_d, void* stream);
 
+/*
+ * mla_kv_append — enqueue the write of the s_q new tokens' key rows into the
+ * paged cache, the step that precedes decode.  Paging as for decode (page
+ * "深度剖析DeepSeek Infra开源全貌", DAY1 FlashMLA, feature ②: 64-token blocks):
+ * token j of request b is row j % 64 of page block_table[b][j / 64].  The
+ * lengths already count the new tokens, so new token t of request b is token
+ * seqlens[b] - s_q + t; positions before 0, page slots at or beyond
+ * bt_stride and page ids outside [0, num_blocks) are skipped (never written).
+ *   new_kv_d      bf16 [batch, s_q, 576] (16-byte aligned), read only
+ *   kcache_d      bf16 [num_blocks, 64, 1, 576] (16-byte aligned), written
+ *   block_table_d int32 [batch, bt_stride]; seqlens_d int32 [batch]
+ * 1 <= s_q <= MLA_MAX_S_Q.  Rows written by two requests (shared pages) get
+ * one of the writes.  Returns MLA_OK or an error status; nothing is enqueued
+ * on error.
+ */
+int mla_kv_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
+                  const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                  int batch, int s_q, void* stream);
+
 /* Static text for a status code. */
 const char* mla_status_string(int status);
 

@@ -4,6 +4,6 @@ The computation runs entirely in the HIP library libmla_decode.so (C ABI in
 include/mla_decode.h); this package only marshals torch tensors into it.
 """
 from .binding import (  # noqa: F401
-    MLAError, combine, device_num_cus, fwd, lib, metadata, num_parts, splitkv,
+    MLAError, combine, device_num_cus, fwd, kv_append, lib, metadata, num_parts, splitkv,
     status_string, workspace_bytes,
 )

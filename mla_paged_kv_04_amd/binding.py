@@ -48,6 +48,8 @@ _SIGNATURES = {
     "mla_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int,
                                 _c_int, _c_int, _c_int, _c_float, _c_int, _c_ptr, _c_ptr,
                                 _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_kv_append": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int, _c_int,
+                               _c_ptr]),
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_last_hip_error": (ctypes.c_char_p, []),
     "mla_device_num_cus": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
@@ -244,3 +246,21 @@ def fwd(q, kcache, block_table, seqlens, scale: float, causal: bool | None = Non
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)),
         "mla_decode_fwd")
     return out, lse
+
+
+def kv_append(new_kv: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
+              seqlens: torch.Tensor) -> torch.Tensor:
+    """Enqueue the write of new_kv [B, s_q, 576] (bf16) into the paged cache
+    (mla_kv_append); the lengths already count the new tokens.  Returns kcache."""
+    _require(new_kv, torch.bfloat16, "new_kv", 3)
+    _require(kcache, torch.bfloat16, "kcache", 4)
+    _require(block_table, torch.int32, "block_table", 2)
+    _require(seqlens, torch.int32, "seqlens", 1)
+    batch, s_q, dk = new_kv.shape
+    if dk != D_K or kcache.shape[1] != BLOCK_SIZE or kcache.shape[3] != D_K:
+        raise ValueError(f"shape mismatch: new_kv {tuple(new_kv.shape)}, "
+                         f"kcache {tuple(kcache.shape)}")
+    _check(lib().mla_kv_append(_ptr(new_kv), _ptr(kcache), kcache.shape[0], _ptr(block_table),
+                               block_table.shape[1], _ptr(seqlens), batch, s_q,
+                               _stream(new_kv.device)), "mla_kv_append")
+    return kcache

@@ -207,6 +207,23 @@ int mla_decode_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
                             workspace_d, workspace_bytes, out_d, lse_d, stream);
 }
 
+int mla_kv_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
+                  const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                  int batch, int s_q, void* stream) {
+  if (batch < 1 || s_q < 1 || s_q > MLA_MAX_S_Q || num_blocks < 1 || bt_stride < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!new_kv_d || !kcache_d || !block_table_d || !seqlens_d) return MLA_ERR_INVALID_ARG;
+  if (!aligned(new_kv_d, 16) || !aligned(kcache_d, 16) || !aligned(block_table_d, 4) ||
+      !aligned(seqlens_d, 4))
+    return MLA_ERR_INVALID_ARG;
+  hipError_t e = mla::launch_kv_append(static_cast<const uint16_t*>(new_kv_d),
+                                       static_cast<uint16_t*>(kcache_d), num_blocks,
+                                       block_table_d, bt_stride, seqlens_d, batch, s_q,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mla_kv_append launch");
+  return MLA_OK;
+}
+
 const char* mla_status_string(int status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";

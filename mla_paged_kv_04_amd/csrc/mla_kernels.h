@@ -69,6 +69,10 @@ hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t st
                           hipEvent_t stop = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
+hipError_t launch_kv_append(const uint16_t* new_kv, uint16_t* kcache, long long num_blocks,
+                            const int32_t* block_table, int bt_stride, const int32_t* seqlens,
+                            int batch, int s_q, hipStream_t stream);
+
 // Row-tile geometry chosen for M query rows (rows per workgroup tile).
 int tile_rows_for(int M);
 

@@ -816,4 +816,32 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------
+// Paged-KV append: one workgroup per (request, new token); 72 lanes copy the
+// 1152-byte row as 16-byte words.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void mla_kv_append_kernel(
+    const uint16_t* __restrict__ new_kv, uint16_t* __restrict__ kcache, long long num_blocks,
+    const int32_t* __restrict__ block_table, int bt_stride,
+    const int32_t* __restrict__ seqlens, int s_q) {
+  const int b = blockIdx.x, t = blockIdx.y;
+  const int c = threadIdx.x;
+  if (c >= kChunksPerRow) return;
+  const int pos = seqlens[b] - s_q + t;
+  if (pos < 0 || pos / kBlock >= bt_stride) return;
+  const int page = block_table[(long long)b * bt_stride + pos / kBlock];
+  if (page < 0 || (long long)page >= num_blocks) return;
+  const uint4* src = reinterpret_cast<const uint4*>(new_kv + ((long long)b * s_q + t) * kDK);
+  uint4* dst = reinterpret_cast<uint4*>(kcache + ((long long)page * kBlock + pos % kBlock) * kDK);
+  dst[c] = src[c];
+}
+
+hipError_t launch_kv_append(const uint16_t* new_kv, uint16_t* kcache, long long num_blocks,
+                            const int32_t* block_table, int bt_stride, const int32_t* seqlens,
+                            int batch, int s_q, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_kv_append_kernel, dim3(batch, s_q), dim3(128), 0, stream, new_kv,
+                     kcache, num_blocks, block_table, bt_stride, seqlens, s_q);
+  return hipGetLastError();
+}
+
 }  // namespace mla

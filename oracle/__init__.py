@@ -5,5 +5,5 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may use it.
 from .mla_decode_oracle import (  # noqa: F401
     decode, decode_bruteforce, lse_merge, split_plan, plan_pieces,
     gather_request_kv, visible_count, attend_rows, fixed_cost_pages, rows_per_tile,
-    num_pages,
+    num_pages, kv_append,
 )

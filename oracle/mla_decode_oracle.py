@@ -99,6 +99,32 @@ def gather_request_kv(kcache, block_table, seqlens, b: int) -> np.ndarray:
     return K[:L]
 
 
+def kv_append(kcache, block_table, seqlens, new_kv) -> np.ndarray:
+    """The cache after writing each request's s_q new key rows into their pages.
+
+    Paging as above (64-token pages, token j in row j % 64 of page
+    block_table[b][j // 64]); the lengths already count the new tokens, so new
+    token t of request b is token L_b - s_q + t.  Positions before 0 (a
+    request shorter than s_q) and positions whose page slot is outside the
+    block table are not written.  Returns a new array (the input's dtype is
+    kept, so bf16 rows are copied bit for bit); new_kv is [B, s_q, 576].
+    """
+    kc = kcache.clone() if hasattr(kcache, "clone") else np.array(kcache, copy=True)
+    bt = _i64(block_table)
+    sl = _i64(seqlens)
+    B, s_q = int(new_kv.shape[0]), int(new_kv.shape[1])
+    for b in range(B):
+        for t in range(s_q):
+            pos = int(sl[b]) - s_q + t
+            if pos < 0 or pos // BLOCK_SIZE >= bt.shape[1]:
+                continue
+            page = int(bt[b, pos // BLOCK_SIZE])
+            if page < 0 or page >= kc.shape[0]:
+                continue
+            kc[page, pos % BLOCK_SIZE, 0, :] = new_kv[b, t, :]
+    return kc
+
+
 def visible_count(L: int, s_q: int, t: int, causal: bool) -> int:
     """Number of keys query token t of a request of length L may see."""
     if not causal:

@@ -113,3 +113,19 @@ def test_combine_rejects_before_launch():
     p = ctypes.c_void_p
     assert L.mla_decode_combine(p(16), 2, 1, 16, p(16), 4, p(256), 10, p(16), p(16), None) == WORKSPACE
     assert L.mla_decode_combine(None, 2, 1, 16, p(16), 4, p(256), 1 << 30, p(16), p(16), None) == INVALID
+
+
+def test_kv_append_rejects_before_launch():
+    L = mla.lib()
+    p = ctypes.c_void_p
+    ok = dict(nkv=p(16), kc=p(16), nblk=8, bt=p(16), bt_stride=2, sl=p(16), batch=2, s_q=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.mla_kv_append(a["nkv"], a["kc"], a["nblk"], a["bt"], a["bt_stride"], a["sl"],
+                               a["batch"], a["s_q"], None)
+
+    for kw in (dict(nkv=None), dict(kc=None), dict(bt=None), dict(sl=None), dict(nkv=p(8)),
+               dict(kc=p(24)), dict(bt=p(2)), dict(sl=p(6)), dict(nblk=0), dict(bt_stride=0),
+               dict(batch=0), dict(s_q=0), dict(s_q=9)):
+        assert call(**kw) == INVALID, kw

@@ -307,3 +307,27 @@ def test_single_token_exact(mla):
         v = inp.kcache[int(inp.block_table[b, 0]), 0, 0, :512]
         assert torch.equal(out[b, 0].cpu().view(torch.int16),
                            v.expand(128, 512).contiguous().view(torch.int16))
+
+
+# ---- paged-KV append --------------------------------------------------------
+
+@pytest.mark.parametrize("s_q", [1, 2, 5])
+def test_kv_append_matches_oracle(mla, s_q):
+    """The cache after the append equals the oracle's, bit for bit (new rows
+    written, everything else untouched), and decode over it matches the
+    oracle's decode over the oracle's cache."""
+    from oracle import kv_append
+    _say(f"case append s_q={s_q}")
+    lens = [1, 63, 64, 65, 130, 0, 2, 1000]
+    inp = build_inputs(lens, s_q, 64, seed=500 + s_q, extra_pool=4)
+    g = inp.to("cuda")
+    new = torch.randn((inp.batch, s_q, 576), generator=torch.Generator().manual_seed(9)).to(
+        torch.bfloat16)
+    mla.kv_append(new.cuda(), g.kcache, g.block_table, g.seqlens)
+    torch.cuda.synchronize()
+    ref = kv_append(inp.kcache, inp.block_table, inp.seqlens, new)
+    assert torch.equal(g.kcache.cpu().view(torch.int16), ref.view(torch.int16))
+    out, lse = mla.fwd(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal)
+    torch.cuda.synchronize()
+    O_ref, L_ref = decode(inp.q, ref, inp.block_table, inp.seqlens, inp.scale, inp.causal)
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"append s{s_q}")

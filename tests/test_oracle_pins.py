@@ -292,3 +292,48 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert not _golden_all_pass()
     monkeypatch.setattr(omod, "gather_request_kv", orig_gather)
     assert _golden_all_pass()
+
+
+# ---- paged-KV append (the cache write that precedes decode) ----------------
+
+def _append_case(seed=7):
+    from workloads import build_inputs
+    inp = build_inputs([1, 63, 64, 65, 130, 0, 2], 3, 16, seed=seed, extra_pool=3)
+    g = torch.Generator().manual_seed(seed + 1)
+    new = torch.randn((inp.batch, 3, 576), generator=g).to(torch.bfloat16)
+    return inp, new
+
+
+def test_append_round_trip():
+    """After the append, gathering each request through its block table gives
+    the new rows at positions L-s_q .. L-1 (bit for bit) and every earlier
+    row unchanged; a request shorter than s_q gets only its last L rows."""
+    from oracle import gather_request_kv, kv_append
+    inp, new = _append_case()
+    kc2 = kv_append(inp.kcache, inp.block_table, inp.seqlens, new)
+    for b, L in enumerate(inp.seqlens.tolist()):
+        before = gather_request_kv(inp.kcache, inp.block_table, inp.seqlens, b)
+        after = gather_request_kv(kc2, inp.block_table, inp.seqlens, b)
+        k0 = max(0, L - 3)
+        np.testing.assert_array_equal(after[:k0], before[:k0])
+        for t in range(3):
+            pos = L - 3 + t
+            if pos >= 0:
+                np.testing.assert_array_equal(after[pos], new[b, t].double().numpy())
+
+
+def test_append_touches_only_new_rows():
+    """Rows not owned by a request's new tokens (other pages, tails, the NaN
+    sentinel page) are left exactly as they were."""
+    from oracle import kv_append
+    inp, new = _append_case(11)
+    kc2 = kv_append(inp.kcache, inp.block_table, inp.seqlens, new)
+    written = set()
+    for b, L in enumerate(inp.seqlens.tolist()):
+        for t in range(3):
+            pos = L - 3 + t
+            if pos >= 0:
+                written.add((int(inp.block_table[b, pos // 64]), pos % 64))
+    diff = ~torch.eq(kc2.view(torch.int16), inp.kcache.view(torch.int16)).all(dim=-1).squeeze(-1)
+    changed = {(int(p), int(r)) for p, r in torch.nonzero(diff).tolist()}
+    assert changed <= written
