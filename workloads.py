@@ -115,6 +115,7 @@ class DecodeInputs:
     causal: bool
     s_q: int
     h_q: int
+    kv_format: str = "bf16"    # "bf16": kcache as above; "fp8": uint8 [num_blocks, 41216]
 
     @property
     def batch(self) -> int:
@@ -123,7 +124,7 @@ class DecodeInputs:
     def to(self, device) -> "DecodeInputs":
         return DecodeInputs(self.q.to(device), self.kcache.to(device),
                             self.block_table.to(device), self.seqlens.to(device),
-                            self.scale, self.causal, self.s_q, self.h_q)
+                            self.scale, self.causal, self.s_q, self.h_q, self.kv_format)
 
 
 def build_inputs(seqlens, s_q: int, h_q: int, seed: int, pool: int | None = None,
@@ -174,13 +175,100 @@ def build_inputs(seqlens, s_q: int, h_q: int, seed: int, pool: int | None = None
                         scale=D_K ** -0.5, causal=s_q > 1, s_q=s_q, h_q=h_q)
 
 
-def make_inputs(key: str, nan_tails: bool = True) -> DecodeInputs:
-    """The seeded inputs of one named workload (see WORKLOADS)."""
+# FP8 cache page: codes uint8 [64][512] | rope bf16 [64][64] | scale fp32 [64]
+FP8_LATENT = 512
+FP8_CODES_OFF = 0
+FP8_ROPE_OFF = BLOCK_SIZE * FP8_LATENT                        # 32768
+FP8_SCALE_OFF = FP8_ROPE_OFF + BLOCK_SIZE * (D_K - FP8_LATENT) * 2   # 40960
+FP8_PAGE_BYTES = FP8_SCALE_OFF + BLOCK_SIZE * 4               # 41216
+FP8_NAN_CODE = 0x7F
+
+
+def build_fp8_inputs(seqlens, s_q: int, h_q: int, seed: int, pool: int | None = None,
+                     extra_pool: int = 64, nan_tails: bool = True,
+                     q_scale: float = 1.0, gen: torch.Generator | None = None) -> DecodeInputs:
+    """Paged FP8-cache inputs for explicit per-request lengths.
+
+    Draw order: permutation, Q (as in ``build_inputs``), then per page slab:
+    latent z ~ N(0,1) fp32 [64, 512] per page, per-token scale exponents
+    e ~ U{-7,-6,-5}, rope ~ N(0,1) fp32 [64, 64].  Codes are torch's E4M3
+    cast of clamp(64*z, -448, 448) and the scale is 2^e, so latent values are
+    about N(0, 2^(e+6)) (the spread of quantised N(0,1) rows).  The sentinel
+    page and the rows beyond each request's length are NaN in all three
+    fields (code 0x7F, NaN rope, NaN scale).
+    """
+    seqlens = torch.as_tensor(seqlens, dtype=torch.int32).reshape(-1)
+    if gen is None:
+        gen = torch.Generator().manual_seed(seed)
+    batch = int(seqlens.shape[0])
+    nblk = [blocks_for(int(x)) for x in seqlens]
+    total = sum(nblk)
+    if pool is None:
+        pool = total + extra_pool
+    if pool < total:
+        raise ValueError(f"pool {pool} smaller than the {total} pages needed")
+    perm = torch.randperm(pool, generator=gen).to(torch.int32)
+    bt_stride = max(1, max(nblk) if nblk else 1)
+    block_table = torch.full((batch, bt_stride), pool, dtype=torch.int32)
+    pos = 0
+    for b, n in enumerate(nblk):
+        block_table[b, :n] = perm[pos:pos + n]
+        pos += n
+    q = torch.randn((batch, s_q, h_q, D_K), generator=gen, dtype=torch.float32)
+    if q_scale != 1.0:
+        q = q * q_scale
+    q = q.to(torch.bfloat16)
+    kv = torch.empty((pool + 1, FP8_PAGE_BYTES), dtype=torch.uint8)
+    slab = 512
+    n_rope = D_K - FP8_LATENT
+    for s in range(0, pool, slab):
+        e = min(pool, s + slab)
+        n = e - s
+        z = torch.randn((n, BLOCK_SIZE, FP8_LATENT), generator=gen, dtype=torch.float32)
+        ex = torch.randint(-7, -4, (n, BLOCK_SIZE), generator=gen, dtype=torch.int64)
+        rope = torch.randn((n, BLOCK_SIZE, n_rope), generator=gen, dtype=torch.float32)
+        codes = (64.0 * z).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        kv[s:e, FP8_CODES_OFF:FP8_ROPE_OFF] = codes.reshape(n, -1)
+        kv[s:e, FP8_ROPE_OFF:FP8_SCALE_OFF] = \
+            rope.to(torch.bfloat16).contiguous().view(torch.uint8).reshape(n, -1)
+        scl = torch.pow(2.0, ex.to(torch.float32))
+        kv[s:e, FP8_SCALE_OFF:] = scl.contiguous().view(torch.uint8).reshape(n, -1)
+    _fp8_nan_rows(kv, pool, 0, BLOCK_SIZE)
+    if nan_tails:
+        for b, n in enumerate(nblk):
+            L = int(seqlens[b])
+            tail = n * BLOCK_SIZE - L
+            if n > 0 and tail > 0:
+                _fp8_nan_rows(kv, int(block_table[b, n - 1]), BLOCK_SIZE - tail, BLOCK_SIZE)
+    return DecodeInputs(q=q, kcache=kv, block_table=block_table, seqlens=seqlens,
+                        scale=D_K ** -0.5, causal=s_q > 1, s_q=s_q, h_q=h_q,
+                        kv_format="fp8")
+
+
+def _fp8_nan_rows(kv: torch.Tensor, page: int, r0: int, r1: int) -> None:
+    """Fill rows [r0, r1) of an FP8 page with NaN in codes, rope and scale."""
+    pg = kv[page]
+    pg[FP8_CODES_OFF + r0 * FP8_LATENT:FP8_CODES_OFF + r1 * FP8_LATENT] = FP8_NAN_CODE
+    n_rope = D_K - FP8_LATENT
+    nan_bf = torch.full(((r1 - r0) * n_rope,), float("nan"), dtype=torch.bfloat16)
+    pg[FP8_ROPE_OFF + r0 * n_rope * 2:FP8_ROPE_OFF + r1 * n_rope * 2] = nan_bf.view(torch.uint8)
+    nan_f = torch.full((r1 - r0,), float("nan"), dtype=torch.float32)
+    pg[FP8_SCALE_OFF + 4 * r0:FP8_SCALE_OFF + 4 * r1] = nan_f.view(torch.uint8)
+
+
+def make_inputs(key: str, nan_tails: bool = True, kv_format: str = "bf16") -> DecodeInputs:
+    """The seeded inputs of one named workload (see WORKLOADS); kv_format
+    "fp8" gives the same lengths, table and Q with an FP8 cache."""
     w = WORKLOADS[key]
     gen = torch.Generator().manual_seed(w.seed)
     seqlens = draw_seqlens(w.seqlen_kind, w.batch, gen)
     total = sum(blocks_for(int(x)) for x in seqlens)
     pool = w.fixed_pool if w.fixed_pool is not None else total + w.extra_pool
+    if kv_format == "fp8":
+        return build_fp8_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
+                                nan_tails=nan_tails, gen=gen)
+    if kv_format != "bf16":
+        raise ValueError(f"unknown kv_format {kv_format}")
     return build_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
                         nan_tails=nan_tails, gen=gen)
 
