@@ -203,6 +203,70 @@ int mla_kv_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
                   const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
                   int batch, int s_q, void* stream);
 
+/*
+ * FP8 key cache.  Page "云上玩转DeepSeek系列之五：实测优化16%，体验FlashMLA加速
+ * DeepSeek-V2-Lite推理" (ruibaoantu.com), section 四, item 2 (monitoring and
+ * tuning), names FP8 precision as a further throughput step and gives no
+ * format; this library's format keeps the attention defined above and stores
+ * the 512 latent dims as OCP FP8 E4M3 codes with one fp32 scale per token,
+ * the 64 rope dims in bf16.  One page of 64 tokens is MLA_FP8_PAGE_BYTES:
+ *   [0, 32768)      codes uint8 [64][512]   E4M3 codes of latent dims 0..511
+ *   [32768, 40960)  rope  bf16  [64][64]    dims 512..575
+ *   [40960, 41216)  scale fp32  [64]        latent value = e4m3(code) * scale
+ * E4M3: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0,
+ * exponent 0 = subnormals m * 2^-9, S.1111.111 = NaN, no infinities, largest
+ * finite 448.  The decode kernels accept any finite scale; mla_kv_append_fp8
+ * writes power-of-two scales.
+ */
+#define MLA_FP8_PAGE_BYTES 41216
+#define MLA_FP8_ROPE_OFFSET 32768
+#define MLA_FP8_SCALE_OFFSET 40960
+
+/*
+ * mla_decode_splitkv_fp8 — mla_decode_splitkv over an FP8 cache:
+ *   kcache_fp8_d  uint8 [num_blocks, MLA_FP8_PAGE_BYTES] (16-byte aligned)
+ * The keys are K[j, 0:512] = e4m3(code) * scale, K[j, 512:576] = rope; the
+ * products run on bf16 MFMA with fp32 accumulation (codes convert to bf16
+ * exactly; the per-token scale multiplies the fp32 score sum and, for the
+ * value product, the probability before its bf16 rounding).  start_event /
+ * stop_event as in mla_decode_splitkv_timed (both may be NULL).  All other
+ * arguments, validation and status codes as mla_decode_splitkv; the partials
+ * go to the same workspace and are merged by mla_decode_combine.
+ */
+int mla_decode_splitkv_fp8(const void* q_d, const void* kcache_fp8_d, int64_t num_blocks,
+                           const int32_t* block_table_d, int bt_stride,
+                           const int32_t* seqlens_d, int batch, int s_q, int h_q,
+                           int h_kv, float scale, int causal,
+                           const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                           int num_parts, void* workspace_d, size_t workspace_bytes,
+                           void* out_d, float* lse_d, void* start_event,
+                           void* stop_event, void* stream);
+
+/*
+ * mla_decode_fwd_fp8 — mla_decode_splitkv_fp8 followed by mla_decode_combine
+ * on the same stream.
+ */
+int mla_decode_fwd_fp8(const void* q_d, const void* kcache_fp8_d, int64_t num_blocks,
+                       const int32_t* block_table_d, int bt_stride,
+                       const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                       float scale, int causal,
+                       const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                       int num_parts, void* workspace_d, size_t workspace_bytes,
+                       void* out_d, float* lse_d, void* stream);
+
+/*
+ * mla_kv_append_fp8 — mla_kv_append into an FP8 cache.  Each new bf16 row x
+ * (new_kv_d bf16 [batch, s_q, 576]) is quantised: amax = max |x[0:512]|, the
+ * scale s is the smallest power of two with amax <= 448*s (1 if amax = 0),
+ * code_d = E4M3 round-to-nearest-even of x_d / s (exact division, no
+ * saturation needed); the rope dims are copied bit for bit and s is stored
+ * as fp32.  Positions, skipping rules, arguments and status codes as
+ * mla_kv_append; kcache_fp8_d uint8 [num_blocks, MLA_FP8_PAGE_BYTES].
+ */
+int mla_kv_append_fp8(const void* new_kv_d, void* kcache_fp8_d, int64_t num_blocks,
+                      const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                      int batch, int s_q, void* stream);
+
 /* Static text for a status code. */
 const char* mla_status_string(int status);
 

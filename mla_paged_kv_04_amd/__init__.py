@@ -4,6 +4,6 @@ The computation runs entirely in the HIP library libmla_decode.so (C ABI in
 include/mla_decode.h); this package only marshals torch tensors into it.
 """
 from .binding import (  # noqa: F401
-    MLAError, combine, device_num_cus, fwd, kv_append, lib, metadata, num_parts, splitkv,
-    status_string, workspace_bytes,
+    FP8_PAGE_BYTES, MLAError, combine, device_num_cus, fwd, fwd_fp8, kv_append, kv_append_fp8,
+    lib, metadata, num_parts, splitkv, splitkv_fp8, status_string, workspace_bytes,
 )

@@ -21,6 +21,7 @@ BLOCK_SIZE = 64
 D_K = 576
 D_V = 512
 TILE_META_INTS = 8
+FP8_PAGE_BYTES = 41216     # codes [64][512] | bf16 rope [64][64] | fp32 scale [64]
 
 _c_int = ctypes.c_int
 _c_ptr = ctypes.c_void_p
@@ -50,6 +51,15 @@ _SIGNATURES = {
                                 _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
     "mla_kv_append": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int, _c_int,
                                _c_ptr]),
+    "mla_decode_splitkv_fp8": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr,
+                                        _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                        _c_ptr, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr,
+                                        _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_decode_fwd_fp8": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int,
+                                    _c_int, _c_int, _c_int, _c_float, _c_int, _c_ptr, _c_ptr,
+                                    _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_kv_append_fp8": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int,
+                                   _c_int, _c_ptr]),
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_last_hip_error": (ctypes.c_char_p, []),
     "mla_device_num_cus": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
@@ -163,12 +173,20 @@ def _alloc_workspace(batch, s_q, h_q, parts, device, workspace):
     return workspace
 
 
-def _decode_args(q, kcache, block_table, seqlens):
+def _decode_args(q, kcache, block_table, seqlens, fp8: bool = False):
     _require(q, torch.bfloat16, "q", 4)
-    _require(kcache, torch.bfloat16, "kcache", 4)
+    if fp8:
+        _require(kcache, torch.uint8, "kcache (FP8 pages)", 2)
+    else:
+        _require(kcache, torch.bfloat16, "kcache", 4)
     _require(block_table, torch.int32, "block_table", 2)
     _require(seqlens, torch.int32, "seqlens", 1)
     batch, s_q, h_q, dk = q.shape
+    if fp8:
+        if dk != D_K or kcache.shape[1] != FP8_PAGE_BYTES:
+            raise ValueError(f"shape mismatch: q {tuple(q.shape)}, FP8 kcache "
+                             f"{tuple(kcache.shape)} (pages of {FP8_PAGE_BYTES} bytes)")
+        return batch, s_q, h_q, 1
     if dk != D_K or kcache.shape[1] != BLOCK_SIZE or kcache.shape[3] != D_K:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kcache {tuple(kcache.shape)}")
     h_kv = kcache.shape[2]
@@ -263,4 +281,59 @@ def kv_append(new_kv: torch.Tensor, kcache: torch.Tensor, block_table: torch.Ten
     _check(lib().mla_kv_append(_ptr(new_kv), _ptr(kcache), kcache.shape[0], _ptr(block_table),
                                block_table.shape[1], _ptr(seqlens), batch, s_q,
                                _stream(new_kv.device)), "mla_kv_append")
+    return kcache
+
+
+def splitkv_fp8(q, kcache, block_table, seqlens, scale: float, causal: bool, meta: Metadata,
+                workspace: torch.Tensor, out=None, lse=None, start_event=None, stop_event=None):
+    """splitkv over an FP8 cache: kcache uint8 [num_blocks, 41216]
+    (mla_decode_splitkv_fp8; the events as in splitkv)."""
+    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens, fp8=True)
+    out, lse = _outputs(q, out, lse)
+    _check(lib().mla_decode_splitkv_fp8(
+        _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
+        _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _event_handle(start_event), _event_handle(stop_event), _stream(q.device)),
+        "mla_decode_splitkv_fp8")
+    return out, lse
+
+
+def fwd_fp8(q, kcache, block_table, seqlens, scale: float, causal: bool | None = None,
+            meta: Metadata | None = None, parts: int | None = None, workspace=None,
+            out=None, lse=None):
+    """Paged MLA decode over an FP8 cache (kcache uint8 [num_blocks, 41216]):
+    returns (O bf16 [B, s_q, h_q, 512], LSE fp32 [B, s_q, h_q])."""
+    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens, fp8=True)
+    if causal is None:
+        causal = s_q > 1
+    if meta is None:
+        meta = metadata(seqlens, s_q, h_q, h_kv, parts)
+    workspace = _alloc_workspace(batch, s_q, h_q, meta.num_parts, q.device, workspace)
+    out, lse = _outputs(q, out, lse)
+    _check(lib().mla_decode_fwd_fp8(
+        _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
+        _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)),
+        "mla_decode_fwd_fp8")
+    return out, lse
+
+
+def kv_append_fp8(new_kv: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
+                  seqlens: torch.Tensor) -> torch.Tensor:
+    """Enqueue the quantising write of new_kv [B, s_q, 576] (bf16) into an FP8
+    cache, uint8 [num_blocks, 41216] (mla_kv_append_fp8).  Returns kcache."""
+    _require(new_kv, torch.bfloat16, "new_kv", 3)
+    _require(kcache, torch.uint8, "kcache (FP8 pages)", 2)
+    _require(block_table, torch.int32, "block_table", 2)
+    _require(seqlens, torch.int32, "seqlens", 1)
+    batch, s_q, dk = new_kv.shape
+    if dk != D_K or kcache.shape[1] != FP8_PAGE_BYTES:
+        raise ValueError(f"shape mismatch: new_kv {tuple(new_kv.shape)}, "
+                         f"FP8 kcache {tuple(kcache.shape)}")
+    _check(lib().mla_kv_append_fp8(_ptr(new_kv), _ptr(kcache), kcache.shape[0],
+                                   _ptr(block_table), block_table.shape[1], _ptr(seqlens),
+                                   batch, s_q, _stream(new_kv.device)), "mla_kv_append_fp8")
     return kcache

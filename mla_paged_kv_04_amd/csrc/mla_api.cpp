@@ -72,6 +72,63 @@ int check_common(const void* seqlens, const void* split_offsets, int batch, int 
   return MLA_OK;
 }
 
+// Validation and launch of the decode kernel for either cache format.
+int splitkv_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                 const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                 int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                 const int32_t* tile_meta_d, const int32_t* split_offsets_d, int num_parts,
+                 void* workspace_d, size_t workspace_bytes, void* out_d, float* lse_d,
+                 int kv_fp8, void* start_event, void* stop_event, void* stream) {
+  int st = check_common(seqlens_d, split_offsets_d, batch, s_q, h_q, h_kv, num_parts,
+                        workspace_d, workspace_bytes, out_d, lse_d);
+  if (st != MLA_OK) return st;
+  if (!q_d || !kcache_d || !block_table_d || !tile_meta_d) return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_d, 16) || !aligned(kcache_d, 16) || !aligned(block_table_d, 4) ||
+      !aligned(tile_meta_d, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (num_blocks < 1 || bt_stride < 1 || !isfinite(scale) || (causal != 0 && causal != 1))
+    return MLA_ERR_INVALID_ARG;
+  mla::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q_d);
+  a.kcache = kcache_d;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table_d;
+  a.seqlens = seqlens_d;
+  a.tile_meta = tile_meta_d;
+  a.split_offsets = split_offsets_d;
+  split_workspace(workspace_d, s_q, h_q, num_parts, &a.part_o, &a.part_lse);
+  a.out = static_cast<uint16_t*>(out_d);
+  a.lse = lse_d;
+  a.bt_stride = bt_stride;
+  a.batch = batch;
+  a.s_q = s_q;
+  a.h_q = h_q;
+  a.M = s_q * h_q;
+  a.causal = causal;
+  a.num_parts = num_parts;
+  a.row_tiles = row_tiles(s_q, h_q);
+  a.row_tile_rows = mla::tile_rows_for(s_q * h_q);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.kv_fp8 = kv_fp8;
+  hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream),
+                                     static_cast<hipEvent_t>(start_event),
+                                     static_cast<hipEvent_t>(stop_event));
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_splitkv launch");
+  return MLA_OK;
+}
+
+int check_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
+                 const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                 int batch, int s_q) {
+  if (batch < 1 || s_q < 1 || s_q > MLA_MAX_S_Q || num_blocks < 1 || bt_stride < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!new_kv_d || !kcache_d || !block_table_d || !seqlens_d) return MLA_ERR_INVALID_ARG;
+  if (!aligned(new_kv_d, 16) || !aligned(kcache_d, 16) || !aligned(block_table_d, 4) ||
+      !aligned(seqlens_d, 4))
+    return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,41 +178,23 @@ int mla_decode_splitkv_timed(const void* q_d, const void* kcache_d, int64_t num_
                              const int32_t* split_offsets_d, int num_parts, void* workspace_d,
                              size_t workspace_bytes, void* out_d, float* lse_d,
                              void* start_event, void* stop_event, void* stream) {
-  int st = check_common(seqlens_d, split_offsets_d, batch, s_q, h_q, h_kv, num_parts,
-                        workspace_d, workspace_bytes, out_d, lse_d);
-  if (st != MLA_OK) return st;
-  if (!q_d || !kcache_d || !block_table_d || !tile_meta_d) return MLA_ERR_INVALID_ARG;
-  if (!aligned(q_d, 16) || !aligned(kcache_d, 16) || !aligned(block_table_d, 4) ||
-      !aligned(tile_meta_d, 4))
-    return MLA_ERR_INVALID_ARG;
-  if (num_blocks < 1 || bt_stride < 1 || !isfinite(scale) || (causal != 0 && causal != 1))
-    return MLA_ERR_INVALID_ARG;
-  mla::DecodeArgs a;
-  a.q = static_cast<const uint16_t*>(q_d);
-  a.kcache = static_cast<const uint16_t*>(kcache_d);
-  a.num_blocks = num_blocks;
-  a.block_table = block_table_d;
-  a.seqlens = seqlens_d;
-  a.tile_meta = tile_meta_d;
-  a.split_offsets = split_offsets_d;
-  split_workspace(workspace_d, s_q, h_q, num_parts, &a.part_o, &a.part_lse);
-  a.out = static_cast<uint16_t*>(out_d);
-  a.lse = lse_d;
-  a.bt_stride = bt_stride;
-  a.batch = batch;
-  a.s_q = s_q;
-  a.h_q = h_q;
-  a.M = s_q * h_q;
-  a.causal = causal;
-  a.num_parts = num_parts;
-  a.row_tiles = row_tiles(s_q, h_q);
-  a.row_tile_rows = mla::tile_rows_for(s_q * h_q);
-  a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream),
-                                     static_cast<hipEvent_t>(start_event),
-                                     static_cast<hipEvent_t>(stop_event));
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_splitkv launch");
-  return MLA_OK;
+  return splitkv_impl(q_d, kcache_d, num_blocks, block_table_d, bt_stride, seqlens_d, batch,
+                      s_q, h_q, h_kv, scale, causal, tile_meta_d, split_offsets_d, num_parts,
+                      workspace_d, workspace_bytes, out_d, lse_d, 0, start_event, stop_event,
+                      stream);
+}
+
+int mla_decode_splitkv_fp8(const void* q_d, const void* kcache_fp8_d, int64_t num_blocks,
+                           const int32_t* block_table_d, int bt_stride,
+                           const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                           float scale, int causal, const int32_t* tile_meta_d,
+                           const int32_t* split_offsets_d, int num_parts, void* workspace_d,
+                           size_t workspace_bytes, void* out_d, float* lse_d,
+                           void* start_event, void* stop_event, void* stream) {
+  return splitkv_impl(q_d, kcache_fp8_d, num_blocks, block_table_d, bt_stride, seqlens_d, batch,
+                      s_q, h_q, h_kv, scale, causal, tile_meta_d, split_offsets_d, num_parts,
+                      workspace_d, workspace_bytes, out_d, lse_d, 1, start_event, stop_event,
+                      stream);
 }
 
 int mla_decode_splitkv(const void* q_d, const void* kcache_d, int64_t num_blocks,
@@ -207,20 +246,46 @@ int mla_decode_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
                             workspace_d, workspace_bytes, out_d, lse_d, stream);
 }
 
+int mla_decode_fwd_fp8(const void* q_d, const void* kcache_fp8_d, int64_t num_blocks,
+                       const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                       int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                       const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                       int num_parts, void* workspace_d, size_t workspace_bytes, void* out_d,
+                       float* lse_d, void* stream) {
+  int st = mla_decode_splitkv_fp8(q_d, kcache_fp8_d, num_blocks, block_table_d, bt_stride,
+                                  seqlens_d, batch, s_q, h_q, h_kv, scale, causal, tile_meta_d,
+                                  split_offsets_d, num_parts, workspace_d, workspace_bytes,
+                                  out_d, lse_d, nullptr, nullptr, stream);
+  if (st != MLA_OK) return st;
+  return mla_decode_combine(seqlens_d, batch, s_q, h_q, split_offsets_d, num_parts,
+                            workspace_d, workspace_bytes, out_d, lse_d, stream);
+}
+
 int mla_kv_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
                   const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
                   int batch, int s_q, void* stream) {
-  if (batch < 1 || s_q < 1 || s_q > MLA_MAX_S_Q || num_blocks < 1 || bt_stride < 1)
-    return MLA_ERR_INVALID_ARG;
-  if (!new_kv_d || !kcache_d || !block_table_d || !seqlens_d) return MLA_ERR_INVALID_ARG;
-  if (!aligned(new_kv_d, 16) || !aligned(kcache_d, 16) || !aligned(block_table_d, 4) ||
-      !aligned(seqlens_d, 4))
-    return MLA_ERR_INVALID_ARG;
+  int st = check_append(new_kv_d, kcache_d, num_blocks, block_table_d, bt_stride, seqlens_d,
+                        batch, s_q);
+  if (st != MLA_OK) return st;
   hipError_t e = mla::launch_kv_append(static_cast<const uint16_t*>(new_kv_d),
                                        static_cast<uint16_t*>(kcache_d), num_blocks,
                                        block_table_d, bt_stride, seqlens_d, batch, s_q,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mla_kv_append launch");
+  return MLA_OK;
+}
+
+int mla_kv_append_fp8(const void* new_kv_d, void* kcache_fp8_d, int64_t num_blocks,
+                      const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                      int batch, int s_q, void* stream) {
+  int st = check_append(new_kv_d, kcache_fp8_d, num_blocks, block_table_d, bt_stride, seqlens_d,
+                        batch, s_q);
+  if (st != MLA_OK) return st;
+  hipError_t e = mla::launch_kv_append_fp8(static_cast<const uint16_t*>(new_kv_d),
+                                           static_cast<uint8_t*>(kcache_fp8_d), num_blocks,
+                                           block_table_d, bt_stride, seqlens_d, batch, s_q,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mla_kv_append_fp8 launch");
   return MLA_OK;
 }
 

@@ -28,7 +28,7 @@ inline int rows_per_tile(int s_q, int h_q) {
 
 struct DecodeArgs {
   const uint16_t* q;          // bf16 [B, s_q, h_q, 576]
-  const uint16_t* kcache;     // bf16 [num_blocks, 64, 1, 576]
+  const void* kcache;         // bf16 [num_blocks, 64, 1, 576], or FP8 pages [num_blocks, 41216 B]
   long long num_blocks;
   const int32_t* block_table; // [B, bt_stride]
   const int32_t* seqlens;     // [B]
@@ -48,6 +48,7 @@ struct DecodeArgs {
   int row_tiles;
   int row_tile_rows;          // query rows per workgroup tile (32, 64 or 128)
   float scale_log2;           // scale * log2(e)
+  int kv_fp8;                 // 1: kcache holds FP8 pages
 };
 
 struct CombineArgs {
@@ -72,6 +73,10 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const uint16_t* new_kv, uint16_t* kcache, long long num_blocks,
                             const int32_t* block_table, int bt_stride, const int32_t* seqlens,
                             int batch, int s_q, hipStream_t stream);
+
+hipError_t launch_kv_append_fp8(const uint16_t* new_kv, uint8_t* kcache, long long num_blocks,
+                                const int32_t* block_table, int bt_stride,
+                                const int32_t* seqlens, int batch, int s_q, hipStream_t stream);
 
 // Row-tile geometry chosen for M query rows (rows per workgroup tile).
 int tile_rows_for(int M);

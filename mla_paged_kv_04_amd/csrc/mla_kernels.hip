@@ -42,6 +42,8 @@ namespace mla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 #define MLA_LDS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
@@ -378,14 +380,141 @@ __device__ __forceinline__ void next_unit(const DecodeArgs& a, int& b, int& k, i
   seek(a, b, k, b1, k1);
 }
 
+// --------------------------------------------------------------------------
+// FP8 cache pages.  A page of 64 tokens is 41216 bytes:
+//   [0, 32768)      E4M3 codes of latent dims 0..511, uint8 [64][512]
+//   [32768, 40960)  rope dims 512..575 in bf16, [64][64]
+//   [40960, 41216)  per-token fp32 scale, [64]; latent = e4m3(code) * scale
+// A half-page unit in LDS holds its 32 rows of codes (16 KB), of rope (4 KB)
+// and its 32 scales (a 256-byte slot): 20736 bytes.
+// --------------------------------------------------------------------------
+constexpr int kF8Latent = 512;
+constexpr int kF8RopeOff = kBlock * kF8Latent;             // 32768
+constexpr int kF8ScaleOff = kF8RopeOff + kBlock * 64 * 2;  // 40960
+constexpr int kF8PageBytes = kF8ScaleOff + kBlock * 4;     // 41216
+constexpr int kF8UnitCodes = 0;
+constexpr int kF8UnitRope = kHalfRows * kF8Latent;         // 16384
+constexpr int kF8UnitScale = kF8UnitRope + kHalfRows * 128;   // 20480
+constexpr int kF8UnitBytes = kF8UnitScale + 256;           // 20736
+
+// Swizzles of the FP8 unit, chosen by measurement on gfx950 (LDS throughput
+// of the kernel's own read patterns under candidate XOR swizzles):
+//  * code rows (512 B = 32 units): unit c of row r at c ^ f8_code_swizzle(r).
+//    Both patterns run at the conflict-free rate — 16 rows at one unit
+//    (ds_read_b128, score operand: 4.9 clk per wave instruction per CU) and
+//    8 rows {4g..4g+3, 16+4g..16+4g+3} x 16 bytes per 16-lane group
+//    (ds_read_b64_tr_b8, value operand: 2.9 clk, against 4.4 for r & 15);
+//  * rope rows (128 B = 8 units): unit c of row r at c ^ ((r >> 1) & 7)
+//    (4.8 clk, against 16.2 unswizzled).
+__device__ __forceinline__ int f8_code_swizzle(int r) { return (r & 15) ^ (8 * ((r >> 4) & 1)); }
+__device__ __forceinline__ int f8_rope_swizzle(int r) { return (r >> 1) & 7; }
+
+// Issue the direct-to-LDS loads of half `h` of FP8 page k of request b for
+// value wave j: code slots j, j+4, j+8, j+12 (1 KB each), rope slot j, and
+// for wave 0 the unit's 32 scales (one dword per lane; lanes past the 32nd
+// fall outside the range and write zeros).  Each of the three regions has
+// its own buffer resource whose range ends at the sequence end, so rows
+// past it are zero-filled: zero codes, rope and scale.  Same asm rationale
+// as issue_half_load; M0 advances by 4 KB between all six loads.
+__device__ __forceinline__ void issue_half_load_f8(char* lds_buf, const DecodeArgs& a, int b,
+                                                   int k, int h, const int (&offc)[4], int offr,
+                                                   int offs, int j) {
+  const int L = ldc(a.seqlens + b);
+  int rows = L - k * kBlock - h * kHalfRows;
+  rows = rows > kHalfRows ? kHalfRows : rows;
+  int page = -1;
+  if (k < a.bt_stride) page = ldc(a.block_table + (long long)b * a.bt_stride + k);
+  const bool ok = page >= 0 && (long long)page < a.num_blocks && rows > 0;
+  const char* pg = reinterpret_cast<const char*>(a.kcache) + (ok ? (long long)page * kF8PageBytes : 0);
+  const int nr = uni(ok ? rows : 0);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(pg + h * kHalfRows * kF8Latent), 0, nr * kF8Latent, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(pg + kF8RopeOff + h * kHalfRows * 128), 0, nr * 128, kRsrcWord3);
+  const uint32_t m0 = uni(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_buf)) + j * 1024));
+#define MLA_DMA(O, R) "s_nop 0\n\tbuffer_load_dwordx4 %[" #O "], %[" #R "], 0 offen lds\n\t"
+#define MLA_M0_NEXT "s_add_u32 m0, m0, 0x1000\n\t"
+  if (j == 0) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(pg + kF8ScaleOff + h * kHalfRows * 4), 0, nr * 4, kRsrcWord3);
+    asm volatile(
+        "s_mov_b32 m0, %[m]\n\t"
+        MLA_DMA(o0, rc) MLA_M0_NEXT MLA_DMA(o1, rc) MLA_M0_NEXT MLA_DMA(o2, rc) MLA_M0_NEXT
+        MLA_DMA(o3, rc) MLA_M0_NEXT MLA_DMA(o4, rr) MLA_M0_NEXT
+        "s_nop 0\n\tbuffer_load_dword %[o5], %[rs], 0 offen lds\n\t"
+        :
+        : [m] "s"(m0), [rc] "s"(rc), [rr] "s"(rr), [rs] "s"(rs), [o0] "v"(offc[0]),
+          [o1] "v"(offc[1]), [o2] "v"(offc[2]), [o3] "v"(offc[3]), [o4] "v"(offr), [o5] "v"(offs)
+        : "memory", "m0", "scc");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %[m]\n\t"
+        MLA_DMA(o0, rc) MLA_M0_NEXT MLA_DMA(o1, rc) MLA_M0_NEXT MLA_DMA(o2, rc) MLA_M0_NEXT
+        MLA_DMA(o3, rc) MLA_M0_NEXT MLA_DMA(o4, rr)
+        :
+        : [m] "s"(m0), [rc] "s"(rc), [rr] "s"(rr), [o0] "v"(offc[0]), [o1] "v"(offc[1]),
+          [o2] "v"(offc[2]), [o3] "v"(offc[3]), [o4] "v"(offr)
+        : "memory", "m0", "scc");
+  }
+#undef MLA_DMA
+#undef MLA_M0_NEXT
+}
+
+// Q rows for the FP8 score product.  A lane's 16-byte code read covers 16
+// consecutive latent dims, 64p + 16g .. +16, which feed two MFMA steps; Q
+// follows the same order: q[2p + e] = dims 64p + 16g + 8e .. +8 (p < 8), and
+// q[16 + s] = rope dims 512 + 32s + 8g .. +8.  qlat points at dim 16g of the
+// row, qrope at dim 512 + 8g.  Same asm rationale as load_q_rows.
+__device__ __forceinline__ void load_q_rows_f8(bf16x8 (&q)[18], const bf16x8* qlat,
+                                               const bf16x8* qrope) {
+  asm volatile(
+      "global_load_dwordx4 %0, %18, off\n\t"
+      "global_load_dwordx4 %1, %18, off offset:16\n\t"
+      "global_load_dwordx4 %2, %18, off offset:128\n\t"
+      "global_load_dwordx4 %3, %18, off offset:144\n\t"
+      "global_load_dwordx4 %4, %18, off offset:256\n\t"
+      "global_load_dwordx4 %5, %18, off offset:272\n\t"
+      "global_load_dwordx4 %6, %18, off offset:384\n\t"
+      "global_load_dwordx4 %7, %18, off offset:400\n\t"
+      "global_load_dwordx4 %8, %18, off offset:512\n\t"
+      "global_load_dwordx4 %9, %18, off offset:528\n\t"
+      "global_load_dwordx4 %10, %18, off offset:640\n\t"
+      "global_load_dwordx4 %11, %18, off offset:656\n\t"
+      "global_load_dwordx4 %12, %18, off offset:768\n\t"
+      "global_load_dwordx4 %13, %18, off offset:784\n\t"
+      "global_load_dwordx4 %14, %18, off offset:896\n\t"
+      "global_load_dwordx4 %15, %18, off offset:912\n\t"
+      "global_load_dwordx4 %16, %19, off\n\t"
+      "global_load_dwordx4 %17, %19, off offset:64\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]),
+        "=&v"(q[6]), "=&v"(q[7]), "=&v"(q[8]), "=&v"(q[9]), "=&v"(q[10]), "=&v"(q[11]),
+        "=&v"(q[12]), "=&v"(q[13]), "=&v"(q[14]), "=&v"(q[15]), "=&v"(q[16]), "=&v"(q[17])
+      : "v"(qlat), "v"(qrope)
+      : "memory");
+}
+
+// Eight E4M3 codes (two dwords, code e in byte e) to bf16, exactly: every
+// E4M3 value is a bf16 value.  Hardware conversion with a unit scale.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // RT: 16-row tiles in the workgroup tile (1, 2 or 4: 16, 32 or 64 query
 // rows); score waves q >= RT have no rows and only keep step with the others.
-template <int RT>
+// F8: the cache holds FP8 pages (layout above) instead of bf16 rows.
+template <int RT, bool F8>
 __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const DecodeArgs a) {
   constexpr int NBUF = kWSBufs;
   constexpr int DL = 8;   // 16-dim output tiles per value wave (128 dims)
+  constexpr int UB = F8 ? kF8UnitBytes : kHalfBytes;   // bytes of one unit buffer
 
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * UB];
   __shared__ bf16x8 p_lds[2][RT][64];   // P^T operands: [unit parity][row tile][lane]
   __shared__ float alpha_lds[2][16 * RT];   // per-row rescale factor of the unit
   __shared__ int grow_lds[2][RT];       // per row tile: any row rescaled
@@ -439,6 +568,14 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     const int fi = lds_swizzle(i & 7);
     const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
     const int a_off1 = a_off0 ^ 64;   // unit 4+g instead of g (row bases are multiples of 128)
+    // FP8 unit: code rows 16kt + i at unit (4p + g) ^ f8_code_swizzle(row),
+    // i.e. address co[kt] ^ 64p; rope rows at unit (4s + g) ^ ((i >> 1) & 7),
+    // i.e. (ro ^ 64s) + 2048kt
+    int co[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+      co[kt] = (16 * kt + i) * kF8Latent + ((g ^ f8_code_swizzle(16 * kt + i)) << 4);
+    const int ro = kF8UnitRope + i * 128 + ((g ^ f8_rope_swizzle(i)) << 4);
 
     bf16x8 qreg[18];
     float m_run = -INFINITY, l_run = 0.f;
@@ -455,18 +592,24 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         lim = a.causal ? cL - a.s_q + 1 + row_own / a.h_q : cL;
         m_run = -INFINITY;
         l_run = 0.f;
-        if (active)
-          load_q_rows(qreg, reinterpret_cast<const bf16x8*>(
-                                a.q + ((long long)b * a.M + row_own) * kDK + 8 * g));
+        if (active) {
+          const uint16_t* qrow = a.q + ((long long)b * a.M + row_own) * kDK;
+          if constexpr (F8)
+            load_q_rows_f8(qreg, reinterpret_cast<const bf16x8*>(qrow + 16 * g),
+                           reinterpret_cast<const bf16x8*>(qrow + kF8Latent + 8 * g));
+          else
+            load_q_rows(qreg, reinterpret_cast<const bf16x8*>(qrow + 8 * g));
+        }
       }
-      const char* ubuf = smem + (t % NBUF) * kHalfBytes;
+      const char* ubuf = smem + (t % NBUF) * UB;
       if (active) {
 
       // ---- S^T[key][row] = K . Q^T: 32 keys x this wave's 16 rows ----
-      // Two accumulators per 16-key tile (even and odd 32-dim steps), so four
-      // independent MFMA chains hide the accumulate latency.
       f32x4 s[2];
-      {
+      f32x4 sc[2];   // FP8: scales of the lane's keys 16kt + 4g + v
+      if constexpr (!F8) {
+        // Two accumulators per 16-key tile (even and odd 32-dim steps), so
+        // four independent MFMA chains hide the accumulate latency.
         f32x4 sp[2][2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -493,6 +636,56 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) s[kt] = sp[kt][0] + sp[kt][1];
+      } else {
+        // Latent dims: raw E4M3 code products in two chains per key tile
+        // (the scale is per key, so it multiplies the finished sum); rope
+        // dims (bf16) in a third chain.
+        f32x4 sp[2][2], sr[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          sp[kt][0] = sp[kt][1] = sr[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        constexpr int DP = 2;   // code reads issued this many steps ahead
+        u32x4 kc[DP + 1][2];
+        bf16x8 ra[2][2];
+#pragma unroll
+        for (int ps = 0; ps < 8 + DP; ++ps) {
+          if (ps < 8) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+              kc[ps % (DP + 1)][kt] = *reinterpret_cast<const u32x4*>(ubuf + (co[kt] ^ (64 * ps)));
+          }
+          if (ps == 0) {
+#pragma unroll
+            for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt)
+                ra[rs][kt] = *reinterpret_cast<const bf16x8*>(ubuf + (ro ^ (64 * rs)) + 2048 * kt);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+              sc[kt] = *reinterpret_cast<const f32x4*>(ubuf + kF8UnitScale + 4 * (16 * kt + 4 * g));
+          }
+          const int cp = ps - DP;
+          if (cp >= 0) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              const u32x4 w = kc[cp % (DP + 1)][kt];
+              sp[kt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(w[0], w[1]),
+                                                                  qreg[2 * cp], sp[kt][0], 0, 0, 0);
+              sp[kt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  e4m3x8_to_bf16(w[2], w[3]), qreg[2 * cp + 1], sp[kt][1], 0, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            sr[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[rs][kt], qreg[16 + rs], sr[kt],
+                                                             0, 0, 0);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) s[kt] = sc[kt] * (sp[kt][0] + sp[kt][1]) + sr[kt];
       }
 
       // ---- online softmax of row_own (fp32, base 2, lazy rescale) ----
@@ -526,7 +719,8 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           for (int v = 0; v < 4; ++v) {
             const float p = __builtin_amdgcn_exp2f(s[kt][v] - m_use);
             lsum += p;
-            pb[kt * 4 + v] = (__bf16)p;
+            // FP8: the value operand holds raw codes, so P carries the key's scale
+            pb[kt * 4 + v] = (__bf16)(F8 ? p * sc[kt][v] : p);
           }
         l_run += lsum;
         p_lds[t & 1][q][lane] = pb;
@@ -578,6 +772,28 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     for (int d4 = 0; d4 < 4; ++d4)
       t_off[d4] = 256 * j + tr_row * kRowBytes + (((2 * d4 + hh) ^ ft) << 4) + ((i & 1) << 3);
 
+    // FP8 unit: direct-load offsets (code slots j + 4m, rope slot j, scales)
+    // and the transposed code read: lanes 2e, 2e+1 of a 16-lane group point
+    // at the two 8-byte halves of key row kap(g, e) (the keys of P's element
+    // e), dims 128j + 16dl .. +16, so lane i receives dim i of all 8 keys.
+    int offc[4], offr, offs, f8_t0;
+    {
+      const int lane = tid & 63;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int p = 64 * (j + 4 * m) + lane;   // 16-byte unit of the code region
+        const int r = p >> 5;
+        offc[m] = r * kF8Latent + (((p & 31) ^ f8_code_swizzle(r)) << 4);
+      }
+      const int pr = 64 * j + lane;               // 16-byte unit of the rope region
+      const int rr = pr >> 3;
+      offr = rr * 128 + (((pr & 7) ^ f8_rope_swizzle(rr)) << 4);
+      offs = 4 * lane;
+      const int e = i >> 1;
+      const int kap = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+      f8_t0 = kap * kF8Latent + ((i & 1) << 3) + (((8 * j) ^ f8_code_swizzle(kap)) << 4);
+    }
+
     f32x4 o[DL][RT];
 #pragma unroll
     for (int dl = 0; dl < DL; ++dl)
@@ -590,21 +806,37 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     int issued = 0;
     auto issue_next = [&]() {
       if (before_end(a, ib, ik, b1, k1)) {
-        issue_half_load(smem + (issued % NBUF) * kHalfBytes, a, ib, ik, ih, off, j);
+        if constexpr (F8)
+          issue_half_load_f8(smem + (issued % NBUF) * UB, a, ib, ik, ih, offc, offr, offs, j);
+        else
+          issue_half_load(smem + (issued % NBUF) * kHalfBytes, a, ib, ik, ih, off, j);
         ++issued;
         unit_next(a, ib, ik, ih, iL, b1, k1);
       }
     };
     // wait until unit u has landed (units issued after it stay in flight)
+    // (loads per unit and wave: 9 for bf16; for FP8 6 on wave 0, 5 on the others)
     auto wait_unit = [&](int u) {
       static_assert(kHalfLoadsPerWave == 9, "wait counts below");
       const int ahead = issued - u - 1;
-      if (ahead >= 2)
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-      else if (ahead == 1)
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      else
+      if (ahead <= 0) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else if constexpr (!F8) {
+        if (ahead >= 2)
+          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else if (j == 0) {
+        if (ahead >= 2)
+          asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      } else {
+        if (ahead >= 2)
+          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      }
     };
 
     issue_next();   // unit 0
@@ -624,7 +856,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       // that it has two phases to land.
       if (t >= 1) issue_next();
       const int b = cb;
-      const char* ubuf = smem + (t % NBUF) * kHalfBytes;
+      const char* ubuf = smem + (t % NBUF) * UB;
       const int par = t & 1;
 
       // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all rows ----
@@ -646,13 +878,23 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) pB[rt] = p_lds[par][rt][lane];
         bf16x8 va[DL];
+        if constexpr (F8) {
+          i32x2 vc[DL];
 #pragma unroll
-        for (int dl = 0; dl < DL; ++dl) {
-          const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
-          const bf16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
-          va[dl] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          for (int dl = 0; dl < DL; ++dl)
+            vc[dl] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (MLA_LDS i32x2*)((MLA_LDS char*)(ubuf) + (f8_t0 ^ (dl << 4))));
+#pragma unroll
+          for (int dl = 0; dl < DL; ++dl) va[dl] = e4m3x8_to_bf16(vc[dl][0], vc[dl][1]);
+        } else {
+#pragma unroll
+          for (int dl = 0; dl < DL; ++dl) {
+            const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
+            va[dl] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -713,28 +955,33 @@ int tile_rows_for(int M) {
   return 64;                 // mla_splitkv_ws_kernel<4> (M = 128, 256: 2 or 4 row tiles)
 }
 
-hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
-                          hipEvent_t stop) {
+template <int RT, bool F8>
+hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid(a.num_parts * a.row_tiles);
   const dim3 block(kThreadsWS);
-  const void* fn = a.row_tile_rows == 16   ? reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<1>)
-                   : a.row_tile_rows == 32 ? reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<2>)
-                                           : reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<4>);
   if (start == nullptr && stop == nullptr) {
     // plain launch (also what a HIP graph capture records)
-    if (a.row_tile_rows == 16)
-      hipLaunchKernelGGL(mla_splitkv_ws_kernel<1>, grid, block, 0, stream, a);
-    else if (a.row_tile_rows == 32)
-      hipLaunchKernelGGL(mla_splitkv_ws_kernel<2>, grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL(mla_splitkv_ws_kernel<4>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mla_splitkv_ws_kernel<RT, F8>), grid, block, 0, stream, a);
   } else {
     // events recorded at the kernel's own start and end
     void* args[] = {const_cast<DecodeArgs*>(&a)};
-    hipError_t e = hipExtLaunchKernel(fn, grid, block, args, 0, stream, start, stop, 0);
+    hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<RT, F8>),
+                                      grid, block, args, 0, stream, start, stop, 0);
     if (e != hipSuccess) return e;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
+  if (a.kv_fp8) {
+    if (a.row_tile_rows == 16) return launch_ws<1, true>(a, stream, start, stop);
+    if (a.row_tile_rows == 32) return launch_ws<2, true>(a, stream, start, stop);
+    return launch_ws<4, true>(a, stream, start, stop);
+  }
+  if (a.row_tile_rows == 16) return launch_ws<1, false>(a, stream, start, stop);
+  if (a.row_tile_rows == 32) return launch_ws<2, false>(a, stream, start, stop);
+  return launch_ws<4, false>(a, stream, start, stop);
 }
 
 // --------------------------------------------------------------------------
@@ -840,6 +1087,87 @@ hipError_t launch_kv_append(const uint16_t* new_kv, uint16_t* kcache, long long 
                             const int32_t* block_table, int bt_stride, const int32_t* seqlens,
                             int batch, int s_q, hipStream_t stream) {
   hipLaunchKernelGGL(mla_kv_append_kernel, dim3(batch, s_q), dim3(128), 0, stream, new_kv,
+                     kcache, num_blocks, block_table, bt_stride, seqlens, s_q);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Paged-KV append into FP8 pages: one wave per (request, new token).  Lane l
+// quantises latent dims 8l .. 8l+7; the scale is the smallest power of two
+// s with amax <= 448 s (1 for an all-zero latent), so x / s is exact and
+// every code is the E4M3 round-to-nearest-even of an exact value.
+// --------------------------------------------------------------------------
+// E4M3 code of y (|y| <= 448), ties to even, from the format's fields: sign
+// bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0
+// holds the subnormals m * 2^-9.  The sign of -0 and of negative values that
+// round to zero is kept.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a < 0.015625f) {                          // below 2^-6: grid of 2^-9
+    return sign | static_cast<uint32_t>(rintf(a * 512.0f));   // 8 = smallest normal
+  }
+  int e;
+  frexpf(a, &e);
+  e -= 1;                                       // a in [2^e, 2^(e+1))
+  uint32_t n = static_cast<uint32_t>(rintf(ldexpf(a, 3 - e)));   // 8 .. 16
+  if (n == 16) {
+    n = 8;
+    e += 1;
+  }
+  return sign | (static_cast<uint32_t>(e + 7) << 3) | (n - 8);
+}
+
+__global__ __launch_bounds__(64) void mla_kv_append_fp8_kernel(
+    const uint16_t* __restrict__ new_kv, uint8_t* __restrict__ kcache, long long num_blocks,
+    const int32_t* __restrict__ block_table, int bt_stride, const int32_t* __restrict__ seqlens,
+    int s_q) {
+  const int b = blockIdx.x, t = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int pos = seqlens[b] - s_q + t;
+  if (pos < 0 || pos / kBlock >= bt_stride) return;
+  const int page = block_table[(long long)b * bt_stride + pos / kBlock];
+  if (page < 0 || (long long)page >= num_blocks) return;
+  const int r = pos % kBlock;
+  const uint16_t* src = new_kv + ((long long)b * s_q + t) * kDK;
+  uint8_t* pg = kcache + (long long)page * kF8PageBytes;
+
+  const uint4 w = reinterpret_cast<const uint4*>(src)[lane];
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(wd[k] << 16);
+    x[2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  int ks = 0;   // s = 2^ks
+  if (amax > 0.f) {
+    int e;
+    frexpf(amax, &e);   // amax = m 2^e, m in [0.5, 1); 448 = 0.875 * 2^9
+    ks = (amax <= ldexpf(448.0f, e - 9)) ? e - 9 : e - 8;
+  }
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    lo |= e4m3_rne(ldexpf(x[k], -ks)) << (8 * k);
+    hi |= e4m3_rne(ldexpf(x[4 + k], -ks)) << (8 * k);
+  }
+  *reinterpret_cast<uint2*>(pg + r * kF8Latent + 8 * lane) = make_uint2(lo, hi);
+  if (lane < 8)
+    reinterpret_cast<uint4*>(pg + kF8RopeOff + r * 128)[lane] =
+        reinterpret_cast<const uint4*>(src + kF8Latent)[lane];
+  if (lane == 0) *reinterpret_cast<float*>(pg + kF8ScaleOff + 4 * r) = ldexpf(1.0f, ks);
+}
+
+hipError_t launch_kv_append_fp8(const uint16_t* new_kv, uint8_t* kcache, long long num_blocks,
+                                const int32_t* block_table, int bt_stride,
+                                const int32_t* seqlens, int batch, int s_q, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_kv_append_fp8_kernel, dim3(batch, s_q), dim3(64), 0, stream, new_kv,
                      kcache, num_blocks, block_table, bt_stride, seqlens, s_q);
   return hipGetLastError();
 }

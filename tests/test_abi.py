@@ -69,13 +69,13 @@ def test_status_strings():
     assert mla.status_string(12345) == "unknown status"
 
 
-def _fwd_raw(**kw):
+def _fwd_raw(fn="mla_decode_fwd", **kw):
     args = dict(q=16, kc=16, nblk=8, bt=16, bt_stride=2, sl=16, batch=2, s_q=1, h_q=16, h_kv=1,
                 scale=0.04, causal=0, tm=16, so=16, parts=4, ws=256, ws_bytes=1 << 30,
                 out=16, lse=16)
     args.update(kw)
     p = lambda v: ctypes.c_void_p(v) if v else None
-    return mla.lib().mla_decode_fwd(
+    return getattr(mla.lib(), fn)(
         p(args["q"]), p(args["kc"]), args["nblk"], p(args["bt"]), args["bt_stride"], p(args["sl"]),
         args["batch"], args["s_q"], args["h_q"], args["h_kv"], args["scale"], args["causal"],
         p(args["tm"]), p(args["so"]), args["parts"], p(args["ws"]), args["ws_bytes"],
@@ -93,9 +93,10 @@ def _fwd_raw(**kw):
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(causal=2), INVALID), (dict(ws_bytes=1024), WORKSPACE),
 ])
-def test_fwd_rejects_before_launch(kw, expect):
+@pytest.mark.parametrize("fn", ["mla_decode_fwd", "mla_decode_fwd_fp8"])
+def test_fwd_rejects_before_launch(fn, kw, expect):
     # Pointers are fake (never dereferenced): validation returns before any launch.
-    assert _fwd_raw(**kw) == expect
+    assert _fwd_raw(fn, **kw) == expect
 
 
 def test_metadata_rejects_before_launch():
@@ -129,3 +130,23 @@ def test_kv_append_rejects_before_launch():
                dict(kc=p(24)), dict(bt=p(2)), dict(sl=p(6)), dict(nblk=0), dict(bt_stride=0),
                dict(batch=0), dict(s_q=0), dict(s_q=9)):
         assert call(**kw) == INVALID, kw
+
+
+def test_fp8_entry_points_reject_before_launch():
+    L = mla.lib()
+    p = ctypes.c_void_p
+    ok = dict(nkv=p(16), kc=p(16), nblk=8, bt=p(16), bt_stride=2, sl=p(16), batch=2, s_q=1)
+    for kw in (dict(nkv=None), dict(kc=p(8)), dict(batch=0), dict(s_q=9), dict(nblk=0)):
+        a = dict(ok, **kw)
+        assert L.mla_kv_append_fp8(a["nkv"], a["kc"], a["nblk"], a["bt"], a["bt_stride"],
+                                   a["sl"], a["batch"], a["s_q"], None) == INVALID, kw
+    # splitkv_fp8 with NULL events: same validation as the bf16 entry point
+    args = [p(16), p(16), 8, p(16), 2, p(16), 2, 1, 16, 1, 0.04, 0, p(16), p(16), 4, p(256),
+            1 << 30, p(16), p(16), None, None, None]
+    bad = list(args)
+    bad[8] = 48
+    assert L.mla_decode_splitkv_fp8(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[1] = p(8)
+    assert L.mla_decode_splitkv_fp8(*bad) == INVALID
+    assert binding.FP8_PAGE_BYTES == 41216
