@@ -35,34 +35,77 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
 # by what the same counter reads for a plain 1 GiB int32 elementwise copy
 # (--copy-calib-mib 1024): FETCH_SIZE reads 0.5 GiB for it, WRITE_SIZE 1 GiB.
-# Keyed by workload; valid only for the kernel source it was measured on
+# Keyed by workload ("<workload>/fp8" for the FP8 cache); valid only for the
+# kernel source it was measured on
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "88e1c09cbed3f7605e73d16795edef7b6e057509ea7e9d20041a8f678000cacd",
-        "fetch_bytes": 307841000,
-        "write_bytes": 9882592,
-        "fetch_scale": 1.99987,
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 307840763,
+        "write_bytes": 9882822,
+        "fetch_scale": 1.99986,
         "write_scale": 1.0
     },
     "ridge": {
-        "kernel_sha256": "88e1c09cbed3f7605e73d16795edef7b6e057509ea7e9d20041a8f678000cacd",
-        "fetch_bytes": 704687645,
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 704751928,
         "write_bytes": 59894272,
-        "fetch_scale": 1.99989,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "long": {
-        "kernel_sha256": "88e1c09cbed3f7605e73d16795edef7b6e057509ea7e9d20041a8f678000cacd",
-        "fetch_bytes": 770863098,
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 770872638,
         "write_bytes": 37559808,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ragged": {
-        "kernel_sha256": "88e1c09cbed3f7605e73d16795edef7b6e057509ea7e9d20041a8f678000cacd",
-        "fetch_bytes": 510510339,
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 510542367,
         "write_bytes": 78838784,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0
+    },
+    "draft": {
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 210897305,
+        "write_bytes": 58843136,
+        "fetch_scale": 1.99989,
+        "write_scale": 1.0
+    },
+    "membound/fp8": {
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 174710825,
+        "write_bytes": 9882496,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0
+    },
+    "ridge/fp8": {
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 410084726,
+        "write_bytes": 59894272,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0
+    },
+    "long/fp8": {
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 437948077,
+        "write_bytes": 37559808,
+        "fetch_scale": 1.9999,
+        "write_scale": 1.0
+    },
+    "ragged/fp8": {
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 310432996,
+        "write_bytes": 78838784,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0
+    },
+    "draft/fp8": {
+        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
+        "fetch_bytes": 133651507,
+        "write_bytes": 58843136,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     }
@@ -76,8 +119,8 @@ def _kernel_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
-    rec = HBM_TRAFFIC.get(workload)
+def measured_traffic(workload: str, kv: str = "bf16"):
+    rec = HBM_TRAFFIC.get(workload if kv == "bf16" else f"{workload}/{kv}")
     if rec is None or rec["kernel_sha256"] != _kernel_source_sha():
         return None
     return rec
@@ -98,8 +141,9 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the workload:
     whole requests in order until about `budget_s` seconds have elapsed."""
     import numpy as np
-    from oracle import decode
+    from oracle import decode, decode_fp8
     from workloads import algorithmic_counts
+    oracle_decode = decode_fp8 if inp.kv_format == "fp8" else decode
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -110,8 +154,8 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     passes = 0
     while True:
         for b in range(inp.batch):
-            decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal,
-                   requests=[b])
+            oracle_decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale,
+                          inp.causal, requests=[b])
             done.append(b)
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -121,7 +165,7 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
         break
     dt = time.perf_counter() - t0
     sl = [int(inp.seqlens[b]) for b in done]
-    c = algorithmic_counts(sl, inp.s_q, inp.h_q)
+    c = algorithmic_counts(sl, inp.s_q, inp.h_q, inp.kv_format)
     return {
         "value": round(c["bytes"] / dt / 1e9, 4),
         "unit": "GB/s",
@@ -134,10 +178,10 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     }
 
 
-def splitkv_kernel_name(m_rows: int) -> str:
-    """HIP kernel that mla_decode_splitkv launches for s_q*h_q = m_rows."""
+def splitkv_kernel_name(m_rows: int, kv: str = "bf16") -> str:
+    """HIP kernel that mla_decode_splitkv(_fp8) launches for s_q*h_q = m_rows."""
     rt = 1 if m_rows <= 16 else 2 if m_rows <= 32 else 4
-    return f"mla_splitkv_ws_kernel<{rt}>"
+    return f"mla_splitkv_ws_kernel<{rt}, {'true' if kv == 'fp8' else 'false'}>"
 
 
 def main(argv=None) -> int:
@@ -148,6 +192,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="membound",
                     help="tiny | membound | ridge | ragged | long | draft")
     ap.add_argument("--parts", type=int, default=None, help="override split-KV part count")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="KV cache format: bf16 rows, or FP8 pages (E4M3 latent codes with a "
+                         "per-token fp32 scale, bf16 rope)")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="cache flush between timed steps (outside the timed events)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -176,9 +223,12 @@ def main(argv=None) -> int:
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    inp = make_inputs(args.workload)
+    fp8 = args.kv == "fp8"
+    inp = make_inputs(args.workload, kv_format=args.kv)
     g = inp.to(dev)
-    counts = algorithmic_counts(inp.seqlens.tolist(), inp.s_q, inp.h_q)
+    counts = algorithmic_counts(inp.seqlens.tolist(), inp.s_q, inp.h_q, args.kv)
+    decode_fn = mla.splitkv_fp8 if fp8 else mla.splitkv
+    append_fn = mla.kv_append_fp8 if fp8 else mla.kv_append
 
     parts = args.parts or mla.num_parts(inp.batch, inp.s_q, inp.h_q, 1, mla.device_num_cus(dev))
     ws = torch.empty((max(256, mla.workspace_bytes(inp.batch, inp.s_q, inp.h_q, parts)),),
@@ -203,11 +253,11 @@ def main(argv=None) -> int:
         if evs is not None:
             evs[0].record()
         if new_kv is not None:
-            mla.kv_append(new_kv, g.kcache, g.block_table, g.seqlens)
+            append_fn(new_kv, g.kcache, g.block_table, g.seqlens)
         meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
-        mla.splitkv(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
-                    out, lse, start_event=evs[2] if evs else None,
-                    stop_event=evs[3] if evs else None)
+        decode_fn(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
+                  out, lse, start_event=evs[2] if evs else None,
+                  stop_event=evs[3] if evs else None)
         mla.combine(g.seqlens, inp.s_q, inp.h_q, meta, ws, out, lse)
         if evs is not None:
             evs[1].record()
@@ -216,12 +266,12 @@ def main(argv=None) -> int:
     # between kernels), in a separate loop after the timed one.
     def step_breakdown(evs):
         if new_kv is not None:
-            mla.kv_append(new_kv, g.kcache, g.block_table, g.seqlens)
+            append_fn(new_kv, g.kcache, g.block_table, g.seqlens)
         evs[0].record()
         meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
         evs[1].record()
-        mla.splitkv(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
-                    out, lse)
+        decode_fn(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
+                  out, lse)
         evs[2].record()
         mla.combine(g.seqlens, inp.s_q, inp.h_q, meta, ws, out, lse)
         evs[3].record()
@@ -299,7 +349,7 @@ def main(argv=None) -> int:
         for k in range(K):
             flush()
             aevs[k][0].record()
-            mla.kv_append(new_kv, g.kcache, g.block_table, g.seqlens)
+            append_fn(new_kv, g.kcache, g.block_table, g.seqlens)
             aevs[k][1].record()
         torch.cuda.synchronize(dev)
         append_ms = [e[0].elapsed_time(e[1]) for e in aevs]
@@ -329,7 +379,10 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
     warm_ms = e0.elapsed_time(e1) / K
 
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, args.kv)
+    # The binding roof of the decode kernel: HBM below the ridge point
+    # (peak flops / peak bytes = 312.5 flop/byte), the bf16 MFMA above it.
+    mfma_bound = counts["flops"] / counts["bytes"] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -348,7 +401,9 @@ def main(argv=None) -> int:
                    "block_size": 64, "total_keys": int(inp.seqlens.sum()),
                    "num_parts": parts, "cache_flush_between_steps": args.flush,
                    "step_launch": "hip_graph" if graph is not None else "eager",
-                   "kv_append_in_step": new_kv is not None},
+                   "kv_append_in_step": new_kv is not None,
+                   "kv_cache": ("fp8_e4m3 latent codes, fp32 per-token scale, bf16 rope "
+                                "(644 B/token)" if fp8 else "bf16 (1152 B/token)")},
         "tflops": round(tfl, 2),
         "algorithmic_bytes": counts["bytes"],
         "algorithmic_flops": counts["flops"],
@@ -362,12 +417,15 @@ def main(argv=None) -> int:
         "warm_ms_per_step": round(warm_ms, 5),
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": {
-            "kernel": splitkv_kernel_name(inp.s_q * inp.h_q),
-            "bound": "hbm",
-            "achieved": round(dec_gbs, 2),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "kernel": splitkv_kernel_name(inp.s_q * inp.h_q, args.kv),
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(dec_tfl if mfma_bound else dec_gbs, 2),
+            "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round(dec_tfl / PEAK_BF16_TFLOPS if mfma_bound else dec_gbs / PEAK_HBM_GBS, 4),
+            "arith_intensity": round(counts["flops"] / counts["bytes"], 1),
+            "hbm_gbs": round(dec_gbs, 2),
+            "hbm_frac": round(dec_gbs / PEAK_HBM_GBS, 4),
             "traffic": (None if traffic is None
                         else traffic["fetch_bytes"] + traffic["write_bytes"]),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "

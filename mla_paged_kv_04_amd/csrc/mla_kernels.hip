@@ -396,6 +396,30 @@ constexpr int kF8UnitCodes = 0;
 constexpr int kF8UnitRope = kHalfRows * kF8Latent;         // 16384
 constexpr int kF8UnitScale = kF8UnitRope + kHalfRows * 128;   // 20480
 constexpr int kF8UnitBytes = kF8UnitScale + 256;           // 20736
+// Ring depth for FP8 units.  The smaller units would leave room for six or
+// seven buffers, but measured on gfx950 both are slower than four (membound
+// 48.8 / 49.6 us against 46.7 us): with one 16-row tile the score wave's own
+// chain, not the load latency, sets the phase.
+constexpr int kWSBufsF8 = 4;
+
+// Wait until at most `ahead` units of this wave's page loads (N loads each,
+// issued after the unit waited for) are still outstanding; A is the largest
+// number of units that can be ahead.
+template <int K>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
+}
+template <int N, int A>
+__device__ __forceinline__ void wait_loads_behind(int ahead) {
+  if constexpr (A <= 0) {
+    vm_wait<0>();
+  } else {
+    if (ahead >= A)
+      vm_wait<N * A>();
+    else
+      wait_loads_behind<N, A - 1>(ahead);
+  }
+}
 
 // Swizzles of the FP8 unit, chosen by measurement on gfx950 (LDS throughput
 // of the kernel's own read patterns under candidate XOR swizzles):
@@ -510,7 +534,7 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // F8: the cache holds FP8 pages (layout above) instead of bf16 rows.
 template <int RT, bool F8>
 __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const DecodeArgs a) {
-  constexpr int NBUF = kWSBufs;
+  constexpr int NBUF = F8 ? kWSBufsF8 : kWSBufs;          // ring of unit buffers
   constexpr int DL = 8;   // 16-dim output tiles per value wave (128 dims)
   constexpr int UB = F8 ? kF8UnitBytes : kHalfBytes;   // bytes of one unit buffer
 
@@ -645,15 +669,18 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         for (int kt = 0; kt < 2; ++kt) {
           sp[kt][0] = sp[kt][1] = sr[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        constexpr int DP = 2;   // code reads issued this many steps ahead
-        u32x4 kc[DP + 1][2];
+        // Three-stage software pipeline over the 8 code reads (64 dims each):
+        // read step ps, convert step ps-1, multiply step ps-2, so that the
+        // conversions of one step overlap the products of the step before.
+        u32x4 kc[2][2];
+        bf16x8 kb[2][2][2];   // [step parity][kt][low / high 8 dims]
         bf16x8 ra[2][2];
 #pragma unroll
-        for (int ps = 0; ps < 8 + DP; ++ps) {
+        for (int ps = 0; ps < 8 + 2; ++ps) {
           if (ps < 8) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
-              kc[ps % (DP + 1)][kt] = *reinterpret_cast<const u32x4*>(ubuf + (co[kt] ^ (64 * ps)));
+              kc[ps & 1][kt] = *reinterpret_cast<const u32x4*>(ubuf + (co[kt] ^ (64 * ps)));
           }
           if (ps == 0) {
 #pragma unroll
@@ -665,15 +692,23 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
             for (int kt = 0; kt < 2; ++kt)
               sc[kt] = *reinterpret_cast<const f32x4*>(ubuf + kF8UnitScale + 4 * (16 * kt + 4 * g));
           }
-          const int cp = ps - DP;
+          const int cv = ps - 1;   // step converted now
+          if (cv >= 0 && cv < 8) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              const u32x4 w = kc[cv & 1][kt];
+              kb[cv & 1][kt][0] = e4m3x8_to_bf16(w[0], w[1]);
+              kb[cv & 1][kt][1] = e4m3x8_to_bf16(w[2], w[3]);
+            }
+          }
+          const int cp = ps - 2;   // step multiplied now
           if (cp >= 0) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-              const u32x4 w = kc[cp % (DP + 1)][kt];
-              sp[kt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(w[0], w[1]),
-                                                                  qreg[2 * cp], sp[kt][0], 0, 0, 0);
+              sp[kt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[cp & 1][kt][0], qreg[2 * cp],
+                                                                  sp[kt][0], 0, 0, 0);
               sp[kt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  e4m3x8_to_bf16(w[2], w[3]), qreg[2 * cp + 1], sp[kt][1], 0, 0, 0);
+                  kb[cp & 1][kt][1], qreg[2 * cp + 1], sp[kt][1], 0, 0, 0);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -817,43 +852,28 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     // wait until unit u has landed (units issued after it stay in flight)
     // (loads per unit and wave: 9 for bf16; for FP8 6 on wave 0, 5 on the others)
     auto wait_unit = [&](int u) {
-      static_assert(kHalfLoadsPerWave == 9, "wait counts below");
       const int ahead = issued - u - 1;
-      if (ahead <= 0) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      } else if constexpr (!F8) {
-        if (ahead >= 2)
-          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      } else if (j == 0) {
-        if (ahead >= 2)
-          asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-      } else {
-        if (ahead >= 2)
-          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-      }
+      if constexpr (!F8)
+        wait_loads_behind<kHalfLoadsPerWave, NBUF - 2>(ahead);
+      else if (j == 0)
+        wait_loads_behind<6, NBUF - 2>(ahead);
+      else
+        wait_loads_behind<5, NBUF - 2>(ahead);
     };
 
-    issue_next();   // unit 0
-    issue_next();   // unit 1
-    issue_next();   // unit 2
+    for (int u = 0; u < NBUF - 1; ++u) issue_next();   // units 0 .. NBUF-2
     wait_unit(0);
     wg_barrier();   // b_0: unit 0 landed
-    issue_next();   // unit 3 (buffer 3)
+    issue_next();   // unit NBUF-1 (its buffer is still unused)
     wait_unit(1);
     wg_barrier();   // b_1: unit 1 landed, P of unit 0 written
 
     int n = n_pages(cL), pbeg = ck;
     int t = 0;   // unit multiplied in this phase
     while (true) {
-      // Unit t+3 goes into the buffer of unit t-1, free since the last
+      // Unit t+NBUF-1 goes into the buffer of unit t-1, free since the last
       // barrier (its product ended in the previous phase); issued first so
-      // that it has two phases to land.
+      // that it has NBUF-2 phases to land.
       if (t >= 1) issue_next();
       const int b = cb;
       const char* ubuf = smem + (t % NBUF) * UB;
@@ -877,16 +897,25 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         bf16x8 pB[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) pB[rt] = p_lds[par][rt][lane];
-        bf16x8 va[DL];
         if constexpr (F8) {
+          // codes converted one 16-dim tile ahead of its products
           i32x2 vc[DL];
 #pragma unroll
           for (int dl = 0; dl < DL; ++dl)
             vc[dl] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (MLA_LDS i32x2*)((MLA_LDS char*)(ubuf) + (f8_t0 ^ (dl << 4))));
+          bf16x8 cur = e4m3x8_to_bf16(vc[0][0], vc[0][1]);
 #pragma unroll
-          for (int dl = 0; dl < DL; ++dl) va[dl] = e4m3x8_to_bf16(vc[dl][0], vc[dl][1]);
+          for (int dl = 0; dl < DL; ++dl) {
+            bf16x8 nxt = cur;
+            if (dl + 1 < DL) nxt = e4m3x8_to_bf16(vc[dl + 1][0], vc[dl + 1][1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              o[dl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pB[rt], o[dl][rt], 0, 0, 0);
+            cur = nxt;
+          }
         } else {
+          bf16x8 va[DL];
 #pragma unroll
           for (int dl = 0; dl < DL; ++dl) {
             const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
@@ -895,13 +924,14 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
                 __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
             va[dl] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int dl = 0; dl < DL; ++dl) {
+          for (int dl = 0; dl < DL; ++dl) {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            o[dl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pB[rt], o[dl][rt], 0, 0, 0);
+            for (int rt = 0; rt < RT; ++rt)
+              o[dl][rt] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pB[rt], o[dl][rt], 0, 0, 0);
+          }
         }
       }
 

@@ -53,3 +53,10 @@ def test_build_inputs_q_scale():
     a = build_inputs([70], 1, 16, seed=3, q_scale=8.0)
     b = build_inputs([70], 1, 16, seed=3)
     assert torch.allclose(a.q.float(), (b.q.float() * 8).bfloat16().float(), atol=0.5)
+
+
+def test_fp8_counts():
+    c = algorithmic_counts([4096] * 64, 1, 16, "fp8")
+    assert c["kv_bytes"] == 64 * 4096 * (512 + 128 + 4)
+    b = algorithmic_counts([4096] * 64, 1, 16)
+    assert c["flops"] == b["flops"] and b["kv_bytes"] == 64 * 4096 * 1152

@@ -273,10 +273,16 @@ def make_inputs(key: str, nan_tails: bool = True, kv_format: str = "bf16") -> De
                         nan_tails=nan_tails, gen=gen)
 
 
-def algorithmic_counts(seqlens, s_q: int, h_q: int) -> dict:
+# Cache bytes per token: a bf16 row, or an FP8 row (512 codes + 64 bf16 rope
+# + one fp32 scale).
+KV_BYTES_PER_TOKEN = {"bf16": D_K * 2, "fp8": FP8_LATENT + (D_K - FP8_LATENT) * 2 + 4}
+
+
+def algorithmic_counts(seqlens, s_q: int, h_q: int, kv_format: str = "bf16") -> dict:
     """Bytes and flops the method must move/compute (no padding, no partials).
 
-    bytes = sum_b L_b*576*2 (each KV row once per request)
+    bytes = sum_b L_b*T (each KV row once per request; T = 1152 bytes per
+            token for bf16 rows, 644 for FP8 rows)
             + B*M*(576*2 + 512*2 + 4) (Q in, O and LSE out)
             + sum_b ceil(L_b/64)*4 (block table) + B*4 (seqlens)
     flops = 2*(576+512) per visible (query row, key) pair; with s_q query
@@ -284,7 +290,7 @@ def algorithmic_counts(seqlens, s_q: int, h_q: int) -> dict:
     """
     seqlens = [int(x) for x in seqlens]
     M = s_q * h_q
-    kv = sum(L * D_K * 2 for L in seqlens)
+    kv = sum(L * KV_BYTES_PER_TOKEN[kv_format] for L in seqlens)
     io = len(seqlens) * M * (D_K * 2 + D_V * 2 + 4)
     meta = sum(blocks_for(L) * 4 for L in seqlens) + len(seqlens) * 4
     pairs = 0
