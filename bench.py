@@ -190,7 +190,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="membound",
-                    help="tiny | membound | ridge | ragged | long | draft")
+                    help="tiny | membound | ridge | ragged | long | draft | prefill")
     ap.add_argument("--parts", type=int, default=None, help="override split-KV part count")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="KV cache format: bf16 rows, or FP8 pages (E4M3 latent codes with a "

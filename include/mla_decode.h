@@ -62,7 +62,7 @@ extern "C" {
 #define MLA_D_K 576              /* key width: 512 latent + 64 rope */
 #define MLA_D_V 512              /* value width: first 512 dims of the key row */
 #define MLA_TILE_META_INTS 8     /* int32 words per part in tile_meta */
-#define MLA_MAX_S_Q 8            /* query tokens per request: 1 (decode) .. 8 (draft tokens) */
+#define MLA_MAX_S_Q 128          /* query tokens per request: 1 (decode), 2..8 (draft tokens), up to 128 (a prefill chunk) */
 
 /*
  * mla_decode_num_parts — host only, no HIP call.

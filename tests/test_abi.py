@@ -37,6 +37,16 @@ def test_library_exports_every_declared_symbol():
     assert set(_declared()) <= set(binding._SIGNATURES)
 
 
+def test_max_s_q_accepted():
+    # the largest token count passes validation (fake pointers: a return
+    # other than INVALID_ARG for s_q would need a launch, so only check the
+    # host-only entry points)
+    assert mla.num_parts(1, 128, 128, 1, 256) == 1
+    assert mla.workspace_bytes(1, 128, 16, 1) == 0
+    with pytest.raises(Exception):
+        mla.num_parts(1, 129, 16, 1, 256)
+
+
 def test_num_parts():
     assert mla.num_parts(64, 1, 16, 1, 256) == 256
     assert mla.num_parts(128, 1, 128, 1, 256) == 128     # two 64-row tiles
@@ -46,7 +56,7 @@ def test_num_parts():
     out = ctypes.c_int(0)
     L = mla.lib()
     assert L.mla_decode_num_parts(2, 1, 48, 1, 256, ctypes.byref(out)) == UNSUPPORTED
-    assert L.mla_decode_num_parts(2, 9, 16, 1, 256, ctypes.byref(out)) == INVALID
+    assert L.mla_decode_num_parts(2, 129, 16, 1, 256, ctypes.byref(out)) == INVALID
     assert L.mla_decode_num_parts(2, 0, 16, 1, 256, ctypes.byref(out)) == INVALID
     assert mla.num_parts(2, 3, 16, 1, 256) == 256          # 48 rows: one 64-row tile
     assert mla.num_parts(2, 8, 128, 1, 256) == 16          # 1024 rows: sixteen tiles
@@ -87,7 +97,7 @@ def _fwd_raw(fn="mla_decode_fwd", **kw):
     (dict(tm=0), INVALID), (dict(so=0), INVALID), (dict(out=0), INVALID), (dict(lse=0), INVALID),
     (dict(q=8), INVALID), (dict(kc=4), INVALID), (dict(out=8), INVALID), (dict(lse=2), INVALID),
     (dict(ws=128), INVALID), (dict(ws=0), INVALID),
-    (dict(batch=0), INVALID), (dict(s_q=9), INVALID), (dict(s_q=0), INVALID), (dict(h_kv=2), INVALID),
+    (dict(batch=0), INVALID), (dict(s_q=129), INVALID), (dict(s_q=0), INVALID), (dict(h_kv=2), INVALID),
     (dict(h_q=48), UNSUPPORTED), (dict(h_q=8), UNSUPPORTED),
     (dict(parts=0), INVALID), (dict(nblk=0), INVALID), (dict(bt_stride=0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
@@ -128,7 +138,7 @@ def test_kv_append_rejects_before_launch():
 
     for kw in (dict(nkv=None), dict(kc=None), dict(bt=None), dict(sl=None), dict(nkv=p(8)),
                dict(kc=p(24)), dict(bt=p(2)), dict(sl=p(6)), dict(nblk=0), dict(bt_stride=0),
-               dict(batch=0), dict(s_q=0), dict(s_q=9)):
+               dict(batch=0), dict(s_q=0), dict(s_q=129)):
         assert call(**kw) == INVALID, kw
 
 
@@ -136,7 +146,7 @@ def test_fp8_entry_points_reject_before_launch():
     L = mla.lib()
     p = ctypes.c_void_p
     ok = dict(nkv=p(16), kc=p(16), nblk=8, bt=p(16), bt_stride=2, sl=p(16), batch=2, s_q=1)
-    for kw in (dict(nkv=None), dict(kc=p(8)), dict(batch=0), dict(s_q=9), dict(nblk=0)):
+    for kw in (dict(nkv=None), dict(kc=p(8)), dict(batch=0), dict(s_q=129), dict(nblk=0)):
         a = dict(ok, **kw)
         assert L.mla_kv_append_fp8(a["nkv"], a["kc"], a["nblk"], a["bt"], a["bt_stride"],
                                    a["sl"], a["batch"], a["s_q"], None) == INVALID, kw

@@ -105,6 +105,15 @@ def test_fp8_draft_tokens(mla, h_q, s_q):
     _assert_parity(out, lse, O_ref, L_ref, tag=f"fp8 draft h{h_q} s{s_q}")
 
 
+def test_fp8_prefill_chunk(mla):
+    _say("case fp8 prefill chunk s_q=64 h_q=64")
+    lens = [64, 65, 300, 3, 0]
+    inp = build_fp8_inputs(lens, 64, 64, seed=871, extra_pool=3)
+    out, lse, _ = _run(mla, inp, 3)
+    O_ref, L_ref = _ref(inp)
+    _assert_parity(out, lse, O_ref, L_ref, tag="fp8 prefill s64 h64")
+
+
 def _sample_requests(seqlens, k=6, seed=0):
     sl = seqlens.tolist()
     B = len(sl)

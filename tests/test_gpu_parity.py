@@ -99,6 +99,20 @@ def test_draft_tokens(mla, h_q, s_q, parts):
     _assert_parity(out, lse, O_ref, L_ref, tag=f"draft h{h_q} s{s_q} P={parts}")
 
 
+# Chunked prefill against the paged cache: up to 128 new tokens per request,
+# causal among themselves (the rule of the draft tokens); up to 256 row tiles
+# of 64 rows.  Lengths below s_q leave leading tokens with no visible key.
+@pytest.mark.parametrize("s_q,h_q,parts", [(16, 16, None), (32, 128, None), (64, 64, 5),
+                                           (128, 16, None), (128, 128, None), (100, 32, 3)])
+def test_prefill_chunks(mla, s_q, h_q, parts):
+    _say(f"case prefill chunk s_q={s_q} h_q={h_q} parts={parts}")
+    lens = [s_q, s_q + 1, 200, 700, 3, 0, 129]
+    inp = build_inputs(lens, s_q, h_q, seed=400 + s_q + h_q, extra_pool=3)
+    out, lse, _ = _run(mla, inp, parts)
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal)
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"prefill s{s_q} h{h_q} P={parts}")
+
+
 def test_non_causal_two_tokens(mla):
     _say("case non-causal s_q=2")
     inp = build_inputs([5, 70, 130], 2, 16, seed=5, extra_pool=2)
@@ -119,7 +133,7 @@ def _sample_requests(seqlens, k=6, seed=0):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("key", ["membound", "ridge", "ragged", "long", "draft"])
+@pytest.mark.parametrize("key", ["membound", "ridge", "ragged", "long", "draft", "prefill"])
 def test_full_workload_sampled(mla, key):
     """Full-size workload in the benchmark's launch configuration; the oracle
     recomputes a sample of requests (incl. the longest and the shortest)."""
@@ -127,7 +141,7 @@ def test_full_workload_sampled(mla, key):
     inp = make_inputs(key)
     _say(f"case full {key}: decode on GPU")
     out, lse, meta = _run(mla, inp)
-    reqs = _sample_requests(inp.seqlens, k=6, seed=WORKLOADS[key].seed)
+    reqs = _sample_requests(inp.seqlens, k=6 if inp.s_q < 64 else 3, seed=WORKLOADS[key].seed)
     _say(f"case full {key}: oracle on requests {reqs}")
     O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale,
                           inp.causal, requests=reqs)
@@ -311,7 +325,7 @@ def test_single_token_exact(mla):
 
 # ---- paged-KV append --------------------------------------------------------
 
-@pytest.mark.parametrize("s_q", [1, 2, 5])
+@pytest.mark.parametrize("s_q", [1, 2, 5, 64])
 def test_kv_append_matches_oracle(mla, s_q):
     """The cache after the append equals the oracle's, bit for bit (new rows
     written, everything else untouched), and decode over it matches the

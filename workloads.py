@@ -75,6 +75,11 @@ WORKLOADS: dict[str, Workload] = {
     "draft": Workload("draft", "4-token draft decode", batch=32, s_q=4, h_q=128,
                       seqlen_kind="uniform2048_8192", seed=1005, extra_pool=64,
                       desc="B=32, s_q=4 causal, h_q=128, seqlens U[2048,8192]"),
+    # A 64-token prefill chunk per request against the paged cache (the
+    # chunk's tokens are already in the cache, causal among themselves).
+    "prefill": Workload("prefill", "64-token chunked prefill", batch=8, s_q=64, h_q=128,
+                        seqlen_kind="uniform2048_8192", seed=1006, extra_pool=64,
+                        desc="B=8, s_q=64 causal, h_q=128, seqlens U[2048,8192]"),
 }
 
 # The order the workloads are listed in (index 0 is the small case).
