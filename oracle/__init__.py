@@ -12,3 +12,6 @@ from .mla_fp8_oracle import (  # noqa: F401
     e4m3_decode, e4m3_encode, quantize_scale, quantize_row, dequant_page,
     gather_request_kv_fp8, decode_fp8, kv_append_fp8,
 )
+from .mla_sparse_oracle import (  # noqa: F401
+    counted_entries, decode_sparse, decode_sparse_bruteforce,
+)

@@ -261,6 +261,31 @@ def _fp8_nan_rows(kv: torch.Tensor, page: int, r0: int, r1: int) -> None:
     pg[FP8_SCALE_OFF + 4 * r0:FP8_SCALE_OFF + 4 * r1] = nan_f.view(torch.uint8)
 
 
+def draw_topk_indices(seqlens, s_q: int, topk: int, causal: bool, gen: torch.Generator,
+                      pad_frac: float = 0.0) -> torch.Tensor:
+    """Selected positions for the sparse mode, int32 [B, s_q, topk]: for token
+    t of request b, `topk` distinct positions drawn uniformly among its
+    visible ones (all of them, in random order, when fewer are visible); the
+    remaining slots and a fraction `pad_frac` of the list are -1 (padding).
+    Only random draws: no selection criterion is applied."""
+    seqlens = [int(x) for x in seqlens]
+    B = len(seqlens)
+    out = torch.full((B, s_q, topk), -1, dtype=torch.int32)
+    for b, L in enumerate(seqlens):
+        for t in range(s_q):
+            vis = max(0, min(L, L - s_q + 1 + t)) if causal else max(0, L)
+            n = min(vis, topk)
+            if n > 0:
+                pick = torch.randperm(vis, generator=gen)[:n].to(torch.int32)
+                out[b, t, :n] = pick
+            if pad_frac > 0 and n > 0:
+                drop = torch.rand((topk,), generator=gen) < pad_frac
+                out[b, t][drop] = -1
+            perm = torch.randperm(topk, generator=gen)
+            out[b, t] = out[b, t][perm]
+    return out
+
+
 def make_inputs(key: str, nan_tails: bool = True, kv_format: str = "bf16") -> DecodeInputs:
     """The seeded inputs of one named workload (see WORKLOADS); kv_format
     "fp8" gives the same lengths, table and Q with an FP8 cache."""
