@@ -141,9 +141,13 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the workload:
     whole requests in order until about `budget_s` seconds have elapsed."""
     import numpy as np
-    from oracle import decode, decode_fp8
-    from workloads import algorithmic_counts
-    oracle_decode = decode_fp8 if inp.kv_format == "fp8" else decode
+    from oracle import decode, decode_fp8, decode_sparse
+    from workloads import algorithmic_counts, sparse_counts
+    if inp.indices is not None:
+        def oracle_decode(q, kc, bt, sl, scale, causal, requests):
+            return decode_sparse(q, kc, bt, sl, inp.indices, scale, causal, requests=requests)
+    else:
+        oracle_decode = decode_fp8 if inp.kv_format == "fp8" else decode
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -165,7 +169,10 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
         break
     dt = time.perf_counter() - t0
     sl = [int(inp.seqlens[b]) for b in done]
-    c = algorithmic_counts(sl, inp.s_q, inp.h_q, inp.kv_format)
+    if inp.indices is not None:
+        c = sparse_counts(inp.indices[done], sl, inp.s_q, inp.h_q, inp.causal)
+    else:
+        c = algorithmic_counts(sl, inp.s_q, inp.h_q, inp.kv_format)
     return {
         "value": round(c["bytes"] / dt / 1e9, 4),
         "unit": "GB/s",
@@ -178,10 +185,12 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     }
 
 
-def splitkv_kernel_name(m_rows: int, kv: str = "bf16") -> str:
-    """HIP kernel that mla_decode_splitkv(_fp8) launches for s_q*h_q = m_rows."""
+def splitkv_kernel_name(m_rows: int, kv: str = "bf16", sparse: bool = False) -> str:
+    """HIP kernel that the decode launches for m_rows query rows per request
+    (per item in the sparse mode)."""
     rt = 1 if m_rows <= 16 else 2 if m_rows <= 32 else 4
-    return f"mla_splitkv_ws_kernel<{rt}, {'true' if kv == 'fp8' else 'false'}>"
+    f = lambda x: "true" if x else "false"
+    return f"mla_splitkv_ws_kernel<{rt}, {f(kv == 'fp8')}, {f(sparse)}>"
 
 
 def main(argv=None) -> int:
@@ -190,7 +199,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="membound",
-                    help="tiny | membound | ridge | ragged | long | draft | prefill")
+                    help="tiny | membound | ridge | ragged | long | draft | prefill | sparse")
     ap.add_argument("--parts", type=int, default=None, help="override split-KV part count")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="KV cache format: bf16 rows, or FP8 pages (E4M3 latent codes with a "
@@ -218,21 +227,35 @@ def main(argv=None) -> int:
 
     import torch
     import mla_paged_kv_04_amd as mla
-    from workloads import WORKLOADS, algorithmic_counts, make_inputs
+    from workloads import WORKLOADS, algorithmic_counts, make_inputs, sparse_counts
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     fp8 = args.kv == "fp8"
+    sparse = w.topk > 0
+    if sparse and (fp8 or args.with_append or args.graph):
+        print("bench.py: the sparse workload runs eagerly over a bf16 cache", file=sys.stderr)
+        return 2
     inp = make_inputs(args.workload, kv_format=args.kv)
     g = inp.to(dev)
-    counts = algorithmic_counts(inp.seqlens.tolist(), inp.s_q, inp.h_q, args.kv)
+    if sparse:
+        counts = sparse_counts(inp.indices, inp.seqlens, inp.s_q, inp.h_q, inp.causal)
+    else:
+        counts = algorithmic_counts(inp.seqlens.tolist(), inp.s_q, inp.h_q, args.kv)
     decode_fn = mla.splitkv_fp8 if fp8 else mla.splitkv
     append_fn = mla.kv_append_fp8 if fp8 else mla.kv_append
 
-    parts = args.parts or mla.num_parts(inp.batch, inp.s_q, inp.h_q, 1, mla.device_num_cus(dev))
-    ws = torch.empty((max(256, mla.workspace_bytes(inp.batch, inp.s_q, inp.h_q, parts)),),
-                     dtype=torch.uint8, device=dev)
+    if sparse:   # (request, token) items of topk entries
+        topk = int(inp.indices.shape[2])
+        parts = args.parts or mla.num_parts(inp.batch * inp.s_q, 1, inp.h_q, 1,
+                                            mla.device_num_cus(dev))
+        ws_bytes = mla.sparse_workspace_bytes(inp.batch, inp.s_q, inp.h_q, topk, parts)
+    else:
+        parts = args.parts or mla.num_parts(inp.batch, inp.s_q, inp.h_q, 1,
+                                            mla.device_num_cus(dev))
+        ws_bytes = mla.workspace_bytes(inp.batch, inp.s_q, inp.h_q, parts)
+    ws = torch.empty((max(256, ws_bytes),), dtype=torch.uint8, device=dev)
     out = torch.empty((inp.batch, inp.s_q, inp.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((inp.batch, inp.s_q, inp.h_q), dtype=torch.float32, device=dev)
     new_kv = (torch.randn((inp.batch, inp.s_q, 576), generator=torch.Generator().manual_seed(5))
@@ -250,6 +273,17 @@ def main(argv=None) -> int:
     # last two are recorded by the decode kernel's own launch, so the step's
     # stream carries no marker between its three kernels.
     def step(evs=None):
+        if sparse:
+            if evs is not None:
+                evs[0].record()
+            meta = mla.sparse_metadata(inp.batch, inp.s_q, inp.h_q, topk, dev, parts=parts)
+            mla.sparse_fwd(g.q, g.kcache, g.block_table, g.seqlens, g.indices, inp.scale,
+                           inp.causal, meta=meta, workspace=ws, out=out, lse=lse,
+                           start_event=evs[2] if evs else None,
+                           stop_event=evs[3] if evs else None)
+            if evs is not None:
+                evs[1].record()
+            return
         if evs is not None:
             evs[0].record()
         if new_kv is not None:
@@ -265,6 +299,15 @@ def main(argv=None) -> int:
     # Per-kernel breakdown of the scheduler and the combine (marker events
     # between kernels), in a separate loop after the timed one.
     def step_breakdown(evs):
+        if sparse:   # scheduler; resolve + decode + combine
+            evs[0].record()
+            meta = mla.sparse_metadata(inp.batch, inp.s_q, inp.h_q, topk, dev, parts=parts)
+            evs[1].record()
+            mla.sparse_fwd(g.q, g.kcache, g.block_table, g.seqlens, g.indices, inp.scale,
+                           inp.causal, meta=meta, workspace=ws, out=out, lse=lse)
+            evs[2].record()
+            evs[3].record()
+            return
         if new_kv is not None:
             append_fn(new_kv, g.kcache, g.block_table, g.seqlens)
         evs[0].record()
@@ -403,7 +446,9 @@ def main(argv=None) -> int:
                    "step_launch": "hip_graph" if graph is not None else "eager",
                    "kv_append_in_step": new_kv is not None,
                    "kv_cache": ("fp8_e4m3 latent codes, fp32 per-token scale, bf16 rope "
-                                "(644 B/token)" if fp8 else "bf16 (1152 B/token)")},
+                                "(644 B/token)" if fp8 else "bf16 (1152 B/token)"),
+                   "sparse_topk": w.topk or None,
+                   "counted_entries": counts.get("counted")},
         "tflops": round(tfl, 2),
         "algorithmic_bytes": counts["bytes"],
         "algorithmic_flops": counts["flops"],
@@ -417,7 +462,8 @@ def main(argv=None) -> int:
         "warm_ms_per_step": round(warm_ms, 5),
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": {
-            "kernel": splitkv_kernel_name(inp.s_q * inp.h_q, args.kv),
+            "kernel": splitkv_kernel_name(inp.h_q if sparse else inp.s_q * inp.h_q, args.kv,
+                                          sparse),
             "bound": "mfma" if mfma_bound else "hbm",
             "achieved": round(dec_tfl if mfma_bound else dec_gbs, 2),
             "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS,

@@ -267,6 +267,53 @@ int mla_kv_append_fp8(const void* new_kv_d, void* kcache_fp8_d, int64_t num_bloc
                       const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
                       int batch, int s_q, void* stream);
 
+/*
+ * Sparse (selected-keys) mode, bf16 cache.  Page "云上玩转DeepSeek系列之五：实测
+ * 优化16%，体验FlashMLA加速DeepSeek-V2-Lite推理" (ruibaoantu.com), section 四,
+ * item 2, recommends FlashMLA's sparse attention mode beyond 8K tokens and
+ * gives no algorithm; this library's reading: the caller selects, for every
+ * query token, topk cache positions (any top-k selector; selection is not
+ * part of the mode), and each head of that token attends exactly over them:
+ *   indices_d int32 [batch, s_q, topk]: logical positions j in request b;
+ *   an entry counts iff 0 <= j < vis(b, t) (the dense visible limit:
+ *   L_b - s_q + 1 + t when causal, else L_b) and its page slot and page id
+ *   are valid; counted entries form a multiset (a position listed twice
+ *   counts twice); O and LSE as in the dense definition over the counted
+ *   entries; none counted gives O = 0, LSE = -inf.
+ * Work is split over (request, token) items of topk entries each:
+ *   - parts: mla_decode_num_parts(batch * s_q, 1, h_q, 1, num_cus, ...)
+ *   - workspace: mla_decode_sparse_workspace_bytes (fp32 partials as for
+ *     mla_decode_workspace_bytes(batch*s_q, 1, h_q, num_parts), then the
+ *     resolved row ids, validity bits and a zero row)
+ *   - metadata: mla_decode_sparse_metadata (device, no host sync)
+ * Constraints: topk a multiple of 32 in [32, 2^20]; batch*s_q*topk < 2^31;
+ * num_blocks <= 2^25 (row ids are int32).
+ */
+int mla_decode_sparse_workspace_bytes(int batch, int s_q, int h_q, int topk, int num_parts,
+                                      size_t* bytes_out);
+
+int mla_decode_sparse_metadata(int batch, int s_q, int h_q, int topk, int num_parts,
+                               int32_t* tile_meta_d, int32_t* split_offsets_d, void* stream);
+
+/*
+ * mla_decode_sparse_fwd — enqueue the sparse-mode decode: resolution of the
+ * selected positions to cache rows, the split-KV kernel over the items
+ * (rows gathered one by one into LDS, bf16 MFMA, fp32 online softmax) and the
+ * combine.  Arguments as mla_decode_fwd plus indices_d / topk; tile_meta_d,
+ * split_offsets_d and num_parts from mla_decode_sparse_metadata; workspace_d
+ * 256-byte aligned, >= mla_decode_sparse_workspace_bytes.  start_event /
+ * stop_event (hipEvent_t, may be NULL) are recorded at the decode kernel's
+ * own start and end.
+ */
+int mla_decode_sparse_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                          const int32_t* block_table_d, int bt_stride,
+                          const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                          float scale, int causal, const int32_t* indices_d, int topk,
+                          const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                          int num_parts, void* workspace_d, size_t workspace_bytes,
+                          void* out_d, float* lse_d, void* start_event, void* stop_event,
+                          void* stream);
+
 /* Static text for a status code. */
 const char* mla_status_string(int status);
 

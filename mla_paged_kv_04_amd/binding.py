@@ -60,6 +60,14 @@ _SIGNATURES = {
                                     _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
     "mla_kv_append_fp8": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int,
                                    _c_int, _c_ptr]),
+    "mla_decode_sparse_workspace_bytes": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
+                                                   ctypes.POINTER(_c_size)]),
+    "mla_decode_sparse_metadata": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr,
+                                            _c_ptr, _c_ptr]),
+    "mla_decode_sparse_fwd": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr, _c_int,
+                                       _c_int, _c_int, _c_int, _c_float, _c_int, _c_ptr, _c_int,
+                                       _c_ptr, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr,
+                                       _c_ptr, _c_ptr, _c_ptr]),
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_last_hip_error": (ctypes.c_char_p, []),
     "mla_device_num_cus": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
@@ -337,3 +345,55 @@ def kv_append_fp8(new_kv: torch.Tensor, kcache: torch.Tensor, block_table: torch
                                    _ptr(block_table), block_table.shape[1], _ptr(seqlens),
                                    batch, s_q, _stream(new_kv.device)), "mla_kv_append_fp8")
     return kcache
+
+
+def sparse_workspace_bytes(batch: int, s_q: int, h_q: int, topk: int, parts: int) -> int:
+    out = _c_size(0)
+    _check(lib().mla_decode_sparse_workspace_bytes(batch, s_q, h_q, topk, parts,
+                                                   ctypes.byref(out)),
+           "mla_decode_sparse_workspace_bytes")
+    return out.value
+
+
+def sparse_metadata(batch: int, s_q: int, h_q: int, topk: int, device,
+                    parts: int | None = None) -> Metadata:
+    """Enqueue the split plan of the sparse mode: batch*s_q items of topk
+    entries each (mla_decode_sparse_metadata)."""
+    device = torch.device(device)
+    if parts is None:
+        parts = num_parts(batch * s_q, 1, h_q, 1, device_num_cus(device))
+    tm = torch.empty((parts, TILE_META_INTS), dtype=torch.int32, device=device)
+    so = torch.empty((batch * s_q + 1,), dtype=torch.int32, device=device)
+    _check(lib().mla_decode_sparse_metadata(batch, s_q, h_q, topk, parts, _ptr(tm), _ptr(so),
+                                            _stream(device)), "mla_decode_sparse_metadata")
+    return Metadata(tm, so, parts, s_q, h_q)
+
+
+def sparse_fwd(q, kcache, block_table, seqlens, indices, scale: float,
+               causal: bool | None = None, meta: Metadata | None = None,
+               parts: int | None = None, workspace=None, out=None, lse=None,
+               start_event=None, stop_event=None):
+    """Sparse-mode decode over a bf16 cache: every head of query token t of
+    request b attends over the cache positions indices[b, t, :] (int32
+    [B, s_q, topk], -1 = padding) that are visible.  Returns (O, LSE) like fwd."""
+    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens)
+    _require(indices, torch.int32, "indices", 3)
+    if tuple(indices.shape[:2]) != (batch, s_q):
+        raise ValueError(f"indices {tuple(indices.shape)} do not match q {tuple(q.shape)}")
+    topk = indices.shape[2]
+    if causal is None:
+        causal = s_q > 1
+    if meta is None:
+        meta = sparse_metadata(batch, s_q, h_q, topk, q.device, parts)
+    need = sparse_workspace_bytes(batch, s_q, h_q, topk, meta.num_parts)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    out, lse = _outputs(q, out, lse)
+    _check(lib().mla_decode_sparse_fwd(
+        _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)), _ptr(indices),
+        topk, _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _event_handle(start_event), _event_handle(stop_event), _stream(q.device)),
+        "mla_decode_sparse_fwd")
+    return out, lse

@@ -110,6 +110,11 @@ int splitkv_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
   a.row_tile_rows = mla::tile_rows_for(s_q * h_q);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.kv_fp8 = kv_fp8;
+  a.sparse = 0;
+  a.const_len = 0;
+  a.rowids = nullptr;
+  a.vmask = nullptr;
+  a.zero_row = nullptr;
   hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream),
                                      static_cast<hipEvent_t>(start_event),
                                      static_cast<hipEvent_t>(stop_event));
@@ -127,6 +132,34 @@ int check_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
       !aligned(seqlens_d, 4))
     return MLA_ERR_INVALID_ARG;
   return MLA_OK;
+}
+
+// Sparse mode: items = batch * s_q (request, token) pairs of topk entries.
+constexpr int kMaxTopk = 1 << 20;
+
+int check_sparse_shape(int batch, int s_q, int h_q, int h_kv, int topk) {
+  int st = check_shape(batch, s_q, h_q, h_kv);
+  if (st != MLA_OK) return st;
+  if (topk < 32 || topk > kMaxTopk || topk % 32 != 0) return MLA_ERR_INVALID_ARG;
+  if ((long long)batch * s_q * (long long)topk > (1LL << 31) - 1) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct SparseWorkspace {
+  size_t partial, rowids, vmask, zero_row, total;   // byte offsets and total size
+};
+
+SparseWorkspace sparse_workspace(int batch, int s_q, int h_q, int topk, int num_parts) {
+  const size_t items = (size_t)batch * s_q;
+  SparseWorkspace w;
+  w.partial = 0;
+  w.rowids = workspace_need(1, h_q, num_parts);
+  w.vmask = w.rowids + round256(items * topk * 4);
+  w.zero_row = w.vmask + round256(items * (topk / 32) * 4);
+  w.total = w.zero_row + round256(mla::kRowBytes);
+  return w;
 }
 
 }  // namespace
@@ -226,6 +259,7 @@ int mla_decode_combine(const int32_t* seqlens_d, int batch, int s_q, int h_q,
   a.lse = lse_d;
   a.batch = batch;
   a.M = s_q * h_q;
+  a.const_len = 0;
   hipError_t e = mla::launch_combine(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mla_decode_combine launch");
   return MLA_OK;
@@ -308,6 +342,108 @@ int mla_device_num_cus(int device, int* num_cus_out) {
   hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   *num_cus_out = v;
+  return MLA_OK;
+}
+
+int mla_decode_sparse_workspace_bytes(int batch, int s_q, int h_q, int topk, int num_parts,
+                                      size_t* bytes_out) {
+  if (!bytes_out) return MLA_ERR_INVALID_ARG;
+  int st = check_sparse_shape(batch, s_q, h_q, 1, topk);
+  if (st != MLA_OK) return st;
+  if (num_parts < 1 || num_parts > kMaxParts) return MLA_ERR_INVALID_ARG;
+  *bytes_out = sparse_workspace(batch, s_q, h_q, topk, num_parts).total;
+  return MLA_OK;
+}
+
+int mla_decode_sparse_metadata(int batch, int s_q, int h_q, int topk, int num_parts,
+                               int32_t* tile_meta_d, int32_t* split_offsets_d, void* stream) {
+  int st = check_sparse_shape(batch, s_q, h_q, 1, topk);
+  if (st != MLA_OK) return st;
+  if (num_parts < 1 || num_parts > kMaxParts) return MLA_ERR_INVALID_ARG;
+  if (!tile_meta_d || !split_offsets_d || !aligned(tile_meta_d, 4) || !aligned(split_offsets_d, 4))
+    return MLA_ERR_INVALID_ARG;
+  const int c = mla::fixed_cost_pages(mla::rows_per_tile(1, h_q));
+  hipError_t e = mla::launch_metadata(nullptr, batch * s_q, c, num_parts, tile_meta_d,
+                                      split_offsets_d, static_cast<hipStream_t>(stream), topk);
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_metadata launch");
+  return MLA_OK;
+}
+
+int mla_decode_sparse_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                          const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                          int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                          const int32_t* indices_d, int topk, const int32_t* tile_meta_d,
+                          const int32_t* split_offsets_d, int num_parts, void* workspace_d,
+                          size_t workspace_bytes, void* out_d, float* lse_d,
+                          void* start_event, void* stop_event, void* stream) {
+  int st = check_sparse_shape(batch, s_q, h_q, h_kv, topk);
+  if (st != MLA_OK) return st;
+  if (num_parts < 1 || num_parts > kMaxParts) return MLA_ERR_INVALID_ARG;
+  if (!q_d || !kcache_d || !block_table_d || !seqlens_d || !indices_d || !tile_meta_d ||
+      !split_offsets_d || !out_d || !lse_d || !workspace_d)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_d, 16) || !aligned(kcache_d, 16) || !aligned(out_d, 16) ||
+      !aligned(block_table_d, 4) || !aligned(seqlens_d, 4) || !aligned(indices_d, 4) ||
+      !aligned(tile_meta_d, 4) || !aligned(split_offsets_d, 4) || !aligned(lse_d, 4) ||
+      !aligned(workspace_d, 256))
+    return MLA_ERR_INVALID_ARG;
+  if (num_blocks < 1 || num_blocks > (1LL << 25) || bt_stride < 1 || !isfinite(scale) ||
+      (causal != 0 && causal != 1))
+    return MLA_ERR_INVALID_ARG;
+  const SparseWorkspace w = sparse_workspace(batch, s_q, h_q, topk, num_parts);
+  if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace_d);
+  int32_t* rowids = reinterpret_cast<int32_t*>(ws + w.rowids);
+  uint32_t* vmask = reinterpret_cast<uint32_t*>(ws + w.vmask);
+  void* zero_row = ws + w.zero_row;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mla::launch_sparse_resolve(indices_d, block_table_d, bt_stride, seqlens_d,
+                                            num_blocks, batch, s_q, topk, causal, rowids, vmask,
+                                            zero_row, s);
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_fwd resolve launch");
+  const int items = batch * s_q;
+  mla::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q_d);
+  a.kcache = kcache_d;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table_d;
+  a.seqlens = seqlens_d;
+  a.tile_meta = tile_meta_d;
+  a.split_offsets = split_offsets_d;
+  split_workspace(workspace_d, 1, h_q, num_parts, &a.part_o, &a.part_lse);
+  a.out = static_cast<uint16_t*>(out_d);
+  a.lse = lse_d;
+  a.bt_stride = bt_stride;
+  a.batch = items;
+  a.s_q = 1;
+  a.h_q = h_q;
+  a.M = h_q;
+  a.causal = 0;
+  a.num_parts = num_parts;
+  a.row_tiles = row_tiles(1, h_q);
+  a.row_tile_rows = mla::tile_rows_for(h_q);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.kv_fp8 = 0;
+  a.sparse = 1;
+  a.const_len = topk;
+  a.rowids = rowids;
+  a.vmask = vmask;
+  a.zero_row = zero_row;
+  e = mla::launch_splitkv(a, s, static_cast<hipEvent_t>(start_event),
+                          static_cast<hipEvent_t>(stop_event));
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_fwd decode launch");
+  mla::CombineArgs c;
+  c.seqlens = nullptr;
+  c.split_offsets = split_offsets_d;
+  c.part_o = a.part_o;
+  c.part_lse = a.part_lse;
+  c.out = a.out;
+  c.lse = lse_d;
+  c.batch = items;
+  c.M = h_q;
+  c.const_len = topk;
+  e = mla::launch_combine(c, s);
+  if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_fwd combine launch");
   return MLA_OK;
 }
 

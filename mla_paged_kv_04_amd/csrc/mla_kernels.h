@@ -49,6 +49,15 @@ struct DecodeArgs {
   int row_tile_rows;          // query rows per workgroup tile (32, 64 or 128)
   float scale_log2;           // scale * log2(e)
   int kv_fp8;                 // 1: kcache holds FP8 pages
+  // Sparse mode (selected keys): requests are (request, token) items of
+  // const_len entries each; entry e of item b is cache row rowids[b*const_len+e]
+  // (page*64 + row, -1 = skipped), bit e%32 of vmask[(b*const_len+e)/32]
+  // says whether it counts; skipped entries load zero_row (1152 zero bytes).
+  int sparse;
+  int const_len;              // > 0: every request has this many keys
+  const int32_t* rowids;
+  const uint32_t* vmask;
+  const void* zero_row;
 };
 
 struct CombineArgs {
@@ -60,11 +69,21 @@ struct CombineArgs {
   float* lse;
   int batch;
   int M;
+  int const_len;              // > 0: every request has this many keys (seqlens unused)
 };
 
 // Launchers (return hipGetLastError() of the launch).
+// const_len > 0: every request has const_len keys and seqlens is not read.
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int c_fix, int num_parts,
-                           int32_t* tile_meta, int32_t* split_offsets, hipStream_t stream);
+                           int32_t* tile_meta, int32_t* split_offsets, hipStream_t stream,
+                           int const_len = 0);
+
+// Sparse mode: resolve selected positions to cache rows (rowids, vmask) and
+// write the zero row.  items = batch * s_q; indices [items, topk].
+hipError_t launch_sparse_resolve(const int32_t* indices, const int32_t* block_table,
+                                 int bt_stride, const int32_t* seqlens, long long num_blocks,
+                                 int batch, int s_q, int topk, int causal, int32_t* rowids,
+                                 uint32_t* vmask, void* zero_row, hipStream_t stream);
 // start/stop (may be null) are recorded at the kernel's own start and end.
 hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start = nullptr,
                           hipEvent_t stop = nullptr);

@@ -122,15 +122,17 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// const_len > 0: every request has const_len keys (seqlens is not read).
 __global__ __launch_bounds__(64) void mla_metadata_kernel(
     const int32_t* __restrict__ seqlens, int batch, int c_fix, int num_parts,
-    int32_t* __restrict__ tile_meta, int32_t* __restrict__ split_offsets) {
+    int32_t* __restrict__ tile_meta, int32_t* __restrict__ split_offsets, int const_len) {
   const int lane = threadIdx.x;
+  auto len = [&](int b) { return const_len > 0 ? const_len : seqlens[b]; };
 
   // total cost C
   long long local = 0;
   for (int b = lane; b < batch; b += 64) {
-    const int n = n_pages(seqlens[b]);
+    const int n = n_pages(len(b));
     local += n > 0 ? (long long)(n + c_fix) : 0;
   }
 #pragma unroll
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(64) void mla_metadata_kernel(
   int carry_slots = 0;
   for (int base = 0; base < batch; base += 64) {
     const int b = base + lane;
-    const int n = b < batch ? n_pages(seqlens[b]) : 0;
+    const int n = b < batch ? n_pages(len(b)) : 0;
     const int cost = n > 0 ? n + c_fix : 0;
     const int incl = wave_incl_scan(cost);
     const long long start = carry_cost + (incl - cost);
@@ -205,9 +207,10 @@ __global__ __launch_bounds__(64) void mla_metadata_kernel(
 }
 
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int c_fix, int num_parts,
-                           int32_t* tile_meta, int32_t* split_offsets, hipStream_t stream) {
+                           int32_t* tile_meta, int32_t* split_offsets, hipStream_t stream,
+                           int const_len) {
   hipLaunchKernelGGL(mla_metadata_kernel, dim3(1), dim3(64), 0, stream, seqlens, batch, c_fix,
-                     num_parts, tile_meta, split_offsets);
+                     num_parts, tile_meta, split_offsets, const_len);
   return hipGetLastError();
 }
 
@@ -266,10 +269,16 @@ __device__ __forceinline__ bool before_end(const DecodeArgs& a, int b, int k, in
   return b < a.batch && (b < b1 || (b == b1 && k < k1));
 }
 
+// Keys of request b: its length, or the fixed entry count of the sparse mode.
+__device__ __forceinline__ int seqlen_of(const DecodeArgs& a, int b) {
+  if (a.const_len > 0) return b < a.batch ? a.const_len : 0;
+  return b < a.batch ? ldc(a.seqlens + b) : 0;
+}
+
 // Move (b, k) to the first page at or after it that belongs to the part.
 __device__ __forceinline__ void seek(const DecodeArgs& a, int& b, int& k, int b1, int k1) {
   while (before_end(a, b, k, b1, k1)) {
-    const int end = (b == b1) ? k1 : n_pages(ldc(a.seqlens + b));
+    const int end = (b == b1) ? k1 : n_pages(seqlen_of(a, b));
     if (k < end) return;
     ++b;
     k = 0;
@@ -345,13 +354,8 @@ __device__ __forceinline__ void issue_half_load(char* lds_buf, const DecodeArgs&
 }
 
 // Unit positions: (request b, page k, half h); the second half of a page is a
-// unit only if the page has keys in it.
-__device__ __forceinline__ int seqlen_of(const DecodeArgs& a, int b) {
-  return b < a.batch ? ldc(a.seqlens + b) : 0;
-}
-
-// Same walk as next_unit with the request length L cached: re-read only when
-// the position moves to another request.
+// unit only if the page has keys in it.  The walk keeps the request length L
+// cached and re-reads it only when the position moves to another request.
 __device__ __forceinline__ void unit_next(const DecodeArgs& a, int& b, int& k, int& h, int& L,
                                           int b1, int k1) {
   if (h == 0 && L - k * kBlock > kHalfRows) {
@@ -369,15 +373,46 @@ __device__ __forceinline__ void unit_next(const DecodeArgs& a, int& b, int& k, i
   }
 }
 
-__device__ __forceinline__ void next_unit(const DecodeArgs& a, int& b, int& k, int& h, int b1,
-                                          int k1) {
-  if (h == 0 && ldc(a.seqlens + b) - k * kBlock > kHalfRows) {
-    h = 1;
-    return;
+// Sparse mode: issue the loads of entries 64k + 32h .. +31 of item b for
+// value wave j.  The unit has the dense layout in LDS (row r of the unit =
+// entry r, units swizzled as lds_swizzle), but every row comes from its own
+// cache row, so each lane carries a 64-bit address (global_load_lds_dwordx4:
+// 16 bytes per lane to M0 + 16 * lane).  Slot j + 4m covers 64 consecutive
+// 16-byte units of the unit buffer, i.e. rows r0 and r0 + 1 at most
+// (72 units per row): their two row ids are wave-uniform scalar loads, and
+// rsel[m] picks the lane's.  Skipped entries (row id -1) load the zero row,
+// so every slot issues exactly one load and the vmcnt accounting of the
+// dense path holds unchanged.  coff[m] is the lane's byte offset in its row.
+__device__ __forceinline__ void issue_half_load_sparse(char* lds_buf, const DecodeArgs& a, int b,
+                                                       int k, int h, const int (&coff)[9],
+                                                       const bool (&rsel)[9], int j) {
+  const long long e0 = (long long)b * a.const_len + k * kBlock + h * kHalfRows;
+  const char* kc = reinterpret_cast<const char*>(a.kcache);
+  const char* zr = reinterpret_cast<const char*>(a.zero_row);
+  const char* src[9];
+#pragma unroll
+  for (int m = 0; m < 9; ++m) {
+    const int r0 = (256 * m + 64 * j) / kChunksPerRow;   // wave-uniform
+    const int rlo = ldc(a.rowids + e0 + r0);
+    const int rhi = r0 + 1 < kHalfRows ? ldc(a.rowids + e0 + r0 + 1) : -1;
+    const int rid = rsel[m] ? rhi : rlo;
+    src[m] = (rid >= 0 ? kc + (long long)rid * kRowBytes : zr) + coff[m];
   }
-  h = 0;
-  ++k;
-  seek(a, b, k, b1, k1);
+  const uint32_t m0 = uni(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_buf)) + j * 1024));
+#define MLA_GDMA(O) "s_nop 0\n\tglobal_load_lds_dwordx4 %[" #O "], off\n\t"
+#define MLA_M0_NEXT "s_add_u32 m0, m0, 0x1000\n\t"
+  asm volatile(
+      "s_mov_b32 m0, %[m]\n\t"
+      MLA_GDMA(a0) MLA_M0_NEXT MLA_GDMA(a1) MLA_M0_NEXT MLA_GDMA(a2) MLA_M0_NEXT
+      MLA_GDMA(a3) MLA_M0_NEXT MLA_GDMA(a4) MLA_M0_NEXT MLA_GDMA(a5) MLA_M0_NEXT
+      MLA_GDMA(a6) MLA_M0_NEXT MLA_GDMA(a7) MLA_M0_NEXT MLA_GDMA(a8)
+      :
+      : [m] "s"(m0), [a0] "v"(src[0]), [a1] "v"(src[1]), [a2] "v"(src[2]), [a3] "v"(src[3]),
+        [a4] "v"(src[4]), [a5] "v"(src[5]), [a6] "v"(src[6]), [a7] "v"(src[7]), [a8] "v"(src[8])
+      : "memory", "m0", "scc");
+#undef MLA_GDMA
+#undef MLA_M0_NEXT
 }
 
 // --------------------------------------------------------------------------
@@ -532,8 +567,11 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // RT: 16-row tiles in the workgroup tile (1, 2 or 4: 16, 32 or 64 query
 // rows); score waves q >= RT have no rows and only keep step with the others.
 // F8: the cache holds FP8 pages (layout above) instead of bf16 rows.
-template <int RT, bool F8>
+// SP: sparse mode (bf16 cache): items of selected entries, rows gathered one
+// by one (issue_half_load_sparse), entries that do not count masked.
+template <int RT, bool F8, bool SP>
 __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const DecodeArgs a) {
+  static_assert(!(F8 && SP), "the sparse mode reads bf16 caches");
   constexpr int NBUF = F8 ? kWSBufsF8 : kWSBufs;          // ring of unit buffers
   constexpr int DL = 8;   // 16-dim output tiles per value wave (128 dims)
   constexpr int UB = F8 ? kF8UnitBytes : kHalfBytes;   // bytes of one unit buffer
@@ -626,6 +664,10 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         }
       }
       const char* ubuf = smem + (t % NBUF) * UB;
+      // sparse: which of the unit's 32 entries count (bit = key in the unit)
+      const uint32_t vm = SP ? static_cast<uint32_t>(ldc(reinterpret_cast<const int32_t*>(a.vmask) +
+                                                         (long long)b * (a.const_len / 32) + 2 * k + h))
+                             : 0xffffffffu;
       if (active) {
 
       // ---- S^T[key][row] = K . Q^T: 32 keys x this wave's 16 rows ----
@@ -734,6 +776,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           for (int v = 0; v < 4; ++v) {
             float xv = s[kt][v] * a.scale_log2;
             if (need_mask && key0 + kt * 16 + v >= lim) xv = -INFINITY;
+            if (SP && !((vm >> (kt * 16 + 4 * g + v)) & 1u)) xv = -INFINITY;
             s[kt][v] = xv;
             mx = fmaxf(mx, xv);
           }
@@ -811,6 +854,17 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     // and the transposed code read: lanes 2e, 2e+1 of a 16-lane group point
     // at the two 8-byte halves of key row kap(g, e) (the keys of P's element
     // e), dims 128j + 16dl .. +16, so lane i receives dim i of all 8 keys.
+    // sparse: the lane's byte offset inside its row and whether its row is
+    // the second one of the slot (see issue_half_load_sparse)
+    int sp_coff[9];
+    bool sp_rsel[9];
+#pragma unroll
+    for (int m = 0; m < 9; ++m) {
+      const int p = 256 * m + tj;
+      const int r = p / kChunksPerRow;
+      sp_coff[m] = ((p - r * kChunksPerRow) ^ lds_swizzle(r)) << 4;
+      sp_rsel[m] = r > (256 * m + 64 * j) / kChunksPerRow;
+    }
     int offc[4], offr, offs, f8_t0;
     {
       const int lane = tid & 63;
@@ -843,6 +897,8 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       if (before_end(a, ib, ik, b1, k1)) {
         if constexpr (F8)
           issue_half_load_f8(smem + (issued % NBUF) * UB, a, ib, ik, ih, offc, offr, offs, j);
+        else if constexpr (SP)
+          issue_half_load_sparse(smem + (issued % NBUF) * UB, a, ib, ik, ih, sp_coff, sp_rsel, j);
         else
           issue_half_load(smem + (issued % NBUF) * kHalfBytes, a, ib, ik, ih, off, j);
         ++issued;
@@ -985,17 +1041,17 @@ int tile_rows_for(int M) {
   return 64;                 // mla_splitkv_ws_kernel<4> (M = 128, 256: 2 or 4 row tiles)
 }
 
-template <int RT, bool F8>
+template <int RT, bool F8, bool SP = false>
 hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid(a.num_parts * a.row_tiles);
   const dim3 block(kThreadsWS);
   if (start == nullptr && stop == nullptr) {
     // plain launch (also what a HIP graph capture records)
-    hipLaunchKernelGGL((mla_splitkv_ws_kernel<RT, F8>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mla_splitkv_ws_kernel<RT, F8, SP>), grid, block, 0, stream, a);
   } else {
     // events recorded at the kernel's own start and end
     void* args[] = {const_cast<DecodeArgs*>(&a)};
-    hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<RT, F8>),
+    hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&mla_splitkv_ws_kernel<RT, F8, SP>),
                                       grid, block, args, 0, stream, start, stop, 0);
     if (e != hipSuccess) return e;
   }
@@ -1004,6 +1060,11 @@ hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, 
 
 hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
+  if (a.sparse) {
+    if (a.row_tile_rows == 16) return launch_ws<1, false, true>(a, stream, start, stop);
+    if (a.row_tile_rows == 32) return launch_ws<2, false, true>(a, stream, start, stop);
+    return launch_ws<4, false, true>(a, stream, start, stop);
+  }
   if (a.kv_fp8) {
     if (a.row_tile_rows == 16) return launch_ws<1, true>(a, stream, start, stop);
     if (a.row_tile_rows == 32) return launch_ws<2, true>(a, stream, start, stop);
@@ -1033,7 +1094,7 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const CombineArgs
   const int ns = a.split_offsets[b + 1] - s0;
   uint16_t* op = a.out + ((long long)b * a.M + r) * kDV + dq;
   if (ns == 0) {
-    if (a.seqlens[b] <= 0) {
+    if ((a.const_len > 0 ? a.const_len : a.seqlens[b]) <= 0) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
         *reinterpret_cast<uint2*>(op + (j + 16 * c) * 4) = make_uint2(0u, 0u);
@@ -1199,6 +1260,52 @@ hipError_t launch_kv_append_fp8(const uint16_t* new_kv, uint8_t* kcache, long lo
                                 const int32_t* seqlens, int batch, int s_q, hipStream_t stream) {
   hipLaunchKernelGGL(mla_kv_append_fp8_kernel, dim3(batch, s_q), dim3(64), 0, stream, new_kv,
                      kcache, num_blocks, block_table, bt_stride, seqlens, s_q);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Sparse mode, step 0: each selected position of item (request b, token t)
+// becomes a cache row id (page * 64 + row) or -1 if the entry does not count
+// (negative, at or beyond the token's visible limit, page slot outside the
+// table or page id outside the pool), plus one validity bit per entry.
+// One thread per entry; a wave covers 64 entries, i.e. two mask words.
+// Block (0, 0) also writes the zero row that skipped entries are loaded from.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mla_sparse_resolve_kernel(
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ block_table, int bt_stride,
+    const int32_t* __restrict__ seqlens, long long num_blocks, int s_q, int topk, int causal,
+    int32_t* __restrict__ rowids, uint32_t* __restrict__ vmask, uint4* __restrict__ zero_row) {
+  const int item = blockIdx.x;
+  const int e = blockIdx.y * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kChunksPerRow)
+    zero_row[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  const int b = item / s_q, t = item - b * s_q;
+  const int L = seqlens[b];
+  int vis = causal ? L - s_q + 1 + t : L;
+  vis = vis < 0 ? 0 : (vis > L ? L : vis);
+  int rid = -1;
+  if (e < topk) {
+    const int pos = indices[(long long)item * topk + e];
+    if (pos >= 0 && pos < vis && pos / kBlock < bt_stride) {
+      const int page = block_table[(long long)b * bt_stride + pos / kBlock];
+      if (page >= 0 && (long long)page < num_blocks) rid = page * kBlock + pos % kBlock;
+    }
+    rowids[(long long)item * topk + e] = rid;
+  }
+  const unsigned long long bal = __ballot(rid >= 0);
+  const int lane = threadIdx.x & 63;
+  if ((lane == 0 || lane == 32) && e < topk)
+    vmask[((long long)item * topk + e) / 32] = static_cast<uint32_t>(lane == 0 ? bal : bal >> 32);
+}
+
+hipError_t launch_sparse_resolve(const int32_t* indices, const int32_t* block_table,
+                                 int bt_stride, const int32_t* seqlens, long long num_blocks,
+                                 int batch, int s_q, int topk, int causal, int32_t* rowids,
+                                 uint32_t* vmask, void* zero_row, hipStream_t stream) {
+  const dim3 grid(batch * s_q, (topk + 255) / 256);
+  hipLaunchKernelGGL(mla_sparse_resolve_kernel, grid, dim3(256), 0, stream, indices, block_table,
+                     bt_stride, seqlens, num_blocks, s_q, topk, causal, rowids, vmask,
+                     static_cast<uint4*>(zero_row));
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ class Workload:
     h_kv: int = 1
     extra_pool: int = 64
     fixed_pool: int | None = None
+    topk: int = 0              # > 0: sparse mode, this many selected positions per token
     desc: str = field(default="", compare=False)
 
     @property
@@ -80,6 +81,13 @@ WORKLOADS: dict[str, Workload] = {
     "prefill": Workload("prefill", "64-token chunked prefill", batch=8, s_q=64, h_q=128,
                         seqlen_kind="uniform2048_8192", seed=1006, extra_pool=64,
                         desc="B=8, s_q=64 causal, h_q=128, seqlens U[2048,8192]"),
+    # Sparse mode on long contexts: each token attends over 2048 selected
+    # positions of a 8K-32K context.
+    "sparse": Workload("sparse", "top-2048 sparse long-context decode", batch=64, s_q=1,
+                       h_q=128, seqlen_kind="uniform8192_32768", seed=1007, extra_pool=64,
+                       topk=2048,
+                       desc="B=64, s_q=1, h_q=128, seqlens U[8192,32768], 2048 selected "
+                            "positions per token"),
 }
 
 # The order the workloads are listed in (index 0 is the small case).
@@ -93,6 +101,8 @@ def draw_seqlens(kind: str, batch: int, gen: torch.Generator) -> torch.Tensor:
         return torch.full((batch,), 4096, dtype=torch.int32)
     if kind == "uniform1024_8192":
         return torch.randint(1024, 8193, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
+    if kind == "uniform8192_32768":
+        return torch.randint(8192, 32769, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
     if kind == "uniform2048_8192":
         return torch.randint(2048, 8193, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
     if kind == "lognormal":
@@ -121,6 +131,7 @@ class DecodeInputs:
     s_q: int
     h_q: int
     kv_format: str = "bf16"    # "bf16": kcache as above; "fp8": uint8 [num_blocks, 41216]
+    indices: torch.Tensor | None = None   # sparse mode: int32 [B, s_q, topk], -1 = padding
 
     @property
     def batch(self) -> int:
@@ -129,7 +140,8 @@ class DecodeInputs:
     def to(self, device) -> "DecodeInputs":
         return DecodeInputs(self.q.to(device), self.kcache.to(device),
                             self.block_table.to(device), self.seqlens.to(device),
-                            self.scale, self.causal, self.s_q, self.h_q, self.kv_format)
+                            self.scale, self.causal, self.s_q, self.h_q, self.kv_format,
+                            None if self.indices is None else self.indices.to(device))
 
 
 def build_inputs(seqlens, s_q: int, h_q: int, seed: int, pool: int | None = None,
@@ -295,17 +307,42 @@ def make_inputs(key: str, nan_tails: bool = True, kv_format: str = "bf16") -> De
     total = sum(blocks_for(int(x)) for x in seqlens)
     pool = w.fixed_pool if w.fixed_pool is not None else total + w.extra_pool
     if kv_format == "fp8":
+        if w.topk:
+            raise ValueError("the sparse mode reads bf16 caches")
         return build_fp8_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
                                 nan_tails=nan_tails, gen=gen)
     if kv_format != "bf16":
         raise ValueError(f"unknown kv_format {kv_format}")
-    return build_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
-                        nan_tails=nan_tails, gen=gen)
+    inp = build_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
+                       nan_tails=nan_tails, gen=gen)
+    if w.topk:
+        inp.indices = draw_topk_indices(seqlens, w.s_q, w.topk, inp.causal, gen)
+    return inp
 
 
 # Cache bytes per token: a bf16 row, or an FP8 row (512 codes + 64 bf16 rope
 # + one fp32 scale).
 KV_BYTES_PER_TOKEN = {"bf16": D_K * 2, "fp8": FP8_LATENT + (D_K - FP8_LATENT) * 2 + 4}
+
+
+def sparse_counts(indices, seqlens, s_q: int, h_q: int, causal: bool) -> dict:
+    """Bytes and flops of the sparse mode: each counted entry's KV row once
+    (1152 B) and its page-table slot (4 B), every index read (4 B), Q/O/LSE
+    of every row, the lengths; 2*(576+512) flops per (row, counted entry)."""
+    seqlens = torch.as_tensor(seqlens).to(torch.int64)
+    ix = torch.as_tensor(indices).to(torch.int64)
+    B, _, topk = ix.shape
+    t = torch.arange(s_q).view(1, s_q)
+    L = seqlens.view(B, 1)
+    vis = (L - s_q + 1 + t).clamp(min=0) if causal else L.expand(B, s_q)
+    vis = torch.minimum(vis, L)
+    counted = int(((ix >= 0) & (ix < vis.unsqueeze(-1))).sum())
+    M = s_q * h_q
+    kv = counted * D_K * 2
+    io = B * M * (D_K * 2 + D_V * 2 + 4)
+    meta = counted * 4 + B * s_q * topk * 4 + B * 4
+    return {"bytes": kv + io + meta, "kv_bytes": kv, "flops": 2 * (D_K + D_V) * h_q * counted,
+            "counted": counted}
 
 
 def algorithmic_counts(seqlens, s_q: int, h_q: int, kv_format: str = "bf16") -> dict:
