@@ -382,20 +382,30 @@ __device__ __forceinline__ void unit_next(const DecodeArgs& a, int& b, int& k, i
 // (72 units per row): their two row ids are wave-uniform scalar loads, and
 // rsel[m] picks the lane's.  Skipped entries (row id -1) load the zero row,
 // so every slot issues exactly one load and the vmcnt accounting of the
-// dense path holds unchanged.  coff[m] is the lane's byte offset in its row.
-__device__ __forceinline__ void issue_half_load_sparse(char* lds_buf, const DecodeArgs& a, int b,
-                                                       int k, int h, const int (&coff)[9],
-                                                       const bool (&rsel)[9], int j) {
+// dense path holds unchanged.  coff[m] is the lane's byte offset in its row;
+// rlo / rhi are the row ids of rows r0(m), r0(m)+1 (load_sparse_rowids),
+// loaded one unit ahead so that their latency is off the issue path.
+__device__ __forceinline__ void load_sparse_rowids(const DecodeArgs& a, int b, int k, int h,
+                                                   int j, int (&rlo)[9], int (&rhi)[9]) {
   const long long e0 = (long long)b * a.const_len + k * kBlock + h * kHalfRows;
+#pragma unroll
+  for (int m = 0; m < 9; ++m) {
+    const int r0 = (256 * m + 64 * j) / kChunksPerRow;   // wave-uniform
+    rlo[m] = ldc(a.rowids + e0 + r0);
+    rhi[m] = r0 + 1 < kHalfRows ? ldc(a.rowids + e0 + r0 + 1) : -1;
+  }
+}
+
+__device__ __forceinline__ void issue_half_load_sparse(char* lds_buf, const DecodeArgs& a,
+                                                       const int (&rlo)[9], const int (&rhi)[9],
+                                                       const int (&coff)[9],
+                                                       const bool (&rsel)[9], int j) {
   const char* kc = reinterpret_cast<const char*>(a.kcache);
   const char* zr = reinterpret_cast<const char*>(a.zero_row);
   const char* src[9];
 #pragma unroll
   for (int m = 0; m < 9; ++m) {
-    const int r0 = (256 * m + 64 * j) / kChunksPerRow;   // wave-uniform
-    const int rlo = ldc(a.rowids + e0 + r0);
-    const int rhi = r0 + 1 < kHalfRows ? ldc(a.rowids + e0 + r0 + 1) : -1;
-    const int rid = rsel[m] ? rhi : rlo;
+    const int rid = rsel[m] ? rhi[m] : rlo[m];
     src[m] = (rid >= 0 ? kc + (long long)rid * kRowBytes : zr) + coff[m];
   }
   const uint32_t m0 = uni(static_cast<uint32_t>(
@@ -893,16 +903,21 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     // the score waves
     int ib = cb, ik = ck, ih = 0, iL = cL;
     int issued = 0;
+    int sp_rlo[9], sp_rhi[9];   // sparse: row ids of the next unit to issue
+    if constexpr (SP) load_sparse_rowids(a, ib, ik, ih, j, sp_rlo, sp_rhi);
     auto issue_next = [&]() {
       if (before_end(a, ib, ik, b1, k1)) {
         if constexpr (F8)
           issue_half_load_f8(smem + (issued % NBUF) * UB, a, ib, ik, ih, offc, offr, offs, j);
         else if constexpr (SP)
-          issue_half_load_sparse(smem + (issued % NBUF) * UB, a, ib, ik, ih, sp_coff, sp_rsel, j);
+          issue_half_load_sparse(smem + (issued % NBUF) * UB, a, sp_rlo, sp_rhi, sp_coff,
+                                 sp_rsel, j);
         else
           issue_half_load(smem + (issued % NBUF) * kHalfBytes, a, ib, ik, ih, off, j);
         ++issued;
         unit_next(a, ib, ik, ih, iL, b1, k1);
+        if constexpr (SP)
+          if (before_end(a, ib, ik, b1, k1)) load_sparse_rowids(a, ib, ik, ih, j, sp_rlo, sp_rhi);
       }
     };
     // wait until unit u has landed (units issued after it stay in flight)
