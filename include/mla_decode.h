@@ -103,9 +103,10 @@ int mla_decode_workspace_bytes(int batch, int s_q, int h_q, int num_parts,
  *                   [split_offsets[b], split_offsets[b+1]) (empty when the
  *                   request is handled by one part and written directly).
  * Balancing rule (all integers): cost_b = ceil(L_b/64) + c for L_b > 0 and 0
- * otherwise, with the per-request overhead c = max(1, min(s_q*h_q, 128)/32)
- * pages; the total cost C is cut into num_parts quotas of q = ceil(C/num_parts)
- * units (a request's first c units are its overhead, then one unit per page).
+ * otherwise, with the per-request overhead c = min(s_q*h_q, 128)/32 pages
+ * (integer division: 0 for 16 rows); the total cost C is cut into num_parts
+ * quotas of q = ceil(C/num_parts) units (a request's first c units are its
+ * overhead, then one unit per page).
  * Deterministic.
  *   seqlens_d int32 [batch]; block_size must be 64; h_kv must be 1.
  */

@@ -15,11 +15,10 @@ constexpr int kPageBytes = kBlock * kRowBytes;  // 73728 bytes per page
 constexpr int kMaxRowsPerTile = 128;       // query rows one workgroup carries
 constexpr int kMetaInts = 8;
 
-// Fixed per-request overhead of the balancing rule, in page units.
-inline int fixed_cost_pages(int rows_per_tile) {
-  int c = rows_per_tile / 32;
-  return c < 1 ? 1 : c;
-}
+// Fixed per-request overhead of the balancing rule, in page units: one page
+// per 32 query rows (none for 16-row tiles, whose start-up cost is below
+// half a page; charging a whole page would unbalance equal requests).
+inline int fixed_cost_pages(int rows_per_tile) { return rows_per_tile / 32; }
 
 inline int rows_per_tile(int s_q, int h_q) {
   int m = s_q * h_q;

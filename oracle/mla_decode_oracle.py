@@ -264,10 +264,10 @@ def fixed_cost_pages(rows_per_tile: int) -> int:
     """Per-request overhead, in page units, charged once per request.
 
     The overhead of starting a request (loading its query rows, writing its
-    result) grows with the rows a workgroup carries: one page per 32 rows,
-    at least one.
+    result) grows with the rows a workgroup carries: one page per 32 rows
+    (none for 16 rows).
     """
-    return max(1, rows_per_tile // 32)
+    return rows_per_tile // 32
 
 
 def rows_per_tile(s_q: int, h_q: int) -> int:
