@@ -322,6 +322,42 @@ constexpr int kHalfLoadsPerWave = 9;                // 36 1 KB slots over 4 valu
 // nothing else in the kernels uses M0 (gfx9 LDS instructions do not), and one
 // wait state separates each M0 write from the load that reads it.  The M0
 // increments are SALU adds, which write SCC: SCC is declared clobbered.
+// A unit's load set up for issue one slot at a time (half_load_slot): the
+// buffer resource of the page half and the LDS address of this wave's first
+// slot.  Spreading a unit's nine loads between the value product's MFMAs
+// keeps the CU's load queue short, so that the issuing wave does not stall
+// behind the loads of the other value waves.
+struct HalfLoad {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t m0;
+};
+
+__device__ __forceinline__ HalfLoad half_load_setup(char* lds_buf, const DecodeArgs& a, int b,
+                                                   int k, int h, int j) {
+  const int L = ldc(a.seqlens + b);
+  int rows = L - k * kBlock - h * kHalfRows;
+  rows = rows > kHalfRows ? kHalfRows : rows;
+  int page = -1;
+  if (k < a.bt_stride) page = ldc(a.block_table + (long long)b * a.bt_stride + k);
+  const bool ok = page >= 0 && (long long)page < a.num_blocks && rows > 0;
+  const char* base = reinterpret_cast<const char*>(a.kcache) +
+                     (ok ? (long long)page * kPageBytes + h * kHalfBytes : 0);
+  const int nrec = uni(ok ? rows * kRowBytes : 0);
+  HalfLoad d;
+  d.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, kRsrcWord3);
+  d.m0 = uni(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_buf)) +
+                                   j * 1024));
+  return d;
+}
+
+// Slot m (0..8) of a unit set up by half_load_setup: 1 KB, 16 bytes per lane.
+__device__ __forceinline__ void half_load_slot(const HalfLoad& d, int off, int m) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[o], %[r], 0 offen lds"
+               :
+               : [m] "s"(d.m0 + m * 0x1000), [r] "s"(d.r), [o] "v"(off)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ void issue_half_load(char* lds_buf, const DecodeArgs& a, int b, int k,
                                                 int h, const int (&off)[9], int j) {
   const int L = ldc(a.seqlens + b);
@@ -932,6 +968,13 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         wait_loads_behind<5, NBUF - 2>(ahead);
     };
 
+    // Loads spread over the value product (bf16 dense cache, 32 or 64 rows):
+    // slot 0 at the start of the phase, slot dl + 1 before the products of
+    // output tile dl.
+    constexpr bool kSpread = !F8 && !SP && RT >= 2;
+    HalfLoad hl;
+    bool hl_on = false;
+
     for (int u = 0; u < NBUF - 1; ++u) issue_next();   // units 0 .. NBUF-2
     wait_unit(0);
     wg_barrier();   // b_0: unit 0 landed
@@ -945,7 +988,19 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       // Unit t+NBUF-1 goes into the buffer of unit t-1, free since the last
       // barrier (its product ended in the previous phase); issued first so
       // that it has NBUF-2 phases to land.
-      if (t >= 1) issue_next();
+      if (t >= 1) {
+        if constexpr (kSpread) {
+          hl_on = before_end(a, ib, ik, b1, k1);
+          if (hl_on) {
+            hl = half_load_setup(smem + (issued % NBUF) * kHalfBytes, a, ib, ik, ih, j);
+            ++issued;
+            unit_next(a, ib, ik, ih, iL, b1, k1);
+            half_load_slot(hl, off[0], 0);
+          }
+        } else {
+          issue_next();
+        }
+      }
       const int b = cb;
       const char* ubuf = smem + (t % NBUF) * UB;
       const int par = t & 1;
@@ -998,6 +1053,10 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int dl = 0; dl < DL; ++dl) {
+            if constexpr (kSpread) {
+              if (hl_on) half_load_slot(hl, off[dl + 1], dl + 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
               o[dl][rt] =
