@@ -975,6 +975,19 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     HalfLoad hl;
     bool hl_on = false;
 
+    // V operands of the value product (bf16 cache), transposed reads
+    bf16x8 va[DL];
+    auto read_v = [&](const char* ub) {
+#pragma unroll
+      for (int dl = 0; dl < DL; ++dl) {
+        const char* tb = ub + t_off[dl & 3] + 128 * (dl >> 2);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
+        const bf16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
+        va[dl] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    };
+
     for (int u = 0; u < NBUF - 1; ++u) issue_next();   // units 0 .. NBUF-2
     wait_unit(0);
     wg_barrier();   // b_0: unit 0 landed
@@ -1006,23 +1019,27 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       const int par = t & 1;
 
       // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all rows ----
+      // The unit's flags, rescale factors and P are read together (one LDS
+      // round trip); the flags first, so the rescale need not wait for P.
       int grown = 0;
+      float al[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         if (tile_row0 + 16 * rt < a.M) grown |= grow_lds[par][rt];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) al[rt] = alpha_lds[par][16 * rt + i];
+      bf16x8 pB[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) pB[rt] = p_lds[par][rt][lane];
       if (grown) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const float al = alpha_lds[par][16 * rt + i];
 #pragma unroll
-          for (int dl = 0; dl < DL; ++dl) o[dl][rt] *= al;
+          for (int dl = 0; dl < DL; ++dl) o[dl][rt] *= al[rt];
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       {
-        bf16x8 pB[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) pB[rt] = p_lds[par][rt][lane];
         if constexpr (F8) {
           // codes converted one 16-dim tile ahead of its products
           i32x2 vc[DL];
@@ -1041,15 +1058,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
             cur = nxt;
           }
         } else {
-          bf16x8 va[DL];
-#pragma unroll
-          for (int dl = 0; dl < DL; ++dl) {
-            const char* tb = ubuf + t_off[dl & 3] + 128 * (dl >> 2);
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb));
-            const bf16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(tb + 16 * kRowBytes));
-            va[dl] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
+          read_v(ubuf);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int dl = 0; dl < DL; ++dl) {
