@@ -625,11 +625,15 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * UB];
   __shared__ bf16x8 p_lds[2][RT][64];   // P^T operands: [unit parity][row tile][lane]
   __shared__ float alpha_lds[2][16 * RT];   // per-row rescale factor of the unit
-  __shared__ int grow_lds[2][RT];       // per row tile: any row rescaled
+  // per 16-row block q, byte q: any of its rows rescaled in the unit (one
+  // dword, so the value waves test all blocks with one read; blocks without
+  // rows keep the 0 written here)
+  __shared__ uint32_t grow_lds[2];
   __shared__ float lfin_lds[2][16 * RT];    // per-row sum of a piece ending at the unit
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < 2) grow_lds[tid] = 0u;   // ordered before every use by the first barrier
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int i = lane & 15;
@@ -727,7 +731,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int e = 0; e < 2; ++e) sp[kt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-        constexpr int D1 = 2;
+        constexpr int D1 = 4;   // K steps read ahead of their products
         bf16x8 ka[D1 + 1][2];
 #pragma unroll
         for (int ks = 0; ks < 18 + D1; ++ks) {
@@ -850,7 +854,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         p_lds[t & 1][q][lane] = pb;
         if (g == 0) alpha_lds[t & 1][16 * q + i] = alpha;
         const int any = __any(grow) ? 1 : 0;
-        if (lane == 0) grow_lds[t & 1][q] = any;
+        if (lane == 0) reinterpret_cast<uint8_t*>(&grow_lds[t & 1])[q] = static_cast<uint8_t>(any);
       }
       }   // active
 
@@ -1021,11 +1025,8 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all rows ----
       // The unit's flags, rescale factors and P are read together (one LDS
       // round trip); the flags first, so the rescale need not wait for P.
-      int grown = 0;
+      const bool grown = grow_lds[par] != 0u;
       float al[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        if (tile_row0 + 16 * rt < a.M) grown |= grow_lds[par][rt];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) al[rt] = alpha_lds[par][16 * rt + i];
       bf16x8 pB[RT];
