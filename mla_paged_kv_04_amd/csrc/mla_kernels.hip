@@ -1023,15 +1023,33 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       const int par = t & 1;
 
       // ---- O^T[dim][row] += V^T . P^T: this wave's 128 dims, all rows ----
-      // The unit's flags, rescale factors and P are read together (one LDS
-      // round trip); the flags first, so the rescale need not wait for P.
+      // With 32 or 64 rows every LDS operand of the unit is requested at once
+      // (one round trip; the rescale factors read as volatile so that the
+      // compiler does not sink them into the rescale branch, a second round
+      // trip).  With 16 rows (memory-bound) V is read after the rescale, which
+      // measured faster there.
+      constexpr bool kEarlyV = RT >= 2;
       const bool grown = grow_lds[par] != 0u;
       float al[RT];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) al[rt] = alpha_lds[par][16 * rt + i];
+      for (int rt = 0; rt < RT; ++rt)
+        al[rt] = kEarlyV ? *(volatile MLA_LDS float*)(&alpha_lds[par][16 * rt + i])
+                         : alpha_lds[par][16 * rt + i];
       bf16x8 pB[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) pB[rt] = p_lds[par][rt][lane];
+      i32x2 vc[DL];   // FP8: transposed code reads
+      auto read_vc = [&]() {
+        if constexpr (F8) {
+#pragma unroll
+          for (int dl = 0; dl < DL; ++dl)
+            vc[dl] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (MLA_LDS i32x2*)((MLA_LDS char*)(ubuf) + (f8_t0 ^ (dl << 4))));
+        } else {
+          read_v(ubuf);
+        }
+      };
+      if constexpr (kEarlyV) read_vc();
       if (grown) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -1040,14 +1058,10 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if constexpr (!kEarlyV) read_vc();
       {
         if constexpr (F8) {
           // codes converted one 16-dim tile ahead of its products
-          i32x2 vc[DL];
-#pragma unroll
-          for (int dl = 0; dl < DL; ++dl)
-            vc[dl] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (MLA_LDS i32x2*)((MLA_LDS char*)(ubuf) + (f8_t0 ^ (dl << 4))));
           bf16x8 cur = e4m3x8_to_bf16(vc[0][0], vc[0][1]);
 #pragma unroll
           for (int dl = 0; dl < DL; ++dl) {
@@ -1059,7 +1073,6 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
             cur = nxt;
           }
         } else {
-          read_v(ubuf);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int dl = 0; dl < DL; ++dl) {
