@@ -40,73 +40,94 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 307840763,
-        "write_bytes": 9882822,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 306969416,
+        "write_bytes": 8404992,
         "fetch_scale": 1.99986,
         "write_scale": 1.0
     },
     "ridge": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 704751928,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 704820108,
         "write_bytes": 59894272,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "long": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 770872638,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 770893003,
         "write_bytes": 37559808,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ragged": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 510542367,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 510580714,
         "write_bytes": 78838784,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "draft": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 210897305,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 210929201,
         "write_bytes": 58843136,
         "fetch_scale": 1.99989,
         "write_scale": 1.0
     },
+    "sparse": {
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 171346404,
+        "write_bytes": 33619968,
+        "fetch_scale": 1.99986,
+        "write_scale": 1.0
+    },
+    "prefill": {
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 405337115,
+        "write_bytes": 92569600,
+        "fetch_scale": 1.99988,
+        "write_scale": 1.0
+    },
     "membound/fp8": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 174710825,
-        "write_bytes": 9882496,
-        "fetch_scale": 1.99992,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 173845069,
+        "write_bytes": 8404992,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0
     },
     "ridge/fp8": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 410084726,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 410128045,
         "write_bytes": 59894272,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "long/fp8": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 437948077,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 437975080,
         "write_bytes": 37559808,
-        "fetch_scale": 1.9999,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ragged/fp8": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 310432996,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 310469401,
         "write_bytes": 78838784,
-        "fetch_scale": 1.99992,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0
     },
     "draft/fp8": {
-        "kernel_sha256": "d350cdb584546e4236d5a5d68402482fe103cde0f36c8535600bc6cc127f54a2",
-        "fetch_bytes": 133651507,
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 133680847,
         "write_bytes": 58843136,
-        "fetch_scale": 1.99992,
+        "fetch_scale": 1.9999,
+        "write_scale": 1.0
+    },
+    "prefill/fp8": {
+        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
+        "fetch_bytes": 264208429,
+        "write_bytes": 92569600,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0
     }
 }
