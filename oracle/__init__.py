@@ -13,5 +13,5 @@ from .mla_fp8_oracle import (  # noqa: F401
     gather_request_kv_fp8, decode_fp8, kv_append_fp8,
 )
 from .mla_sparse_oracle import (  # noqa: F401
-    counted_entries, decode_sparse, decode_sparse_bruteforce,
+    counted_entries, decode_sparse, decode_sparse_bruteforce, decode_sparse_fp8,
 )

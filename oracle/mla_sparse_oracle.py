@@ -23,6 +23,9 @@ that keeps everything else of the dense definition:
   O = sum_i exp(s_i - LSE) K_b[j_i, :512];  no counted entry: O = 0,
   LSE = -inf.  Keys are gathered through the block table as in the dense
   mode (token j is row j % 64 of page block_table[b][j // 64]).
+* Over an FP8 page pool (the same page names FP8 as its other throughput
+  step) each selected row is dequantised exactly as the FP8 oracle does
+  (latent = e4m3(code) * scale, rope as stored); nothing else changes.
 """
 from __future__ import annotations
 
@@ -51,6 +54,24 @@ def _gather_rows(kcache, block_table_b, positions) -> np.ndarray:
         sel = kcache[torch.as_tensor(pages), torch.as_tensor(rows), 0]
         return _f64(sel)
     return np.asarray(kcache[pages, rows, 0], dtype=np.float64)
+
+
+def _gather_rows_fp8(pool, block_table_b, positions, cache: dict) -> np.ndarray:
+    """Key rows (fp64 [n, 576], exact) of the given logical positions of one
+    request in an FP8 page pool; dequantised pages are memoised in ``cache``."""
+    from .mla_fp8_oracle import dequant_page, FP8_PAGE_BYTES
+    pos = np.asarray(positions, dtype=np.int64)
+    out = np.zeros((pos.size, 576), dtype=np.float64)
+    if pos.size == 0:
+        return out
+    pool8 = pool.reshape(-1, FP8_PAGE_BYTES)
+    bt = np.asarray(block_table_b, dtype=np.int64)
+    for i, j in enumerate(pos):
+        page = int(bt[j // BLOCK_SIZE])
+        if page not in cache:
+            cache[page] = dequant_page(pool8[page])
+        out[i] = cache[page][j % BLOCK_SIZE]
+    return out
 
 
 def decode_sparse(q, kcache, block_table, seqlens, indices, scale: float, causal: bool,
@@ -114,4 +135,35 @@ def decode_sparse_bruteforce(q, kcache, block_table, seqlens, indices, scale: fl
                 O[b, t, h] = [math.fsum(w[i] * rows[i][d] for i in range(len(rows)))
                               for d in range(D_V)]
                 LSE[b, t, h] = lse
+    return O, LSE
+
+
+def decode_sparse_fp8(q, pool, block_table, seqlens, indices, scale: float, causal: bool,
+                      requests=None):
+    """fp64 reference of the sparse mode over an FP8 page pool: the definition
+    of ``decode_sparse`` with every selected key row dequantised exactly as in
+    ``mla_fp8_oracle`` (latent = e4m3(code) * scale, rope as stored).
+
+    pool uint8 [pages, 41216]; other arguments and the result as
+    ``decode_sparse``."""
+    from .mla_fp8_oracle import _u8
+    qf = _f64(q)
+    B, s_q, h_q, dk = qf.shape
+    sl = _i64(seqlens)
+    bt = _i64(block_table)
+    ix = _i64(indices)
+    pool8 = _u8(pool)
+    O = np.full((B, s_q, h_q, D_V), np.nan, dtype=np.float64)
+    LSE = np.full((B, s_q, h_q), np.nan, dtype=np.float64)
+    cache: dict = {}
+    reqs = range(B) if requests is None else requests
+    for b in reqs:
+        L = int(sl[b])
+        for t in range(s_q):
+            ent = counted_entries(ix[b, t], visible_count(L, s_q, t, causal))
+            K = _gather_rows_fp8(pool8, bt[b], ent, cache)
+            nvis = np.full((h_q,), K.shape[0], dtype=np.int64)
+            Ob, lb = attend_rows(qf[b, t], K, scale, nvis)
+            O[b, t] = Ob
+            LSE[b, t] = lb
     return O, LSE

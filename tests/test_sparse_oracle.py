@@ -92,3 +92,62 @@ def test_multiset_closed_form_and_empty():
         assert np.allclose(O[0, 0, h], k[:512], rtol=1e-14, atol=0)
         assert math.isclose(L[0, 0, h], s + math.log(3.0), rel_tol=0, abs_tol=1e-12)
     assert np.all(O[1] == 0.0) and np.all(L[1] == -np.inf)
+
+
+# ------------------------------------------------ sparse mode over FP8 pages
+
+def _fp8_case(seqlens, s_q, h_q, seed):
+    from workloads import build_fp8_inputs
+    return build_fp8_inputs(seqlens, s_q, h_q, seed=seed, extra_pool=3)
+
+
+def test_fp8_all_visible_selection_is_fp8_dense():
+    """Selecting every visible position is the (separately pinned) dense FP8
+    oracle."""
+    from oracle import decode_fp8, decode_sparse_fp8
+    seqlens, s_q, causal = [70, 3, 150], 2, True
+    inp = _fp8_case(seqlens, s_q, 4, seed=71)
+    ix = _all_visible(seqlens, s_q, causal, max(seqlens) + 5)
+    Os, Ls = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix, inp.scale,
+                               causal)
+    Od, Ld = decode_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, causal)
+    assert np.array_equal(np.isinf(Ls), np.isinf(Ld))
+    assert np.allclose(Os, Od, rtol=0, atol=1e-12)
+    assert np.allclose(Ls, Ld, rtol=0, atol=1e-12)
+
+
+def test_fp8_equals_bf16_sparse_over_dequantised_pages():
+    """Every dequantised FP8 value is a bf16 value (at most 4 significant bits
+    times a power of two), so the sparse mode over FP8 pages equals the bf16
+    sparse oracle over a bf16 cache holding the dequantised rows, entry for
+    entry — which pins the FP8 row addressing (page, row, the three fields)
+    to the bf16 gathering."""
+    from oracle import decode_sparse_fp8, dequant_page
+    seqlens, s_q = [300, 65, 129], 1
+    inp = _fp8_case(seqlens, s_q, 3, seed=72)
+    pool8 = inp.kcache.view(torch.uint8).reshape(inp.kcache.shape[0], -1).numpy()
+    K = np.stack([dequant_page(pool8[p]) for p in range(pool8.shape[0])])   # [pages, 64, 576]
+    fin = np.isfinite(K)
+    assert np.array_equal(torch.from_numpy(K[fin]).to(torch.bfloat16).double().numpy(), K[fin])
+    kc16 = torch.from_numpy(K).to(torch.bfloat16).unsqueeze(2).contiguous()   # [pages, 64, 1, 576]
+    g = torch.Generator().manual_seed(8)
+    ix = draw_topk_indices(seqlens, s_q, 96, True, g, pad_frac=0.2)
+    ix[0, 0, :3] = 17                       # a duplicate
+    a = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix, inp.scale, True)
+    b = decode_sparse(inp.q, kc16, inp.block_table, inp.seqlens, ix, inp.scale, True)
+    assert np.array_equal(np.isinf(a[1]), np.isinf(b[1]))
+    assert np.allclose(a[0], b[0], rtol=0, atol=1e-13)
+    assert np.allclose(a[1], b[1], rtol=0, atol=1e-13)
+
+
+def test_fp8_non_counting_entries_change_nothing():
+    from oracle import decode_sparse_fp8
+    inp = _fp8_case([200, 90], 2, 2, seed=73)
+    g = torch.Generator().manual_seed(9)
+    ix = draw_topk_indices([200, 90], 2, 32, True, g)
+    base = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix, inp.scale, True)
+    extra = torch.tensor([-1, -3, 200, 10 ** 5], dtype=torch.int32)
+    ix2 = torch.cat([ix, extra.expand(2, 2, 4)], dim=2).contiguous()
+    ix2[1, 0, -1] = 89      # request 1, token 0 sees positions < 89
+    got = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix2, inp.scale, True)
+    assert np.array_equal(base[0], got[0]) and np.array_equal(base[1], got[1])

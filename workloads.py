@@ -307,10 +307,11 @@ def make_inputs(key: str, nan_tails: bool = True, kv_format: str = "bf16") -> De
     total = sum(blocks_for(int(x)) for x in seqlens)
     pool = w.fixed_pool if w.fixed_pool is not None else total + w.extra_pool
     if kv_format == "fp8":
+        inp = build_fp8_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
+                               nan_tails=nan_tails, gen=gen)
         if w.topk:
-            raise ValueError("the sparse mode reads bf16 caches")
-        return build_fp8_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
-                                nan_tails=nan_tails, gen=gen)
+            inp.indices = draw_topk_indices(seqlens, w.s_q, w.topk, inp.causal, gen)
+        return inp
     if kv_format != "bf16":
         raise ValueError(f"unknown kv_format {kv_format}")
     inp = build_inputs(seqlens, w.s_q, w.h_q, seed=w.seed, pool=pool,
@@ -325,10 +326,12 @@ def make_inputs(key: str, nan_tails: bool = True, kv_format: str = "bf16") -> De
 KV_BYTES_PER_TOKEN = {"bf16": D_K * 2, "fp8": FP8_LATENT + (D_K - FP8_LATENT) * 2 + 4}
 
 
-def sparse_counts(indices, seqlens, s_q: int, h_q: int, causal: bool) -> dict:
+def sparse_counts(indices, seqlens, s_q: int, h_q: int, causal: bool,
+                  kv_format: str = "bf16") -> dict:
     """Bytes and flops of the sparse mode: each counted entry's KV row once
-    (1152 B) and its page-table slot (4 B), every index read (4 B), Q/O/LSE
-    of every row, the lengths; 2*(576+512) flops per (row, counted entry)."""
+    (1152 B, or 644 B for an FP8 row) and its page-table slot (4 B), every
+    index read (4 B), Q/O/LSE of every row, the lengths; 2*(576+512) flops per
+    (row, counted entry)."""
     seqlens = torch.as_tensor(seqlens).to(torch.int64)
     ix = torch.as_tensor(indices).to(torch.int64)
     B, _, topk = ix.shape
@@ -338,7 +341,7 @@ def sparse_counts(indices, seqlens, s_q: int, h_q: int, causal: bool) -> dict:
     vis = torch.minimum(vis, L)
     counted = int(((ix >= 0) & (ix < vis.unsqueeze(-1))).sum())
     M = s_q * h_q
-    kv = counted * D_K * 2
+    kv = counted * KV_BYTES_PER_TOKEN[kv_format]
     io = B * M * (D_K * 2 + D_V * 2 + 4)
     meta = counted * 4 + B * s_q * topk * 4 + B * 4
     return {"bytes": kv + io + meta, "kv_bytes": kv, "flops": 2 * (D_K + D_V) * h_q * counted,
