@@ -162,11 +162,13 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the workload:
     whole requests in order until about `budget_s` seconds have elapsed."""
     import numpy as np
-    from oracle import decode, decode_fp8, decode_sparse
+    from oracle import decode, decode_fp8, decode_sparse, decode_sparse_fp8
     from workloads import algorithmic_counts, sparse_counts
     if inp.indices is not None:
+        sparse_ref = decode_sparse_fp8 if inp.kv_format == "fp8" else decode_sparse
+
         def oracle_decode(q, kc, bt, sl, scale, causal, requests):
-            return decode_sparse(q, kc, bt, sl, inp.indices, scale, causal, requests=requests)
+            return sparse_ref(q, kc, bt, sl, inp.indices, scale, causal, requests=requests)
     else:
         oracle_decode = decode_fp8 if inp.kv_format == "fp8" else decode
     try:
@@ -191,7 +193,7 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     dt = time.perf_counter() - t0
     sl = [int(inp.seqlens[b]) for b in done]
     if inp.indices is not None:
-        c = sparse_counts(inp.indices[done], sl, inp.s_q, inp.h_q, inp.causal)
+        c = sparse_counts(inp.indices[done], sl, inp.s_q, inp.h_q, inp.causal, inp.kv_format)
     else:
         c = algorithmic_counts(sl, inp.s_q, inp.h_q, inp.kv_format)
     return {
@@ -255,16 +257,17 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     fp8 = args.kv == "fp8"
     sparse = w.topk > 0
-    if sparse and (fp8 or args.with_append or args.graph):
-        print("bench.py: the sparse workload runs eagerly over a bf16 cache", file=sys.stderr)
+    if sparse and (args.with_append or args.graph):
+        print("bench.py: the sparse workload runs eagerly, without the append", file=sys.stderr)
         return 2
     inp = make_inputs(args.workload, kv_format=args.kv)
     g = inp.to(dev)
     if sparse:
-        counts = sparse_counts(inp.indices, inp.seqlens, inp.s_q, inp.h_q, inp.causal)
+        counts = sparse_counts(inp.indices, inp.seqlens, inp.s_q, inp.h_q, inp.causal, args.kv)
     else:
         counts = algorithmic_counts(inp.seqlens.tolist(), inp.s_q, inp.h_q, args.kv)
     decode_fn = mla.splitkv_fp8 if fp8 else mla.splitkv
+    sparse_fn = mla.sparse_fwd_fp8 if fp8 else mla.sparse_fwd
     append_fn = mla.kv_append_fp8 if fp8 else mla.kv_append
 
     if sparse:   # (request, token) items of topk entries
@@ -298,10 +301,10 @@ def main(argv=None) -> int:
             if evs is not None:
                 evs[0].record()
             meta = mla.sparse_metadata(inp.batch, inp.s_q, inp.h_q, topk, dev, parts=parts)
-            mla.sparse_fwd(g.q, g.kcache, g.block_table, g.seqlens, g.indices, inp.scale,
-                           inp.causal, meta=meta, workspace=ws, out=out, lse=lse,
-                           start_event=evs[2] if evs else None,
-                           stop_event=evs[3] if evs else None)
+            sparse_fn(g.q, g.kcache, g.block_table, g.seqlens, g.indices, inp.scale,
+                      inp.causal, meta=meta, workspace=ws, out=out, lse=lse,
+                      start_event=evs[2] if evs else None,
+                      stop_event=evs[3] if evs else None)
             if evs is not None:
                 evs[1].record()
             return
@@ -324,8 +327,8 @@ def main(argv=None) -> int:
             evs[0].record()
             meta = mla.sparse_metadata(inp.batch, inp.s_q, inp.h_q, topk, dev, parts=parts)
             evs[1].record()
-            mla.sparse_fwd(g.q, g.kcache, g.block_table, g.seqlens, g.indices, inp.scale,
-                           inp.causal, meta=meta, workspace=ws, out=out, lse=lse)
+            sparse_fn(g.q, g.kcache, g.block_table, g.seqlens, g.indices, inp.scale,
+                      inp.causal, meta=meta, workspace=ws, out=out, lse=lse)
             evs[2].record()
             evs[3].record()
             return

@@ -269,7 +269,7 @@ int mla_kv_append_fp8(const void* new_kv_d, void* kcache_fp8_d, int64_t num_bloc
                       int batch, int s_q, void* stream);
 
 /*
- * Sparse (selected-keys) mode, bf16 cache.  Page "云上玩转DeepSeek系列之五：实测
+ * Sparse (selected-keys) mode.  Page "云上玩转DeepSeek系列之五：实测
  * 优化16%，体验FlashMLA加速DeepSeek-V2-Lite推理" (ruibaoantu.com), section 四,
  * item 2, recommends FlashMLA's sparse attention mode beyond 8K tokens and
  * gives no algorithm; this library's reading: the caller selects, for every
@@ -314,6 +314,24 @@ int mla_decode_sparse_fwd(const void* q_d, const void* kcache_d, int64_t num_blo
                           int num_parts, void* workspace_d, size_t workspace_bytes,
                           void* out_d, float* lse_d, void* start_event, void* stop_event,
                           void* stream);
+
+/*
+ * mla_decode_sparse_fwd_fp8 — the sparse mode over an FP8 cache: kcache_d
+ * an array of num_blocks FP8 pages (MLA_FP8_PAGE_BYTES each, the layout of
+ * mla_decode_splitkv_fp8), every other argument, the workspace, metadata
+ * and outputs as mla_decode_sparse_fwd.  A selected row is used exactly as
+ * the dense FP8 path uses it (latent = e4m3(code) * scale, rope bf16);
+ * its three fields are gathered row by row (codes, rope, scale).  Same
+ * errors and constraints as mla_decode_sparse_fwd.
+ */
+int mla_decode_sparse_fwd_fp8(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                              const int32_t* block_table_d, int bt_stride,
+                              const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                              float scale, int causal, const int32_t* indices_d, int topk,
+                              const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                              int num_parts, void* workspace_d, size_t workspace_bytes,
+                              void* out_d, float* lse_d, void* start_event, void* stop_event,
+                              void* stream);
 
 /* Static text for a status code. */
 const char* mla_status_string(int status);

@@ -68,6 +68,10 @@ _SIGNATURES = {
                                        _c_int, _c_int, _c_int, _c_float, _c_int, _c_ptr, _c_int,
                                        _c_ptr, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr,
                                        _c_ptr, _c_ptr, _c_ptr]),
+    "mla_decode_sparse_fwd_fp8": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr,
+                                           _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                           _c_ptr, _c_int, _c_ptr, _c_ptr, _c_int, _c_ptr,
+                                           _c_size, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_last_hip_error": (ctypes.c_char_p, []),
     "mla_device_num_cus": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
@@ -376,7 +380,23 @@ def sparse_fwd(q, kcache, block_table, seqlens, indices, scale: float,
     """Sparse-mode decode over a bf16 cache: every head of query token t of
     request b attends over the cache positions indices[b, t, :] (int32
     [B, s_q, topk], -1 = padding) that are visible.  Returns (O, LSE) like fwd."""
-    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens)
+    return _sparse_fwd(q, kcache, block_table, seqlens, indices, scale, causal, meta, parts,
+                       workspace, out, lse, start_event, stop_event, fp8=False)
+
+
+def sparse_fwd_fp8(q, kcache, block_table, seqlens, indices, scale: float,
+                   causal: bool | None = None, meta: Metadata | None = None,
+                   parts: int | None = None, workspace=None, out=None, lse=None,
+                   start_event=None, stop_event=None):
+    """sparse_fwd over an FP8 cache, kcache uint8 [num_blocks, 41216]
+    (mla_decode_sparse_fwd_fp8)."""
+    return _sparse_fwd(q, kcache, block_table, seqlens, indices, scale, causal, meta, parts,
+                       workspace, out, lse, start_event, stop_event, fp8=True)
+
+
+def _sparse_fwd(q, kcache, block_table, seqlens, indices, scale, causal, meta, parts,
+                workspace, out, lse, start_event, stop_event, fp8: bool):
+    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens, fp8=fp8)
     _require(indices, torch.int32, "indices", 3)
     if tuple(indices.shape[:2]) != (batch, s_q):
         raise ValueError(f"indices {tuple(indices.shape)} do not match q {tuple(q.shape)}")
@@ -389,11 +409,11 @@ def sparse_fwd(q, kcache, block_table, seqlens, indices, scale: float,
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
     out, lse = _outputs(q, out, lse)
-    _check(lib().mla_decode_sparse_fwd(
+    name = "mla_decode_sparse_fwd_fp8" if fp8 else "mla_decode_sparse_fwd"
+    _check(getattr(lib(), name)(
         _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
         _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)), _ptr(indices),
         topk, _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
-        _event_handle(start_event), _event_handle(stop_event), _stream(q.device)),
-        "mla_decode_sparse_fwd")
+        _event_handle(start_event), _event_handle(stop_event), _stream(q.device)), name)
     return out, lse

@@ -369,13 +369,17 @@ int mla_decode_sparse_metadata(int batch, int s_q, int h_q, int topk, int num_pa
   return MLA_OK;
 }
 
-int mla_decode_sparse_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
-                          const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
-                          int batch, int s_q, int h_q, int h_kv, float scale, int causal,
-                          const int32_t* indices_d, int topk, const int32_t* tile_meta_d,
-                          const int32_t* split_offsets_d, int num_parts, void* workspace_d,
-                          size_t workspace_bytes, void* out_d, float* lse_d,
-                          void* start_event, void* stop_event, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int sparse_fwd_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                    const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                    int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                    const int32_t* indices_d, int topk, const int32_t* tile_meta_d,
+                    const int32_t* split_offsets_d, int num_parts, void* workspace_d,
+                    size_t workspace_bytes, void* out_d, float* lse_d, void* start_event,
+                    void* stop_event, void* stream, int kv_fp8) {
   int st = check_sparse_shape(batch, s_q, h_q, h_kv, topk);
   if (st != MLA_OK) return st;
   if (num_parts < 1 || num_parts > kMaxParts) return MLA_ERR_INVALID_ARG;
@@ -423,7 +427,7 @@ int mla_decode_sparse_fwd(const void* q_d, const void* kcache_d, int64_t num_blo
   a.row_tiles = row_tiles(1, h_q);
   a.row_tile_rows = mla::tile_rows_for(h_q);
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.kv_fp8 = 0;
+  a.kv_fp8 = kv_fp8;
   a.sparse = 1;
   a.const_len = topk;
   a.rowids = rowids;
@@ -445,6 +449,37 @@ int mla_decode_sparse_fwd(const void* q_d, const void* kcache_d, int64_t num_blo
   e = mla::launch_combine(c, s);
   if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_fwd combine launch");
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_sparse_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                          const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                          int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                          const int32_t* indices_d, int topk, const int32_t* tile_meta_d,
+                          const int32_t* split_offsets_d, int num_parts, void* workspace_d,
+                          size_t workspace_bytes, void* out_d, float* lse_d,
+                          void* start_event, void* stop_event, void* stream) {
+  return sparse_fwd_impl(q_d, kcache_d, num_blocks, block_table_d, bt_stride, seqlens_d, batch,
+                         s_q, h_q, h_kv, scale, causal, indices_d, topk, tile_meta_d,
+                         split_offsets_d, num_parts, workspace_d, workspace_bytes, out_d, lse_d,
+                         start_event, stop_event, stream, 0);
+}
+
+int mla_decode_sparse_fwd_fp8(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                              const int32_t* block_table_d, int bt_stride,
+                              const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                              float scale, int causal, const int32_t* indices_d, int topk,
+                              const int32_t* tile_meta_d, const int32_t* split_offsets_d,
+                              int num_parts, void* workspace_d, size_t workspace_bytes,
+                              void* out_d, float* lse_d, void* start_event, void* stop_event,
+                              void* stream) {
+  return sparse_fwd_impl(q_d, kcache_d, num_blocks, block_table_d, bt_stride, seqlens_d, batch,
+                         s_q, h_q, h_kv, scale, causal, indices_d, topk, tile_meta_d,
+                         split_offsets_d, num_parts, workspace_d, workspace_bytes, out_d, lse_d,
+                         start_event, stop_event, stream, 1);
 }
 
 }  // extern "C"

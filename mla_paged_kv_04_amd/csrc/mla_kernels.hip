@@ -477,6 +477,13 @@ constexpr int kF8UnitCodes = 0;
 constexpr int kF8UnitRope = kHalfRows * kF8Latent;         // 16384
 constexpr int kF8UnitScale = kF8UnitRope + kHalfRows * 128;   // 20480
 constexpr int kF8UnitBytes = kF8UnitScale + 256;           // 20736
+// Sparse mode over FP8 pages: the scales of a unit's rows are gathered one
+// row at a time, value wave j fetching rows 8j .. 8j+7 with one 64-lane dword
+// load into its own 256-byte window (lanes 8..63 load zeros from the zero
+// row), so a unit ends in four windows: scale of row r at window r / 8,
+// byte 4 (r % 8).
+constexpr int kF8SpUnitBytes = kF8UnitScale + 4 * 256;     // 21504
+__device__ __forceinline__ int f8sp_scale_off(int r) { return (r >> 3) * 256 + (r & 7) * 4; }
 // Ring depth for FP8 units.  The smaller units would leave room for six or
 // seven buffers, but measured on gfx950 both are slower than four (membound
 // 48.8 / 49.6 us against 46.7 us): with one 16-row tile the score wave's own
@@ -600,6 +607,89 @@ __device__ __forceinline__ void load_q_rows_f8(bf16x8 (&q)[18], const bf16x8* ql
       : "memory");
 }
 
+// Sparse mode over FP8 pages: row ids of the unit's rows that value wave j
+// gathers (entries 64k + 32h .. +31 of item b): rc = rows 2(j + 4m) and
+// 2(j + 4m) + 1 of code slot m, r8 = rows 8j .. 8j+7 (its rope slot and its
+// scales).  Loaded one unit ahead, like load_sparse_rowids.
+__device__ __forceinline__ void load_sparse_rowids_f8(const DecodeArgs& a, int b, int k, int h,
+                                                      int j, int (&rc)[8], int (&r8)[8]) {
+  const long long e0 = (long long)b * a.const_len + k * kBlock + h * kHalfRows;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    rc[2 * m] = ldc(a.rowids + e0 + 2 * (j + 4 * m));
+    rc[2 * m + 1] = ldc(a.rowids + e0 + 2 * (j + 4 * m) + 1);
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) r8[x] = ldc(a.rowids + e0 + 8 * j + x);
+}
+
+// Select v[idx] from eight wave-uniform values with a per-lane idx (0..7).
+__device__ __forceinline__ int select8(const int (&v)[8], int idx) {
+  const int a0 = (idx & 1) ? v[1] : v[0], a1 = (idx & 1) ? v[3] : v[2];
+  const int a2 = (idx & 1) ? v[5] : v[4], a3 = (idx & 1) ? v[7] : v[6];
+  const int b0 = (idx & 2) ? a1 : a0, b1 = (idx & 2) ? a3 : a2;
+  return (idx & 4) ? b1 : b0;
+}
+
+// Issue value wave j's six loads of a sparse FP8 unit: code slots j + 4m
+// (rows 2s and 2s + 1, 512 bytes each, 32 lanes per row), rope slot j (rows
+// 8j .. 8j+7, 128 bytes each, 8 lanes per row) and the scales of rows
+// 8j .. 8j+7 (lanes 0..7).  Every row comes from its own cache row, so each
+// lane carries a 64-bit address (global_load_lds); entries that do not
+// count (row id -1) read the zero row, and every slot issues exactly one
+// load, so a wave always has six loads per unit.  The LDS side keeps the
+// dense FP8 unit layout and swizzles (code rows c ^ f8_code_swizzle(r), rope
+// rows c ^ f8_rope_swizzle(r)); the scales go to f8sp_scale_off windows.
+__device__ __forceinline__ void issue_half_load_f8_sparse(char* lds_buf, const DecodeArgs& a,
+                                                          const int (&rc)[8], const int (&r8)[8],
+                                                          int j) {
+  const int lane = threadIdx.x & 63;
+  const char* kc = reinterpret_cast<const char*>(a.kcache);
+  const char* zr = reinterpret_cast<const char*>(a.zero_row);
+  auto row_base = [&](int rid) {   // first byte of the row's page, and the row
+    return kc + (long long)(rid >> 6) * kF8PageBytes;
+  };
+  const char* src[6];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = 2 * (j + 4 * m) + (lane >> 5);          // unit row of this lane
+    const int rid = (lane >> 5) ? rc[2 * m + 1] : rc[2 * m];
+    const int cb = ((lane & 31) ^ f8_code_swizzle(r)) << 4;
+    src[m] = rid >= 0 ? row_base(rid) + (rid & 63) * kF8Latent + cb : zr + cb;
+  }
+  {
+    const int r = 8 * j + (lane >> 3);
+    const int rid = select8(r8, lane >> 3);
+    const int cb = ((lane & 7) ^ f8_rope_swizzle(r)) << 4;
+    src[4] = rid >= 0 ? row_base(rid) + kF8RopeOff + (rid & 63) * 128 + cb : zr + cb;
+  }
+  {
+    const int rid = lane < 8 ? select8(r8, lane) : -1;
+    src[5] = rid >= 0 ? row_base(rid) + kF8ScaleOff + (rid & 63) * 4 : zr;
+  }
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MLA_LDS char*)(lds_buf)));
+  const uint32_t m0c = uni(base + j * 1024);
+  const uint32_t m0r = uni(base + kF8UnitRope + j * 1024);
+  const uint32_t m0s = uni(base + kF8UnitScale + j * 256);
+  asm volatile(
+      "s_mov_b32 m0, %[c]\n\t"
+      "s_nop 0\n\tglobal_load_lds_dwordx4 %[a0], off\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\tglobal_load_lds_dwordx4 %[a1], off\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\tglobal_load_lds_dwordx4 %[a2], off\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "s_nop 0\n\tglobal_load_lds_dwordx4 %[a3], off\n\t"
+      "s_mov_b32 m0, %[r]\n\t"
+      "s_nop 0\n\tglobal_load_lds_dwordx4 %[a4], off\n\t"
+      "s_mov_b32 m0, %[s]\n\t"
+      "s_nop 0\n\tglobal_load_lds_dword %[a5], off\n\t"
+      :
+      : [c] "s"(m0c), [r] "s"(m0r), [s] "s"(m0s), [a0] "v"(src[0]), [a1] "v"(src[1]),
+        [a2] "v"(src[2]), [a3] "v"(src[3]), [a4] "v"(src[4]), [a5] "v"(src[5])
+      : "memory", "m0", "scc");
+}
+
 // Eight E4M3 codes (two dwords, code e in byte e) to bf16, exactly: every
 // E4M3 value is a bf16 value.  Hardware conversion with a unit scale.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -613,14 +703,14 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // RT: 16-row tiles in the workgroup tile (1, 2 or 4: 16, 32 or 64 query
 // rows); score waves q >= RT have no rows and only keep step with the others.
 // F8: the cache holds FP8 pages (layout above) instead of bf16 rows.
-// SP: sparse mode (bf16 cache): items of selected entries, rows gathered one
-// by one (issue_half_load_sparse), entries that do not count masked.
+// SP: sparse mode: items of selected entries, rows gathered one by one
+// (issue_half_load_sparse, or issue_half_load_f8_sparse over FP8 pages),
+// entries that do not count masked.
 template <int RT, bool F8, bool SP>
 __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const DecodeArgs a) {
-  static_assert(!(F8 && SP), "the sparse mode reads bf16 caches");
   constexpr int NBUF = F8 ? kWSBufsF8 : kWSBufs;          // ring of unit buffers
   constexpr int DL = 8;   // 16-dim output tiles per value wave (128 dims)
-  constexpr int UB = F8 ? kF8UnitBytes : kHalfBytes;   // bytes of one unit buffer
+  constexpr int UB = F8 ? (SP ? kF8SpUnitBytes : kF8UnitBytes) : kHalfBytes;   // one unit buffer
 
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * UB];
   __shared__ bf16x8 p_lds[2][RT][64];   // P^T operands: [unit parity][row tile][lane]
@@ -782,7 +872,8 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
                 ra[rs][kt] = *reinterpret_cast<const bf16x8*>(ubuf + (ro ^ (64 * rs)) + 2048 * kt);
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
-              sc[kt] = *reinterpret_cast<const f32x4*>(ubuf + kF8UnitScale + 4 * (16 * kt + 4 * g));
+              sc[kt] = *reinterpret_cast<const f32x4*>(
+                  ubuf + kF8UnitScale + (SP ? f8sp_scale_off(16 * kt + 4 * g) : 4 * (16 * kt + 4 * g)));
           }
           const int cv = ps - 1;   // step converted now
           if (cv >= 0 && cv < 8) {
@@ -944,10 +1035,19 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     int ib = cb, ik = ck, ih = 0, iL = cL;
     int issued = 0;
     int sp_rlo[9], sp_rhi[9];   // sparse: row ids of the next unit to issue
-    if constexpr (SP) load_sparse_rowids(a, ib, ik, ih, j, sp_rlo, sp_rhi);
+    int f8_rc[8], f8_r8[8];     // sparse over FP8 pages: the same
+    auto load_rowids = [&]() {
+      if constexpr (SP && F8)
+        load_sparse_rowids_f8(a, ib, ik, ih, j, f8_rc, f8_r8);
+      else if constexpr (SP)
+        load_sparse_rowids(a, ib, ik, ih, j, sp_rlo, sp_rhi);
+    };
+    if constexpr (SP) load_rowids();
     auto issue_next = [&]() {
       if (before_end(a, ib, ik, b1, k1)) {
-        if constexpr (F8)
+        if constexpr (F8 && SP)
+          issue_half_load_f8_sparse(smem + (issued % NBUF) * UB, a, f8_rc, f8_r8, j);
+        else if constexpr (F8)
           issue_half_load_f8(smem + (issued % NBUF) * UB, a, ib, ik, ih, offc, offr, offs, j);
         else if constexpr (SP)
           issue_half_load_sparse(smem + (issued % NBUF) * UB, a, sp_rlo, sp_rhi, sp_coff,
@@ -957,15 +1057,18 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         ++issued;
         unit_next(a, ib, ik, ih, iL, b1, k1);
         if constexpr (SP)
-          if (before_end(a, ib, ik, b1, k1)) load_sparse_rowids(a, ib, ik, ih, j, sp_rlo, sp_rhi);
+          if (before_end(a, ib, ik, b1, k1)) load_rowids();
       }
     };
     // wait until unit u has landed (units issued after it stay in flight)
-    // (loads per unit and wave: 9 for bf16; for FP8 6 on wave 0, 5 on the others)
+    // (loads per unit and wave: 9 for bf16; for FP8 6 on wave 0, 5 on the
+    // others; 6 on every wave for sparse FP8)
     auto wait_unit = [&](int u) {
       const int ahead = issued - u - 1;
       if constexpr (!F8)
         wait_loads_behind<kHalfLoadsPerWave, NBUF - 2>(ahead);
+      else if constexpr (SP)
+        wait_loads_behind<6, NBUF - 2>(ahead);
       else if (j == 0)
         wait_loads_behind<6, NBUF - 2>(ahead);
       else
@@ -1157,6 +1260,11 @@ hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, 
 
 hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
+  if (a.sparse && a.kv_fp8) {
+    if (a.row_tile_rows == 16) return launch_ws<1, true, true>(a, stream, start, stop);
+    if (a.row_tile_rows == 32) return launch_ws<2, true, true>(a, stream, start, stop);
+    return launch_ws<4, true, true>(a, stream, start, stop);
+  }
   if (a.sparse) {
     if (a.row_tile_rows == 16) return launch_ws<1, false, true>(a, stream, start, stop);
     if (a.row_tile_rows == 32) return launch_ws<2, false, true>(a, stream, start, stop);

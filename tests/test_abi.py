@@ -160,3 +160,29 @@ def test_fp8_entry_points_reject_before_launch():
     bad[1] = p(8)
     assert L.mla_decode_splitkv_fp8(*bad) == INVALID
     assert binding.FP8_PAGE_BYTES == 41216
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_sparse_fwd", "mla_decode_sparse_fwd_fp8"])
+def test_sparse_entry_points_reject_before_launch(fn):
+    """Shape, size and pointer checks of both sparse entry points run on the
+    host before anything is enqueued (no GPU needed)."""
+    L = mla.lib()
+    p = ctypes.c_void_p
+    # q, kcache, num_blocks, block_table, bt_stride, seqlens, batch, s_q, h_q, h_kv, scale,
+    # causal, indices, topk, tile_meta, split_offsets, num_parts, workspace, bytes, out, lse,
+    # start, stop, stream
+    ok = [p(16), p(16), 8, p(16), 2, p(16), 2, 1, 16, 1, 0.04, 0, p(16), 64, p(16), p(16), 4,
+          p(256), 1 << 30, p(16), p(16), None, None, None]
+    f = getattr(L, fn)
+    for idx, val, expect in ((13, 48, INVALID),          # topk not a multiple of 32
+                             (13, 0, INVALID),
+                             (13, (1 << 20) + 32, INVALID),
+                             (12, None, INVALID),        # indices
+                             (2, 0, INVALID),            # num_blocks
+                             (2, (1 << 25) + 1, INVALID),
+                             (8, 48, UNSUPPORTED),       # h_q
+                             (17, p(128), INVALID),      # workspace alignment
+                             (18, 1024, WORKSPACE)):     # workspace too small
+        a = list(ok)
+        a[idx] = val
+        assert f(*a) == expect, (fn, idx, val)

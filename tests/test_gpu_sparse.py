@@ -140,3 +140,99 @@ def test_sparse_full_workload_sampled(mla):
     _assert_parity(out, lse, O_ref, L_ref, reqs=reqs, tag="sparse full")
     assert not torch.isnan(out.float()).any().item()
     assert torch.isfinite(lse).all().item()
+
+
+# ------------------------------------------------ sparse mode over FP8 pages
+
+def _run_fp8(mla, inp, indices, parts=None, causal=None):
+    g = inp.to("cuda")
+    causal = inp.causal if causal is None else causal
+    out, lse = mla.sparse_fwd_fp8(g.q, g.kcache, g.block_table, g.seqlens, indices.cuda(),
+                                  inp.scale, causal, parts=parts)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("h_q", [16, 32, 64, 128])
+@pytest.mark.parametrize("s_q,topk", [(1, 32), (1, 96), (2, 64), (4, 256)])
+@pytest.mark.parametrize("parts", [None, 5])
+def test_sparse_fp8_small(mla, h_q, s_q, topk, parts):
+    from oracle import decode_sparse_fp8
+    from workloads import build_fp8_inputs
+    _say(f"case sparse fp8 h_q={h_q} s_q={s_q} topk={topk} parts={parts}")
+    inp = build_fp8_inputs(LENS, s_q, h_q, seed=1300 + h_q + s_q + topk, extra_pool=5)
+    g = torch.Generator().manual_seed(h_q * 11 + topk)
+    ix = draw_topk_indices(LENS, s_q, topk, inp.causal, g, pad_frac=0.15)
+    out, lse = _run_fp8(mla, inp, ix, parts)
+    O_ref, L_ref = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix,
+                                     inp.scale, inp.causal)
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"sparse fp8 h{h_q} s{s_q} k{topk} P={parts}")
+
+
+def test_sparse_fp8_edge_entries(mla):
+    """Duplicates, padding, positions at/after the limit, an all-padding item
+    and a zero-length request, over FP8 pages."""
+    from oracle import decode_sparse_fp8
+    from workloads import build_fp8_inputs
+    _say("case sparse fp8 edge entries")
+    lens = [200, 0, 100, 70]
+    inp = build_fp8_inputs(lens, 2, 32, seed=1401, extra_pool=3)
+    g = torch.Generator().manual_seed(14)
+    ix = draw_topk_indices(lens, 2, 64, True, g)
+    ix[0, 0, :4] = torch.tensor([5, 5, 5, 199], dtype=torch.int32)
+    ix[0, 1, :3] = torch.tensor([199, 200, -5], dtype=torch.int32)
+    ix[2, 0] = -1
+    ix[3, 1, :2] = torch.tensor([10 ** 6, 69], dtype=torch.int32)
+    out, lse = _run_fp8(mla, inp, ix)
+    O_ref, L_ref = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix,
+                                     inp.scale, True)
+    assert np.all(L_ref[2, 0] == -np.inf) and np.all(L_ref[1] == -np.inf)
+    _assert_parity(out, lse, O_ref, L_ref, tag="sparse fp8 edges")
+
+
+def test_sparse_fp8_all_visible_matches_dense_fp8(mla):
+    """Selecting every visible position is the dense FP8 mode: the two GPU
+    paths agree to the bar."""
+    from workloads import build_fp8_inputs
+    _say("case sparse fp8 = dense fp8")
+    lens = [64, 96, 160, 20]
+    inp = build_fp8_inputs(lens, 1, 64, seed=1402, extra_pool=2)
+    ix = torch.full((4, 1, 160), -1, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        ix[b, 0, :L] = torch.arange(L, dtype=torch.int32)
+    out_s, lse_s = _run_fp8(mla, inp, ix)
+    g = inp.to("cuda")
+    out_d, lse_d = mla.fwd_fp8(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, False)
+    torch.cuda.synchronize()
+    _assert_parity(out_s, lse_s, out_d.float().cpu().numpy().astype(np.float64),
+                   lse_d.cpu().numpy().astype(np.float64), tag="sparse fp8 vs dense fp8 GPU")
+
+
+def test_sparse_fp8_run_to_run_bitwise(mla):
+    from workloads import build_fp8_inputs
+    _say("case sparse fp8 determinism")
+    lens = [3000, 500, 64]
+    inp = build_fp8_inputs(lens, 1, 128, seed=1403, extra_pool=3)
+    ix = draw_topk_indices(lens, 1, 512, False, torch.Generator().manual_seed(15), 0.1)
+    a = _run_fp8(mla, inp, ix)
+    b = _run_fp8(mla, inp, ix)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+
+
+def test_sparse_fp8_full_workload_sampled(mla):
+    """The sparse workload over FP8 pages in the benchmark's launch
+    configuration; sampled requests vs the oracle."""
+    from oracle import decode_sparse_fp8
+    _say("case sparse fp8 full: generating inputs")
+    inp = make_inputs("sparse", kv_format="fp8")
+    _say("case sparse fp8 full: decode on GPU")
+    out, lse = _run_fp8(mla, inp, inp.indices)
+    sl = inp.seqlens.tolist()
+    reqs = sorted({0, len(sl) - 1, int(np.argmax(sl)), int(np.argmin(sl)), 23})
+    _say(f"case sparse fp8 full: oracle on requests {reqs}")
+    O_ref, L_ref = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens,
+                                     inp.indices, inp.scale, inp.causal, requests=reqs)
+    _assert_parity(out, lse, O_ref, L_ref, reqs=reqs, tag="sparse fp8 full")
+    assert not torch.isnan(out.float()).any().item()
+    assert torch.isfinite(lse).all().item()
