@@ -40,94 +40,101 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 306969416,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 306977653,
         "write_bytes": 8404992,
-        "fetch_scale": 1.99986,
-        "write_scale": 1.0
-    },
-    "ridge": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 704820108,
-        "write_bytes": 59894272,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
+    "ridge": {
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 704822049,
+        "write_bytes": 59894272,
+        "fetch_scale": 1.99993,
+        "write_scale": 1.0
+    },
     "long": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 770893003,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 770908267,
         "write_bytes": 37559808,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ragged": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 510580714,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 510584583,
         "write_bytes": 78838784,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "draft": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 210929201,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 210930552,
         "write_bytes": 58843136,
-        "fetch_scale": 1.99989,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "sparse": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 171346404,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 171348996,
         "write_bytes": 33619968,
         "fetch_scale": 1.99986,
         "write_scale": 1.0
     },
     "prefill": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 405337115,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 405330135,
         "write_bytes": 92569600,
-        "fetch_scale": 1.99988,
-        "write_scale": 1.0
-    },
-    "membound/fp8": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 173845069,
-        "write_bytes": 8404992,
-        "fetch_scale": 1.99989,
-        "write_scale": 1.0
-    },
-    "ridge/fp8": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 410128045,
-        "write_bytes": 59894272,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
+    "membound/fp8": {
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 173832475,
+        "write_bytes": 8404992,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0
+    },
+    "ridge/fp8": {
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 410190512,
+        "write_bytes": 59894272,
+        "fetch_scale": 1.9999,
+        "write_scale": 1.0
+    },
     "long/fp8": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 437975080,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 438007982,
         "write_bytes": 37559808,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ragged/fp8": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 310469401,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 310508205,
         "write_bytes": 78838784,
-        "fetch_scale": 1.99989,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "draft/fp8": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 133680847,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 133710218,
         "write_bytes": 58843136,
         "fetch_scale": 1.9999,
         "write_scale": 1.0
     },
     "prefill/fp8": {
-        "kernel_sha256": "c2ab02ce6c72505a2bcd121a409fcd024b7c27d9289e25cf4e14dc90d56743d2",
-        "fetch_bytes": 264208429,
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 264198916,
         "write_bytes": 92569600,
-        "fetch_scale": 1.99989,
+        "fetch_scale": 1.99993,
+        "write_scale": 1.0
+    },
+    "sparse/fp8": {
+        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
+        "fetch_bytes": 115170827,
+        "write_bytes": 33619968,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0
     }
 }
