@@ -246,6 +246,10 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the step instead of eager launches "
                          "(slower on this stack: replays add ~4-14 us per step)")
+    ap.add_argument("--launch", choices=["three", "inline"], default="three",
+                    help="three: scheduler, decode and combine kernels; inline: the decode "
+                         "kernel derives its split plan itself (mla_decode_fwd_inline_plan), "
+                         "two launches per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args(argv)
@@ -264,6 +268,9 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     fp8 = args.kv == "fp8"
     sparse = w.topk > 0
+    if args.launch == "inline" and (sparse or args.graph):
+        print("bench.py: --launch inline applies to the eager dense decode", file=sys.stderr)
+        return 2
     if sparse and (args.with_append or args.graph):
         print("bench.py: the sparse workload runs eagerly, without the append", file=sys.stderr)
         return 2
@@ -300,6 +307,15 @@ def main(argv=None) -> int:
         elif args.flush == "write":
             flush_buf.fill_(1)
 
+    # --launch inline: the plan buffers the decode kernel writes (the combine
+    # reads split_offsets from them).
+    inline_meta = None
+    if args.launch == "inline":
+        inline_meta = mla.binding.Metadata(
+            torch.empty((parts, mla.binding.TILE_META_INTS), dtype=torch.int32, device=dev),
+            torch.empty((inp.batch + 1,), dtype=torch.int32, device=dev), parts, inp.s_q,
+            inp.h_q)
+
     # evs: [step start, step end, decode kernel start, decode kernel end]; the
     # last two are recorded by the decode kernel's own launch, so the step's
     # stream carries no marker between its three kernels.
@@ -319,11 +335,17 @@ def main(argv=None) -> int:
             evs[0].record()
         if new_kv is not None:
             append_fn(new_kv, g.kcache, g.block_table, g.seqlens)
-        meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
-        decode_fn(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
-                  out, lse, start_event=evs[2] if evs else None,
-                  stop_event=evs[3] if evs else None)
-        mla.combine(g.seqlens, inp.s_q, inp.h_q, meta, ws, out, lse)
+        if inline_meta is not None:
+            mla.fwd_inline_plan(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal,
+                                meta=inline_meta, workspace=ws, out=out, lse=lse,
+                                start_event=evs[2] if evs else None,
+                                stop_event=evs[3] if evs else None, fp8=fp8)
+        else:
+            meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
+            decode_fn(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
+                      out, lse, start_event=evs[2] if evs else None,
+                      stop_event=evs[3] if evs else None)
+            mla.combine(g.seqlens, inp.s_q, inp.h_q, meta, ws, out, lse)
         if evs is not None:
             evs[1].record()
 
@@ -342,6 +364,14 @@ def main(argv=None) -> int:
         if new_kv is not None:
             append_fn(new_kv, g.kcache, g.block_table, g.seqlens)
         evs[0].record()
+        if inline_meta is not None:   # no scheduler kernel; the merge timed on its own
+            evs[1].record()
+            mla.fwd_inline_plan(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal,
+                                meta=inline_meta, workspace=ws, out=out, lse=lse, fp8=fp8)
+            evs[2].record()
+            mla.combine(g.seqlens, inp.s_q, inp.h_q, inline_meta, ws, out, lse)
+            evs[3].record()
+            return
         meta = mla.metadata(g.seqlens, inp.s_q, inp.h_q, parts=parts)
         evs[1].record()
         decode_fn(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta, ws,
@@ -474,7 +504,9 @@ def main(argv=None) -> int:
                    "s_q": inp.s_q, "h_q": inp.h_q, "h_kv": 1, "d_k": 576, "d_v": 512,
                    "block_size": 64, "total_keys": int(inp.seqlens.sum()),
                    "num_parts": parts, "cache_flush_between_steps": args.flush,
-                   "step_launch": "hip_graph" if graph is not None else "eager",
+                   "step_launch": ("hip_graph" if graph is not None else
+                                   "eager, in-kernel plan (decode + combine)"
+                                   if inline_meta is not None else "eager"),
                    "kv_append_in_step": new_kv is not None,
                    "kv_cache": ("fp8_e4m3 latent codes, fp32 per-token scale, bf16 rope "
                                 "(644 B/token)" if fp8 else "bf16 (1152 B/token)"),
@@ -483,7 +515,8 @@ def main(argv=None) -> int:
         "tflops": round(tfl, 2),
         "algorithmic_bytes": counts["bytes"],
         "algorithmic_flops": counts["flops"],
-        "kernels_ms": {"metadata": round(mean(meta_ms), 5), "splitkv": round(dec, 5),
+        "kernels_ms": {"metadata": None if inline_meta is not None else round(mean(meta_ms), 5),
+                       "splitkv": round(dec, 5),
                        "combine": round(mean(comb_ms), 5),
                        "splitkv_median": round(med(dec_ms), 5),
                        "splitkv_p90": round(sorted(dec_ms)[int(0.9 * (len(dec_ms) - 1))], 5),

@@ -269,6 +269,38 @@ int mla_kv_append_fp8(const void* new_kv_d, void* kcache_fp8_d, int64_t num_bloc
                       int batch, int s_q, void* stream);
 
 /*
+ * mla_decode_fwd_inline_plan — the whole decode in two launches instead of
+ * three: the decode kernel derives its split plan itself (every workgroup
+ * computes its part from seqlens with the rule of mla_decode_metadata; page
+ * "深度剖析DeepSeek Infra开源全貌", DAY1 FlashMLA, feature ⑤: the dynamic load
+ * split for variable lengths), then mla_decode_combine merges the pieces.
+ * Arguments as mla_decode_fwd, except that tile_meta_d (int32 [num_parts, 8])
+ * and split_offsets_d (int32 [batch + 1]) are OUTPUTS: the kernel writes the
+ * same plan mla_decode_metadata would (the combine reads split_offsets_d
+ * from it).  start_event / stop_event (may be NULL) as in
+ * mla_decode_splitkv_timed.  num_parts from mla_decode_num_parts; batch at
+ * most 1024 (MLA_ERR_UNSUPPORTED above: use the three-launch path); other
+ * validation and status codes as mla_decode_fwd.
+ */
+int mla_decode_fwd_inline_plan(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                               const int32_t* block_table_d, int bt_stride,
+                               const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                               float scale, int causal, int32_t* tile_meta_d,
+                               int32_t* split_offsets_d, int num_parts, void* workspace_d,
+                               size_t workspace_bytes, void* out_d, float* lse_d,
+                               void* start_event, void* stop_event, void* stream);
+
+/* mla_decode_fwd_inline_plan over an FP8 cache (the pages of mla_decode_splitkv_fp8). */
+int mla_decode_fwd_inline_plan_fp8(const void* q_d, const void* kcache_fp8_d,
+                                   int64_t num_blocks, const int32_t* block_table_d,
+                                   int bt_stride, const int32_t* seqlens_d, int batch, int s_q,
+                                   int h_q, int h_kv, float scale, int causal,
+                                   int32_t* tile_meta_d, int32_t* split_offsets_d,
+                                   int num_parts, void* workspace_d, size_t workspace_bytes,
+                                   void* out_d, float* lse_d, void* start_event,
+                                   void* stop_event, void* stream);
+
+/*
  * Sparse (selected-keys) mode.  Page "云上玩转DeepSeek系列之五：实测
  * 优化16%，体验FlashMLA加速DeepSeek-V2-Lite推理" (ruibaoantu.com), section 四,
  * item 2, recommends FlashMLA's sparse attention mode beyond 8K tokens and

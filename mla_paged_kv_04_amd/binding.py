@@ -72,6 +72,15 @@ _SIGNATURES = {
                                            _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                            _c_ptr, _c_int, _c_ptr, _c_ptr, _c_int, _c_ptr,
                                            _c_size, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_decode_fwd_inline_plan": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr,
+                                            _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                            _c_ptr, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr,
+                                            _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_decode_fwd_inline_plan_fp8": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int,
+                                                _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                                                _c_float, _c_int, _c_ptr, _c_ptr, _c_int,
+                                                _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr,
+                                                _c_ptr, _c_ptr]),
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_last_hip_error": (ctypes.c_char_p, []),
     "mla_device_num_cus": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
@@ -330,6 +339,33 @@ def fwd_fp8(q, kcache, block_table, seqlens, scale: float, causal: bool | None =
         _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)),
         "mla_decode_fwd_fp8")
+    return out, lse
+
+
+def fwd_inline_plan(q, kcache, block_table, seqlens, scale: float, causal: bool | None = None,
+                    parts: int | None = None, workspace=None, out=None, lse=None,
+                    meta: Metadata | None = None, start_event=None, stop_event=None,
+                    fp8: bool = False):
+    """The decode in two launches: the decode kernel derives the split plan
+    itself (mla_decode_fwd_inline_plan[_fp8]).  ``meta`` (optional) receives
+    the plan the kernel wrote; returns (O, LSE) like fwd."""
+    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens, fp8=fp8)
+    if causal is None:
+        causal = s_q > 1
+    if meta is None:
+        p = parts or num_parts(batch, s_q, h_q, h_kv, device_num_cus(q.device))
+        meta = Metadata(torch.empty((p, TILE_META_INTS), dtype=torch.int32, device=q.device),
+                        torch.empty((batch + 1,), dtype=torch.int32, device=q.device), p,
+                        s_q, h_q)
+    workspace = _alloc_workspace(batch, s_q, h_q, meta.num_parts, q.device, workspace)
+    out, lse = _outputs(q, out, lse)
+    name = "mla_decode_fwd_inline_plan_fp8" if fp8 else "mla_decode_fwd_inline_plan"
+    _check(getattr(lib(), name)(
+        _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
+        _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _event_handle(start_event), _event_handle(stop_event), _stream(q.device)), name)
     return out, lse
 
 

@@ -78,7 +78,8 @@ int splitkv_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
                  int batch, int s_q, int h_q, int h_kv, float scale, int causal,
                  const int32_t* tile_meta_d, const int32_t* split_offsets_d, int num_parts,
                  void* workspace_d, size_t workspace_bytes, void* out_d, float* lse_d,
-                 int kv_fp8, void* start_event, void* stop_event, void* stream) {
+                 int kv_fp8, void* start_event, void* stop_event, void* stream,
+                 int inplan = 0) {
   int st = check_common(seqlens_d, split_offsets_d, batch, s_q, h_q, h_kv, num_parts,
                         workspace_d, workspace_bytes, out_d, lse_d);
   if (st != MLA_OK) return st;
@@ -115,6 +116,10 @@ int splitkv_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
   a.rowids = nullptr;
   a.vmask = nullptr;
   a.zero_row = nullptr;
+  a.inplan = inplan;
+  a.c_fix = mla::fixed_cost_pages(mla::rows_per_tile(s_q, h_q));
+  a.tile_meta_out = const_cast<int32_t*>(tile_meta_d);
+  a.split_offsets_out = const_cast<int32_t*>(split_offsets_d);
   hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream),
                                      static_cast<hipEvent_t>(start_event),
                                      static_cast<hipEvent_t>(stop_event));
@@ -295,6 +300,41 @@ int mla_decode_fwd_fp8(const void* q_d, const void* kcache_fp8_d, int64_t num_bl
                             workspace_d, workspace_bytes, out_d, lse_d, stream);
 }
 
+int mla_decode_fwd_inline_plan(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                               const int32_t* block_table_d, int bt_stride,
+                               const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                               float scale, int causal, int32_t* tile_meta_d,
+                               int32_t* split_offsets_d, int num_parts, void* workspace_d,
+                               size_t workspace_bytes, void* out_d, float* lse_d,
+                               void* start_event, void* stop_event, void* stream) {
+  if (batch > mla::kPlanMaxBatch) return MLA_ERR_UNSUPPORTED;
+  int st = splitkv_impl(q_d, kcache_d, num_blocks, block_table_d, bt_stride, seqlens_d, batch,
+                        s_q, h_q, h_kv, scale, causal, tile_meta_d, split_offsets_d, num_parts,
+                        workspace_d, workspace_bytes, out_d, lse_d, 0, start_event, stop_event,
+                        stream, 1);
+  if (st != MLA_OK) return st;
+  return mla_decode_combine(seqlens_d, batch, s_q, h_q, split_offsets_d, num_parts,
+                            workspace_d, workspace_bytes, out_d, lse_d, stream);
+}
+
+int mla_decode_fwd_inline_plan_fp8(const void* q_d, const void* kcache_fp8_d,
+                                   int64_t num_blocks, const int32_t* block_table_d,
+                                   int bt_stride, const int32_t* seqlens_d, int batch, int s_q,
+                                   int h_q, int h_kv, float scale, int causal,
+                                   int32_t* tile_meta_d, int32_t* split_offsets_d,
+                                   int num_parts, void* workspace_d, size_t workspace_bytes,
+                                   void* out_d, float* lse_d, void* start_event,
+                                   void* stop_event, void* stream) {
+  if (batch > mla::kPlanMaxBatch) return MLA_ERR_UNSUPPORTED;
+  int st = splitkv_impl(q_d, kcache_fp8_d, num_blocks, block_table_d, bt_stride, seqlens_d,
+                        batch, s_q, h_q, h_kv, scale, causal, tile_meta_d, split_offsets_d,
+                        num_parts, workspace_d, workspace_bytes, out_d, lse_d, 1, start_event,
+                        stop_event, stream, 1);
+  if (st != MLA_OK) return st;
+  return mla_decode_combine(seqlens_d, batch, s_q, h_q, split_offsets_d, num_parts,
+                            workspace_d, workspace_bytes, out_d, lse_d, stream);
+}
+
 int mla_kv_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
                   const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
                   int batch, int s_q, void* stream) {
@@ -433,6 +473,10 @@ int sparse_fwd_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
   a.rowids = rowids;
   a.vmask = vmask;
   a.zero_row = zero_row;
+  a.inplan = 0;
+  a.c_fix = 0;
+  a.tile_meta_out = nullptr;
+  a.split_offsets_out = nullptr;
   e = mla::launch_splitkv(a, s, static_cast<hipEvent_t>(start_event),
                           static_cast<hipEvent_t>(stop_event));
   if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_fwd decode launch");

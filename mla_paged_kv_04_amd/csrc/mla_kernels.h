@@ -57,7 +57,19 @@ struct DecodeArgs {
   const int32_t* rowids;
   const uint32_t* vmask;
   const void* zero_row;
+  // In-kernel plan: each workgroup derives its part of the split plan from
+  // the lengths (the rule of mla_metadata_kernel, c_fix overhead pages per
+  // request) instead of reading tile_meta / split_offsets; it writes its
+  // part's tile_meta entry, and part 0 writes split_offsets for the combine.
+  int inplan;
+  int c_fix;
+  int32_t* tile_meta_out;       // [P, 8]
+  int32_t* split_offsets_out;   // [B+1]
 };
+
+// Largest batch whose plan a workgroup derives in-kernel (its lengths are
+// held in registers, its split offsets in LDS).
+constexpr int kPlanMaxBatch = 1024;
 
 struct CombineArgs {
   const int32_t* seqlens;

@@ -214,6 +214,97 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int c_fix, int num
   return hipGetLastError();
 }
 
+// The split plan of part p, derived by one wave inside the decode kernel
+// with the rule of mla_metadata_kernel (same scans, same boundary map, same
+// split counts): plan[0..4] = b0, k0, b1, k1, first_split of the part, and
+// so[b] = split_offsets[b] for every request b <= batch.  Requests are held
+// kPlanMaxBatch / 64 per lane in registers, so the lengths are read once,
+// all loads in flight together.
+__device__ void plan_part_wave(const DecodeArgs& a, int p, int* plan, int* so) {
+  constexpr int NC = kPlanMaxBatch / 64;
+  const int lane = threadIdx.x & 63;
+  const int B = a.batch, cf = a.c_fix;
+  int n[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int b = 64 * c + lane;
+    const int L = b < B ? (a.const_len > 0 ? a.const_len : a.seqlens[b]) : 0;
+    n[c] = n_pages(L);
+  }
+  long long start[NC];
+  long long carry = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (64 * c >= B) {
+      start[c] = carry;
+      continue;
+    }
+    const int cost = n[c] > 0 ? n[c] + cf : 0;
+    const int incl = wave_incl_scan(cost);
+    start[c] = carry + (incl - cost);
+    carry += __shfl(incl, 63);
+  }
+  const long long C = carry;
+  const long long P = a.num_parts;
+  const long long q = C > 0 ? (C + P - 1) / P : 1;
+
+  // Boundary x: (b, clamp(x - start_b - c, 0, n_b)) for the request whose
+  // units contain x, (B, 0) for x >= C.
+  auto boundary = [&](long long x, int& bb, int& kk, long long& st, int& nn) {
+    bb = B;
+    kk = 0;
+    st = 0;
+    nn = 0;
+    if (x >= C) return;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (64 * c >= B) break;
+      const int cost = n[c] > 0 ? n[c] + cf : 0;
+      const bool hit = cost > 0 && start[c] <= x && x < start[c] + cost;
+      const unsigned long long m = __ballot(hit);
+      if (m) {
+        const int l = __ffsll(static_cast<long long>(m)) - 1;
+        bb = 64 * c + l;
+        st = __shfl(start[c], l);
+        nn = __shfl(n[c], l);
+        long long k = x - st - cf;
+        kk = static_cast<int>(k < 0 ? 0 : (k > nn ? nn : k));
+        return;
+      }
+    }
+  };
+  int b0, k0, b1, k1, n0;
+  long long st0, st1;
+  int n1;
+  boundary((long long)p * q, b0, k0, st0, n0);
+  boundary((long long)(p + 1) * q, b1, k1, st1, n1);
+  const int first = (b0 < B && k0 > 0 && k0 < n0) ? (int)(p - (st0 + cf) / q) : 0;
+  if (lane == 0) {
+    plan[0] = b0;
+    plan[1] = k0;
+    plan[2] = b1;
+    plan[3] = k1;
+    plan[4] = first;
+  }
+  // split offsets: prefix sums of the slot counts of split requests
+  int carry_s = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (64 * c >= B) break;
+    const int b = 64 * c + lane;
+    int nsplit = 1;
+    if (n[c] > 0) {
+      const long long lo = start[c] + cf;
+      nsplit = 1 + (int)((lo + n[c] - 1) / q - lo / q);
+    }
+    const int slots = nsplit >= 2 ? nsplit : 0;
+    const int incl = wave_incl_scan(slots);
+    if (b < B) so[b] = carry_s + incl - slots;
+    carry_s += __shfl(incl, 63);
+  }
+  if (lane == 0) so[B] = carry_s;
+}
+
 // Values the hardware needs in SGPRs (buffer resources, M0) are read from
 // global memory with vector loads (the kernel also stores, so loads are not
 // provably invariant); readfirstlane tells the compiler they are wave-uniform
@@ -738,9 +829,33 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     part = x / R;
     rtile = x % R;
   }
-  const int32_t* tm = a.tile_meta + part * kMetaInts;
-  const int b0 = ldc(tm + 0), k0 = ldc(tm + 1), b1 = ldc(tm + 2), k1 = ldc(tm + 3);
-  const int first_split = ldc(tm + 4);
+  __shared__ int plan_lds[8];
+  __shared__ int so_lds[kPlanMaxBatch + 1];   // split offsets (in-kernel plan)
+  int b0, k0, b1, k1, first_split;
+  const bool inplan = !SP && a.inplan;   // the sparse mode always reads its plan
+  if (inplan) {
+    if (w == 0) {
+      plan_part_wave(a, part, plan_lds, so_lds);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (rtile == 0 && lane < kMetaInts)   // this part's entry, as the metadata kernel's
+        a.tile_meta_out[part * kMetaInts + lane] = lane < 5 ? plan_lds[lane] : 0;
+      if (part == 0 && rtile == 0)
+        for (int b = lane; b <= a.batch; b += 64) a.split_offsets_out[b] = so_lds[b];
+    }
+    wg_barrier();   // the plan is in LDS for every wave
+    b0 = uni(plan_lds[0]);
+    k0 = uni(plan_lds[1]);
+    b1 = uni(plan_lds[2]);
+    k1 = uni(plan_lds[3]);
+    first_split = uni(plan_lds[4]);
+  } else {
+    const int32_t* tm = a.tile_meta + part * kMetaInts;
+    b0 = ldc(tm + 0);
+    k0 = ldc(tm + 1);
+    b1 = ldc(tm + 2);
+    k1 = ldc(tm + 3);
+    first_split = ldc(tm + 4);
+  }
 
   int cb = b0, ck = k0, ch = 0;
   seek(a, cb, ck, b1, k1);
@@ -753,7 +868,8 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
   auto piece_slot = [&](int b, int pbeg, int pend, int n, bool& whole) {
     whole = pbeg == 0 && pend == n;
     const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
-    return whole ? 0LL : (long long)ldc(a.split_offsets + b) + sidx;
+    if (whole) return 0LL;
+    return (long long)(inplan ? uni(so_lds[b]) : ldc(a.split_offsets + b)) + sidx;
   };
 
   if (w < 4) {

@@ -186,3 +186,23 @@ def test_sparse_entry_points_reject_before_launch(fn):
         a = list(ok)
         a[idx] = val
         assert f(*a) == expect, (fn, idx, val)
+
+
+@pytest.mark.parametrize("fn", ["mla_decode_fwd_inline_plan", "mla_decode_fwd_inline_plan_fp8"])
+def test_inline_plan_rejects_before_launch(fn):
+    """Host-side checks of the in-kernel-plan entry points: batches above
+    1024 are unsupported (the three-launch path serves them)."""
+    L = mla.lib()
+    p = ctypes.c_void_p
+    # q, kcache, num_blocks, block_table, bt_stride, seqlens, batch, s_q, h_q, h_kv, scale,
+    # causal, tile_meta, split_offsets, num_parts, workspace, bytes, out, lse, start, stop,
+    # stream
+    ok = [p(16), p(16), 8, p(16), 2, p(16), 2, 1, 16, 1, 0.04, 0, p(16), p(16), 4, p(256),
+          1 << 30, p(16), p(16), None, None, None]
+    f = getattr(L, fn)
+    for idx, val, expect in ((6, 1025, UNSUPPORTED), (6, 0, INVALID), (8, 48, UNSUPPORTED),
+                             (2, 0, INVALID), (12, None, INVALID), (13, None, INVALID),
+                             (15, p(128), INVALID), (16, 1024, WORKSPACE)):
+        a = list(ok)
+        a[idx] = val
+        assert f(*a) == expect, (fn, idx, val)
