@@ -40,99 +40,99 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 306977653,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 307003425,
         "write_bytes": 8404992,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ridge": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 704822049,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 704764983,
         "write_bytes": 59894272,
-        "fetch_scale": 1.99993,
+        "fetch_scale": 1.9999,
         "write_scale": 1.0
     },
     "long": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 770908267,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 770912260,
         "write_bytes": 37559808,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ragged": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 510584583,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 510565643,
         "write_bytes": 78838784,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "draft": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 210930552,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 210924958,
         "write_bytes": 58843136,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "sparse": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 171348996,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 171348665,
         "write_bytes": 33619968,
         "fetch_scale": 1.99986,
         "write_scale": 1.0
     },
     "prefill": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 405330135,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 405355105,
         "write_bytes": 92569600,
-        "fetch_scale": 1.99992,
+        "fetch_scale": 1.99988,
         "write_scale": 1.0
     },
     "membound/fp8": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 173832475,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 173875417,
         "write_bytes": 8404992,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ridge/fp8": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 410190512,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 410156944,
         "write_bytes": 59894272,
         "fetch_scale": 1.9999,
         "write_scale": 1.0
     },
     "long/fp8": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 438007982,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 438003101,
         "write_bytes": 37559808,
-        "fetch_scale": 1.99992,
+        "fetch_scale": 1.9999,
         "write_scale": 1.0
     },
     "ragged/fp8": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 310508205,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 310504161,
         "write_bytes": 78838784,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "draft/fp8": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 133710218,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 133712206,
         "write_bytes": 58843136,
-        "fetch_scale": 1.9999,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0
     },
     "prefill/fp8": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 264198916,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 264245843,
         "write_bytes": 92569600,
-        "fetch_scale": 1.99993,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "sparse/fp8": {
-        "kernel_sha256": "22613d9b2162b71c2569daa3058fe470e9be98fa31a1eb79cc165a5095b6f87d",
-        "fetch_bytes": 115170827,
+        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
+        "fetch_bytes": 115152781,
         "write_bytes": 33619968,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
