@@ -896,6 +896,17 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     const int ro = kF8UnitRope + i * 128 + ((g ^ f8_rope_swizzle(i)) << 4);
 
     bf16x8 qreg[18];
+    auto load_q = [&](int b) {
+      const uint16_t* qrow = a.q + ((long long)b * a.M + row_own) * kDK;
+      if constexpr (F8)
+        load_q_rows_f8(qreg, reinterpret_cast<const bf16x8*>(qrow + 16 * g),
+                       reinterpret_cast<const bf16x8*>(qrow + kF8Latent + 8 * g));
+      else
+        load_q_rows(qreg, reinterpret_cast<const bf16x8*>(qrow + 8 * g));
+    };
+    // Q of the first piece is loaded before the first barrier, so its latency
+    // overlaps that of the first page loads instead of following them.
+    if (active) load_q(cb);
     float m_run = -INFINITY, l_run = 0.f;
     int lim = 0, lim_min = 0, n = 0, pbeg = 0;
     bool new_piece = true;
@@ -910,14 +921,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         lim = a.causal ? cL - a.s_q + 1 + row_own / a.h_q : cL;
         m_run = -INFINITY;
         l_run = 0.f;
-        if (active) {
-          const uint16_t* qrow = a.q + ((long long)b * a.M + row_own) * kDK;
-          if constexpr (F8)
-            load_q_rows_f8(qreg, reinterpret_cast<const bf16x8*>(qrow + 16 * g),
-                           reinterpret_cast<const bf16x8*>(qrow + kF8Latent + 8 * g));
-          else
-            load_q_rows(qreg, reinterpret_cast<const bf16x8*>(qrow + 8 * g));
-        }
+        if (active && t > 0) load_q(b);
       }
       const char* ubuf = smem + (t % NBUF) * UB;
       // sparse: which of the unit's 32 entries count (bit = key in the unit)
