@@ -40,99 +40,99 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 307003425,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 307020633,
         "write_bytes": 8404992,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ridge": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 704764983,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 704764656,
         "write_bytes": 59894272,
-        "fetch_scale": 1.9999,
-        "write_scale": 1.0
-    },
-    "long": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 770912260,
-        "write_bytes": 37559808,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
+    "long": {
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 770936002,
+        "write_bytes": 37559808,
+        "fetch_scale": 1.99989,
+        "write_scale": 1.0
+    },
     "ragged": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 510565643,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 510572798,
         "write_bytes": 78838784,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "draft": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 210924958,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 210932775,
         "write_bytes": 58843136,
-        "fetch_scale": 1.99992,
+        "fetch_scale": 1.99993,
         "write_scale": 1.0
     },
     "sparse": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 171348665,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 171351819,
         "write_bytes": 33619968,
         "fetch_scale": 1.99986,
         "write_scale": 1.0
     },
     "prefill": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 405355105,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 405363435,
         "write_bytes": 92569600,
-        "fetch_scale": 1.99988,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "membound/fp8": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 173875417,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 173871138,
         "write_bytes": 8404992,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "ridge/fp8": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 410156944,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 410163666,
         "write_bytes": 59894272,
-        "fetch_scale": 1.9999,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0
     },
     "long/fp8": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 438003101,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 438015799,
         "write_bytes": 37559808,
-        "fetch_scale": 1.9999,
+        "fetch_scale": 1.99993,
         "write_scale": 1.0
     },
     "ragged/fp8": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 310504161,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 310500893,
         "write_bytes": 78838784,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "draft/fp8": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 133712206,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 133711684,
         "write_bytes": 58843136,
-        "fetch_scale": 1.99989,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "prefill/fp8": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 264245843,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 264231629,
         "write_bytes": 92569600,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
     },
     "sparse/fp8": {
-        "kernel_sha256": "ca05767cd70ed5769fdf93fa7e5511548542e258dada9d55ffd47055ffff159e",
-        "fetch_bytes": 115152781,
+        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
+        "fetch_bytes": 114837473,
         "write_bytes": 33619968,
         "fetch_scale": 1.99992,
         "write_scale": 1.0
