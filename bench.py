@@ -255,8 +255,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not "
-              "part of it (see DESIGN.md for how the path would shard).", file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU only; --gpus above 1 (or a "
+              "multi-rank launch) is not supported.", file=sys.stderr)
         return 2
 
     import torch
