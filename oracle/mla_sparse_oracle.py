@@ -15,8 +15,10 @@ that keeps everything else of the dense definition:
   indices[b, t, 0:topk] (chosen by any top-k selector; the selection itself
   is not part of the mode).
 * An entry counts iff 0 <= j < vis(b, t), the dense mode's visible limit
-  (L_b - s_q + 1 + t when causal, else L_b); other entries (negative
-  padding, positions beyond the limit) are skipped.
+  (L_b - s_q + 1 + t when causal, else L_b), and its table slot j // 64 is
+  inside the request's row with a page id in the pool; other entries
+  (negative padding, positions beyond the limit, unmapped positions) are
+  skipped.
 * The attention of every head h of token t is the dense definition restricted
   to the counted entries, taken as a multiset (an entry listed twice counts
   twice):  s_i = scale * q . K_b[j_i],  LSE = ln sum_i exp(s_i),
@@ -36,10 +38,20 @@ import numpy as np
 from .mla_decode_oracle import BLOCK_SIZE, D_V, _f64, _i64, attend_rows, visible_count
 
 
-def counted_entries(indices_bt, vis: int) -> np.ndarray:
-    """The entries of one token's index list that count (multiset, in order)."""
+def counted_entries(indices_bt, vis: int, block_table_b=None, num_pages_pool=None) -> np.ndarray:
+    """The entries of one token's index list that count (multiset, in order):
+    0 <= j < vis and, when the request's table row and the pool size are
+    given, a table slot j // 64 inside the row holding a page id in
+    [0, num_pages_pool)."""
     ix = np.asarray(indices_bt, dtype=np.int64).reshape(-1)
-    return ix[(ix >= 0) & (ix < vis)]
+    ix = ix[(ix >= 0) & (ix < vis)]
+    if block_table_b is None:
+        return ix
+    bt = np.asarray(block_table_b, dtype=np.int64).reshape(-1)
+    slot = ix // BLOCK_SIZE
+    inrow = slot < bt.size
+    page = np.where(inrow, bt[np.minimum(slot, bt.size - 1)], -1)
+    return ix[inrow & (page >= 0) & (page < num_pages_pool)]
 
 
 def _gather_rows(kcache, block_table_b, positions) -> np.ndarray:
@@ -91,10 +103,11 @@ def decode_sparse(q, kcache, block_table, seqlens, indices, scale: float, causal
     O = np.full((B, s_q, h_q, D_V), np.nan, dtype=np.float64)
     LSE = np.full((B, s_q, h_q), np.nan, dtype=np.float64)
     reqs = range(B) if requests is None else requests
+    n_pool = int(kcache.shape[0])
     for b in reqs:
         L = int(sl[b])
         for t in range(s_q):
-            ent = counted_entries(ix[b, t], visible_count(L, s_q, t, causal))
+            ent = counted_entries(ix[b, t], visible_count(L, s_q, t, causal), bt[b], n_pool)
             K = _gather_rows(kcache, bt[b], ent)
             nvis = np.full((h_q,), K.shape[0], dtype=np.int64)
             Ob, lb = attend_rows(qf[b, t], K, scale, nvis)
@@ -120,8 +133,11 @@ def decode_sparse_bruteforce(q, kcache, block_table, seqlens, indices, scale: fl
             vis = visible_count(sl[b], s_q, t, causal)
             rows = []
             for j in ix[b][t]:
-                if 0 <= j < vis:
-                    rows.append(kf[bt[b][j // BLOCK_SIZE], j % BLOCK_SIZE, 0].tolist())
+                if not 0 <= j < vis or j // BLOCK_SIZE >= len(bt[b]):
+                    continue
+                page = bt[b][j // BLOCK_SIZE]
+                if 0 <= page < kf.shape[0]:
+                    rows.append(kf[page, j % BLOCK_SIZE, 0].tolist())
             for h in range(h_q):
                 qv = qf[b][t][h]
                 if not rows:
@@ -156,11 +172,13 @@ def decode_sparse_fp8(q, pool, block_table, seqlens, indices, scale: float, caus
     O = np.full((B, s_q, h_q, D_V), np.nan, dtype=np.float64)
     LSE = np.full((B, s_q, h_q), np.nan, dtype=np.float64)
     cache: dict = {}
+    from .mla_fp8_oracle import FP8_PAGE_BYTES
+    n_pool = pool8.reshape(-1, FP8_PAGE_BYTES).shape[0]
     reqs = range(B) if requests is None else requests
     for b in reqs:
         L = int(sl[b])
         for t in range(s_q):
-            ent = counted_entries(ix[b, t], visible_count(L, s_q, t, causal))
+            ent = counted_entries(ix[b, t], visible_count(L, s_q, t, causal), bt[b], n_pool)
             K = _gather_rows_fp8(pool8, bt[b], ent, cache)
             nvis = np.full((h_q,), K.shape[0], dtype=np.int64)
             Ob, lb = attend_rows(qf[b, t], K, scale, nvis)

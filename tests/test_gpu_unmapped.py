@@ -1,0 +1,86 @@
+"""Block-table entries that name no page of the pool (negative or >= the pool
+size) on MI355X, as the header documents them: the dense decode reads such a
+page as all-zero key rows (they count as keys with score 0), the sparse mode
+skips the entries that land on it.  Dense: checked against the fp64 oracle
+over the same cache with one extra all-zero page that the unmapped slots
+point to; sparse: against the sparse oracle, which skips unmapped entries.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decode, decode_fp8, decode_sparse, decode_sparse_fp8
+from workloads import build_fp8_inputs, build_inputs, draw_topk_indices
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 1e-2
+TOL_LSE = 1e-3
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_kv_04_amd as m
+    m.lib()
+    return m
+
+
+def _check(out, lse, O_ref, L_ref, tag):
+    O = out.float().cpu().numpy().astype(np.float64)
+    L = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(L_ref)
+    assert np.array_equal(np.isfinite(L), fin), tag
+    tol = TOL_O * float(np.max(np.abs(O_ref[fin])))
+    assert float(np.max(np.abs(O - O_ref))) <= tol, tag
+    assert float(np.max(np.abs(L[fin] - L_ref[fin]))) <= TOL_LSE, tag
+
+
+def _unmap(bt, n_pool):
+    bt = bt.clone()
+    bt[0, 1] = n_pool + 5
+    bt[1, 0] = -3
+    bt[2, 2] = 1 << 30
+    return bt
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 1), (32, 2)])
+def test_dense_unmapped_pages_read_as_zero_rows(mla, kv, h_q, s_q):
+    print(f"case unmapped dense {kv} h_q={h_q} s_q={s_q}", flush=True)
+    fp8 = kv == "fp8"
+    lens = [200, 130, 300]
+    inp = (build_fp8_inputs if fp8 else build_inputs)(lens, s_q, h_q, seed=77, extra_pool=3)
+    n_pool = int(inp.kcache.shape[0])
+    bt = _unmap(inp.block_table, n_pool)
+    g = inp.to("cuda")
+    fwd = mla.fwd_fp8 if fp8 else mla.fwd
+    out, lse = fwd(g.q, g.kcache, bt.cuda(), g.seqlens, inp.scale, inp.causal)
+    torch.cuda.synchronize()
+    # reference: the unmapped slots point at one extra all-zero page
+    zero = torch.zeros_like(inp.kcache[:1])
+    kc2 = torch.cat([inp.kcache, zero]).contiguous()
+    bt2 = bt.clone()
+    bt2[(bt2 < 0) | (bt2 >= n_pool)] = n_pool
+    ref = decode_fp8 if fp8 else decode
+    O_ref, L_ref = ref(inp.q, kc2, bt2, inp.seqlens, inp.scale, inp.causal)
+    _check(out, lse, O_ref, L_ref, f"dense {kv}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_sparse_unmapped_pages_are_skipped(mla, kv):
+    print(f"case unmapped sparse {kv}", flush=True)
+    fp8 = kv == "fp8"
+    lens = [200, 130, 300]
+    inp = (build_fp8_inputs if fp8 else build_inputs)(lens, 1, 64, seed=78, extra_pool=3)
+    n_pool = int(inp.kcache.shape[0])
+    bt = _unmap(inp.block_table, n_pool)
+    ix = draw_topk_indices(lens, 1, 96, False, torch.Generator().manual_seed(11))
+    g = inp.to("cuda")
+    fn = mla.sparse_fwd_fp8 if fp8 else mla.sparse_fwd
+    out, lse = fn(g.q, g.kcache, bt.cuda(), g.seqlens, ix.cuda(), inp.scale, False)
+    torch.cuda.synchronize()
+    ref = decode_sparse_fp8 if fp8 else decode_sparse
+    O_ref, L_ref = ref(inp.q, inp.kcache, bt, inp.seqlens, ix, inp.scale, False)
+    _check(out, lse, O_ref, L_ref, f"sparse {kv}")

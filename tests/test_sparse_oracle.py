@@ -151,3 +151,31 @@ def test_fp8_non_counting_entries_change_nothing():
     ix2[1, 0, -1] = 89      # request 1, token 0 sees positions < 89
     got = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix2, inp.scale, True)
     assert np.array_equal(base[0], got[0]) and np.array_equal(base[1], got[1])
+
+
+def test_unmapped_pages_are_skipped():
+    """Entries whose table slot holds a page id outside the pool count for
+    nothing: the result equals the one with those entries removed from the
+    list (bf16 and FP8 pages; brute force agrees)."""
+    from oracle import decode_sparse_fp8
+    from workloads import build_fp8_inputs
+    for fp8 in (False, True):
+        build = build_fp8_inputs if fp8 else build_inputs
+        inp = build([200, 130], 1, 4, seed=74, extra_pool=3)
+        n_pool = int(inp.kcache.shape[0])
+        bt = inp.block_table.clone()
+        bt[0, 1] = n_pool + 5          # positions 64..127 of request 0 unmapped
+        bt[1, 0] = -3                  # positions 0..63 of request 1 unmapped
+        g = torch.Generator().manual_seed(10)
+        ix = draw_topk_indices([200, 130], 1, 64, False, g)
+        keep = ix.clone()
+        j0, j1 = keep[0, 0], keep[1, 0]
+        j0[(j0 >= 64) & (j0 < 128)] = -1
+        j1[(j1 >= 0) & (j1 < 64)] = -1
+        ref = decode_sparse_fp8 if fp8 else decode_sparse
+        a = ref(inp.q, inp.kcache, bt, inp.seqlens, ix, inp.scale, False)
+        b = ref(inp.q, inp.kcache, inp.block_table, inp.seqlens, keep, inp.scale, False)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        if not fp8:
+            c = decode_sparse_bruteforce(inp.q, inp.kcache, bt, inp.seqlens, ix, inp.scale, False)
+            assert np.allclose(a[0], c[0], rtol=1e-12, atol=1e-12)
