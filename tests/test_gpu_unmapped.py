@@ -84,3 +84,28 @@ def test_sparse_unmapped_pages_are_skipped(mla, kv):
     ref = decode_sparse_fp8 if fp8 else decode_sparse
     O_ref, L_ref = ref(inp.q, inp.kcache, bt, inp.seqlens, ix, inp.scale, False)
     _check(out, lse, O_ref, L_ref, f"sparse {kv}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_skips_unmapped_pages(mla, kv):
+    """The append writes nothing for new tokens whose page slot names no page
+    of the pool; the whole cache equals the oracle's bit for bit."""
+    from oracle import kv_append, kv_append_fp8
+    print(f"case unmapped append {kv}", flush=True)
+    fp8 = kv == "fp8"
+    lens = [200, 130, 300]
+    s_q = 4
+    inp = (build_fp8_inputs if fp8 else build_inputs)(lens, s_q, 16, seed=79, extra_pool=3)
+    n_pool = int(inp.kcache.shape[0])
+    bt = inp.block_table.clone()
+    bt[0, 3] = n_pool + 1         # the page of request 0's new tokens (positions 196..199)
+    bt[2, 4] = -1                 # request 2's new tokens (296..299)
+    new = torch.randn((3, s_q, 576), generator=torch.Generator().manual_seed(12)).to(torch.bfloat16)
+    g = inp.to("cuda")
+    fn = mla.kv_append_fp8 if fp8 else mla.kv_append
+    fn(new.cuda(), g.kcache, bt.cuda(), g.seqlens)
+    torch.cuda.synchronize()
+    ref = (kv_append_fp8 if fp8 else kv_append)(inp.kcache, bt, inp.seqlens, new)
+    ref = torch.as_tensor(ref)
+    got = g.kcache.cpu()
+    assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8))
