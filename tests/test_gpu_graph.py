@@ -110,3 +110,107 @@ def test_graph_decode_step_with_append(mla):
         assert torch.equal(out, ref_o), f"replay {rep}: O"
         assert torch.equal(lse, ref_l), f"replay {rep}: LSE"
         assert torch.equal(g.kcache.view(torch.int16), ref_k.view(torch.int16)), f"replay {rep}"
+
+
+def _replay_matches(step, outs, reps=3, keep=()):
+    """Run step eagerly, capture it, then replay `reps` times with the outputs
+    cleared and unrelated eager work in between: every replay must give the
+    eager bits.  Tensors in `keep` (inputs the step also writes, such as the
+    cache it appends to) are compared but not cleared."""
+    outs = list(outs) + list(keep)
+    keep_ids = {id(k) for k in keep}
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    junk = torch.randn(1 << 20, device="cuda")
+    for rep in range(reps):
+        for o in outs:
+            if id(o) not in keep_ids:
+                o.view(torch.uint8).fill_(0x5a)
+        junk.mul_(1.0001)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: output {i}"
+
+
+def test_graph_fp8_step_with_append(mla):
+    """FP8 cache: quantising append + scheduler + decode + combine in one graph."""
+    from workloads import build_fp8_inputs
+    print("case graph fp8 append step", flush=True)
+    s_q, h_q = 2, 64
+    inp = build_fp8_inputs([700, 65, 3, 2049, 0], s_q, h_q, seed=78)
+    g = inp.to("cuda")
+    new = torch.randn((inp.batch, s_q, 576), generator=torch.Generator().manual_seed(4)).to(
+        torch.bfloat16).cuda()
+    parts = mla.num_parts(inp.batch, s_q, h_q, 1, mla.device_num_cus(torch.device("cuda", 0)))
+    ws = torch.zeros((max(256, mla.workspace_bytes(inp.batch, s_q, h_q, parts)),),
+                     dtype=torch.uint8, device="cuda")
+    meta = mla.metadata(g.seqlens, s_q, h_q, parts=parts)
+    out = torch.empty((inp.batch, s_q, h_q, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((inp.batch, s_q, h_q), dtype=torch.float32, device="cuda")
+
+    def step():
+        mla.kv_append_fp8(new, g.kcache, g.block_table, g.seqlens)
+        mla.fwd_fp8(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, inp.causal, meta=meta,
+                    workspace=ws, out=out, lse=lse)
+
+    _replay_matches(step, [out, lse], keep=[g.kcache])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_graph_sparse_step(mla, kv):
+    """Sparse mode: resolve + decode + combine captured and replayed."""
+    from workloads import build_fp8_inputs, draw_topk_indices
+    print(f"case graph sparse {kv}", flush=True)
+    fp8 = kv == "fp8"
+    lens = [900, 64, 1, 2500, 0, 300]
+    inp = (build_fp8_inputs if fp8 else build_inputs)(lens, 1, 128, seed=79)
+    g = inp.to("cuda")
+    ix = draw_topk_indices(lens, 1, 128, False, torch.Generator().manual_seed(5),
+                           pad_frac=0.1).cuda()
+    topk = ix.shape[2]
+    parts = mla.num_parts(inp.batch, 1, 128, 1, mla.device_num_cus(torch.device("cuda", 0)))
+    meta = mla.sparse_metadata(inp.batch, 1, 128, topk, "cuda", parts=parts)
+    ws = torch.zeros((mla.sparse_workspace_bytes(inp.batch, 1, 128, topk, parts),),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((inp.batch, 1, 128, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((inp.batch, 1, 128), dtype=torch.float32, device="cuda")
+    fn = mla.sparse_fwd_fp8 if fp8 else mla.sparse_fwd
+
+    def step():
+        fn(g.q, g.kcache, g.block_table, g.seqlens, ix, inp.scale, False, meta=meta,
+           workspace=ws, out=out, lse=lse)
+
+    _replay_matches(step, [out, lse])
+
+
+def test_graph_inline_plan(mla):
+    """The two-launch decode (plan inside the decode kernel) captured and replayed;
+    the plan it writes is compared too."""
+    print("case graph inline plan", flush=True)
+    s_q, h_q = 1, 128
+    inp = build_inputs([1000, 65, 0, 300, 2049, 7], s_q, h_q, seed=80)
+    g = inp.to("cuda")
+    parts = mla.num_parts(inp.batch, s_q, h_q, 1, mla.device_num_cus(torch.device("cuda", 0)))
+    meta = mla.metadata(g.seqlens, s_q, h_q, parts=parts)   # buffers the kernel's plan goes to
+    ws = torch.zeros((max(256, mla.workspace_bytes(inp.batch, s_q, h_q, parts)),),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((inp.batch, s_q, h_q, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((inp.batch, s_q, h_q), dtype=torch.float32, device="cuda")
+
+    def step():
+        mla.fwd_inline_plan(g.q, g.kcache, g.block_table, g.seqlens, inp.scale, meta=meta,
+                            workspace=ws, out=out, lse=lse)
+
+    _replay_matches(step, [out, lse, meta.tile_meta, meta.split_offsets])
