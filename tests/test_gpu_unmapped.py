@@ -109,3 +109,67 @@ def test_append_skips_unmapped_pages(mla, kv):
     ref = torch.as_tensor(ref)
     got = g.kcache.cpu()
     assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8))
+
+
+# Lengths that run past the table's columns (bt_stride): the slots beyond it
+# are documented like unmapped pages (zero rows in the dense mode, skipped
+# entries in the sparse mode, nothing written by the append).
+def _short_table(inp, cols):
+    return inp.block_table[:, :cols].contiguous()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 2)])
+def test_dense_slots_beyond_table_read_as_zero_rows(mla, kv, h_q, s_q):
+    print(f"case dense beyond table {kv} h_q={h_q} s_q={s_q}", flush=True)
+    fp8 = kv == "fp8"
+    lens = [200, 130, 300]          # 4, 3 and 5 pages; the table keeps 3 columns
+    inp = (build_fp8_inputs if fp8 else build_inputs)(lens, s_q, h_q, seed=81, extra_pool=3)
+    n_pool = int(inp.kcache.shape[0])
+    bt = _short_table(inp, 3)
+    g = inp.to("cuda")
+    fwd = mla.fwd_fp8 if fp8 else mla.fwd
+    out, lse = fwd(g.q, g.kcache, bt.cuda(), g.seqlens, inp.scale, inp.causal)
+    torch.cuda.synchronize()
+    # reference: the missing columns point at one extra all-zero page
+    kc2 = torch.cat([inp.kcache, torch.zeros_like(inp.kcache[:1])]).contiguous()
+    bt2 = torch.full((3, 5), n_pool, dtype=torch.int32)
+    bt2[:, :3] = bt
+    ref = decode_fp8 if fp8 else decode
+    O_ref, L_ref = ref(inp.q, kc2, bt2, inp.seqlens, inp.scale, inp.causal)
+    _check(out, lse, O_ref, L_ref, f"dense beyond table {kv}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_sparse_slots_beyond_table_are_skipped(mla, kv):
+    print(f"case sparse beyond table {kv}", flush=True)
+    fp8 = kv == "fp8"
+    lens = [200, 130, 300]
+    inp = (build_fp8_inputs if fp8 else build_inputs)(lens, 1, 64, seed=82, extra_pool=3)
+    bt = _short_table(inp, 3)
+    ix = draw_topk_indices(lens, 1, 128, False, torch.Generator().manual_seed(15))
+    g = inp.to("cuda")
+    fn = mla.sparse_fwd_fp8 if fp8 else mla.sparse_fwd
+    out, lse = fn(g.q, g.kcache, bt.cuda(), g.seqlens, ix.cuda(), inp.scale, False)
+    torch.cuda.synchronize()
+    ref = decode_sparse_fp8 if fp8 else decode_sparse
+    O_ref, L_ref = ref(inp.q, inp.kcache, bt, inp.seqlens, ix, inp.scale, False)
+    _check(out, lse, O_ref, L_ref, f"sparse beyond table {kv}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_skips_slots_beyond_table(mla, kv):
+    from oracle import kv_append, kv_append_fp8
+    print(f"case append beyond table {kv}", flush=True)
+    fp8 = kv == "fp8"
+    lens, s_q = [200, 130, 300], 4   # new tokens at slots 3, 2 and 4: two beyond 3 columns
+    inp = (build_fp8_inputs if fp8 else build_inputs)(lens, s_q, 16, seed=83, extra_pool=3)
+    bt = _short_table(inp, 3)
+    new = torch.randn((3, s_q, 576), generator=torch.Generator().manual_seed(16)).to(torch.bfloat16)
+    g = inp.to("cuda")
+    fn = mla.kv_append_fp8 if fp8 else mla.kv_append
+    fn(new.cuda(), g.kcache, bt.cuda(), g.seqlens)
+    torch.cuda.synchronize()
+    ref = torch.as_tensor((kv_append_fp8 if fp8 else kv_append)(inp.kcache, bt, inp.seqlens, new))
+    assert torch.equal(g.kcache.cpu().view(torch.uint8), ref.view(torch.uint8))
+    assert not torch.equal(ref.view(torch.uint8), inp.kcache.view(torch.uint8))   # request 1 wrote
