@@ -345,3 +345,23 @@ def test_kv_append_matches_oracle(mla, s_q):
     torch.cuda.synchronize()
     O_ref, L_ref = decode(inp.q, ref, inp.block_table, inp.seqlens, inp.scale, inp.causal)
     _assert_parity(out, lse, O_ref, L_ref, tag=f"append s{s_q}")
+
+
+# Many short requests: the scheduler's 64-request chunks carry costs and split
+# offsets across 16 chunks, and most parts hold several whole requests.
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (64, 2)])
+def test_large_batch(mla, h_q, s_q):
+    _say(f"case large batch h_q={h_q} s_q={s_q}")
+    gen = np.random.default_rng(17 + h_q)
+    lens = gen.integers(0, 400, size=1000).tolist()
+    lens[5] = 0
+    lens[6] = 1
+    lens[7] = 5000                  # one long request among them: split many ways
+    inp = build_inputs(lens, s_q, h_q, seed=900 + h_q, extra_pool=2)
+    out, lse, meta = _run(mla, inp)
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale, inp.causal)
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"large batch h{h_q} s{s_q}")
+    # the metadata equals the integer model's
+    tm_ref, so_ref = split_plan(inp.seqlens, s_q, h_q, meta.num_parts)
+    assert np.array_equal(meta.split_offsets.cpu().numpy(), so_ref)
+    assert np.array_equal(meta.tile_meta.cpu().numpy(), tm_ref)
