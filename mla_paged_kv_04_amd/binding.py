@@ -225,6 +225,47 @@ def _outputs(q, out, lse):
     return out, lse
 
 
+def _check_batch_shapes(q, block_table, seqlens, out=None, lse=None, meta=None,
+                        items=None, workspace=None):
+    """Host-side shape agreement of everything a launch will index, so that a
+    mismatched tensor raises here instead of reaching a kernel (which trusts
+    these shapes and would read or write out of bounds).  ``items`` is the
+    number of split-plan entries the metadata must cover (batch, or
+    batch * s_q in the sparse mode)."""
+    batch, s_q, h_q, _ = q.shape
+    dev = q.device
+    for name, t in (("block_table", block_table), ("seqlens", seqlens), ("out", out),
+                    ("lse", lse), ("workspace", workspace)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+    if tuple(seqlens.shape) != (batch,):
+        raise ValueError(f"seqlens {tuple(seqlens.shape)} does not match batch {batch}")
+    if block_table.shape[0] != batch:
+        raise ValueError(f"block_table {tuple(block_table.shape)} does not match batch {batch}")
+    if out is not None and tuple(out.shape) != (batch, s_q, h_q, D_V):
+        raise ValueError(f"out {tuple(out.shape)} must be {(batch, s_q, h_q, D_V)}")
+    if lse is not None and tuple(lse.shape) != (batch, s_q, h_q):
+        raise ValueError(f"lse {tuple(lse.shape)} must be {(batch, s_q, h_q)}")
+    if meta is not None:
+        _check_meta(meta, s_q, h_q, batch if items is None else items, dev)
+
+
+def _check_meta(meta, s_q, h_q, items, dev):
+    if (meta.s_q, meta.h_q) != (s_q, h_q):
+        raise ValueError(f"metadata was built for s_q={meta.s_q}, h_q={meta.h_q}, "
+                         f"not s_q={s_q}, h_q={h_q}")
+    _require(meta.tile_meta, torch.int32, "meta.tile_meta", 2)
+    _require(meta.split_offsets, torch.int32, "meta.split_offsets", 1)
+    if tuple(meta.tile_meta.shape) != (meta.num_parts, TILE_META_INTS):
+        raise ValueError(f"meta.tile_meta {tuple(meta.tile_meta.shape)} must be "
+                         f"{(meta.num_parts, TILE_META_INTS)}")
+    if meta.split_offsets.numel() != items + 1:
+        raise ValueError(f"meta.split_offsets has {meta.split_offsets.numel()} entries, "
+                         f"{items + 1} expected")
+    if meta.tile_meta.device != dev or meta.split_offsets.device != dev:
+        raise ValueError("metadata is on another device")
+
+
 def _event_handle(ev):
     """Raw hipEvent_t of a torch.cuda.Event (None -> NULL).  torch creates the
     event on its first record, so an unrecorded event is recorded once here."""
@@ -244,6 +285,8 @@ def splitkv(q, kcache, block_table, seqlens, scale: float, causal: bool, meta: M
     (mla_decode_splitkv_timed)."""
     batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens)
     out, lse = _outputs(q, out, lse)
+    _require_workspace(workspace, q.device)
+    _check_batch_shapes(q, block_table, seqlens, out, lse, meta, workspace=workspace)
     args = (_ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
             _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
             _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
@@ -259,7 +302,20 @@ def splitkv(q, kcache, block_table, seqlens, scale: float, causal: bool, meta: M
 
 def combine(seqlens, s_q: int, h_q: int, meta: Metadata, workspace: torch.Tensor, out, lse):
     """Enqueue only the log-sum-exp merge of the split partials."""
+    _require(seqlens, torch.int32, "seqlens", 1)
     batch = seqlens.shape[0]
+    _require(out, torch.bfloat16, "out", 4)
+    _require(lse, torch.float32, "lse", 3)
+    _require_workspace(workspace, seqlens.device)
+    if tuple(out.shape) != (batch, s_q, h_q, D_V) or tuple(lse.shape) != (batch, s_q, h_q):
+        raise ValueError(f"out {tuple(out.shape)} / lse {tuple(lse.shape)} do not match "
+                         f"batch {batch}, s_q {s_q}, h_q {h_q}")
+    if out.device != seqlens.device or lse.device != seqlens.device:
+        raise ValueError("out / lse are on another device than seqlens")
+    _require(meta.split_offsets, torch.int32, "meta.split_offsets", 1)
+    if meta.split_offsets.numel() != batch + 1 or meta.split_offsets.device != seqlens.device:
+        raise ValueError(f"meta.split_offsets has {meta.split_offsets.numel()} entries, "
+                         f"{batch + 1} expected")
     _check(lib().mla_decode_combine(
         _ptr(seqlens), batch, s_q, h_q, _ptr(meta.split_offsets), meta.num_parts,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
@@ -274,16 +330,69 @@ def fwd(q, kcache, block_table, seqlens, scale: float, causal: bool | None = Non
     batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens)
     if causal is None:
         causal = s_q > 1
+    _check_batch_shapes(q, block_table, seqlens)
     if meta is None:
         meta = metadata(seqlens, s_q, h_q, h_kv, parts)
     workspace = _alloc_workspace(batch, s_q, h_q, meta.num_parts, q.device, workspace)
     out, lse = _outputs(q, out, lse)
+    _check_batch_shapes(q, block_table, seqlens, out, lse, meta, workspace=workspace)
     _check(lib().mla_decode_fwd(
         _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
         _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
         _ptr(meta.tile_meta), _ptr(meta.split_offsets), meta.num_parts, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)),
         "mla_decode_fwd")
+    return out, lse
+
+
+def _check_append_shapes(new_kv, kcache, block_table, seqlens):
+    batch = new_kv.shape[0]
+    if tuple(seqlens.shape) != (batch,) or block_table.shape[0] != batch:
+        raise ValueError(f"seqlens {tuple(seqlens.shape)} / block_table "
+                         f"{tuple(block_table.shape)} do not match new_kv batch {batch}")
+    for name, t in (("kcache", kcache), ("block_table", block_table), ("seqlens", seqlens)):
+        if t.device != new_kv.device:
+            raise ValueError(f"{name} is on {t.device}, new_kv on {new_kv.device}")
+
+
+def _require_workspace(ws, dev):
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != dev:
+        raise ValueError("workspace must be a device tensor on the inputs' device")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def _check_append_shapes(new_kv, kcache, block_table, seqlens):
+    batch = new_kv.shape[0]
+    if tuple(seqlens.shape) != (batch,) or block_table.shape[0] != batch:
+        raise ValueError(f"seqlens {tuple(seqlens.shape)} / block_table "
+                         f"{tuple(block_table.shape)} do not match new_kv batch {batch}")
+    for name, t in (("kcache", kcache), ("block_table", block_table), ("seqlens", seqlens)):
+        if t.device != new_kv.device:
+            raise ValueError(f"{name} is on {t.device}, new_kv on {new_kv.device}")
+
+
+def _require_workspace(ws, dev):
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != dev:
+        raise ValueError("workspace must be a device tensor on the inputs' device")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def fwd_noalloc(q, kcache, block_table, seqlens, scale: float, causal: bool | None = None,
+                out=None, lse=None):
+    """The decode through mla_decode_fwd_noalloc: plan and partials in the
+    library's own device array (nothing allocated by the call itself; out /
+    lse are allocated here only when not given)."""
+    batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens)
+    if causal is None:
+        causal = s_q > 1
+    out, lse = _outputs(q, out, lse)
+    _check_batch_shapes(q, block_table, seqlens, out, lse)
+    _check(lib().mla_decode_fwd_noalloc(
+        _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)), _ptr(out),
+        _ptr(lse), _stream(q.device)), "mla_decode_fwd_noalloc")
     return out, lse
 
 
@@ -299,6 +408,7 @@ def kv_append(new_kv: torch.Tensor, kcache: torch.Tensor, block_table: torch.Ten
     if dk != D_K or kcache.shape[1] != BLOCK_SIZE or kcache.shape[3] != D_K:
         raise ValueError(f"shape mismatch: new_kv {tuple(new_kv.shape)}, "
                          f"kcache {tuple(kcache.shape)}")
+    _check_append_shapes(new_kv, kcache, block_table, seqlens)
     _check(lib().mla_kv_append(_ptr(new_kv), _ptr(kcache), kcache.shape[0], _ptr(block_table),
                                block_table.shape[1], _ptr(seqlens), batch, s_q,
                                _stream(new_kv.device)), "mla_kv_append")
@@ -311,6 +421,8 @@ def splitkv_fp8(q, kcache, block_table, seqlens, scale: float, causal: bool, met
     (mla_decode_splitkv_fp8; the events as in splitkv)."""
     batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens, fp8=True)
     out, lse = _outputs(q, out, lse)
+    _require_workspace(workspace, q.device)
+    _check_batch_shapes(q, block_table, seqlens, out, lse, meta, workspace=workspace)
     _check(lib().mla_decode_splitkv_fp8(
         _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
         _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
@@ -329,10 +441,12 @@ def fwd_fp8(q, kcache, block_table, seqlens, scale: float, causal: bool | None =
     batch, s_q, h_q, h_kv = _decode_args(q, kcache, block_table, seqlens, fp8=True)
     if causal is None:
         causal = s_q > 1
+    _check_batch_shapes(q, block_table, seqlens)
     if meta is None:
         meta = metadata(seqlens, s_q, h_q, h_kv, parts)
     workspace = _alloc_workspace(batch, s_q, h_q, meta.num_parts, q.device, workspace)
     out, lse = _outputs(q, out, lse)
+    _check_batch_shapes(q, block_table, seqlens, out, lse, meta, workspace=workspace)
     _check(lib().mla_decode_fwd_fp8(
         _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
         _ptr(seqlens), batch, s_q, h_q, h_kv, float(scale), int(bool(causal)),
@@ -359,6 +473,7 @@ def fwd_inline_plan(q, kcache, block_table, seqlens, scale: float, causal: bool 
                         s_q, h_q)
     workspace = _alloc_workspace(batch, s_q, h_q, meta.num_parts, q.device, workspace)
     out, lse = _outputs(q, out, lse)
+    _check_batch_shapes(q, block_table, seqlens, out, lse, meta, workspace=workspace)
     name = "mla_decode_fwd_inline_plan_fp8" if fp8 else "mla_decode_fwd_inline_plan"
     _check(getattr(lib(), name)(
         _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
@@ -381,6 +496,7 @@ def kv_append_fp8(new_kv: torch.Tensor, kcache: torch.Tensor, block_table: torch
     if dk != D_K or kcache.shape[1] != FP8_PAGE_BYTES:
         raise ValueError(f"shape mismatch: new_kv {tuple(new_kv.shape)}, "
                          f"FP8 kcache {tuple(kcache.shape)}")
+    _check_append_shapes(new_kv, kcache, block_table, seqlens)
     _check(lib().mla_kv_append_fp8(_ptr(new_kv), _ptr(kcache), kcache.shape[0],
                                    _ptr(block_table), block_table.shape[1], _ptr(seqlens),
                                    batch, s_q, _stream(new_kv.device)), "mla_kv_append_fp8")
@@ -437,6 +553,9 @@ def _sparse_fwd(q, kcache, block_table, seqlens, indices, scale, causal, meta, p
     if tuple(indices.shape[:2]) != (batch, s_q):
         raise ValueError(f"indices {tuple(indices.shape)} do not match q {tuple(q.shape)}")
     topk = indices.shape[2]
+    if indices.device != q.device:
+        raise ValueError(f"indices is on {indices.device}, q on {q.device}")
+    _check_batch_shapes(q, block_table, seqlens)
     if causal is None:
         causal = s_q > 1
     if meta is None:
@@ -445,6 +564,9 @@ def _sparse_fwd(q, kcache, block_table, seqlens, indices, scale, causal, meta, p
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
     out, lse = _outputs(q, out, lse)
+    _require_workspace(workspace, q.device)
+    _check_batch_shapes(q, block_table, seqlens, out, lse, meta, items=batch * s_q,
+                        workspace=workspace)
     name = "mla_decode_sparse_fwd_fp8" if fp8 else "mla_decode_sparse_fwd"
     _check(getattr(lib(), name)(
         _ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],

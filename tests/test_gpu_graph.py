@@ -1,13 +1,17 @@
 """The decode step (scheduler, decode kernel, combine) captured as a HIP graph
-and replayed: every replay must reproduce the eager result bit for bit.
+and replayed: every replay must reproduce the eager result bit for bit, and
+the replayed output is also checked against the fp64 oracle (max|dO| <=
+1e-2 * max|O_ref|, |dLSE| <= 1e-3, empty rows exactly O = 0, LSE = -inf).
 
 The outputs are cleared by eager work between replays, and the replays are
 interleaved with other eager kernels and host synchronisations, so a replay
 that silently skipped or repeated work would show up as a mismatch.
 """
+import numpy as np
 import pytest
 import torch
 
+from oracle import decode
 from workloads import build_inputs
 
 pytestmark = pytest.mark.gpu
@@ -20,6 +24,20 @@ def mla():
     import mla_paged_kv_04_amd as m
     m.lib()
     return m
+
+
+def _assert_oracle(out, lse, O_ref, L_ref, tag):
+    O = out.float().cpu().numpy().astype(np.float64)
+    L = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(L_ref)
+    assert np.array_equal(np.isfinite(L), fin), f"{tag}: -inf rows differ"
+    if np.any(~fin):
+        assert np.all(L[~fin] == -np.inf) and np.all(O[~fin] == 0.0), f"{tag}: empty rows"
+    tol_o = 1e-2 * float(np.max(np.abs(O_ref[fin])))
+    err_o = float(np.max(np.abs(O - O_ref)))
+    err_l = float(np.max(np.abs(L[fin] - L_ref[fin])))
+    print(f"  {tag}: max|dO|={err_o:.3e} (tol {tol_o:.3e}) max|dLSE|={err_l:.3e}", flush=True)
+    assert err_o <= tol_o and err_l <= 1e-3, tag
 
 
 @pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 1), (128, 2)])
@@ -64,6 +82,10 @@ def test_graph_replays_match_eager(mla, h_q, s_q):
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o), f"replay {rep}: O differs from the eager step"
         assert torch.equal(lse, ref_l), f"replay {rep}: LSE differs from the eager step"
+    # the last replay's output against the oracle
+    O_ref, L_ref = decode(inp.q, inp.kcache, inp.block_table, inp.seqlens, inp.scale,
+                          inp.causal)
+    _assert_oracle(out, lse, O_ref, L_ref, f"graph replay h{h_q} s{s_q} vs oracle")
 
 
 def test_graph_decode_step_with_append(mla):
