@@ -365,6 +365,34 @@ int mla_decode_sparse_fwd_fp8(const void* q_d, const void* kcache_d, int64_t num
                               void* out_d, float* lse_d, void* start_event, void* stop_event,
                               void* stream);
 
+/*
+ * mla_decode_fwd_noalloc — the whole decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It runs mla_decode_metadata, mla_decode_splitkv and
+ * mla_decode_combine on `stream` with the plan (tile_meta, split_offsets) and
+ * the fp32 partials in one device array that the library holds for the life
+ * of the process, MLA_NOALLOC_SCRATCH_BYTES per device, instead of caller
+ * buffers; it allocates and frees nothing and calls no allocating routine.
+ *   Arguments as mla_decode_fwd without tile_meta_d / split_offsets_d /
+ *   num_parts / workspace_d / workspace_bytes; the caller still owns q, the
+ *   cache, the table, the lengths and the outputs.  The stream must belong to
+ *   the current device.
+ *   Parts: mla_decode_num_parts for the current device, halved until the
+ *   partials (mla_decode_workspace_bytes) fit in the array; results equal
+ *   mla_decode_fwd's with that part count.
+ *   batch above MLA_NOALLOC_MAX_BATCH returns MLA_ERR_INVALID_ARG; every other
+ *   check and status code as mla_decode_fwd; nothing is enqueued on error.
+ * All calls on one device share its array, which keeps the last call's
+ * contents: two calls that overlap on one device (concurrent streams or host
+ * threads) race and must be serialised by the caller.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+#define MLA_NOALLOC_MAX_BATCH 16384
+int mla_decode_fwd_noalloc(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                           const int32_t* block_table_d, int bt_stride,
+                           const int32_t* seqlens_d, int batch, int s_q, int h_q, int h_kv,
+                           float scale, int causal, void* out_d, float* lse_d, void* stream);
+
 /* Static text for a status code. */
 const char* mla_status_string(int status);
 

@@ -81,6 +81,9 @@ _SIGNATURES = {
                                                 _c_float, _c_int, _c_ptr, _c_ptr, _c_int,
                                                 _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr,
                                                 _c_ptr, _c_ptr]),
+    "mla_decode_fwd_noalloc": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_int, _c_ptr,
+                                        _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                        _c_ptr, _c_ptr, _c_ptr]),
     "mla_status_string": (ctypes.c_char_p, [_c_int]),
     "mla_last_hip_error": (ctypes.c_char_p, []),
     "mla_device_num_cus": (_c_int, [_c_int, ctypes.POINTER(_c_int)]),
@@ -343,23 +346,6 @@ def fwd(q, kcache, block_table, seqlens, scale: float, causal: bool | None = Non
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(q.device)),
         "mla_decode_fwd")
     return out, lse
-
-
-def _check_append_shapes(new_kv, kcache, block_table, seqlens):
-    batch = new_kv.shape[0]
-    if tuple(seqlens.shape) != (batch,) or block_table.shape[0] != batch:
-        raise ValueError(f"seqlens {tuple(seqlens.shape)} / block_table "
-                         f"{tuple(block_table.shape)} do not match new_kv batch {batch}")
-    for name, t in (("kcache", kcache), ("block_table", block_table), ("seqlens", seqlens)):
-        if t.device != new_kv.device:
-            raise ValueError(f"{name} is on {t.device}, new_kv on {new_kv.device}")
-
-
-def _require_workspace(ws, dev):
-    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != dev:
-        raise ValueError("workspace must be a device tensor on the inputs' device")
-    if not ws.is_contiguous():
-        raise ValueError("workspace must be contiguous")
 
 
 def _check_append_shapes(new_kv, kcache, block_table, seqlens):

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["mla_kernels.hip", "mla_api.cpp"]
+SOURCES = ["mla_kernels.hip", "mla_api.cpp", "mla_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -79,7 +79,7 @@ int splitkv_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
                  const int32_t* tile_meta_d, const int32_t* split_offsets_d, int num_parts,
                  void* workspace_d, size_t workspace_bytes, void* out_d, float* lse_d,
                  int kv_fp8, void* start_event, void* stop_event, void* stream,
-                 int inplan = 0) {
+                 int inplan = 0, int dry_run = 0) {
   int st = check_common(seqlens_d, split_offsets_d, batch, s_q, h_q, h_kv, num_parts,
                         workspace_d, workspace_bytes, out_d, lse_d);
   if (st != MLA_OK) return st;
@@ -89,6 +89,7 @@ int splitkv_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
     return MLA_ERR_INVALID_ARG;
   if (num_blocks < 1 || bt_stride < 1 || !isfinite(scale) || (causal != 0 && causal != 1))
     return MLA_ERR_INVALID_ARG;
+  if (dry_run) return MLA_OK;
   mla::DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q_d);
   a.kcache = kcache_d;
@@ -168,6 +169,29 @@ SparseWorkspace sparse_workspace(int batch, int s_q, int h_q, int topk, int num_
 }
 
 }  // namespace
+
+namespace mla {
+
+int set_hip_error(hipError_t e, const char* where) { return hip_fail(e, where); }
+
+int validate_decode(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                    const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                    int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                    const int32_t* tile_meta_d, const int32_t* split_offsets_d, int num_parts,
+                    void* workspace_d, size_t workspace_bytes, void* out_d, float* lse_d) {
+  return splitkv_impl(q_d, kcache_d, num_blocks, block_table_d, bt_stride, seqlens_d, batch,
+                      s_q, h_q, h_kv, scale, causal, tile_meta_d, split_offsets_d, num_parts,
+                      workspace_d, workspace_bytes, out_d, lse_d, 0, nullptr, nullptr, nullptr,
+                      0, 1);
+}
+
+size_t decode_workspace_need(int s_q, int h_q, int num_parts) {
+  return workspace_need(s_q, h_q, num_parts);
+}
+
+int decode_row_tiles(int s_q, int h_q) { return row_tiles(s_q, h_q); }
+
+}  // namespace mla
 
 extern "C" {
 

@@ -12,7 +12,7 @@ constexpr int kDK = 576;                   // key width (512 latent + 64 rope)
 constexpr int kDV = 512;                   // value width (first 512 key dims)
 constexpr int kRowBytes = kDK * 2;         // 1152 bytes per bf16 cache row
 constexpr int kPageBytes = kBlock * kRowBytes;  // 73728 bytes per page
-constexpr int kMaxRowsPerTile = 128;       // query rows one workgroup carries
+constexpr int kMaxRowsPerTile = 128;       // cap of the query rows charged in the split plan's per-request overhead
 constexpr int kMetaInts = 8;
 
 // Fixed per-request overhead of the balancing rule, in page units: one page
@@ -45,7 +45,7 @@ struct DecodeArgs {
   int causal;
   int num_parts;
   int row_tiles;
-  int row_tile_rows;          // query rows per workgroup tile (32, 64 or 128)
+  int row_tile_rows;          // query rows per workgroup tile (16, 32 or 64)
   float scale_log2;           // scale * log2(e)
   int kv_fp8;                 // 1: kcache holds FP8 pages
   // Sparse mode (selected keys): requests are (request, token) items of
@@ -110,5 +110,19 @@ hipError_t launch_kv_append_fp8(const uint16_t* new_kv, uint8_t* kcache, long lo
 
 // Row-tile geometry chosen for M query rows (rows per workgroup tile).
 int tile_rows_for(int M);
+
+// Host layer helpers shared with the entry point that allocates nothing
+// (mla_noalloc.hip); defined in mla_api.cpp.
+// validate_decode: every check of mla_decode_splitkv, launching nothing.
+int validate_decode(const void* q_d, const void* kcache_d, int64_t num_blocks,
+                    const int32_t* block_table_d, int bt_stride, const int32_t* seqlens_d,
+                    int batch, int s_q, int h_q, int h_kv, float scale, int causal,
+                    const int32_t* tile_meta_d, const int32_t* split_offsets_d, int num_parts,
+                    void* workspace_d, size_t workspace_bytes, void* out_d, float* lse_d);
+// Records the HIP error text (mla_last_hip_error) and returns MLA_ERR_HIP.
+int set_hip_error(hipError_t e, const char* where);
+// Bytes of mla_decode_workspace_bytes, and the row tiles of a launch.
+size_t decode_workspace_need(int s_q, int h_q, int num_parts);
+int decode_row_tiles(int s_q, int h_q);
 
 }  // namespace mla
