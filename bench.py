@@ -11,7 +11,14 @@ Prints one JSON line (rank 0).  `value` is algorithmic HBM GB/s of the whole
 step; `roofline` reports the dominant kernel (mla_decode_splitkv) measured
 with HIP events on the stream it is launched on.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload membound]
+By default the five configurations of the metric (tiny, membound, ridge,
+ragged, long) run one after another, each with W warm-up and K timed steps;
+the line is that of the long-context configuration (the largest one by
+bytes), with a `per_config` map holding every configuration's step and
+kernel times, GB/s, TFLOP/s, roofline fractions and traffic ratio.
+`--workload X` times one workload alone.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
 """
 from __future__ import annotations
 
@@ -223,58 +230,22 @@ def splitkv_kernel_name(m_rows: int, kv: str = "bf16", sparse: bool = False) -> 
     return f"mla_splitkv_ws_kernel<{rt}, {f(kv == 'fp8')}, {f(sparse)}>"
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="membound",
-                    help="tiny | membound | ridge | ragged | long | draft | prefill | sparse")
-    ap.add_argument("--parts", type=int, default=None, help="override split-KV part count")
-    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
-                    help="KV cache format: bf16 rows, or FP8 pages (E4M3 latent codes with a "
-                         "per-token fp32 scale, bf16 rope)")
-    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
-                    help="cache flush between timed steps (outside the timed events)")
-    ap.add_argument("--copy-calib-mib", type=int, default=0,
-                    help="run one plain elementwise copy of this many MiB (int32 -> int32) "
-                         "after warmup, outside the timed region: the known-size kernel "
-                         "that HBM byte counters are scaled against")
-    ap.add_argument("--with-append", action="store_true",
-                    help="include the paged-KV append of the step's new tokens "
-                         "(mla_kv_append) in every step")
-    ap.add_argument("--graph", action="store_true",
-                    help="time HIP-graph replays of the step instead of eager launches "
-                         "(slower on this stack: replays add ~4-14 us per step)")
-    ap.add_argument("--launch", choices=["three", "inline"], default="three",
-                    help="three: scheduler, decode and combine kernels; inline: the decode "
-                         "kernel derives its split plan itself (mla_decode_fwd_inline_plan), "
-                         "two launches per step")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: the benchmark runs on one GPU only; --gpus above 1 (or a "
-              "multi-rank launch) is not supported.", file=sys.stderr)
-        return 2
-
+def run_one(args, key: str, cpu_budget: float) -> dict:
+    """Time one workload; returns its JSON line (a dict)."""
     import torch
     import mla_paged_kv_04_amd as mla
     from workloads import WORKLOADS, algorithmic_counts, make_inputs, sparse_counts
 
-    w = WORKLOADS[args.workload]
+    w = WORKLOADS[key]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     fp8 = args.kv == "fp8"
     sparse = w.topk > 0
     if args.launch == "inline" and (sparse or args.graph):
-        print("bench.py: --launch inline applies to the eager dense decode", file=sys.stderr)
-        return 2
+        raise ValueError("--launch inline applies to the eager dense decode")
     if sparse and (args.with_append or args.graph):
-        print("bench.py: the sparse workload runs eagerly, without the append", file=sys.stderr)
-        return 2
-    inp = make_inputs(args.workload, kv_format=args.kv)
+        raise ValueError("the sparse workload runs eagerly, without the append")
+    inp = make_inputs(key, kv_format=args.kv)
     g = inp.to(dev)
     if sparse:
         counts = sparse_counts(inp.indices, inp.seqlens, inp.s_q, inp.h_q, inp.causal, args.kv)
@@ -483,7 +454,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
     warm_ms = e0.elapsed_time(e1) / K
 
-    traffic = measured_traffic(args.workload, args.kv)
+    traffic = measured_traffic(key, args.kv)
     # The binding roof of the decode kernel: HBM below the ridge point
     # (peak flops / peak bytes = 312.5 flop/byte), the bf16 MFMA above it.
     mfma_bound = counts["flops"] / counts["bytes"] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -500,7 +471,7 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "desc": w.desc, "batch": inp.batch,
+        "config": {"workload": key, "desc": w.desc, "batch": inp.batch,
                    "s_q": inp.s_q, "h_q": inp.h_q, "h_kv": 1, "d_k": 576, "d_v": 512,
                    "block_size": 64, "total_keys": int(inp.seqlens.sum()),
                    "num_parts": parts, "cache_flush_between_steps": args.flush,
@@ -545,8 +516,101 @@ def main(argv=None) -> int:
             "mfma_frac": round(dec_tfl / PEAK_BF16_TFLOPS, 4),
         },
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    if not args.no_cpu_baseline and cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(inp, cpu_budget)
+    del g, ws, out, lse, flush_buf
+    torch.cuda.empty_cache()
+    return line
+
+
+# The five configurations of the metric, in order; the last is the headline
+# of the default run (the largest single-GPU configuration by bytes).
+SUITE = ["tiny", "membound", "ridge", "ragged", "long"]
+HEADLINE = "long"
+
+
+def summary(line: dict) -> dict:
+    """The per-configuration figures of a workload's line."""
+    r = line["roofline"]
+    traffic = r.get("traffic")
+    return {
+        "ms_per_step": line["ms_per_step"],
+        "decode_ms": line["kernels_ms"]["splitkv"],
+        "kernels_ms": line["kernels_ms"],
+        "step_gbs": line["value"],
+        "step_tflops": line["tflops"],
+        "decode_gbs": r["hbm_gbs"],
+        "decode_tflops": r["mfma_tflops"],
+        "hbm_frac": r["hbm_frac"],
+        "mfma_frac": r["mfma_frac"],
+        "bound": r["bound"],
+        "frac": r["frac"],
+        "mfma_busy": r.get("mfma_busy"),
+        "traffic_ratio": (None if traffic is None
+                          else round(traffic / line["algorithmic_bytes"], 4)),
+        "algorithmic_bytes": line["algorithmic_bytes"],
+        "algorithmic_flops": line["algorithmic_flops"],
+        "cpu_baseline": line.get("cpu_baseline"),
+        "desc": line["config"]["desc"],
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None,
+                    help="tiny | membound | ridge | ragged | long | draft | prefill | sparse; "
+                         "default: the five configurations tiny, membound, ridge, ragged, "
+                         "long in one run, the line headed by long with a per_config map")
+    ap.add_argument("--parts", type=int, default=None, help="override split-KV part count")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="KV cache format: bf16 rows, or FP8 pages (E4M3 latent codes with a "
+                         "per-token fp32 scale, bf16 rope)")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="cache flush between timed steps (outside the timed events)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run one plain elementwise copy of this many MiB (int32 -> int32) "
+                         "after warmup, outside the timed region: the known-size kernel "
+                         "that HBM byte counters are scaled against")
+    ap.add_argument("--with-append", action="store_true",
+                    help="include the paged-KV append of the step's new tokens "
+                         "(mla_kv_append) in every step")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the step instead of eager launches "
+                         "(slower on this stack: replays add ~4-14 us per step)")
+    ap.add_argument("--launch", choices=["three", "inline"], default="three",
+                    help="three: scheduler, decode and combine kernels; inline: the decode "
+                         "kernel derives its split plan itself (mla_decode_fwd_inline_plan), "
+                         "two launches per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for the cpu_baseline of the reported workload")
+    ap.add_argument("--cpu-budget-each", type=float, default=3.0,
+                    help="seconds of oracle time for each other configuration of the default "
+                         "run (its per_config cpu_baseline)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: the benchmark runs on one GPU only; --gpus above 1 (or a "
+              "multi-rank launch) is not supported.", file=sys.stderr)
+        return 2
+    try:
+        if args.workload is not None:
+            line = run_one(args, args.workload, args.cpu_budget)
+        else:
+            lines = {}
+            for key in SUITE:
+                budget = args.cpu_budget if key == HEADLINE else args.cpu_budget_each
+                lines[key] = run_one(args, key, budget)
+                print(f"bench.py: {key} done: step {lines[key]['ms_per_step']} ms, decode "
+                      f"{lines[key]['kernels_ms']['splitkv']} ms", file=sys.stderr, flush=True)
+            line = lines[HEADLINE]
+            line["per_config"] = {k: summary(v) for k, v in lines.items()}
+    except ValueError as e:
+        print(f"bench.py: {e}", file=sys.stderr)
+        return 2
     print(json.dumps(line), flush=True)
     return 0
 
