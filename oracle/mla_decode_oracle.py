@@ -26,6 +26,12 @@ What it computes (sources are the pages this project is built from):
   with query row r = t*h_q + h of request b, and the visible set
   j < L_b - s_q + 1 + t when causal (the s_q newest tokens are already in the
   cache), else j < L_b.  An empty visible set gives O = 0, LSE = -inf.
+* A position whose table slot j // 64 lies past the end of the request's
+  table row, or whose slot names no page of the pool (a negative id or one
+  at or beyond the pool size), holds no key: it is left out of the visible
+  set.  The pages do not cover such a caller error; this project reads it as
+  the sparse mode reads the same entries (skipped), so both modes agree and
+  the result stays a softmax over real keys (``mapped_keys``).
 * Variable lengths are balanced by splitting one request's keys over several
   workers and merging the pieces (same page, DAY1 feature ⑤, dynamic load for
   variable-length input); the merge by log-sum-exp (``lse_merge``) is exact.
@@ -75,12 +81,26 @@ def num_pages(seqlen: int, block_size: int = BLOCK_SIZE) -> int:
     return (int(seqlen) + block_size - 1) // block_size
 
 
+def mapped_keys(block_table, seqlens, b: int, num_pool_pages: int) -> np.ndarray:
+    """Which of request b's positions j < L_b hold a key (bool [L_b]): the
+    table slot j // 64 lies inside the request's row and names a page id in
+    [0, num_pool_pages)."""
+    bt = _i64(block_table)
+    L = int(_i64(seqlens)[b])
+    slot = np.arange(L) // BLOCK_SIZE
+    inrow = slot < bt.shape[1]
+    page = np.where(inrow, bt[b, np.minimum(slot, bt.shape[1] - 1)], -1)
+    return inrow & (page >= 0) & (page < num_pool_pages)
+
+
 def gather_request_kv(kcache, block_table, seqlens, b: int) -> np.ndarray:
     """K_b[j, :] for j < L_b, gathered page by page (fp64, [L_b, 576]).
 
     Follows the paging of DAY1 feature ② (64-token pages) on the page cited in
     the module docstring: token j is row j % 64 of page block_table[b][j//64].
-    Only the first ceil(L_b/64) table slots and only rows j < L_b are read.
+    Only the first ceil(L_b/64) table slots and only rows j < L_b are read;
+    positions without a key (``mapped_keys``) come back as zero rows, which
+    the attention leaves out.
     """
     kc = kcache if isinstance(kcache, np.ndarray) else None
     bt = _i64(block_table)
@@ -89,14 +109,27 @@ def gather_request_kv(kcache, block_table, seqlens, b: int) -> np.ndarray:
     n = num_pages(L, bs)
     if n == 0:
         return np.zeros((0, kcache.shape[-1]), dtype=np.float64)
-    pages = bt[b, :n]
+    n_pool = int(kcache.shape[0])
+    slots = np.arange(n)
+    pages = np.where(slots < bt.shape[1], bt[b, np.minimum(slots, bt.shape[1] - 1)], -1)
+    ok = (pages >= 0) & (pages < n_pool)
+    safe = np.where(ok, pages, 0)
     if kc is None:
         import torch
-        rows = kcache[torch.as_tensor(pages)]          # [n, 64, 1, 576], still bf16
-        K = _f64(rows).reshape(n * bs, -1)
+        rows = kcache[torch.as_tensor(safe)]           # [n, 64, 1, 576], still bf16
+        K = _f64(rows).reshape(n, bs, -1)
     else:
-        K = np.asarray(kc[pages], dtype=np.float64).reshape(n * bs, -1)
-    return K[:L]
+        K = np.asarray(kc[safe], dtype=np.float64).reshape(n, bs, -1)
+    K[~ok] = 0.0
+    return K.reshape(n * bs, -1)[:L]
+
+
+def counted_view(K: np.ndarray, counted: np.ndarray, nvis: np.ndarray):
+    """The keys that count, in position order, and each row's visible count
+    among them: the first nvis_c[r] rows of K[counted] are exactly the
+    counted positions j < nvis[r]."""
+    ccum = np.concatenate([[0], np.cumsum(counted.astype(np.int64))])
+    return K[counted], ccum[np.minimum(nvis, K.shape[0])]
 
 
 def kv_append(kcache, block_table, seqlens, new_kv) -> np.ndarray:
@@ -182,7 +215,8 @@ def decode(q, kcache, block_table, seqlens, scale: float, causal: bool,
         qrows = qf[b].reshape(s_q * h_q, dk)
         nvis = np.array([visible_count(L, s_q, r // h_q, causal)
                          for r in range(s_q * h_q)], dtype=np.int64)
-        Ob, lb = attend_rows(qrows, K, scale, nvis)
+        Kc, nvis_c = counted_view(K, mapped_keys(block_table, seqlens, b, int(kcache.shape[0])), nvis)
+        Ob, lb = attend_rows(qrows, Kc, scale, nvis_c)
         O[b] = Ob.reshape(s_q, h_q, D_V)
         LSE[b] = lb.reshape(s_q, h_q)
     return O, LSE
@@ -213,10 +247,12 @@ def decode_bruteforce(q, kcache, block_table, seqlens, scale: float, causal: boo
                 scores = []
                 rows = []
                 for j in range(nv):
+                    if j // bs >= len(bt[b]) or not 0 <= bt[b][j // bs] < len(kl):
+                        continue          # no page: no key at this position
                     row = kl[bt[b][j // bs]][j % bs][0]
                     rows.append(row)
                     scores.append(scale * math.fsum(qv[d] * row[d] for d in range(len(qv))))
-                if nv == 0:
+                if not rows:
                     O[b][t][h] = [0.0] * D_V
                     LSE[b][t][h] = -math.inf
                     continue
@@ -224,7 +260,7 @@ def decode_bruteforce(q, kcache, block_table, seqlens, scale: float, causal: boo
                 denom = math.fsum(math.exp(s - m) for s in scores)
                 lse = m + math.log(denom)
                 w = [math.exp(s - lse) for s in scores]
-                O[b][t][h] = [math.fsum(w[j] * rows[j][d] for j in range(nv))
+                O[b][t][h] = [math.fsum(w[j] * rows[j][d] for j in range(len(rows)))
                               for d in range(D_V)]
                 LSE[b][t][h] = lse
     return np.array(O, dtype=np.float64), np.array(LSE, dtype=np.float64)

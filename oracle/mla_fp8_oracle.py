@@ -43,8 +43,8 @@ import math
 
 import numpy as np
 
-from .mla_decode_oracle import BLOCK_SIZE, D_K, D_V, _i64, attend_rows, num_pages, \
-    visible_count
+from .mla_decode_oracle import BLOCK_SIZE, D_K, D_V, _i64, attend_rows, counted_view, \
+    mapped_keys, num_pages, visible_count
 
 FP8_LATENT = 512
 FP8_ROPE = D_K - FP8_LATENT                      # 64
@@ -153,15 +153,23 @@ def dequant_page(page_bytes) -> np.ndarray:
 
 def gather_request_kv_fp8(pool, block_table, seqlens, b: int) -> np.ndarray:
     """K_b[j, :] for j < L_b (fp64 [L_b, 576]), paging as in the bf16 path:
-    token j is row j % 64 of page block_table[b][j // 64]."""
+    token j is row j % 64 of page block_table[b][j // 64]; positions without
+    a page (slot past the row, id outside the pool) come back as zero rows,
+    which the attention leaves out."""
     pool8 = _u8(pool).reshape(-1, FP8_PAGE_BYTES)
     bt = _i64(block_table)
     L = int(_i64(seqlens)[b])
     n = num_pages(L)
     if n == 0:
         return np.zeros((0, D_K), dtype=np.float64)
-    K = np.concatenate([dequant_page(pool8[int(p)]) for p in bt[b, :n]], axis=0)
-    return K[:L]
+    blocks = []
+    for slot in range(n):
+        p = int(bt[b, slot]) if slot < bt.shape[1] else -1
+        if 0 <= p < pool8.shape[0]:
+            blocks.append(dequant_page(pool8[p]))
+        else:
+            blocks.append(np.zeros((BLOCK_SIZE, D_K), dtype=np.float64))
+    return np.concatenate(blocks, axis=0)[:L]
 
 
 def decode_fp8(q, pool, block_table, seqlens, scale: float, causal: bool, requests=None):
@@ -184,7 +192,9 @@ def decode_fp8(q, pool, block_table, seqlens, scale: float, causal: bool, reques
         qrows = qf[b].reshape(s_q * h_q, dk)
         nvis = np.array([visible_count(L, s_q, r // h_q, causal)
                          for r in range(s_q * h_q)], dtype=np.int64)
-        Ob, lb = attend_rows(qrows, K, scale, nvis)
+        n_pool = _u8(pool).reshape(-1, FP8_PAGE_BYTES).shape[0]
+        Kc, nvis_c = counted_view(K, mapped_keys(block_table, seqlens, b, n_pool), nvis)
+        Ob, lb = attend_rows(qrows, Kc, scale, nvis_c)
         O[b] = Ob.reshape(s_q, h_q, D_V)
         LSE[b] = lb.reshape(s_q, h_q)
     return O, LSE
