@@ -36,9 +36,10 @@
  *     q, kcache and out must be 16-byte aligned; int32 and fp32 buffers
  *     4-byte aligned; workspace 256-byte aligned.
  *   - Device data (seqlens, block_table) is not visible to host validation.
- *     Page ids outside [0, num_blocks) and table slots at or beyond bt_stride
- *     are read as all-zero key rows (never out of bounds); seqlens must lie in
- *     [0, bt_stride*64] for the result to be the attention defined above.
+ *     A position whose table slot is at or beyond bt_stride, or whose slot
+ *     holds a page id outside [0, num_blocks), holds no key: it is left out of
+ *     the attention (nothing is read there), in the dense mode as in the
+ *     sparse mode.  A row with no key left gets O = 0, LSE = -inf.
  */
 #ifndef MLA_DECODE_H_
 #define MLA_DECODE_H_

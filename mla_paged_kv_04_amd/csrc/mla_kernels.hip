@@ -361,6 +361,12 @@ __device__ __forceinline__ bool before_end(const DecodeArgs& a, int b, int k, in
 }
 
 // Keys of request b: its length, or the fixed entry count of the sparse mode.
+// The page id in table slot k of request b; -1 for a slot at or beyond the
+// table's column count.
+__device__ __forceinline__ int unit_page(const DecodeArgs& a, int b, int k) {
+  return k < a.bt_stride ? ldc(a.block_table + (long long)b * a.bt_stride + k) : -1;
+}
+
 __device__ __forceinline__ int seqlen_of(const DecodeArgs& a, int b) {
   if (a.const_len > 0) return b < a.batch ? a.const_len : 0;
   return b < a.batch ? ldc(a.seqlens + b) : 0;
@@ -910,10 +916,14 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     float m_run = -INFINITY, l_run = 0.f;
     int lim = 0, lim_min = 0, n = 0, pbeg = 0;
     bool new_piece = true;
+    // dense mode: the page id of the unit (loaded before the barrier that
+    // precedes the unit); a slot that names no page of the pool holds no keys
+    int pg = SP ? 0 : unit_page(a, cb, ck);
     int t = 0;
     while (true) {
       wg_barrier();   // unit t landed; P of unit t-2 consumed
       const int b = cb, k = ck, h = ch;
+      const bool pvalid = SP || (pg >= 0 && (long long)pg < a.num_blocks);
       if (new_piece) {
         n = n_pages(cL);
         pbeg = k;
@@ -1029,14 +1039,15 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       // ---- online softmax of row_own (fp32, base 2, lazy rescale) ----
       {
         const int key0 = k * kBlock + h * kHalfRows + 4 * g;
-        const bool need_mask = k * kBlock + (h + 1) * kHalfRows > lim_min;
+        const bool need_mask = !pvalid || k * kBlock + (h + 1) * kHalfRows > lim_min;
+        const int lim_u = pvalid ? lim : -1;
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             float xv = s[kt][v] * a.scale_log2;
-            if (need_mask && key0 + kt * 16 + v >= lim) xv = -INFINITY;
+            if (need_mask && key0 + kt * 16 + v >= lim_u) xv = -INFINITY;
             if (SP && !((vm >> (kt * 16 + 4 * g + v)) & 1u)) xv = -INFINITY;
             s[kt][v] = xv;
             mx = fmaxf(mx, xv);
@@ -1089,6 +1100,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P, alpha, flags, sums written
       ++t;
       if (!more) break;
+      if (!SP) pg = unit_page(a, cb, ck);
     }
     wg_barrier();   // the value waves' last product may start
   } else {
@@ -1354,12 +1366,779 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
   }
 }
 
-// Rows per workgroup tile.
+// --------------------------------------------------------------------------
+// Row-wave kernel for tiles of 128 query rows (s_q*h_q a multiple of 128,
+// bf16 cache, dense mode).  Four waves, one per SIMD, each owning 32 query
+// rows end to end, so nothing but the page ring is shared:
+//   scores  S^T[key][row] = K . Q^T on v_mfma_f32_32x32x16_bf16: A = 32 keys x
+//           16 dims of the LDS unit (ds_read_b128), B = Q^T held in VGPRs for
+//           the piece (32 rows x 576 dims = 144 VGPRs);
+//   softmax the C layout gives lane l row l % 32 and 16 of the unit's 32 keys
+//           (the other 16 in lane l ^ 32): in-lane max, one permlane32 swap,
+//           exp2; the running sum stays per lane until the piece ends;
+//   values  O^T[dim][row] += V^T . P^T on the same MFMA: A = 32 dims x 16 keys
+//           read with ds_read_b64_tr_b16 (two 4-key reads per operand), B = the
+//           lane's own probabilities, in the key order the score C layout
+//           already holds (key 8j + 4h + i of the unit is held by lane half h
+//           as element 4j + i; step u of the value product takes j = 2u,
+//           2u + 1), so P never leaves the registers; O^T (32 rows x 512 dims,
+//           fp32) is 256 accumulator registers and every row's rescale and
+//           normalisation are lane-local.
+// The wave computes scores of unit t and values of unit t-1 in one phase,
+// one workgroup barrier per unit, over the same four-buffer ring of 36 KB
+// half-page units as the ws kernel (two units in flight; every wave issues
+// 9 of a unit's 36 direct-to-LDS slots).  A 128-row tile puts each page into
+// LDS once per part (the 64-row ws tiles load it twice, once per tile).
+// --------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kRWThreads = 256;
+constexpr int kRWRows = 128;
+
+// 16-byte unit swizzle of row r in this kernel's unit buffers: unit c is
+// stored at c ^ rw_swizzle(r), inside its aligned group of 8 (72 units per
+// row).  Both read patterns of the kernel then hit every LDS bank at most
+// once per 256 bytes: the score operand (8 consecutive rows at one unit per
+// 8 lanes: even and odd rows differ by 128 bytes, and the XOR takes four
+// distinct values on the even and on the odd rows of any 8) and the
+// transposed value operand (per 32 lanes 4 consecutive rows x 4 consecutive
+// units of an aligned group of 4: bit 2 of the XOR follows row bit 1, so
+// rows r and r + 2 land in the two halves of the group of 8).  The r & 7
+// swizzle of the ws kernel puts rows r and r + 2 of that value pattern on
+// the same banks.
+__device__ __forceinline__ int rw_swizzle(int r) { return ((r & 2) << 1) | ((r & 4) >> 1); }
+
+// Page validity of unit (b, k): its table slot exists and names a page of
+// the pool.  Units of invalid pages are zero-filled by the loads and their
+// keys do not count.
+__device__ __forceinline__ bool page_ok(const DecodeArgs& a, int b, int k) {
+  if (k >= a.bt_stride) return false;
+  const int page = ldc(a.block_table + (long long)b * a.bt_stride + k);
+  return page >= 0 && (long long)page < a.num_blocks;
+}
+
+// The score accumulator is kept in VGPRs (the softmax reads it with VALU
+// instructions) while the 256 output accumulators take the AGPRs: the
+// product is written as inline asm with a VGPR constraint on the
+// accumulator (early-clobber where it is only written: a product's result
+// must not share registers with its operands).  The compiler does not see
+// these asm statements as matrix products, so the asm carries the hazard
+// waits itself: five wait states
+// before each product (a VALU write of an operand register, e.g. a move the
+// compiler placed just before, must be that far ahead of the read);
+// consecutive products on the same accumulator of the same shape need none
+// between them.  The last product of a chain, score_mfma_last, waits out
+// the wait states before a VALU instruction may read its result (a 16-pass
+// product: at most 19; 24 are inserted) inside its own asm block: the
+// compiler may place a copy of the accumulator right after the statement
+// that produced it, and that copy must already see the result.
+#define MLA_SACC "{v[236:251]}"
+__device__ __forceinline__ void score_mfma_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC(s) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void score_mfma(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC(s) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void score_mfma_last(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+" MLA_SACC(s)
+               : "v"(k), "v"(q));
+}
+// The 256 output accumulators of a wave (O^T for its 32 rows x 512 dims,
+// fp32) live in fixed AGPRs, block db of 32 dims in a[16db .. 16db+15], and
+// are touched only by the inline asm below, which names the registers it
+// writes as clobbers.  The compiler therefore never holds them (it keeps Q,
+// the scores and everything else in VGPRs, which fit) and never moves them
+// through VGPRs.  A test checks the built code for AGPR writes outside these
+// asm blocks.
+// ---- output accumulators in fixed AGPRs (block db: a[16db .. 16db+15]) ----
+#define MLA_AGPR_CLOBBERS_ALL \
+  "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15", \
+  "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31", \
+  "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47", \
+  "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63", \
+  "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79", \
+  "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95", \
+  "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111", \
+  "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", \
+  "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143", \
+  "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159", \
+  "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175", \
+  "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191", \
+  "a192", "a193", "a194", "a195", "a196", "a197", "a198", "a199", "a200", "a201", "a202", "a203", "a204", "a205", "a206", "a207", \
+  "a208", "a209", "a210", "a211", "a212", "a213", "a214", "a215", "a216", "a217", "a218", "a219", "a220", "a221", "a222", "a223", \
+  "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", "a234", "a235", "a236", "a237", "a238", "a239", \
+  "a240", "a241", "a242", "a243", "a244", "a245", "a246", "a247", "a248", "a249", "a250", "a251", "a252", "a253", "a254", "a255"
+
+#define MLA_AGPR_CLOBBERS_B0 "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15"
+#define MLA_AGPR_CLOBBERS_B1 "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31"
+#define MLA_AGPR_CLOBBERS_B2 "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47"
+#define MLA_AGPR_CLOBBERS_B3 "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63"
+#define MLA_AGPR_CLOBBERS_B4 "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79"
+#define MLA_AGPR_CLOBBERS_B5 "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95"
+#define MLA_AGPR_CLOBBERS_B6 "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111"
+#define MLA_AGPR_CLOBBERS_B7 "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127"
+#define MLA_AGPR_CLOBBERS_B8 "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143"
+#define MLA_AGPR_CLOBBERS_B9 "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159"
+#define MLA_AGPR_CLOBBERS_B10 "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175"
+#define MLA_AGPR_CLOBBERS_B11 "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191"
+#define MLA_AGPR_CLOBBERS_B12 "a192", "a193", "a194", "a195", "a196", "a197", "a198", "a199", "a200", "a201", "a202", "a203", "a204", "a205", "a206", "a207"
+#define MLA_AGPR_CLOBBERS_B13 "a208", "a209", "a210", "a211", "a212", "a213", "a214", "a215", "a216", "a217", "a218", "a219", "a220", "a221", "a222", "a223"
+#define MLA_AGPR_CLOBBERS_B14 "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", "a234", "a235", "a236", "a237", "a238", "a239"
+#define MLA_AGPR_CLOBBERS_B15 "a240", "a241", "a242", "a243", "a244", "a245", "a246", "a247", "a248", "a249", "a250", "a251", "a252", "a253", "a254", "a255"
+
+template <int DB>
+__device__ __forceinline__ void acc_mfma(const bf16x8& v, const bf16x8& p) {
+  if constexpr (DB == 0) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[0:15], %0, %1, a[0:15]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B0);
+  } else if constexpr (DB == 1) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[16:31], %0, %1, a[16:31]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B1);
+  } else if constexpr (DB == 2) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[32:47], %0, %1, a[32:47]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B2);
+  } else if constexpr (DB == 3) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[48:63], %0, %1, a[48:63]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B3);
+  } else if constexpr (DB == 4) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[64:79], %0, %1, a[64:79]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B4);
+  } else if constexpr (DB == 5) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[80:95], %0, %1, a[80:95]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B5);
+  } else if constexpr (DB == 6) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[96:111], %0, %1, a[96:111]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B6);
+  } else if constexpr (DB == 7) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[112:127], %0, %1, a[112:127]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B7);
+  } else if constexpr (DB == 8) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[128:143], %0, %1, a[128:143]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B8);
+  } else if constexpr (DB == 9) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[144:159], %0, %1, a[144:159]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B9);
+  } else if constexpr (DB == 10) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[160:175], %0, %1, a[160:175]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B10);
+  } else if constexpr (DB == 11) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[176:191], %0, %1, a[176:191]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B11);
+  } else if constexpr (DB == 12) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[192:207], %0, %1, a[192:207]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B12);
+  } else if constexpr (DB == 13) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[208:223], %0, %1, a[208:223]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B13);
+  } else if constexpr (DB == 14) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[224:239], %0, %1, a[224:239]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B14);
+  } else if constexpr (DB == 15) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[240:255], %0, %1, a[240:255]" ::"v"(v), "v"(p)
+                 : MLA_AGPR_CLOBBERS_B15);
+  }
+}
+
+template <int DB>
+__device__ __forceinline__ void acc_read(float (&e)[16]) {
+  if constexpr (DB == 0) {
+    asm volatile("v_accvgpr_read_b32 %0, a0\n\tv_accvgpr_read_b32 %1, a1\n\tv_accvgpr_read_b32 %2, a2\n\tv_accvgpr_read_b32 %3, a3\n\tv_accvgpr_read_b32 %4, a4\n\tv_accvgpr_read_b32 %5, a5\n\tv_accvgpr_read_b32 %6, a6\n\tv_accvgpr_read_b32 %7, a7\n\tv_accvgpr_read_b32 %8, a8\n\tv_accvgpr_read_b32 %9, a9\n\tv_accvgpr_read_b32 %10, a10\n\tv_accvgpr_read_b32 %11, a11\n\tv_accvgpr_read_b32 %12, a12\n\tv_accvgpr_read_b32 %13, a13\n\tv_accvgpr_read_b32 %14, a14\n\tv_accvgpr_read_b32 %15, a15"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 1) {
+    asm volatile("v_accvgpr_read_b32 %0, a16\n\tv_accvgpr_read_b32 %1, a17\n\tv_accvgpr_read_b32 %2, a18\n\tv_accvgpr_read_b32 %3, a19\n\tv_accvgpr_read_b32 %4, a20\n\tv_accvgpr_read_b32 %5, a21\n\tv_accvgpr_read_b32 %6, a22\n\tv_accvgpr_read_b32 %7, a23\n\tv_accvgpr_read_b32 %8, a24\n\tv_accvgpr_read_b32 %9, a25\n\tv_accvgpr_read_b32 %10, a26\n\tv_accvgpr_read_b32 %11, a27\n\tv_accvgpr_read_b32 %12, a28\n\tv_accvgpr_read_b32 %13, a29\n\tv_accvgpr_read_b32 %14, a30\n\tv_accvgpr_read_b32 %15, a31"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 2) {
+    asm volatile("v_accvgpr_read_b32 %0, a32\n\tv_accvgpr_read_b32 %1, a33\n\tv_accvgpr_read_b32 %2, a34\n\tv_accvgpr_read_b32 %3, a35\n\tv_accvgpr_read_b32 %4, a36\n\tv_accvgpr_read_b32 %5, a37\n\tv_accvgpr_read_b32 %6, a38\n\tv_accvgpr_read_b32 %7, a39\n\tv_accvgpr_read_b32 %8, a40\n\tv_accvgpr_read_b32 %9, a41\n\tv_accvgpr_read_b32 %10, a42\n\tv_accvgpr_read_b32 %11, a43\n\tv_accvgpr_read_b32 %12, a44\n\tv_accvgpr_read_b32 %13, a45\n\tv_accvgpr_read_b32 %14, a46\n\tv_accvgpr_read_b32 %15, a47"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 3) {
+    asm volatile("v_accvgpr_read_b32 %0, a48\n\tv_accvgpr_read_b32 %1, a49\n\tv_accvgpr_read_b32 %2, a50\n\tv_accvgpr_read_b32 %3, a51\n\tv_accvgpr_read_b32 %4, a52\n\tv_accvgpr_read_b32 %5, a53\n\tv_accvgpr_read_b32 %6, a54\n\tv_accvgpr_read_b32 %7, a55\n\tv_accvgpr_read_b32 %8, a56\n\tv_accvgpr_read_b32 %9, a57\n\tv_accvgpr_read_b32 %10, a58\n\tv_accvgpr_read_b32 %11, a59\n\tv_accvgpr_read_b32 %12, a60\n\tv_accvgpr_read_b32 %13, a61\n\tv_accvgpr_read_b32 %14, a62\n\tv_accvgpr_read_b32 %15, a63"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 4) {
+    asm volatile("v_accvgpr_read_b32 %0, a64\n\tv_accvgpr_read_b32 %1, a65\n\tv_accvgpr_read_b32 %2, a66\n\tv_accvgpr_read_b32 %3, a67\n\tv_accvgpr_read_b32 %4, a68\n\tv_accvgpr_read_b32 %5, a69\n\tv_accvgpr_read_b32 %6, a70\n\tv_accvgpr_read_b32 %7, a71\n\tv_accvgpr_read_b32 %8, a72\n\tv_accvgpr_read_b32 %9, a73\n\tv_accvgpr_read_b32 %10, a74\n\tv_accvgpr_read_b32 %11, a75\n\tv_accvgpr_read_b32 %12, a76\n\tv_accvgpr_read_b32 %13, a77\n\tv_accvgpr_read_b32 %14, a78\n\tv_accvgpr_read_b32 %15, a79"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 5) {
+    asm volatile("v_accvgpr_read_b32 %0, a80\n\tv_accvgpr_read_b32 %1, a81\n\tv_accvgpr_read_b32 %2, a82\n\tv_accvgpr_read_b32 %3, a83\n\tv_accvgpr_read_b32 %4, a84\n\tv_accvgpr_read_b32 %5, a85\n\tv_accvgpr_read_b32 %6, a86\n\tv_accvgpr_read_b32 %7, a87\n\tv_accvgpr_read_b32 %8, a88\n\tv_accvgpr_read_b32 %9, a89\n\tv_accvgpr_read_b32 %10, a90\n\tv_accvgpr_read_b32 %11, a91\n\tv_accvgpr_read_b32 %12, a92\n\tv_accvgpr_read_b32 %13, a93\n\tv_accvgpr_read_b32 %14, a94\n\tv_accvgpr_read_b32 %15, a95"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 6) {
+    asm volatile("v_accvgpr_read_b32 %0, a96\n\tv_accvgpr_read_b32 %1, a97\n\tv_accvgpr_read_b32 %2, a98\n\tv_accvgpr_read_b32 %3, a99\n\tv_accvgpr_read_b32 %4, a100\n\tv_accvgpr_read_b32 %5, a101\n\tv_accvgpr_read_b32 %6, a102\n\tv_accvgpr_read_b32 %7, a103\n\tv_accvgpr_read_b32 %8, a104\n\tv_accvgpr_read_b32 %9, a105\n\tv_accvgpr_read_b32 %10, a106\n\tv_accvgpr_read_b32 %11, a107\n\tv_accvgpr_read_b32 %12, a108\n\tv_accvgpr_read_b32 %13, a109\n\tv_accvgpr_read_b32 %14, a110\n\tv_accvgpr_read_b32 %15, a111"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 7) {
+    asm volatile("v_accvgpr_read_b32 %0, a112\n\tv_accvgpr_read_b32 %1, a113\n\tv_accvgpr_read_b32 %2, a114\n\tv_accvgpr_read_b32 %3, a115\n\tv_accvgpr_read_b32 %4, a116\n\tv_accvgpr_read_b32 %5, a117\n\tv_accvgpr_read_b32 %6, a118\n\tv_accvgpr_read_b32 %7, a119\n\tv_accvgpr_read_b32 %8, a120\n\tv_accvgpr_read_b32 %9, a121\n\tv_accvgpr_read_b32 %10, a122\n\tv_accvgpr_read_b32 %11, a123\n\tv_accvgpr_read_b32 %12, a124\n\tv_accvgpr_read_b32 %13, a125\n\tv_accvgpr_read_b32 %14, a126\n\tv_accvgpr_read_b32 %15, a127"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 8) {
+    asm volatile("v_accvgpr_read_b32 %0, a128\n\tv_accvgpr_read_b32 %1, a129\n\tv_accvgpr_read_b32 %2, a130\n\tv_accvgpr_read_b32 %3, a131\n\tv_accvgpr_read_b32 %4, a132\n\tv_accvgpr_read_b32 %5, a133\n\tv_accvgpr_read_b32 %6, a134\n\tv_accvgpr_read_b32 %7, a135\n\tv_accvgpr_read_b32 %8, a136\n\tv_accvgpr_read_b32 %9, a137\n\tv_accvgpr_read_b32 %10, a138\n\tv_accvgpr_read_b32 %11, a139\n\tv_accvgpr_read_b32 %12, a140\n\tv_accvgpr_read_b32 %13, a141\n\tv_accvgpr_read_b32 %14, a142\n\tv_accvgpr_read_b32 %15, a143"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 9) {
+    asm volatile("v_accvgpr_read_b32 %0, a144\n\tv_accvgpr_read_b32 %1, a145\n\tv_accvgpr_read_b32 %2, a146\n\tv_accvgpr_read_b32 %3, a147\n\tv_accvgpr_read_b32 %4, a148\n\tv_accvgpr_read_b32 %5, a149\n\tv_accvgpr_read_b32 %6, a150\n\tv_accvgpr_read_b32 %7, a151\n\tv_accvgpr_read_b32 %8, a152\n\tv_accvgpr_read_b32 %9, a153\n\tv_accvgpr_read_b32 %10, a154\n\tv_accvgpr_read_b32 %11, a155\n\tv_accvgpr_read_b32 %12, a156\n\tv_accvgpr_read_b32 %13, a157\n\tv_accvgpr_read_b32 %14, a158\n\tv_accvgpr_read_b32 %15, a159"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 10) {
+    asm volatile("v_accvgpr_read_b32 %0, a160\n\tv_accvgpr_read_b32 %1, a161\n\tv_accvgpr_read_b32 %2, a162\n\tv_accvgpr_read_b32 %3, a163\n\tv_accvgpr_read_b32 %4, a164\n\tv_accvgpr_read_b32 %5, a165\n\tv_accvgpr_read_b32 %6, a166\n\tv_accvgpr_read_b32 %7, a167\n\tv_accvgpr_read_b32 %8, a168\n\tv_accvgpr_read_b32 %9, a169\n\tv_accvgpr_read_b32 %10, a170\n\tv_accvgpr_read_b32 %11, a171\n\tv_accvgpr_read_b32 %12, a172\n\tv_accvgpr_read_b32 %13, a173\n\tv_accvgpr_read_b32 %14, a174\n\tv_accvgpr_read_b32 %15, a175"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 11) {
+    asm volatile("v_accvgpr_read_b32 %0, a176\n\tv_accvgpr_read_b32 %1, a177\n\tv_accvgpr_read_b32 %2, a178\n\tv_accvgpr_read_b32 %3, a179\n\tv_accvgpr_read_b32 %4, a180\n\tv_accvgpr_read_b32 %5, a181\n\tv_accvgpr_read_b32 %6, a182\n\tv_accvgpr_read_b32 %7, a183\n\tv_accvgpr_read_b32 %8, a184\n\tv_accvgpr_read_b32 %9, a185\n\tv_accvgpr_read_b32 %10, a186\n\tv_accvgpr_read_b32 %11, a187\n\tv_accvgpr_read_b32 %12, a188\n\tv_accvgpr_read_b32 %13, a189\n\tv_accvgpr_read_b32 %14, a190\n\tv_accvgpr_read_b32 %15, a191"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 12) {
+    asm volatile("v_accvgpr_read_b32 %0, a192\n\tv_accvgpr_read_b32 %1, a193\n\tv_accvgpr_read_b32 %2, a194\n\tv_accvgpr_read_b32 %3, a195\n\tv_accvgpr_read_b32 %4, a196\n\tv_accvgpr_read_b32 %5, a197\n\tv_accvgpr_read_b32 %6, a198\n\tv_accvgpr_read_b32 %7, a199\n\tv_accvgpr_read_b32 %8, a200\n\tv_accvgpr_read_b32 %9, a201\n\tv_accvgpr_read_b32 %10, a202\n\tv_accvgpr_read_b32 %11, a203\n\tv_accvgpr_read_b32 %12, a204\n\tv_accvgpr_read_b32 %13, a205\n\tv_accvgpr_read_b32 %14, a206\n\tv_accvgpr_read_b32 %15, a207"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 13) {
+    asm volatile("v_accvgpr_read_b32 %0, a208\n\tv_accvgpr_read_b32 %1, a209\n\tv_accvgpr_read_b32 %2, a210\n\tv_accvgpr_read_b32 %3, a211\n\tv_accvgpr_read_b32 %4, a212\n\tv_accvgpr_read_b32 %5, a213\n\tv_accvgpr_read_b32 %6, a214\n\tv_accvgpr_read_b32 %7, a215\n\tv_accvgpr_read_b32 %8, a216\n\tv_accvgpr_read_b32 %9, a217\n\tv_accvgpr_read_b32 %10, a218\n\tv_accvgpr_read_b32 %11, a219\n\tv_accvgpr_read_b32 %12, a220\n\tv_accvgpr_read_b32 %13, a221\n\tv_accvgpr_read_b32 %14, a222\n\tv_accvgpr_read_b32 %15, a223"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 14) {
+    asm volatile("v_accvgpr_read_b32 %0, a224\n\tv_accvgpr_read_b32 %1, a225\n\tv_accvgpr_read_b32 %2, a226\n\tv_accvgpr_read_b32 %3, a227\n\tv_accvgpr_read_b32 %4, a228\n\tv_accvgpr_read_b32 %5, a229\n\tv_accvgpr_read_b32 %6, a230\n\tv_accvgpr_read_b32 %7, a231\n\tv_accvgpr_read_b32 %8, a232\n\tv_accvgpr_read_b32 %9, a233\n\tv_accvgpr_read_b32 %10, a234\n\tv_accvgpr_read_b32 %11, a235\n\tv_accvgpr_read_b32 %12, a236\n\tv_accvgpr_read_b32 %13, a237\n\tv_accvgpr_read_b32 %14, a238\n\tv_accvgpr_read_b32 %15, a239"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  } else if constexpr (DB == 15) {
+    asm volatile("v_accvgpr_read_b32 %0, a240\n\tv_accvgpr_read_b32 %1, a241\n\tv_accvgpr_read_b32 %2, a242\n\tv_accvgpr_read_b32 %3, a243\n\tv_accvgpr_read_b32 %4, a244\n\tv_accvgpr_read_b32 %5, a245\n\tv_accvgpr_read_b32 %6, a246\n\tv_accvgpr_read_b32 %7, a247\n\tv_accvgpr_read_b32 %8, a248\n\tv_accvgpr_read_b32 %9, a249\n\tv_accvgpr_read_b32 %10, a250\n\tv_accvgpr_read_b32 %11, a251\n\tv_accvgpr_read_b32 %12, a252\n\tv_accvgpr_read_b32 %13, a253\n\tv_accvgpr_read_b32 %14, a254\n\tv_accvgpr_read_b32 %15, a255"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]), "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]), "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15]));
+  }
+}
+// all 256 accumulators to zero: 16 products of zero operands with no accumulation
+// (the trailing wait states keep the operand register unwritten while the
+// last products may still read it)
+__device__ __forceinline__ void acc_zero_all(const bf16x8& z) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[0:15], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[16:31], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[32:47], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[48:63], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[64:79], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[80:95], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[96:111], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[112:127], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[128:143], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[144:159], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[160:175], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[176:191], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[192:207], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[208:223], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[224:239], %0, %0, 0\n\tv_mfma_f32_32x32x16_bf16 a[240:255], %0, %0, 0\n\ts_nop 7\n\ts_nop 7" ::"v"(z) : MLA_AGPR_CLOBBERS_ALL);
+}
+
+// all 256 accumulators times the lane's x (the wait states of a 16-pass
+// product before the first read, and of a VALU write before a product
+// reads the register as its accumulator, are included)
+__device__ __forceinline__ void acc_scale_all(float x) {
+  float t0, t1, t2, t3;
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_accvgpr_read_b32 %0, a0\n\tv_accvgpr_read_b32 %1, a1\n\tv_accvgpr_read_b32 %2, a2\n\tv_accvgpr_read_b32 %3, a3\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a0, %0\n\tv_accvgpr_write_b32 a1, %1\n\tv_accvgpr_write_b32 a2, %2\n\tv_accvgpr_write_b32 a3, %3\n\tv_accvgpr_read_b32 %0, a4\n\tv_accvgpr_read_b32 %1, a5\n\tv_accvgpr_read_b32 %2, a6\n\tv_accvgpr_read_b32 %3, a7\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a4, %0\n\tv_accvgpr_write_b32 a5, %1\n\tv_accvgpr_write_b32 a6, %2\n\tv_accvgpr_write_b32 a7, %3\n\tv_accvgpr_read_b32 %0, a8\n\tv_accvgpr_read_b32 %1, a9\n\tv_accvgpr_read_b32 %2, a10\n\tv_accvgpr_read_b32 %3, a11\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a8, %0\n\tv_accvgpr_write_b32 a9, %1\n\tv_accvgpr_write_b32 a10, %2\n\tv_accvgpr_write_b32 a11, %3\n\tv_accvgpr_read_b32 %0, a12\n\tv_accvgpr_read_b32 %1, a13\n\tv_accvgpr_read_b32 %2, a14\n\tv_accvgpr_read_b32 %3, a15\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a12, %0\n\tv_accvgpr_write_b32 a13, %1\n\tv_accvgpr_write_b32 a14, %2\n\tv_accvgpr_write_b32 a15, %3\n\tv_accvgpr_read_b32 %0, a16\n\tv_accvgpr_read_b32 %1, a17\n\tv_accvgpr_read_b32 %2, a18\n\tv_accvgpr_read_b32 %3, a19\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a16, %0\n\tv_accvgpr_write_b32 a17, %1\n\tv_accvgpr_write_b32 a18, %2\n\tv_accvgpr_write_b32 a19, %3\n\tv_accvgpr_read_b32 %0, a20\n\tv_accvgpr_read_b32 %1, a21\n\tv_accvgpr_read_b32 %2, a22\n\tv_accvgpr_read_b32 %3, a23\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a20, %0\n\tv_accvgpr_write_b32 a21, %1\n\tv_accvgpr_write_b32 a22, %2\n\tv_accvgpr_write_b32 a23, %3\n\tv_accvgpr_read_b32 %0, a24\n\tv_accvgpr_read_b32 %1, a25\n\tv_accvgpr_read_b32 %2, a26\n\tv_accvgpr_read_b32 %3, a27\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a24, %0\n\tv_accvgpr_write_b32 a25, %1\n\tv_accvgpr_write_b32 a26, %2\n\tv_accvgpr_write_b32 a27, %3\n\tv_accvgpr_read_b32 %0, a28\n\tv_accvgpr_read_b32 %1, a29\n\tv_accvgpr_read_b32 %2, a30\n\tv_accvgpr_read_b32 %3, a31\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a28, %0\n\tv_accvgpr_write_b32 a29, %1\n\tv_accvgpr_write_b32 a30, %2\n\tv_accvgpr_write_b32 a31, %3\n\tv_accvgpr_read_b32 %0, a32\n\tv_accvgpr_read_b32 %1, a33\n\tv_accvgpr_read_b32 %2, a34\n\tv_accvgpr_read_b32 %3, a35\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a32, %0\n\tv_accvgpr_write_b32 a33, %1\n\tv_accvgpr_write_b32 a34, %2\n\tv_accvgpr_write_b32 a35, %3\n\tv_accvgpr_read_b32 %0, a36\n\tv_accvgpr_read_b32 %1, a37\n\tv_accvgpr_read_b32 %2, a38\n\tv_accvgpr_read_b32 %3, a39\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a36, %0\n\tv_accvgpr_write_b32 a37, %1\n\tv_accvgpr_write_b32 a38, %2\n\tv_accvgpr_write_b32 a39, %3\n\tv_accvgpr_read_b32 %0, a40\n\tv_accvgpr_read_b32 %1, a41\n\tv_accvgpr_read_b32 %2, a42\n\tv_accvgpr_read_b32 %3, a43\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a40, %0\n\tv_accvgpr_write_b32 a41, %1\n\tv_accvgpr_write_b32 a42, %2\n\tv_accvgpr_write_b32 a43, %3\n\tv_accvgpr_read_b32 %0, a44\n\tv_accvgpr_read_b32 %1, a45\n\tv_accvgpr_read_b32 %2, a46\n\tv_accvgpr_read_b32 %3, a47\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a44, %0\n\tv_accvgpr_write_b32 a45, %1\n\tv_accvgpr_write_b32 a46, %2\n\tv_accvgpr_write_b32 a47, %3\n\tv_accvgpr_read_b32 %0, a48\n\tv_accvgpr_read_b32 %1, a49\n\tv_accvgpr_read_b32 %2, a50\n\tv_accvgpr_read_b32 %3, a51\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a48, %0\n\tv_accvgpr_write_b32 a49, %1\n\tv_accvgpr_write_b32 a50, %2\n\tv_accvgpr_write_b32 a51, %3\n\tv_accvgpr_read_b32 %0, a52\n\tv_accvgpr_read_b32 %1, a53\n\tv_accvgpr_read_b32 %2, a54\n\tv_accvgpr_read_b32 %3, a55\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a52, %0\n\tv_accvgpr_write_b32 a53, %1\n\tv_accvgpr_write_b32 a54, %2\n\tv_accvgpr_write_b32 a55, %3\n\tv_accvgpr_read_b32 %0, a56\n\tv_accvgpr_read_b32 %1, a57\n\tv_accvgpr_read_b32 %2, a58\n\tv_accvgpr_read_b32 %3, a59\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a56, %0\n\tv_accvgpr_write_b32 a57, %1\n\tv_accvgpr_write_b32 a58, %2\n\tv_accvgpr_write_b32 a59, %3\n\tv_accvgpr_read_b32 %0, a60\n\tv_accvgpr_read_b32 %1, a61\n\tv_accvgpr_read_b32 %2, a62\n\tv_accvgpr_read_b32 %3, a63\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a60, %0\n\tv_accvgpr_write_b32 a61, %1\n\tv_accvgpr_write_b32 a62, %2\n\tv_accvgpr_write_b32 a63, %3\n\tv_accvgpr_read_b32 %0, a64\n\tv_accvgpr_read_b32 %1, a65\n\tv_accvgpr_read_b32 %2, a66\n\tv_accvgpr_read_b32 %3, a67\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a64, %0\n\tv_accvgpr_write_b32 a65, %1\n\tv_accvgpr_write_b32 a66, %2\n\tv_accvgpr_write_b32 a67, %3\n\tv_accvgpr_read_b32 %0, a68\n\tv_accvgpr_read_b32 %1, a69\n\tv_accvgpr_read_b32 %2, a70\n\tv_accvgpr_read_b32 %3, a71\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a68, %0\n\tv_accvgpr_write_b32 a69, %1\n\tv_accvgpr_write_b32 a70, %2\n\tv_accvgpr_write_b32 a71, %3\n\tv_accvgpr_read_b32 %0, a72\n\tv_accvgpr_read_b32 %1, a73\n\tv_accvgpr_read_b32 %2, a74\n\tv_accvgpr_read_b32 %3, a75\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a72, %0\n\tv_accvgpr_write_b32 a73, %1\n\tv_accvgpr_write_b32 a74, %2\n\tv_accvgpr_write_b32 a75, %3\n\tv_accvgpr_read_b32 %0, a76\n\tv_accvgpr_read_b32 %1, a77\n\tv_accvgpr_read_b32 %2, a78\n\tv_accvgpr_read_b32 %3, a79\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a76, %0\n\tv_accvgpr_write_b32 a77, %1\n\tv_accvgpr_write_b32 a78, %2\n\tv_accvgpr_write_b32 a79, %3\n\tv_accvgpr_read_b32 %0, a80\n\tv_accvgpr_read_b32 %1, a81\n\tv_accvgpr_read_b32 %2, a82\n\tv_accvgpr_read_b32 %3, a83\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a80, %0\n\tv_accvgpr_write_b32 a81, %1\n\tv_accvgpr_write_b32 a82, %2\n\tv_accvgpr_write_b32 a83, %3\n\tv_accvgpr_read_b32 %0, a84\n\tv_accvgpr_read_b32 %1, a85\n\tv_accvgpr_read_b32 %2, a86\n\tv_accvgpr_read_b32 %3, a87\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a84, %0\n\tv_accvgpr_write_b32 a85, %1\n\tv_accvgpr_write_b32 a86, %2\n\tv_accvgpr_write_b32 a87, %3\n\tv_accvgpr_read_b32 %0, a88\n\tv_accvgpr_read_b32 %1, a89\n\tv_accvgpr_read_b32 %2, a90\n\tv_accvgpr_read_b32 %3, a91\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a88, %0\n\tv_accvgpr_write_b32 a89, %1\n\tv_accvgpr_write_b32 a90, %2\n\tv_accvgpr_write_b32 a91, %3\n\tv_accvgpr_read_b32 %0, a92\n\tv_accvgpr_read_b32 %1, a93\n\tv_accvgpr_read_b32 %2, a94\n\tv_accvgpr_read_b32 %3, a95\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a92, %0\n\tv_accvgpr_write_b32 a93, %1\n\tv_accvgpr_write_b32 a94, %2\n\tv_accvgpr_write_b32 a95, %3\n\tv_accvgpr_read_b32 %0, a96\n\tv_accvgpr_read_b32 %1, a97\n\tv_accvgpr_read_b32 %2, a98\n\tv_accvgpr_read_b32 %3, a99\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a96, %0\n\tv_accvgpr_write_b32 a97, %1\n\tv_accvgpr_write_b32 a98, %2\n\tv_accvgpr_write_b32 a99, %3\n\tv_accvgpr_read_b32 %0, a100\n\tv_accvgpr_read_b32 %1, a101\n\tv_accvgpr_read_b32 %2, a102\n\tv_accvgpr_read_b32 %3, a103\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a100, %0\n\tv_accvgpr_write_b32 a101, %1\n\tv_accvgpr_write_b32 a102, %2\n\tv_accvgpr_write_b32 a103, %3\n\tv_accvgpr_read_b32 %0, a104\n\tv_accvgpr_read_b32 %1, a105\n\tv_accvgpr_read_b32 %2, a106\n\tv_accvgpr_read_b32 %3, a107\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a104, %0\n\tv_accvgpr_write_b32 a105, %1\n\tv_accvgpr_write_b32 a106, %2\n\tv_accvgpr_write_b32 a107, %3\n\tv_accvgpr_read_b32 %0, a108\n\tv_accvgpr_read_b32 %1, a109\n\tv_accvgpr_read_b32 %2, a110\n\tv_accvgpr_read_b32 %3, a111\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a108, %0\n\tv_accvgpr_write_b32 a109, %1\n\tv_accvgpr_write_b32 a110, %2\n\tv_accvgpr_write_b32 a111, %3\n\tv_accvgpr_read_b32 %0, a112\n\tv_accvgpr_read_b32 %1, a113\n\tv_accvgpr_read_b32 %2, a114\n\tv_accvgpr_read_b32 %3, a115\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a112, %0\n\tv_accvgpr_write_b32 a113, %1\n\tv_accvgpr_write_b32 a114, %2\n\tv_accvgpr_write_b32 a115, %3\n\tv_accvgpr_read_b32 %0, a116\n\tv_accvgpr_read_b32 %1, a117\n\tv_accvgpr_read_b32 %2, a118\n\tv_accvgpr_read_b32 %3, a119\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a116, %0\n\tv_accvgpr_write_b32 a117, %1\n\tv_accvgpr_write_b32 a118, %2\n\tv_accvgpr_write_b32 a119, %3\n\tv_accvgpr_read_b32 %0, a120\n\tv_accvgpr_read_b32 %1, a121\n\tv_accvgpr_read_b32 %2, a122\n\tv_accvgpr_read_b32 %3, a123\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a120, %0\n\tv_accvgpr_write_b32 a121, %1\n\tv_accvgpr_write_b32 a122, %2\n\tv_accvgpr_write_b32 a123, %3\n\tv_accvgpr_read_b32 %0, a124\n\tv_accvgpr_read_b32 %1, a125\n\tv_accvgpr_read_b32 %2, a126\n\tv_accvgpr_read_b32 %3, a127\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a124, %0\n\tv_accvgpr_write_b32 a125, %1\n\tv_accvgpr_write_b32 a126, %2\n\tv_accvgpr_write_b32 a127, %3\n\tv_accvgpr_read_b32 %0, a128\n\tv_accvgpr_read_b32 %1, a129\n\tv_accvgpr_read_b32 %2, a130\n\tv_accvgpr_read_b32 %3, a131\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a128, %0\n\tv_accvgpr_write_b32 a129, %1\n\tv_accvgpr_write_b32 a130, %2\n\tv_accvgpr_write_b32 a131, %3\n\tv_accvgpr_read_b32 %0, a132\n\tv_accvgpr_read_b32 %1, a133\n\tv_accvgpr_read_b32 %2, a134\n\tv_accvgpr_read_b32 %3, a135\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a132, %0\n\tv_accvgpr_write_b32 a133, %1\n\tv_accvgpr_write_b32 a134, %2\n\tv_accvgpr_write_b32 a135, %3\n\tv_accvgpr_read_b32 %0, a136\n\tv_accvgpr_read_b32 %1, a137\n\tv_accvgpr_read_b32 %2, a138\n\tv_accvgpr_read_b32 %3, a139\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a136, %0\n\tv_accvgpr_write_b32 a137, %1\n\tv_accvgpr_write_b32 a138, %2\n\tv_accvgpr_write_b32 a139, %3\n\tv_accvgpr_read_b32 %0, a140\n\tv_accvgpr_read_b32 %1, a141\n\tv_accvgpr_read_b32 %2, a142\n\tv_accvgpr_read_b32 %3, a143\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a140, %0\n\tv_accvgpr_write_b32 a141, %1\n\tv_accvgpr_write_b32 a142, %2\n\tv_accvgpr_write_b32 a143, %3\n\tv_accvgpr_read_b32 %0, a144\n\tv_accvgpr_read_b32 %1, a145\n\tv_accvgpr_read_b32 %2, a146\n\tv_accvgpr_read_b32 %3, a147\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a144, %0\n\tv_accvgpr_write_b32 a145, %1\n\tv_accvgpr_write_b32 a146, %2\n\tv_accvgpr_write_b32 a147, %3\n\tv_accvgpr_read_b32 %0, a148\n\tv_accvgpr_read_b32 %1, a149\n\tv_accvgpr_read_b32 %2, a150\n\tv_accvgpr_read_b32 %3, a151\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a148, %0\n\tv_accvgpr_write_b32 a149, %1\n\tv_accvgpr_write_b32 a150, %2\n\tv_accvgpr_write_b32 a151, %3\n\tv_accvgpr_read_b32 %0, a152\n\tv_accvgpr_read_b32 %1, a153\n\tv_accvgpr_read_b32 %2, a154\n\tv_accvgpr_read_b32 %3, a155\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a152, %0\n\tv_accvgpr_write_b32 a153, %1\n\tv_accvgpr_write_b32 a154, %2\n\tv_accvgpr_write_b32 a155, %3\n\tv_accvgpr_read_b32 %0, a156\n\tv_accvgpr_read_b32 %1, a157\n\tv_accvgpr_read_b32 %2, a158\n\tv_accvgpr_read_b32 %3, a159\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a156, %0\n\tv_accvgpr_write_b32 a157, %1\n\tv_accvgpr_write_b32 a158, %2\n\tv_accvgpr_write_b32 a159, %3\n\tv_accvgpr_read_b32 %0, a160\n\tv_accvgpr_read_b32 %1, a161\n\tv_accvgpr_read_b32 %2, a162\n\tv_accvgpr_read_b32 %3, a163\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a160, %0\n\tv_accvgpr_write_b32 a161, %1\n\tv_accvgpr_write_b32 a162, %2\n\tv_accvgpr_write_b32 a163, %3\n\tv_accvgpr_read_b32 %0, a164\n\tv_accvgpr_read_b32 %1, a165\n\tv_accvgpr_read_b32 %2, a166\n\tv_accvgpr_read_b32 %3, a167\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a164, %0\n\tv_accvgpr_write_b32 a165, %1\n\tv_accvgpr_write_b32 a166, %2\n\tv_accvgpr_write_b32 a167, %3\n\tv_accvgpr_read_b32 %0, a168\n\tv_accvgpr_read_b32 %1, a169\n\tv_accvgpr_read_b32 %2, a170\n\tv_accvgpr_read_b32 %3, a171\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a168, %0\n\tv_accvgpr_write_b32 a169, %1\n\tv_accvgpr_write_b32 a170, %2\n\tv_accvgpr_write_b32 a171, %3\n\tv_accvgpr_read_b32 %0, a172\n\tv_accvgpr_read_b32 %1, a173\n\tv_accvgpr_read_b32 %2, a174\n\tv_accvgpr_read_b32 %3, a175\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a172, %0\n\tv_accvgpr_write_b32 a173, %1\n\tv_accvgpr_write_b32 a174, %2\n\tv_accvgpr_write_b32 a175, %3\n\tv_accvgpr_read_b32 %0, a176\n\tv_accvgpr_read_b32 %1, a177\n\tv_accvgpr_read_b32 %2, a178\n\tv_accvgpr_read_b32 %3, a179\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a176, %0\n\tv_accvgpr_write_b32 a177, %1\n\tv_accvgpr_write_b32 a178, %2\n\tv_accvgpr_write_b32 a179, %3\n\tv_accvgpr_read_b32 %0, a180\n\tv_accvgpr_read_b32 %1, a181\n\tv_accvgpr_read_b32 %2, a182\n\tv_accvgpr_read_b32 %3, a183\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a180, %0\n\tv_accvgpr_write_b32 a181, %1\n\tv_accvgpr_write_b32 a182, %2\n\tv_accvgpr_write_b32 a183, %3\n\tv_accvgpr_read_b32 %0, a184\n\tv_accvgpr_read_b32 %1, a185\n\tv_accvgpr_read_b32 %2, a186\n\tv_accvgpr_read_b32 %3, a187\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a184, %0\n\tv_accvgpr_write_b32 a185, %1\n\tv_accvgpr_write_b32 a186, %2\n\tv_accvgpr_write_b32 a187, %3\n\tv_accvgpr_read_b32 %0, a188\n\tv_accvgpr_read_b32 %1, a189\n\tv_accvgpr_read_b32 %2, a190\n\tv_accvgpr_read_b32 %3, a191\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a188, %0\n\tv_accvgpr_write_b32 a189, %1\n\tv_accvgpr_write_b32 a190, %2\n\tv_accvgpr_write_b32 a191, %3\n\tv_accvgpr_read_b32 %0, a192\n\tv_accvgpr_read_b32 %1, a193\n\tv_accvgpr_read_b32 %2, a194\n\tv_accvgpr_read_b32 %3, a195\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a192, %0\n\tv_accvgpr_write_b32 a193, %1\n\tv_accvgpr_write_b32 a194, %2\n\tv_accvgpr_write_b32 a195, %3\n\tv_accvgpr_read_b32 %0, a196\n\tv_accvgpr_read_b32 %1, a197\n\tv_accvgpr_read_b32 %2, a198\n\tv_accvgpr_read_b32 %3, a199\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a196, %0\n\tv_accvgpr_write_b32 a197, %1\n\tv_accvgpr_write_b32 a198, %2\n\tv_accvgpr_write_b32 a199, %3\n\tv_accvgpr_read_b32 %0, a200\n\tv_accvgpr_read_b32 %1, a201\n\tv_accvgpr_read_b32 %2, a202\n\tv_accvgpr_read_b32 %3, a203\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a200, %0\n\tv_accvgpr_write_b32 a201, %1\n\tv_accvgpr_write_b32 a202, %2\n\tv_accvgpr_write_b32 a203, %3\n\tv_accvgpr_read_b32 %0, a204\n\tv_accvgpr_read_b32 %1, a205\n\tv_accvgpr_read_b32 %2, a206\n\tv_accvgpr_read_b32 %3, a207\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a204, %0\n\tv_accvgpr_write_b32 a205, %1\n\tv_accvgpr_write_b32 a206, %2\n\tv_accvgpr_write_b32 a207, %3\n\tv_accvgpr_read_b32 %0, a208\n\tv_accvgpr_read_b32 %1, a209\n\tv_accvgpr_read_b32 %2, a210\n\tv_accvgpr_read_b32 %3, a211\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a208, %0\n\tv_accvgpr_write_b32 a209, %1\n\tv_accvgpr_write_b32 a210, %2\n\tv_accvgpr_write_b32 a211, %3\n\tv_accvgpr_read_b32 %0, a212\n\tv_accvgpr_read_b32 %1, a213\n\tv_accvgpr_read_b32 %2, a214\n\tv_accvgpr_read_b32 %3, a215\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a212, %0\n\tv_accvgpr_write_b32 a213, %1\n\tv_accvgpr_write_b32 a214, %2\n\tv_accvgpr_write_b32 a215, %3\n\tv_accvgpr_read_b32 %0, a216\n\tv_accvgpr_read_b32 %1, a217\n\tv_accvgpr_read_b32 %2, a218\n\tv_accvgpr_read_b32 %3, a219\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a216, %0\n\tv_accvgpr_write_b32 a217, %1\n\tv_accvgpr_write_b32 a218, %2\n\tv_accvgpr_write_b32 a219, %3\n\tv_accvgpr_read_b32 %0, a220\n\tv_accvgpr_read_b32 %1, a221\n\tv_accvgpr_read_b32 %2, a222\n\tv_accvgpr_read_b32 %3, a223\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a220, %0\n\tv_accvgpr_write_b32 a221, %1\n\tv_accvgpr_write_b32 a222, %2\n\tv_accvgpr_write_b32 a223, %3\n\tv_accvgpr_read_b32 %0, a224\n\tv_accvgpr_read_b32 %1, a225\n\tv_accvgpr_read_b32 %2, a226\n\tv_accvgpr_read_b32 %3, a227\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a224, %0\n\tv_accvgpr_write_b32 a225, %1\n\tv_accvgpr_write_b32 a226, %2\n\tv_accvgpr_write_b32 a227, %3\n\tv_accvgpr_read_b32 %0, a228\n\tv_accvgpr_read_b32 %1, a229\n\tv_accvgpr_read_b32 %2, a230\n\tv_accvgpr_read_b32 %3, a231\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a228, %0\n\tv_accvgpr_write_b32 a229, %1\n\tv_accvgpr_write_b32 a230, %2\n\tv_accvgpr_write_b32 a231, %3\n\tv_accvgpr_read_b32 %0, a232\n\tv_accvgpr_read_b32 %1, a233\n\tv_accvgpr_read_b32 %2, a234\n\tv_accvgpr_read_b32 %3, a235\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a232, %0\n\tv_accvgpr_write_b32 a233, %1\n\tv_accvgpr_write_b32 a234, %2\n\tv_accvgpr_write_b32 a235, %3\n\tv_accvgpr_read_b32 %0, a236\n\tv_accvgpr_read_b32 %1, a237\n\tv_accvgpr_read_b32 %2, a238\n\tv_accvgpr_read_b32 %3, a239\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a236, %0\n\tv_accvgpr_write_b32 a237, %1\n\tv_accvgpr_write_b32 a238, %2\n\tv_accvgpr_write_b32 a239, %3\n\tv_accvgpr_read_b32 %0, a240\n\tv_accvgpr_read_b32 %1, a241\n\tv_accvgpr_read_b32 %2, a242\n\tv_accvgpr_read_b32 %3, a243\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a240, %0\n\tv_accvgpr_write_b32 a241, %1\n\tv_accvgpr_write_b32 a242, %2\n\tv_accvgpr_write_b32 a243, %3\n\tv_accvgpr_read_b32 %0, a244\n\tv_accvgpr_read_b32 %1, a245\n\tv_accvgpr_read_b32 %2, a246\n\tv_accvgpr_read_b32 %3, a247\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a244, %0\n\tv_accvgpr_write_b32 a245, %1\n\tv_accvgpr_write_b32 a246, %2\n\tv_accvgpr_write_b32 a247, %3\n\tv_accvgpr_read_b32 %0, a248\n\tv_accvgpr_read_b32 %1, a249\n\tv_accvgpr_read_b32 %2, a250\n\tv_accvgpr_read_b32 %3, a251\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a248, %0\n\tv_accvgpr_write_b32 a249, %1\n\tv_accvgpr_write_b32 a250, %2\n\tv_accvgpr_write_b32 a251, %3\n\tv_accvgpr_read_b32 %0, a252\n\tv_accvgpr_read_b32 %1, a253\n\tv_accvgpr_read_b32 %2, a254\n\tv_accvgpr_read_b32 %3, a255\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\tv_accvgpr_write_b32 a252, %0\n\tv_accvgpr_write_b32 a253, %1\n\tv_accvgpr_write_b32 a254, %2\n\tv_accvgpr_write_b32 a255, %3\n\ts_nop 7"
+               : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+               : "v"(x)
+               : MLA_AGPR_CLOBBERS_ALL);
+}
+
+// the wait states of a 16-pass product before its accumulators are read
+__device__ __forceinline__ void acc_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+
+__device__ __forceinline__ void acc_mfma_i(int db, const bf16x8& v, const bf16x8& p) {
+  switch (db) {
+    case 0: acc_mfma<0>(v, p); break;
+    case 1: acc_mfma<1>(v, p); break;
+    case 2: acc_mfma<2>(v, p); break;
+    case 3: acc_mfma<3>(v, p); break;
+    case 4: acc_mfma<4>(v, p); break;
+    case 5: acc_mfma<5>(v, p); break;
+    case 6: acc_mfma<6>(v, p); break;
+    case 7: acc_mfma<7>(v, p); break;
+    case 8: acc_mfma<8>(v, p); break;
+    case 9: acc_mfma<9>(v, p); break;
+    case 10: acc_mfma<10>(v, p); break;
+    case 11: acc_mfma<11>(v, p); break;
+    case 12: acc_mfma<12>(v, p); break;
+    case 13: acc_mfma<13>(v, p); break;
+    case 14: acc_mfma<14>(v, p); break;
+    default: acc_mfma<15>(v, p); break;
+  }
+}
+
+__device__ __forceinline__ void acc_read_i(int db, float (&e)[16]) {
+  switch (db) {
+    case 0: acc_read<0>(e); break;
+    case 1: acc_read<1>(e); break;
+    case 2: acc_read<2>(e); break;
+    case 3: acc_read<3>(e); break;
+    case 4: acc_read<4>(e); break;
+    case 5: acc_read<5>(e); break;
+    case 6: acc_read<6>(e); break;
+    case 7: acc_read<7>(e); break;
+    case 8: acc_read<8>(e); break;
+    case 9: acc_read<9>(e); break;
+    case 10: acc_read<10>(e); break;
+    case 11: acc_read<11>(e); break;
+    case 12: acc_read<12>(e); break;
+    case 13: acc_read<13>(e); break;
+    case 14: acc_read<14>(e); break;
+    default: acc_read<15>(e); break;
+  }
+}
+
+__global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const DecodeArgs a) {
+  constexpr int NBUF = kWSBufs;
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kHalfBytes];
+  __shared__ int plan_lds[8];
+  __shared__ int so_lds[kPlanMaxBatch + 1];
+
+  const int tid = threadIdx.x;
+  const int w = uni(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 31;    // the lane's query row within the wave
+  const int lh = lane >> 5;    // lane half: keys 4lh + 8j + i of a 32-key unit
+
+  int part, rtile;
+  const int x = blockIdx.x;
+  const int R = a.row_tiles;
+  if (R > 1 && (a.num_parts % 8) == 0) {
+    part = (x / (8 * R)) * 8 + (x & 7);
+    rtile = (x >> 3) % R;
+  } else {
+    part = x / R;
+    rtile = x % R;
+  }
+  int b0, k0, b1, k1, first_split;
+  const bool inplan = a.inplan;
+  if (inplan) {
+    if (w == 0) {
+      plan_part_wave(a, part, plan_lds, so_lds);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (rtile == 0 && lane < kMetaInts)
+        a.tile_meta_out[part * kMetaInts + lane] = lane < 5 ? plan_lds[lane] : 0;
+      if (part == 0 && rtile == 0)
+        for (int b = lane; b <= a.batch; b += 64) a.split_offsets_out[b] = so_lds[b];
+    }
+    wg_barrier();
+    b0 = uni(plan_lds[0]);
+    k0 = uni(plan_lds[1]);
+    b1 = uni(plan_lds[2]);
+    k1 = uni(plan_lds[3]);
+    first_split = uni(plan_lds[4]);
+  } else {
+    const int32_t* tm = a.tile_meta + part * kMetaInts;
+    b0 = ldc(tm + 0);
+    k0 = ldc(tm + 1);
+    b1 = ldc(tm + 2);
+    k1 = ldc(tm + 3);
+    first_split = ldc(tm + 4);
+  }
+
+  int cb = b0, ck = k0, ch = 0;
+  seek(a, cb, ck, b1, k1);
+  if (!before_end(a, cb, ck, b1, k1)) return;   // uniform: empty part
+  int cL = seqlen_of(a, cb);
+  const int row = rtile * kRWRows + 32 * w + lr;   // < M (M is a multiple of 128)
+  const int tok = row / a.h_q;
+
+  auto piece_slot = [&](int b, int pbeg, int pend, int n, bool& whole) {
+    whole = pbeg == 0 && pend == n;
+    const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
+    if (whole) return 0LL;
+    return (long long)(inplan ? uni(so_lds[b]) : ldc(a.split_offsets + b)) + sidx;
+  };
+
+  // ---- LDS operand offsets (unit buffer relative; rows swizzled by rw_swizzle) ----
+  // K (score A operand) of step s: row lr, 16-byte unit 2s + lh, i.e.
+  // ko[s & 3] + 128 (s >> 2).
+  int ko[4];
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) ko[qd] = lr * kRowBytes + (((2 * qd + lh) ^ rw_swizzle(lr)) << 4);
+  // V (value A operand) of dim block db, key step u, read jj: 16-lane group G
+  // reads keys 16u + 8jj + 4(G >> 1) + (i >> 2), 8 bytes at dims
+  // 32db + 16(G & 1) + 4(i & 3); the transpose hands lane i the four keys of
+  // dim 32db + 16(G & 1) + i.  Offset: vo[db & 1] + (16u + 8jj) rows + 128 (db >> 1).
+  int vo[2];
+  {
+    const int G = lane >> 4, i = lane & 15;
+    const int vr = 4 * (G >> 1) + (i >> 2);
+    const int c0 = 2 * (G & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int d1 = 0; d1 < 2; ++d1)
+      vo[d1] = vr * kRowBytes + (((4 * d1 + c0) ^ rw_swizzle(vr)) << 4) + ((i & 1) << 3);
+  }
+
+  // ---- Q of the first piece (B operand of the score product) ----
+  bf16x8 qreg[36];
+  auto load_q = [&](int b) {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + ((long long)b * a.M + row) * kDK) + lh;
+#pragma unroll
+    for (int s = 0; s < 36; ++s) qreg[s] = qp[2 * s];
+  };
+  // The compiler's view of Q: every register has arrived (it then waits here,
+  // once per piece, instead of before the score products of every phase,
+  // where its count would also cover the page loads issued in between).
+  auto q_ready = [&]() {
+    asm volatile("" ::"v"(qreg[0]), "v"(qreg[1]), "v"(qreg[2]), "v"(qreg[3]), "v"(qreg[4]),
+                 "v"(qreg[5]), "v"(qreg[6]), "v"(qreg[7]), "v"(qreg[8]), "v"(qreg[9]),
+                 "v"(qreg[10]), "v"(qreg[11]), "v"(qreg[12]), "v"(qreg[13]), "v"(qreg[14]),
+                 "v"(qreg[15]), "v"(qreg[16]), "v"(qreg[17]));
+    asm volatile("" ::"v"(qreg[18]), "v"(qreg[19]), "v"(qreg[20]), "v"(qreg[21]), "v"(qreg[22]),
+                 "v"(qreg[23]), "v"(qreg[24]), "v"(qreg[25]), "v"(qreg[26]), "v"(qreg[27]),
+                 "v"(qreg[28]), "v"(qreg[29]), "v"(qreg[30]), "v"(qreg[31]), "v"(qreg[32]),
+                 "v"(qreg[33]), "v"(qreg[34]), "v"(qreg[35]));
+  };
+  load_q(cb);
+
+  // ---- page ring: issue cursor (ib, ik, ih) ----
+  // A unit is issued in two steps so that no scalar load waits on the issue
+  // path: prefetch_next() (at the end of a phase, before its barrier) moves
+  // the cursor and loads the next unit's page id; issue_setup() (at the start
+  // of the next phase) builds the buffer resource, records the page's
+  // validity in a four-unit ring and the 9 slots of this wave then go out one
+  // at a time between the score products (issue_slot).
+  int ib = cb, ik = ck, ih = 0, iL = cL;
+  int issued = 0;
+  int off[9];   // the global offsets of this wave's slots w, w + 4, ..., w + 32
+#pragma unroll
+  for (int m = 0; m < 9; ++m) {
+    const int p = 256 * m + tid;
+    const int r = p / kChunksPerRow;
+    const int pc = p - r * kChunksPerRow;
+    off[m] = r * kRowBytes + ((pc ^ rw_swizzle(r)) << 4);
+  }
+  bool pf_on = false;       // a unit is at the cursor
+  int pf_page = -1, pf_rows = 0;
+  bool hl_on = false;       // the slots of an issued unit are pending
+  HalfLoad hl;
+  uint32_t vring = 0;       // bit u & 3: unit u's page slot names a page of the pool
+  auto prefetch_next = [&](bool advance) {
+    if (advance) unit_next(a, ib, ik, ih, iL, b1, k1);
+    pf_on = before_end(a, ib, ik, b1, k1);
+    if (pf_on) {
+      const int rows = iL - ik * kBlock - ih * kHalfRows;
+      pf_rows = rows > kHalfRows ? kHalfRows : rows;
+      pf_page = ik < a.bt_stride ? ldc(a.block_table + (long long)ib * a.bt_stride + ik) : -1;
+    }
+  };
+  auto issue_setup = [&]() {
+    hl_on = pf_on;
+    if (hl_on) {
+      const bool in_pool = pf_page >= 0 && (long long)pf_page < a.num_blocks;
+      const bool ok = in_pool && pf_rows > 0;
+      const char* base = reinterpret_cast<const char*>(a.kcache) +
+                         (ok ? (long long)pf_page * kPageBytes + ih * kHalfBytes : 0);
+      const int nrec = uni(ok ? pf_rows * kRowBytes : 0);
+      hl.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, kRsrcWord3);
+      hl.m0 = uni(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((MLA_LDS char*)(smem + (issued % NBUF) * kHalfBytes)) +
+          w * 1024));
+      const uint32_t bit = 1u << (issued & 3);
+      vring = in_pool ? (vring | bit) : (vring & ~bit);
+      ++issued;
+    }
+  };
+  auto issue_slot = [&](int m) {
+    if (hl_on) half_load_slot(hl, off[m], m);
+  };
+  auto wait_unit = [&](int u) { wait_loads_behind<kHalfLoadsPerWave, NBUF - 2>(issued - u - 1); };
+
+  // units 0 and 1, all slots at once
+  prefetch_next(false);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    issue_setup();
+#pragma unroll
+    for (int m = 0; m < 9; ++m) issue_slot(m);
+    prefetch_next(true);
+  }
+  wait_unit(0);
+  q_ready();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wg_barrier();
+
+  const bf16x8 zero8 = bf16x8{};
+  acc_zero_all(zero8);
+
+  // ---- the pipeline ----
+  // Phase t: scores of unit t (the score chain) with the softmax of unit t-1
+  // interleaved between its products (the scores of unit t-1 are kept from the
+  // phase before), then the value product of unit t-1.  Units t-1 (values)
+  // and t (keys) are in the ring, t+1 and t+2 in flight.
+  //
+  // State of the unit whose softmax and values run in the phase (unit t-1):
+  f32x16 sp;                // its scores (S^T, raw q.k sums)
+  int u_k = 0, u_h = 0;     // its page and half
+  bool u_first = true;      // it starts a piece: the running max and sum restart
+  bool u_last = false;      // it ends a piece
+  bool u_valid = true;      // its page slot names a page of the pool
+  int u_lim = 0, u_lim_min = 0;
+  int u_b = 0, u_pbeg = 0, u_n = 0;
+  // running softmax state of the current piece (per row, lane-local)
+  float m_run = -INFINITY, l_run = 0.f;
+  // a finished piece whose O is written at the start of the next phase,
+  // before that phase's page loads (so that the end-of-phase page wait does
+  // not also wait for these stores)
+  bool e_pending = false;
+  float e_linv = 0.f;
+  int e_b = 0;
+  bool e_whole = false;
+  long long e_slot = 0;
+
+  // score-side piece state of the unit being scored (unit t)
+  int s_pbeg = ck, s_n = n_pages(cL);
+  int s_lim = a.causal ? cL - a.s_q + 1 + tok : cL;
+  int s_lim_min = a.causal ? cL - a.s_q + 1 : cL;
+  bool s_first = true;
+
+  auto value_epilogue = [&]() {
+    // O / l of the finished piece: bf16 to out for a whole request, fp32
+    // partial otherwise; then the accumulators restart
+    acc_drain();
+    if (e_whole) {
+      uint16_t* op = a.out + ((long long)e_b * a.M + row) * kDV + 4 * lh;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        float e[16];
+        acc_read_i(db, e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x4 bv = {(__bf16)(e[4 * j] * e_linv), (__bf16)(e[4 * j + 1] * e_linv),
+                             (__bf16)(e[4 * j + 2] * e_linv), (__bf16)(e[4 * j + 3] * e_linv)};
+          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j) = bv;
+        }
+      }
+    } else {
+      float* op = a.part_o + (e_slot * a.M + row) * kDV + 4 * lh;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        float e[16];
+        acc_read_i(db, e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = {e[4 * j] * e_linv, e[4 * j + 1] * e_linv, e[4 * j + 2] * e_linv,
+                           e[4 * j + 3] * e_linv};
+          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * j) = v;
+        }
+      }
+    }
+    acc_zero_all(zero8);
+  };
+
+  // Softmax of the held unit, in steps placed between the score products:
+  // step 0 takes the in-lane maximum (and masks, when the unit holds keys
+  // past the visible count or its page slot is invalid); step 1 the row
+  // maximum (one permlane32 swap) and the lazy-rescale decision; steps 2-9
+  // the exponentials, two keys each; step 10 the row-sum update.
+  // Exponent: exp2(x * cx - m) as one fma.  An unmasked unit keeps the raw
+  // q.k sums (x = s, cx = scale * log2 e; for a scale >= 0 the scaled maximum
+  // is the maximum of the raw sums times it); a masked unit is rewritten in
+  // place as scaled sums with -inf at the masked keys (cx = 1).
+  const bool scale_neg = a.scale_log2 < 0.f;
+  float mx = -INFINITY, neg_m = 0.f, cx = 1.f, alpha = 1.f, lsum = 0.f;
+  bool resc_any = false;
+  bf16x8 pv[2];
+  auto softmax_step = [&](int st) {
+    if (st == 0) {
+      if (u_first) {
+        m_run = -INFINITY;
+        l_run = 0.f;
+      }
+      const bool need_mask = scale_neg || !u_valid || u_k * kBlock + (u_h + 1) * kHalfRows > u_lim_min;
+      if (!need_mask) {
+        float m0 = fmaxf(fmaxf(sp[0], sp[1]), sp[2]);
+        float m1 = fmaxf(fmaxf(sp[3], sp[4]), sp[5]);
+        float m2 = fmaxf(fmaxf(sp[6], sp[7]), sp[8]);
+        float m3 = fmaxf(fmaxf(sp[9], sp[10]), sp[11]);
+        float m4 = fmaxf(fmaxf(sp[12], sp[13]), sp[14]);
+        m0 = fmaxf(fmaxf(m0, m1), m2);
+        m3 = fmaxf(fmaxf(m3, m4), sp[15]);
+        mx = fmaxf(m0, m3) * a.scale_log2;
+        cx = a.scale_log2;
+      } else {
+        asm volatile("");   // a branch of its own: the unmasked path does none of this
+        const int key0 = u_k * kBlock + u_h * kHalfRows + 4 * lh;   // element 4j + i: key0 + 8j + i
+        const int lim_u = u_valid ? u_lim : -1;
+        mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float xv = sp[4 * j + i] * a.scale_log2;
+            if (key0 + 8 * j + i >= lim_u) xv = -INFINITY;
+            sp[4 * j + i] = xv;
+            mx = fmaxf(mx, xv);
+          }
+        cx = 1.f;
+      }
+    } else if (st == 1) {
+      const unsigned mi = __float_as_uint(mx);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(mi, mi, false, false);
+      mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+      const float m_new = fmaxf(m_run, mx);
+      const bool grow = m_new > m_run + kRescaleSlack;
+      alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      // O of a piece is still zero when its first maximum arrives
+      resc_any = __any(grow && m_run != -INFINITY);
+      if (grow) m_run = m_new;
+      l_run *= alpha;
+      neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      lsum = 0.f;
+    } else if (st < 10) {
+      const int e0 = 2 * (st - 2);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[e0], cx, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[e0 + 1], cx, neg_m));
+      lsum += p0 + p1;
+      pv[e0 >> 3][e0 & 7] = (__bf16)p0;
+      pv[e0 >> 3][(e0 & 7) + 1] = (__bf16)p1;
+    } else {
+      l_run += lsum;
+    }
+  };
+
+  // the value product of the held unit: 16 dim blocks x 2 key steps, blocks
+  // innermost, V read D2 products ahead
+  auto value_product = [&](const char* vbuf) {
+    constexpr int D2 = 3;
+    bf16x4 vlo[D2 + 1], vhi[D2 + 1];
+    auto read_v = [&](int st) {
+      const int u = st >> 4, db = st & 15;
+      const char* vb = vbuf + vo[db & 1] + 128 * (db >> 1) + 16 * u * kRowBytes;
+      vlo[st % (D2 + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb));
+      vhi[st % (D2 + 1)] =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + 8 * kRowBytes));
+    };
+#pragma unroll
+    for (int st = 0; st < D2; ++st) read_v(st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + D2 < 32) read_v(i + D2);
+      const bf16x4 lo = vlo[i % (D2 + 1)], hi = vhi[i % (D2 + 1)];
+      const bf16x8 va = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc_mfma_i(i & 15, va, pv[i >> 4]);
+      asm volatile("" ::"v"(va));   // operand registers held past the product's issue
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the last products may still read P: wait states before its registers
+    // can be reused
+    asm volatile("s_nop 7" ::"v"(pv[0]), "v"(pv[1]));
+  };
+
+  // the held unit's piece end: its LSE out, its O queued for the next phase
+  auto piece_end = [&]() {
+    float lt = l_run;
+    {
+      const unsigned li = __float_as_uint(lt);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(li, li, false, false);
+      lt = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    }
+    const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
+    bool whole;
+    const long long slot = piece_slot(u_b, u_pbeg, (u_b == b1) ? k1 : u_n, u_n, whole);
+    if (lh == 0) {
+      if (whole)
+        a.lse[(long long)u_b * a.M + row] = lse2 * kLn2;
+      else
+        a.part_lse[slot * a.M + row] = lse2;
+    }
+    e_pending = true;
+    e_linv = lt > 0.f ? 1.f / lt : 0.f;
+    e_b = u_b;
+    e_whole = whole;
+    e_slot = slot;
+  };
+
+  // the score chain of unit t (K read D1 products ahead); with SOFTMAX the
+  // held unit's softmax steps sit between the products
+  constexpr int D1 = 3;
+  auto score_chain = [&](const char* kbuf, f32x16& sacc, bool with_softmax) {
+    constexpr int NK = D1 + 2;   // K operand ring: a slot is rewritten two steps after its product
+    bf16x8 ka[NK];
+    auto read_k = [&](int ks) {
+      ka[ks % NK] = *reinterpret_cast<const bf16x8*>(kbuf + ko[ks & 3] + 128 * (ks >> 2));
+    };
+#pragma unroll
+    for (int ks = 0; ks < D1; ++ks) read_k(ks);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 36; ++i) {
+      if (i + D1 < 36) read_k(i + D1);
+      if (i == 0)
+        score_mfma_first(sacc, ka[0], qreg[0]);
+      else if (i < 35)
+        score_mfma(sacc, ka[i % NK], qreg[i]);
+      else
+        score_mfma_last(sacc, ka[i % NK], qreg[i]);
+      if ((i & 3) == 1) issue_slot(i >> 2);
+      if (with_softmax && i >= 2 && (i & 1) == 0 && (i - 2) / 2 <= 10) softmax_step((i - 2) / 2);
+      // the products may still be reading their K operands: the registers of
+      // this step's and the previous step's operand stay allocated (no VALU
+      // result lands in them) until here
+      asm volatile("" ::"v"(ka[i % NK]), "v"(ka[(i + NK - 1) % NK]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- phase 0: scores of unit 0 only ----
+  {
+    issue_setup();   // unit 2
+    score_chain(smem, sp, false);
+    u_k = ck;
+    u_h = ch;
+    u_first = true;
+    u_valid = (vring & 1u) != 0;
+    u_lim = s_lim;
+    u_lim_min = s_lim_min;
+    u_b = cb;
+    u_pbeg = s_pbeg;
+    u_n = s_n;
+  }
+  int t = 1;
+  while (true) {
+    // advance the score cursor to unit t; the held unit t-1 ends its piece
+    // if unit t is in another request or does not exist
+    const int pb = cb;
+    unit_next(a, cb, ck, ch, cL, b1, k1);
+    const bool more = before_end(a, cb, ck, b1, k1);
+    s_first = !(more && cb == pb);
+    u_last = s_first;
+    if (!more) break;
+    if (s_first) {
+      s_pbeg = ck;
+      s_n = n_pages(cL);
+      s_lim = a.causal ? cL - a.s_q + 1 + tok : cL;
+      s_lim_min = a.causal ? cL - a.s_q + 1 : cL;
+    }
+    prefetch_next(true);   // completes while this wave waits at the barrier
+    wait_unit(t);
+    wg_barrier();   // unit t landed in every wave's slots; unit t-2's buffer is free
+
+    // ------- phase t: scores of unit t, softmax and values of unit t-1 -------
+    if (e_pending) {
+      value_epilogue();
+      e_pending = false;
+    }
+    if (s_first) {
+      // Q of the new piece, before this phase's page loads (so that waiting
+      // for it does not also wait for them: loads complete in order)
+      load_q(cb);
+      q_ready();
+    }
+    issue_setup();   // unit t+2 into the buffer of unit t-2
+    const char* kbuf = smem + (t % NBUF) * kHalfBytes;
+    const char* vbuf = smem + ((t + NBUF - 1) % NBUF) * kHalfBytes;
+    f32x16 sc;
+    score_chain(kbuf, sc, true);
+    if (resc_any) acc_scale_all(alpha);
+    value_product(vbuf);
+    if (u_last) piece_end();
+    // unit t becomes the held unit
+    sp = sc;
+    u_k = ck;
+    u_h = ch;
+    u_first = s_first;
+    u_valid = ((vring >> (t & 3)) & 1u) != 0;
+    u_lim = s_lim;
+    u_lim_min = s_lim_min;
+    u_b = cb;
+    u_pbeg = s_pbeg;
+    u_n = s_n;
+    ++t;
+  }
+  // ---------------- last phase: softmax and values of the last unit ----------------
+  // (its buffer is published: it was the score unit of the phase before)
+  if (e_pending) {
+    value_epilogue();
+    e_pending = false;
+  }
+#pragma unroll
+  for (int st = 0; st <= 10; ++st) softmax_step(st);
+  if (resc_any) acc_scale_all(alpha);
+  value_product(smem + ((t + NBUF - 1) % NBUF) * kHalfBytes);
+  piece_end();
+  value_epilogue();
+}
+
+// Rows per workgroup tile of the split plan: 128 when s_q*h_q is a multiple
+// of 128 (mla_rowwave_kernel), else the ws kernel's 16, 32 or 64.
 int tile_rows_for(int M) {
+  if (M % kRWRows == 0) return kRWRows;
   if (M <= 16) return 16;    // mla_splitkv_ws_kernel<1>
   if (M <= 32) return 32;    // mla_splitkv_ws_kernel<2>
-  return 64;                 // mla_splitkv_ws_kernel<4> (M = 128, 256: 2 or 4 row tiles)
+  return 64;                 // mla_splitkv_ws_kernel<4>
 }
+
+// Rows per tile of the ws kernel (16, 32 or 64).
+static int ws_tile_rows(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
 
 template <int RT, bool F8, bool SP = false>
 hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
@@ -1378,8 +2157,26 @@ hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, 
   return hipGetLastError();
 }
 
-hipError_t launch_splitkv(const DecodeArgs& a, hipStream_t stream, hipEvent_t start,
+hipError_t launch_splitkv(const DecodeArgs& args, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
+  DecodeArgs a = args;
+  if (!a.sparse && !a.kv_fp8 && a.M % kRWRows == 0) {
+    a.row_tile_rows = kRWRows;
+    a.row_tiles = a.M / kRWRows;
+    const dim3 grid(a.num_parts * a.row_tiles);
+    const dim3 block(kRWThreads);
+    if (start == nullptr && stop == nullptr) {
+      hipLaunchKernelGGL(mla_rowwave_kernel, grid, block, 0, stream, a);
+    } else {
+      void* kargs[] = {&a};
+      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&mla_rowwave_kernel), grid,
+                                        block, kargs, 0, stream, start, stop, 0);
+      if (e != hipSuccess) return e;
+    }
+    return hipGetLastError();
+  }
+  a.row_tile_rows = ws_tile_rows(a.M);
+  a.row_tiles = (a.M + a.row_tile_rows - 1) / a.row_tile_rows;
   if (a.sparse && a.kv_fp8) {
     if (a.row_tile_rows == 16) return launch_ws<1, true, true>(a, stream, start, stop);
     if (a.row_tile_rows == 32) return launch_ws<2, true, true>(a, stream, start, stop);

@@ -41,7 +41,7 @@ def test_max_s_q_accepted():
     # the largest token count passes validation (fake pointers: a return
     # other than INVALID_ARG for s_q would need a launch, so only check the
     # host-only entry points)
-    assert mla.num_parts(1, 128, 128, 1, 256) == 1
+    assert mla.num_parts(1, 128, 128, 1, 256) == 2         # 16384 rows: 128 row tiles of 128
     assert mla.workspace_bytes(1, 128, 16, 1) == 0
     with pytest.raises(Exception):
         mla.num_parts(1, 129, 16, 1, 256)
@@ -49,8 +49,8 @@ def test_max_s_q_accepted():
 
 def test_num_parts():
     assert mla.num_parts(64, 1, 16, 1, 256) == 256
-    assert mla.num_parts(128, 1, 128, 1, 256) == 128     # two 64-row tiles
-    assert mla.num_parts(132, 2, 128, 1, 256) == 64      # four 64-row tiles
+    assert mla.num_parts(128, 1, 128, 1, 256) == 256     # one 128-row tile
+    assert mla.num_parts(132, 2, 128, 1, 256) == 128     # two 128-row tiles
     assert mla.num_parts(2, 1, 32, 1, 256) == 256
     assert mla.num_parts(2, 1, 16, 1, 1) == 1
     out = ctypes.c_int(0)
@@ -59,7 +59,7 @@ def test_num_parts():
     assert L.mla_decode_num_parts(2, 129, 16, 1, 256, ctypes.byref(out)) == INVALID
     assert L.mla_decode_num_parts(2, 0, 16, 1, 256, ctypes.byref(out)) == INVALID
     assert mla.num_parts(2, 3, 16, 1, 256) == 256          # 48 rows: one 64-row tile
-    assert mla.num_parts(2, 8, 128, 1, 256) == 16          # 1024 rows: sixteen tiles
+    assert mla.num_parts(2, 8, 128, 1, 256) == 32          # 1024 rows: eight 128-row tiles
     assert L.mla_decode_num_parts(2, 1, 16, 2, 256, ctypes.byref(out)) == INVALID
     assert L.mla_decode_num_parts(0, 1, 16, 1, 256, ctypes.byref(out)) == INVALID
     assert L.mla_decode_num_parts(2, 1, 16, 1, 0, ctypes.byref(out)) == INVALID

@@ -1,9 +1,8 @@
 """Block-table entries that name no page of the pool (negative or >= the pool
-size) on MI355X, as the header documents them: the dense decode reads such a
-page as all-zero key rows (they count as keys with score 0), the sparse mode
-skips the entries that land on it.  Dense: checked against the fp64 oracle
-over the same cache with one extra all-zero page that the unmapped slots
-point to; sparse: against the sparse oracle, which skips unmapped entries.
+size), and slots past the table's columns, on MI355X: the positions they
+cover hold no key and are left out of the attention, in the dense and the
+sparse mode alike.  Checked against the fp64 oracles, which take the same
+reading, over the very same table.
 """
 import numpy as np
 import pytest
@@ -46,8 +45,8 @@ def _unmap(bt, n_pool):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-@pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 1), (32, 2)])
-def test_dense_unmapped_pages_read_as_zero_rows(mla, kv, h_q, s_q):
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 1), (32, 2), (64, 2)])
+def test_dense_unmapped_pages_are_skipped(mla, kv, h_q, s_q):
     print(f"case unmapped dense {kv} h_q={h_q} s_q={s_q}", flush=True)
     fp8 = kv == "fp8"
     lens = [200, 130, 300]
@@ -58,14 +57,31 @@ def test_dense_unmapped_pages_read_as_zero_rows(mla, kv, h_q, s_q):
     fwd = mla.fwd_fp8 if fp8 else mla.fwd
     out, lse = fwd(g.q, g.kcache, bt.cuda(), g.seqlens, inp.scale, inp.causal)
     torch.cuda.synchronize()
-    # reference: the unmapped slots point at one extra all-zero page
-    zero = torch.zeros_like(inp.kcache[:1])
-    kc2 = torch.cat([inp.kcache, zero]).contiguous()
-    bt2 = bt.clone()
-    bt2[(bt2 < 0) | (bt2 >= n_pool)] = n_pool
     ref = decode_fp8 if fp8 else decode
-    O_ref, L_ref = ref(inp.q, kc2, bt2, inp.seqlens, inp.scale, inp.causal)
+    O_ref, L_ref = ref(inp.q, inp.kcache, bt, inp.seqlens, inp.scale, inp.causal)
     _check(out, lse, O_ref, L_ref, f"dense {kv}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_dense_request_without_any_page(mla, kv, h_q):
+    """Every slot of request 1 unmapped: its rows get O = 0, LSE = -inf; the
+    other requests are unaffected."""
+    print(f"case dense no page {kv} h_q={h_q}", flush=True)
+    fp8 = kv == "fp8"
+    inp = (build_fp8_inputs if fp8 else build_inputs)([200, 130, 300], 1, h_q, seed=80,
+                                                       extra_pool=3)
+    bt = inp.block_table.clone()
+    bt[1, :] = -1
+    g = inp.to("cuda")
+    fwd = mla.fwd_fp8 if fp8 else mla.fwd
+    out, lse = fwd(g.q, g.kcache, bt.cuda(), g.seqlens, inp.scale, inp.causal)
+    torch.cuda.synchronize()
+    assert torch.all(out[1] == 0)
+    assert torch.all(torch.isneginf(lse[1]))
+    ref = decode_fp8 if fp8 else decode
+    O_ref, L_ref = ref(inp.q, inp.kcache, bt, inp.seqlens, inp.scale, inp.causal)
+    _check(out, lse, O_ref, L_ref, f"dense no page {kv}")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
@@ -111,32 +127,26 @@ def test_append_skips_unmapped_pages(mla, kv):
     assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8))
 
 
-# Lengths that run past the table's columns (bt_stride): the slots beyond it
-# are documented like unmapped pages (zero rows in the dense mode, skipped
-# entries in the sparse mode, nothing written by the append).
+# Lengths that run past the table's columns (bt_stride): the positions beyond
+# it hold no key in either mode, and the append writes nothing there.
 def _short_table(inp, cols):
     return inp.block_table[:, :cols].contiguous()
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("h_q,s_q", [(16, 1), (128, 2)])
-def test_dense_slots_beyond_table_read_as_zero_rows(mla, kv, h_q, s_q):
+def test_dense_slots_beyond_table_are_skipped(mla, kv, h_q, s_q):
     print(f"case dense beyond table {kv} h_q={h_q} s_q={s_q}", flush=True)
     fp8 = kv == "fp8"
     lens = [200, 130, 300]          # 4, 3 and 5 pages; the table keeps 3 columns
     inp = (build_fp8_inputs if fp8 else build_inputs)(lens, s_q, h_q, seed=81, extra_pool=3)
-    n_pool = int(inp.kcache.shape[0])
     bt = _short_table(inp, 3)
     g = inp.to("cuda")
     fwd = mla.fwd_fp8 if fp8 else mla.fwd
     out, lse = fwd(g.q, g.kcache, bt.cuda(), g.seqlens, inp.scale, inp.causal)
     torch.cuda.synchronize()
-    # reference: the missing columns point at one extra all-zero page
-    kc2 = torch.cat([inp.kcache, torch.zeros_like(inp.kcache[:1])]).contiguous()
-    bt2 = torch.full((3, 5), n_pool, dtype=torch.int32)
-    bt2[:, :3] = bt
     ref = decode_fp8 if fp8 else decode
-    O_ref, L_ref = ref(inp.q, kc2, bt2, inp.seqlens, inp.scale, inp.causal)
+    O_ref, L_ref = ref(inp.q, inp.kcache, bt, inp.seqlens, inp.scale, inp.causal)
     _check(out, lse, O_ref, L_ref, f"dense beyond table {kv}")
 
 
