@@ -16,7 +16,8 @@
  *     partial results (feature ⑤, dynamic load for variable-length input).
  *
  *   For query row r = t*h_q + h of request b (t < s_q, h < h_q):
- *     visible keys  J = { j < L_b - s_q + 1 + t }  if causal, else { j < L_b }
+ *     visible keys  J = { j < L_b - s_q + 1 + t }  if causal, else { j < L_b },
+ *                   less the positions whose table slot holds no page (below)
  *     s_j  = scale * dot(q[b,t,h,0:576], K_b[j,0:576])
  *     LSE  = ln( sum_{j in J} exp(s_j) )                (natural log, fp32)
  *     O    = sum_{j in J} exp(s_j - LSE) * K_b[j,0:512]  (bf16, RNE)
@@ -26,7 +27,8 @@
  *   - All pointers named *_d are DEVICE pointers; the caller allocates and owns
  *     every buffer (inputs, outputs, metadata, workspace).  The library never
  *     allocates or frees and keeps no mutable global state, so calls on
- *     different streams may run concurrently.
+ *     different streams may run concurrently (the one exception is
+ *     mla_decode_fwd_noalloc and its static per-device array, below).
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Enqueueing entry points are asynchronous: results are valid once the
  *     stream has been synchronised.  They never synchronise the host.
@@ -95,6 +97,9 @@ int mla_decode_workspace_bytes(int batch, int s_q, int h_q, int num_parts,
 
 /*
  * mla_decode_metadata — enqueue the split-KV scheduler (one workgroup).
+ * Passage: page "深度剖析DeepSeek Infra开源全貌", DAY1 FlashMLA, feature ⑤
+ * (dynamic load computation for variable-length input); the pages give no
+ * rule, so the balancing rule below is this library's own.
  * Reads seqlens_d on the device (no host sync) and writes the partition of
  * all requests' pages over num_parts parts:
  *   tile_meta_d     int32 [num_parts][8] = {begin_req, begin_page, end_req,
@@ -118,6 +123,10 @@ int mla_decode_metadata(const int32_t* seqlens_d, int batch, int s_q, int h_q,
 
 /*
  * mla_decode_splitkv — enqueue the main decode kernel only.
+ * Passage: page "深度剖析DeepSeek Infra开源全貌", DAY1 FlashMLA: the MLA
+ * terminology paragraph (one shared latent head), feature ② (64-token
+ * pages), feature ④ (scores, then probabilities times values) and feature ⑤
+ * (a long request's keys split over several workers).
  * For every part and row tile: gathers the part's pages through the block
  * table into LDS, computes scores (bf16 MFMA, fp32 accumulate), the online
  * softmax in fp32, and probabilities times values (bf16 MFMA).  A request
@@ -163,6 +172,8 @@ int mla_decode_splitkv_timed(const void* q_d, const void* kcache_d, int64_t num_
 
 /*
  * mla_decode_combine — enqueue the log-sum-exp merge of split partials.
+ * Passage: page "深度剖析DeepSeek Infra开源全貌", DAY1 FlashMLA, feature ⑤
+ * (the pieces of a split request merged into one result).
  * For every request with split_offsets[b+1] > split_offsets[b]:
  *   LSE = ln sum_i exp(LSE_i),  O = sum_i exp(LSE_i - LSE) * O_i  (exact merge),
  * written to out_d (bf16) / lse_d.  Requests with seqlens[b] <= 0 get O = 0,
@@ -176,7 +187,9 @@ int mla_decode_combine(const int32_t* seqlens_d, int batch, int s_q, int h_q,
 
 /*
  * mla_decode_fwd — mla_decode_splitkv followed by mla_decode_combine on the
- * same stream: the whole decode attention for one batch.
+ * same stream: the whole decode attention for one batch (page
+ * "深度剖析DeepSeek Infra开源全貌", DAY1 FlashMLA: the operation defined at the
+ * top of this file).
  */
 int mla_decode_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
                    const int32_t* block_table_d, int bt_stride,
