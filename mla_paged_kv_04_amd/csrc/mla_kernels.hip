@@ -360,13 +360,13 @@ __device__ __forceinline__ bool before_end(const DecodeArgs& a, int b, int k, in
   return b < a.batch && (b < b1 || (b == b1 && k < k1));
 }
 
-// Keys of request b: its length, or the fixed entry count of the sparse mode.
 // The page id in table slot k of request b; -1 for a slot at or beyond the
 // table's column count.
 __device__ __forceinline__ int unit_page(const DecodeArgs& a, int b, int k) {
   return k < a.bt_stride ? ldc(a.block_table + (long long)b * a.bt_stride + k) : -1;
 }
 
+// Keys of request b: its length, or the fixed entry count of the sparse mode.
 __device__ __forceinline__ int seqlen_of(const DecodeArgs& a, int b) {
   if (a.const_len > 0) return b < a.batch ? a.const_len : 0;
   return b < a.batch ? ldc(a.seqlens + b) : 0;
@@ -496,6 +496,19 @@ __device__ __forceinline__ void unit_next(const DecodeArgs& a, int& b, int& k, i
     return;
   }
   h = 0;
+  ++k;
+  while (before_end(a, b, k, b1, k1)) {
+    const int end = (b == b1) ? k1 : n_pages(L);
+    if (k < end) return;
+    ++b;
+    k = 0;
+    L = seqlen_of(a, b);
+  }
+}
+
+// Advance (b, k) to the part's next page (L: the length of request b).
+__device__ __forceinline__ void page_next(const DecodeArgs& a, int& b, int& k, int& L, int b1,
+                                          int k1) {
   ++k;
   while (before_end(a, b, k, b1, k1)) {
     const int end = (b == b1) ? k1 : n_pages(L);
@@ -1431,17 +1444,33 @@ __device__ __forceinline__ bool page_ok(const DecodeArgs& a, int b, int k) {
 // product: at most 19; 24 are inserted) inside its own asm block: the
 // compiler may place a copy of the accumulator right after the statement
 // that produced it, and that copy must already see the result.
-#define MLA_SACC "{v[236:251]}"
+// Two fixed accumulator blocks (one per half of a page).
+#define MLA_SACC0 "{v[236:251]}"
+#define MLA_SACC1 "{v[220:235]}"
+template <int BLK>
 __device__ __forceinline__ void score_mfma_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC(s) : "v"(k), "v"(q));
+  if constexpr (BLK == 0)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC0(s) : "v"(k), "v"(q));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC1(s) : "v"(k), "v"(q));
 }
+template <int BLK>
 __device__ __forceinline__ void score_mfma(f32x16& s, const bf16x8& k, const bf16x8& q) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC(s) : "v"(k), "v"(q));
+  if constexpr (BLK == 0)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC0(s) : "v"(k), "v"(q));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC1(s) : "v"(k), "v"(q));
 }
+template <int BLK>
 __device__ __forceinline__ void score_mfma_last(f32x16& s, const bf16x8& k, const bf16x8& q) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+" MLA_SACC(s)
-               : "v"(k), "v"(q));
+  if constexpr (BLK == 0)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+" MLA_SACC0(s)
+                 : "v"(k), "v"(q));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+" MLA_SACC1(s)
+                 : "v"(k), "v"(q));
 }
 // The 256 output accumulators of a wave (O^T for its 32 rows x 512 dims,
 // fp32) live in fixed AGPRs, block db of 32 dims in a[16db .. 16db+15], and
@@ -1758,16 +1787,18 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
   };
   load_q(cb);
 
-  // ---- page ring: issue cursor (ib, ik, ih) ----
-  // A unit is issued in two steps so that no scalar load waits on the issue
-  // path: prefetch_next() (at the end of a phase, before its barrier) moves
-  // the cursor and loads the next unit's page id; issue_setup() (at the start
-  // of the next phase) builds the buffer resource, records the page's
-  // validity in a four-unit ring and the 9 slots of this wave then go out one
-  // at a time between the score products (issue_slot).
-  int ib = cb, ik = ck, ih = 0, iL = cL;
-  int issued = 0;
-  int off[9];   // the global offsets of this wave's slots w, w + 4, ..., w + 32
+  // ---- page ring: two page slots of two 36 KB halves ----
+  // Page p of the part lands in slot p & 1 (ring buffers 2(p & 1) and
+  // 2(p & 1) + 1 hold its key rows 0-31 and 32-63).  Phase p computes page p
+  // while page p + 1 streams into the other slot.  A page is issued in two
+  // steps so that no scalar load waits on the issue path: prefetch_page()
+  // (end of a phase, before its barrier) moves the issue cursor and loads the
+  // page id; issue_page() (after the barrier) builds the two halves' buffer
+  // resources, and this wave's 18 slots then go out one at a time between
+  // the score products (issue_slot).
+  int ib = cb, ik = ck, iL = cL;
+  int issued = 0;           // pages issued
+  int off[9];   // the global offsets of this wave's slots w, w + 4, ..., w + 32 of a half
 #pragma unroll
   for (int m = 0; m < 9; ++m) {
     const int p = 256 * m + tid;
@@ -1775,52 +1806,57 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
     const int pc = p - r * kChunksPerRow;
     off[m] = r * kRowBytes + ((pc ^ rw_swizzle(r)) << 4);
   }
-  bool pf_on = false;       // a unit is at the cursor
+  bool pf_on = false;       // a page is at the issue cursor
   int pf_page = -1, pf_rows = 0;
-  bool hl_on = false;       // the slots of an issued unit are pending
-  HalfLoad hl;
-  uint32_t vring = 0;       // bit u & 3: unit u's page slot names a page of the pool
-  auto prefetch_next = [&](bool advance) {
-    if (advance) unit_next(a, ib, ik, ih, iL, b1, k1);
+  bool hl_on = false;       // the slots of an issued page are pending
+  HalfLoad hla, hlb;
+  uint32_t vring = 0;       // bit p & 1: page p's slot names a page of the pool
+  auto prefetch_page = [&](bool advance) {
+    if (advance) page_next(a, ib, ik, iL, b1, k1);
     pf_on = before_end(a, ib, ik, b1, k1);
     if (pf_on) {
-      const int rows = iL - ik * kBlock - ih * kHalfRows;
-      pf_rows = rows > kHalfRows ? kHalfRows : rows;
+      const int rows = iL - ik * kBlock;
+      pf_rows = rows > kBlock ? kBlock : rows;
       pf_page = ik < a.bt_stride ? ldc(a.block_table + (long long)ib * a.bt_stride + ik) : -1;
     }
   };
-  auto issue_setup = [&]() {
+  auto issue_page = [&]() {
     hl_on = pf_on;
     if (hl_on) {
       const bool in_pool = pf_page >= 0 && (long long)pf_page < a.num_blocks;
       const bool ok = in_pool && pf_rows > 0;
       const char* base = reinterpret_cast<const char*>(a.kcache) +
-                         (ok ? (long long)pf_page * kPageBytes + ih * kHalfBytes : 0);
-      const int nrec = uni(ok ? pf_rows * kRowBytes : 0);
-      hl.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, kRsrcWord3);
-      hl.m0 = uni(static_cast<uint32_t>(
-          reinterpret_cast<uintptr_t>((MLA_LDS char*)(smem + (issued % NBUF) * kHalfBytes)) +
+                         (ok ? (long long)pf_page * kPageBytes : 0);
+      const int ra = ok ? (pf_rows > kHalfRows ? kHalfRows : pf_rows) : 0;
+      const int rb = ok && pf_rows > kHalfRows ? pf_rows - kHalfRows : 0;
+      hla.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, uni(ra * kRowBytes),
+                                                kRsrcWord3);
+      hlb.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + kHalfBytes), 0,
+                                                uni(rb * kRowBytes), kRsrcWord3);
+      hla.m0 = uni(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((MLA_LDS char*)(smem + 2 * (issued & 1) * kHalfBytes)) +
           w * 1024));
-      const uint32_t bit = 1u << (issued & 3);
+      hlb.m0 = hla.m0 + kHalfBytes;
+      const uint32_t bit = 1u << (issued & 1);
       vring = in_pool ? (vring | bit) : (vring & ~bit);
       ++issued;
     }
   };
+  // slot m of the page: half m / 9, slot m % 9 of that half
   auto issue_slot = [&](int m) {
-    if (hl_on) half_load_slot(hl, off[m], m);
+    if (hl_on) half_load_slot(m < 9 ? hla : hlb, off[m % 9], m % 9);
   };
-  auto wait_unit = [&](int u) { wait_loads_behind<kHalfLoadsPerWave, NBUF - 2>(issued - u - 1); };
+  auto wait_page = [&](int p) {
+    wait_loads_behind<2 * kHalfLoadsPerWave, 1>(issued - p - 1);
+  };
 
-  // units 0 and 1, all slots at once
-  prefetch_next(false);
+  // page 0, all slots at once; page 1's id on its way
+  prefetch_page(false);
+  issue_page();
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    issue_setup();
-#pragma unroll
-    for (int m = 0; m < 9; ++m) issue_slot(m);
-    prefetch_next(true);
-  }
-  wait_unit(0);
+  for (int m = 0; m < 18; ++m) issue_slot(m);
+  prefetch_page(true);
+  wait_page(0);
   q_ready();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   wg_barrier();
@@ -1828,64 +1864,56 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
   const bf16x8 zero8 = bf16x8{};
   acc_zero_all(zero8);
 
-  // ---- the pipeline ----
-  // Phase t: scores of unit t (the score chain) with the softmax of unit t-1
-  // interleaved between its products (the scores of unit t-1 are kept from the
-  // phase before), then the value product of unit t-1.  Units t-1 (values)
-  // and t (keys) are in the ring, t+1 and t+2 in flight.
-  //
-  // State of the unit whose softmax and values run in the phase (unit t-1):
-  f32x16 sp;                // its scores (S^T, raw q.k sums)
-  int u_k = 0, u_h = 0;     // its page and half
-  bool u_first = true;      // it starts a piece: the running max and sum restart
-  bool u_last = false;      // it ends a piece
-  bool u_valid = true;      // its page slot names a page of the pool
-  int u_lim = 0, u_lim_min = 0;
-  int u_b = 0, u_pbeg = 0, u_n = 0;
-  // running softmax state of the current piece (per row, lane-local)
-  float m_run = -INFINITY, l_run = 0.f;
-  // a finished piece whose O is written at the start of the next phase,
-  // before that phase's page loads (so that the end-of-phase page wait does
-  // not also wait for these stores)
-  bool e_pending = false;
-  float e_linv = 0.f;
-  int e_b = 0;
-  bool e_whole = false;
-  long long e_slot = 0;
+  // ---- per piece (the run of the part's pages of one request) ----
+  float m_run = -INFINITY, l_run = 0.f;   // running max (log2 units) and sum of the lane's row
+  int pbeg = ck, npg = n_pages(cL);
+  int lim = a.causal ? cL - a.s_q + 1 + tok : cL;
+  int lim_min = a.causal ? cL - a.s_q + 1 : cL;
+  bool first = true;        // the phase's page starts a piece
 
-  // score-side piece state of the unit being scored (unit t)
-  int s_pbeg = ck, s_n = n_pages(cL);
-  int s_lim = a.causal ? cL - a.s_q + 1 + tok : cL;
-  int s_lim_min = a.causal ? cL - a.s_q + 1 : cL;
-  bool s_first = true;
-
-  auto value_epilogue = [&]() {
-    // O / l of the finished piece: bf16 to out for a whole request, fp32
-    // partial otherwise; then the accumulators restart
+  // O / l of the finished piece: bf16 to out for a whole request, fp32
+  // partial otherwise, with its LSE; then the accumulators restart
+  auto piece_end = [&](int b) {
+    float lt = l_run;
+    {
+      const unsigned li = __float_as_uint(lt);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(li, li, false, false);
+      lt = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    }
+    const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
+    bool whole;
+    const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : npg, npg, whole);
+    const float linv = lt > 0.f ? 1.f / lt : 0.f;
+    if (lh == 0) {
+      if (whole)
+        a.lse[(long long)b * a.M + row] = lse2 * kLn2;
+      else
+        a.part_lse[slot * a.M + row] = lse2;
+    }
     acc_drain();
-    if (e_whole) {
-      uint16_t* op = a.out + ((long long)e_b * a.M + row) * kDV + 4 * lh;
+    if (whole) {
+      uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + 4 * lh;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         float e[16];
         acc_read_i(db, e);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x4 bv = {(__bf16)(e[4 * j] * e_linv), (__bf16)(e[4 * j + 1] * e_linv),
-                             (__bf16)(e[4 * j + 2] * e_linv), (__bf16)(e[4 * j + 3] * e_linv)};
+          const bf16x4 bv = {(__bf16)(e[4 * j] * linv), (__bf16)(e[4 * j + 1] * linv),
+                             (__bf16)(e[4 * j + 2] * linv), (__bf16)(e[4 * j + 3] * linv)};
           *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j) = bv;
         }
       }
     } else {
-      float* op = a.part_o + (e_slot * a.M + row) * kDV + 4 * lh;
+      float* op = a.part_o + (slot * a.M + row) * kDV + 4 * lh;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         float e[16];
         acc_read_i(db, e);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 v = {e[4 * j] * e_linv, e[4 * j + 1] * e_linv, e[4 * j + 2] * e_linv,
-                           e[4 * j + 3] * e_linv};
+          const f32x4 v = {e[4 * j] * linv, e[4 * j + 1] * linv, e[4 * j + 2] * linv,
+                           e[4 * j + 3] * linv};
           *reinterpret_cast<f32x4*>(op + 32 * db + 8 * j) = v;
         }
       }
@@ -1893,48 +1921,53 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
     acc_zero_all(zero8);
   };
 
-  // Softmax of the held unit, in steps placed between the score products:
-  // step 0 takes the in-lane maximum (and masks, when the unit holds keys
-  // past the visible count or its page slot is invalid); step 1 the row
-  // maximum (one permlane32 swap) and the lazy-rescale decision; steps 2-9
-  // the exponentials, two keys each; step 10 the row-sum update.
-  // Exponent: exp2(x * cx - m) as one fma.  An unmasked unit keeps the raw
+  // Softmax of one 32-key half, in steps placed between matrix products,
+  // each small enough to issue within one product's execution: step 0 takes
+  // the in-lane maximum (and masks, when the half holds keys past the
+  // visible count or its page slot is invalid); step 1 the row maximum (one
+  // permlane32 swap) and the lazy-rescale decision; steps 2-17 one
+  // exponential each (the odd ones pack two probabilities into bf16);
+  // step 18 the row-sum update.
+  // Exponent: exp2(x * cx - m) as one fma.  An unmasked half keeps the raw
   // q.k sums (x = s, cx = scale * log2 e; for a scale >= 0 the scaled maximum
-  // is the maximum of the raw sums times it); a masked unit is rewritten in
+  // is the maximum of the raw sums times it); a masked half is rewritten in
   // place as scaled sums with -inf at the masked keys (cx = 1).
+  constexpr int kSmxSteps = 19;
   const bool scale_neg = a.scale_log2 < 0.f;
-  float mx = -INFINITY, neg_m = 0.f, cx = 1.f, alpha = 1.f, lsum = 0.f;
+  float mx = -INFINITY, neg_m = 0.f, cx = 1.f, alpha = 1.f, lsum = 0.f, p_even = 0.f;
   bool resc_any = false;
-  bf16x8 pv[2];
-  auto softmax_step = [&](int st) {
+  // kbase: position of the half's first key; valid: its page is in the pool;
+  // restart: the half starts a piece
+  auto softmax_step = [&](int st, f32x16& sv, bf16x8 (&pv)[2], int kbase, bool valid,
+                          bool restart) {
     if (st == 0) {
-      if (u_first) {
+      if (restart) {
         m_run = -INFINITY;
         l_run = 0.f;
       }
-      const bool need_mask = scale_neg || !u_valid || u_k * kBlock + (u_h + 1) * kHalfRows > u_lim_min;
+      const bool need_mask = scale_neg || !valid || kbase + kHalfRows > lim_min;
       if (!need_mask) {
-        float m0 = fmaxf(fmaxf(sp[0], sp[1]), sp[2]);
-        float m1 = fmaxf(fmaxf(sp[3], sp[4]), sp[5]);
-        float m2 = fmaxf(fmaxf(sp[6], sp[7]), sp[8]);
-        float m3 = fmaxf(fmaxf(sp[9], sp[10]), sp[11]);
-        float m4 = fmaxf(fmaxf(sp[12], sp[13]), sp[14]);
+        float m0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+        float m1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
+        float m2 = fmaxf(fmaxf(sv[6], sv[7]), sv[8]);
+        float m3 = fmaxf(fmaxf(sv[9], sv[10]), sv[11]);
+        float m4 = fmaxf(fmaxf(sv[12], sv[13]), sv[14]);
         m0 = fmaxf(fmaxf(m0, m1), m2);
-        m3 = fmaxf(fmaxf(m3, m4), sp[15]);
+        m3 = fmaxf(fmaxf(m3, m4), sv[15]);
         mx = fmaxf(m0, m3) * a.scale_log2;
         cx = a.scale_log2;
       } else {
         asm volatile("");   // a branch of its own: the unmasked path does none of this
-        const int key0 = u_k * kBlock + u_h * kHalfRows + 4 * lh;   // element 4j + i: key0 + 8j + i
-        const int lim_u = u_valid ? u_lim : -1;
+        const int key0 = kbase + 4 * lh;   // element 4j + i: key key0 + 8j + i
+        const int lim_u = valid ? lim : -1;
         mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float xv = sp[4 * j + i] * a.scale_log2;
+            float xv = sv[4 * j + i] * a.scale_log2;
             if (key0 + 8 * j + i >= lim_u) xv = -INFINITY;
-            sp[4 * j + i] = xv;
+            sv[4 * j + i] = xv;
             mx = fmaxf(mx, xv);
           }
         cx = 1.f;
@@ -1952,22 +1985,27 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
       l_run *= alpha;
       neg_m = m_run == -INFINITY ? 0.f : -m_run;
       lsum = 0.f;
-    } else if (st < 10) {
-      const int e0 = 2 * (st - 2);
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[e0], cx, neg_m));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[e0 + 1], cx, neg_m));
-      lsum += p0 + p1;
-      pv[e0 >> 3][e0 & 7] = (__bf16)p0;
-      pv[e0 >> 3][(e0 & 7) + 1] = (__bf16)p1;
+    } else if (st < 18) {
+      const int e = st - 2;
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], cx, neg_m));
+      lsum += p;
+      if ((e & 1) == 0) {
+        p_even = p;
+      } else {
+        pv[e >> 3][(e & 7) - 1] = (__bf16)p_even;
+        pv[e >> 3][e & 7] = (__bf16)p;
+      }
     } else {
       l_run += lsum;
     }
   };
 
-  // the value product of the held unit: 16 dim blocks x 2 key steps, blocks
-  // innermost, V read D2 products ahead
-  auto value_product = [&](const char* vbuf) {
-    constexpr int D2 = 3;
+  // The value product of one half: 16 dim blocks x 2 key steps, blocks
+  // innermost, V read D2 products ahead; with SMX the softmax steps of
+  // another half sit between its products.
+  auto value_product = [&](const char* vbuf, bf16x8 (&pv)[2], bool smx, f32x16& s2,
+                           bf16x8 (&p2)[2], int kb2, bool valid2) {
+    constexpr int D2 = 2;
     bf16x4 vlo[D2 + 1], vhi[D2 + 1];
     auto read_v = [&](int st) {
       const int u = st >> 4, db = st & 15;
@@ -1985,43 +2023,27 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
       const bf16x4 lo = vlo[i % (D2 + 1)], hi = vhi[i % (D2 + 1)];
       const bf16x8 va = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc_mfma_i(i & 15, va, pv[i >> 4]);
+      // the other half's exponentials come after the products that read
+      // P[0], so that its P[0] can take those registers
+      if (smx && i == 2) softmax_step(0, s2, p2, kb2, valid2, false);
+      if (smx && i == 4) softmax_step(1, s2, p2, kb2, valid2, false);
+      if (smx && i >= 16) softmax_step(i - 14, s2, p2, kb2, valid2, false);
       asm volatile("" ::"v"(va));   // operand registers held past the product's issue
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (smx) softmax_step(kSmxSteps - 1, s2, p2, kb2, valid2, false);
     // the last products may still read P: wait states before its registers
     // can be reused
     asm volatile("s_nop 7" ::"v"(pv[0]), "v"(pv[1]));
   };
 
-  // the held unit's piece end: its LSE out, its O queued for the next phase
-  auto piece_end = [&]() {
-    float lt = l_run;
-    {
-      const unsigned li = __float_as_uint(lt);
-      const auto p32 = __builtin_amdgcn_permlane32_swap(li, li, false, false);
-      lt = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
-    }
-    const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
-    bool whole;
-    const long long slot = piece_slot(u_b, u_pbeg, (u_b == b1) ? k1 : u_n, u_n, whole);
-    if (lh == 0) {
-      if (whole)
-        a.lse[(long long)u_b * a.M + row] = lse2 * kLn2;
-      else
-        a.part_lse[slot * a.M + row] = lse2;
-    }
-    e_pending = true;
-    e_linv = lt > 0.f ? 1.f / lt : 0.f;
-    e_b = u_b;
-    e_whole = whole;
-    e_slot = slot;
-  };
-
-  // the score chain of unit t (K read D1 products ahead); with SOFTMAX the
-  // held unit's softmax steps sit between the products
+  // The score product of one half (K read D1 products ahead), the page's
+  // slots SLOT0 .. SLOT0 + 8 issued between its products; with SMX the
+  // softmax steps of another half sit between them too.
   constexpr int D1 = 3;
-  auto score_chain = [&](const char* kbuf, f32x16& sacc, bool with_softmax) {
-    constexpr int NK = D1 + 2;   // K operand ring: a slot is rewritten two steps after its product
+  auto score_chain = [&](const char* kbuf, f32x16& sacc, int slot0, bool smx, f32x16& s2,
+                         bf16x8 (&p2)[2], int kb2, bool valid2, bool restart2) {
+    constexpr int NK = D1 + 1;   // K operand ring: a slot is rewritten one step after its product
     bf16x8 ka[NK];
     auto read_k = [&](int ks) {
       ka[ks % NK] = *reinterpret_cast<const bf16x8*>(kbuf + ko[ks & 3] + 128 * (ks >> 2));
@@ -2032,100 +2054,81 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
 #pragma unroll
     for (int i = 0; i < 36; ++i) {
       if (i + D1 < 36) read_k(i + D1);
-      if (i == 0)
-        score_mfma_first(sacc, ka[0], qreg[0]);
-      else if (i < 35)
-        score_mfma(sacc, ka[i % NK], qreg[i]);
-      else
-        score_mfma_last(sacc, ka[i % NK], qreg[i]);
-      if ((i & 3) == 1) issue_slot(i >> 2);
-      if (with_softmax && i >= 2 && (i & 1) == 0 && (i - 2) / 2 <= 10) softmax_step((i - 2) / 2);
-      // the products may still be reading their K operands: the registers of
-      // this step's and the previous step's operand stay allocated (no VALU
-      // result lands in them) until here
-      asm volatile("" ::"v"(ka[i % NK]), "v"(ka[(i + NK - 1) % NK]));
+      if (slot0 == 0) {
+        if (i == 0)
+          score_mfma_first<0>(sacc, ka[0], qreg[0]);
+        else if (i < 35)
+          score_mfma<0>(sacc, ka[i % NK], qreg[i]);
+        else
+          score_mfma_last<0>(sacc, ka[i % NK], qreg[i]);
+      } else {
+        if (i == 0)
+          score_mfma_first<1>(sacc, ka[0], qreg[0]);
+        else if (i < 35)
+          score_mfma<1>(sacc, ka[i % NK], qreg[i]);
+        else
+          score_mfma_last<1>(sacc, ka[i % NK], qreg[i]);
+      }
+      if ((i & 3) == 1) issue_slot(slot0 + (i >> 2));
+      if (smx && i >= 2 && i - 2 < kSmxSteps)
+        softmax_step(i - 2, s2, p2, kb2, valid2, restart2);
+      // the product may still be reading its K operand: the register stays
+      // allocated (no VALU result lands in it) until here.  (Only this step's
+      // operand: naming the register of a read still in flight would make
+      // the compiler wait for that read here.)
+      asm volatile("" ::"v"(ka[i % NK]));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- phase 0: scores of unit 0 only ----
-  {
-    issue_setup();   // unit 2
-    score_chain(smem, sp, false);
-    u_k = ck;
-    u_h = ch;
-    u_first = true;
-    u_valid = (vring & 1u) != 0;
-    u_lim = s_lim;
-    u_lim_min = s_lim_min;
-    u_b = cb;
-    u_pbeg = s_pbeg;
-    u_n = s_n;
-  }
-  int t = 1;
+  // ---- the pipeline: phase t computes page t (slot t & 1) ----
+  //   scores of half A (page rows 0-31);
+  //   scores of half B (rows 32-63) with A's softmax between the products;
+  //   values of A with B's softmax between the products; values of B.
+  // Page t + 1 is issued between the score products; a page with 32 rows or
+  // fewer has no half B.
+  int t = 0;
   while (true) {
-    // advance the score cursor to unit t; the held unit t-1 ends its piece
-    // if unit t is in another request or does not exist
-    const int pb = cb;
-    unit_next(a, cb, ck, ch, cL, b1, k1);
-    const bool more = before_end(a, cb, ck, b1, k1);
-    s_first = !(more && cb == pb);
-    u_last = s_first;
-    if (!more) break;
-    if (s_first) {
-      s_pbeg = ck;
-      s_n = n_pages(cL);
-      s_lim = a.causal ? cL - a.s_q + 1 + tok : cL;
-      s_lim_min = a.causal ? cL - a.s_q + 1 : cL;
-    }
-    prefetch_next(true);   // completes while this wave waits at the barrier
-    wait_unit(t);
-    wg_barrier();   // unit t landed in every wave's slots; unit t-2's buffer is free
-
-    // ------- phase t: scores of unit t, softmax and values of unit t-1 -------
-    if (e_pending) {
-      value_epilogue();
-      e_pending = false;
-    }
-    if (s_first) {
+    const bool valid = ((vring >> (t & 1)) & 1u) != 0;
+    if (first && t > 0) {
       // Q of the new piece, before this phase's page loads (so that waiting
       // for it does not also wait for them: loads complete in order)
       load_q(cb);
       q_ready();
     }
-    issue_setup();   // unit t+2 into the buffer of unit t-2
-    const char* kbuf = smem + (t % NBUF) * kHalfBytes;
-    const char* vbuf = smem + ((t + NBUF - 1) % NBUF) * kHalfBytes;
-    f32x16 sc;
-    score_chain(kbuf, sc, true);
+    issue_page();   // page t + 1 into the other slot
+    const char* bufa = smem + 2 * (t & 1) * kHalfBytes;
+    const char* bufb = bufa + kHalfBytes;
+    const int kb = ck * kBlock;
+    f32x16 sa, sb;
+    bf16x8 pa[2], pb[2];
+    // (a page of 32 rows or fewer runs half B too: its rows were loaded as
+    // zeros and all of its keys are masked)
+    score_chain(bufa, sa, 0, false, sa, pa, kb, valid, first);
+    score_chain(bufb, sb, 9, true, sa, pa, kb, valid, first);
     if (resc_any) acc_scale_all(alpha);
-    value_product(vbuf);
-    if (u_last) piece_end();
-    // unit t becomes the held unit
-    sp = sc;
-    u_k = ck;
-    u_h = ch;
-    u_first = s_first;
-    u_valid = ((vring >> (t & 3)) & 1u) != 0;
-    u_lim = s_lim;
-    u_lim_min = s_lim_min;
-    u_b = cb;
-    u_pbeg = s_pbeg;
-    u_n = s_n;
+    value_product(bufa, pa, true, sb, pb, kb + kHalfRows, valid);
+    if (resc_any) acc_scale_all(alpha);
+    value_product(bufb, pb, false, sb, pb, kb + kHalfRows, valid);
+
+    // the compute cursor moves to the next page; a piece ends with its request
+    const int pbi = cb;
+    page_next(a, cb, ck, cL, b1, k1);
+    const bool more = before_end(a, cb, ck, b1, k1);
+    first = !(more && cb == pbi);
+    if (first) piece_end(pbi);
+    if (!more) break;
+    if (first) {
+      pbeg = ck;
+      npg = n_pages(cL);
+      lim = a.causal ? cL - a.s_q + 1 + tok : cL;
+      lim_min = a.causal ? cL - a.s_q + 1 : cL;
+    }
+    prefetch_page(true);   // completes while this wave waits at the barrier
+    wait_page(t + 1);
+    wg_barrier();   // page t + 1 landed in every wave's slots; page t's slot is free
     ++t;
   }
-  // ---------------- last phase: softmax and values of the last unit ----------------
-  // (its buffer is published: it was the score unit of the phase before)
-  if (e_pending) {
-    value_epilogue();
-    e_pending = false;
-  }
-#pragma unroll
-  for (int st = 0; st <= 10; ++st) softmax_step(st);
-  if (resc_any) acc_scale_all(alpha);
-  value_product(smem + ((t + NBUF - 1) % NBUF) * kHalfBytes);
-  piece_end();
-  value_epilogue();
 }
 
 // Rows per workgroup tile of the split plan: 128 when s_q*h_q is a multiple
