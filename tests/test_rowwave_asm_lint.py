@@ -1,0 +1,138 @@
+"""Static checks of mla_rowwave_kernel's gfx950 assembly (no GPU needed).
+
+The kernel keeps its 512-dim output accumulators in AGPRs a0-a255 that only
+inline asm touches, and issues some matrix products as inline asm, which the
+compiler does not see as matrix products.  That design holds only if the
+compiled code keeps these properties, which these tests read off the
+assembly that hipcc emits for the library source:
+
+* no AGPR is named outside the inline asm blocks (the compiler never spills
+  to, or allocates in, the accumulator file);
+* the kernel has no register spills and no scratch memory;
+* no instruction other than a matrix product reads or writes the VGPR
+  result of a matrix product within the wait states that a 32x32x16 bf16
+  product needs before its result may be read (12 on gfx950; the compiler
+  itself inserts 12);
+* every inline-asm matrix product is preceded, inside its asm block, by the
+  two wait states that a VALU write of an operand needs (s_nop 1).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mla_paged_kv_04_amd", "csrc")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+KERNEL = "_ZN3mla18mla_rowwave_kernelENS_10DecodeArgsE"
+RESULT_WAIT_STATES = 12
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not installed")
+    out = str(tmp_path_factory.mktemp("asm") / "mla_kernels.s")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "--cuda-device-only", "-S", os.path.join(CSRC, "mla_kernels.hip"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-3000:]
+    return open(out).read()
+
+
+def _body(text):
+    start = text.index("\n" + KERNEL + ":")
+    end = text.index("s_endpgm", start)
+    return text[start:end].split("\n")
+
+
+def _vregs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def test_no_agpr_outside_inline_asm(asm):
+    inside = False
+    bad = []
+    for ln in _body(asm):
+        t = ln.strip()
+        if t.startswith(";;#ASMSTART"):
+            inside = True
+        elif t.startswith(";;#ASMEND"):
+            inside = False
+        elif t and not t.startswith((";", ".")) and re.search(r"\ba\[?\d", t) and not inside:
+            bad.append(t)
+    assert not bad, bad[:10]
+
+
+def test_no_spills(asm):
+    meta = asm[asm.index(".name:           " + KERNEL) - 3000:asm.index(".name:           " + KERNEL) + 3000]
+    assert re.search(r"\.vgpr_spill_count:\s+0\b", meta)
+    assert re.search(r"\.sgpr_spill_count:\s+0\b", meta)
+    assert re.search(r"\.private_segment_fixed_size:\s+0\b", meta)
+
+
+def test_mfma_results_not_touched_early(asm):
+    lines = [l.strip() for l in _body(asm)]
+    bad = []
+    for i, l in enumerate(lines):
+        if not l.startswith("v_mfma"):
+            continue
+        dst = _vregs(l.split(None, 1)[1].split(",")[0].strip())
+        if not dst:
+            continue   # AGPR result
+        states = 0
+        for l2 in lines[i + 1:]:
+            if not l2 or l2.startswith((";", ".")) or l2.endswith(":"):
+                continue
+            m = re.match(r"s_nop (\d+)", l2)
+            states += int(m.group(1)) + 1 if m else 1
+            if states > RESULT_WAIT_STATES:
+                break
+            if l2.startswith("v_mfma"):
+                ops = [o.strip() for o in l2.split(None, 1)[1].split(",")]
+                if (_vregs(ops[1]) | _vregs(ops[2])) & dst:
+                    bad.append((l, l2))
+                continue
+            parts = l2.split(None, 1)
+            if len(parts) < 2:
+                continue
+            regs = set()
+            for tok in re.split(r",\s*", parts[1].split(";")[0]):
+                if tok:
+                    regs |= _vregs(tok.split()[0])
+            if regs & dst:
+                bad.append((l, l2))
+    assert not bad, bad[:10]
+
+
+def test_inline_asm_products_carry_operand_wait_states(asm):
+    lines = [l.strip() for l in _body(asm)]
+    inside = False
+    prev = None
+    n = 0
+    bad = []
+    for l in lines:
+        if l.startswith(";;#ASMSTART"):
+            inside, prev = True, None
+            continue
+        if l.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if not inside or not l or l.startswith(";"):
+            continue
+        if l.startswith("v_mfma"):
+            n += 1
+            ok = prev is not None and (prev.startswith("v_mfma") or
+                                       re.match(r"s_nop ([1-9]|1\d)\b", prev))
+            if not ok:
+                bad.append(l)
+        prev = l
+    assert n > 0
+    assert not bad, bad[:10]
