@@ -42,37 +42,44 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
 # by what the same counter reads for a plain 1 GiB int32 elementwise copy
 # (--copy-calib-mib 1024): FETCH_SIZE reads 0.5 GiB for it, WRITE_SIZE 1 GiB.
+# mfma_util: rocprofv3's MfmaUtil for the decode kernel (a third --pmc run:
+# sum of SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs / (GRBM_GUI_ACTIVE of the
+# busiest XCD x 1024 SIMDs); a 32x32x16 bf16 product counts 32 busy cycles).
 # Keyed by workload ("<workload>/fp8" for the FP8 cache); valid only for the
 # kernel source it was measured on
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 307020633,
+        "kernel_sha256": "130cd4231b68ea28c5b0fbc7bd90669a65930818fc91805e5b917855e27afbf2",
+        "fetch_bytes": 306999109,
         "write_bytes": 8404992,
-        "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "fetch_scale": 1.99986,
+        "write_scale": 1.0,
+        "mfma_util": 0.0568
     },
     "ridge": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 704764656,
-        "write_bytes": 59894272,
-        "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "kernel_sha256": "130cd4231b68ea28c5b0fbc7bd90669a65930818fc91805e5b917855e27afbf2",
+        "fetch_bytes": 722800187,
+        "write_bytes": 93390688,
+        "fetch_scale": 1.99989,
+        "write_scale": 1.0,
+        "mfma_util": 0.3944
     },
     "long": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 770936002,
-        "write_bytes": 37559808,
-        "fetch_scale": 1.99989,
-        "write_scale": 1.0
+        "kernel_sha256": "130cd4231b68ea28c5b0fbc7bd90669a65930818fc91805e5b917855e27afbf2",
+        "fetch_bytes": 774442583,
+        "write_bytes": 69608809,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0,
+        "mfma_util": 0.4257
     },
     "ragged": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 510572798,
-        "write_bytes": 78838784,
+        "kernel_sha256": "130cd4231b68ea28c5b0fbc7bd90669a65930818fc91805e5b917855e27afbf2",
+        "fetch_bytes": 528743745,
+        "write_bytes": 118483104,
         "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "write_scale": 1.0,
+        "mfma_util": 0.4294
     },
     "draft": {
         "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
@@ -514,6 +521,8 @@ def run_one(args, key: str, cpu_budget: float) -> dict:
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                             "copy-calibrated)",
             "traffic_detail": traffic,
+            "mfma_busy": (None if traffic is None else traffic.get("mfma_util")),
+            "mfma_busy_source": "rocprofv3 MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs), profiles/",
             "mfma_tflops": round(dec_tfl, 2),
             "mfma_frac": round(dec_tfl / PEAK_BF16_TFLOPS, 4),
         },
