@@ -31,7 +31,12 @@
  *     mla_decode_fwd_noalloc and its static per-device array, below).
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
  *     Enqueueing entry points are asynchronous: results are valid once the
- *     stream has been synchronised.  They never synchronise the host.
+ *     stream has been synchronised.  They never synchronise the host, except
+ *     in the checked mode: with the environment variable MLA_DEBUG_SYNC set
+ *     to anything but "" or "0" (read at every call), each launch is followed
+ *     by a wait on its stream, so that a kernel fault is returned as
+ *     MLA_ERR_HIP by the call that launched it, the launch named in
+ *     mla_last_hip_error().  A stream under graph capture is not waited on.
  *   - All arguments are validated on the host BEFORE anything is enqueued; an
  *     invalid call returns a negative status and enqueues nothing.
  *   - Tensors are dense, row-major ("contiguous") with the stated shapes.

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/mla_decode.h: argument
-// validation, workspace sizing and kernel launches.  No allocation, no host
-// synchronisation, no global mutable state except a thread-local error text.
+// validation, workspace sizing and kernel launches.  No allocation, no global
+// mutable state except a thread-local error text, and no host synchronisation
+// outside the checked mode (MLA_DEBUG_SYNC, below).
 #include "../../include/mla_decode.h"
 
 #include <hip/hip_runtime.h>
@@ -8,6 +9,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "mla_kernels.h"
@@ -19,6 +21,29 @@ thread_local char g_last_hip_error[256] = "";
 int hip_fail(hipError_t e, const char* where) {
   snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s: %s", where, hipGetErrorString(e));
   return MLA_ERR_HIP;
+}
+
+// Checked mode: with MLA_DEBUG_SYNC set to anything but "" or "0" in the
+// environment (read at every call), each launch is followed by a wait on its
+// stream, so that a kernel fault is reported by the call that launched it, as
+// MLA_ERR_HIP with that launch named in mla_last_hip_error().  A stream under
+// graph capture is not waited on (the launch is only recorded there).
+bool debug_sync() {
+  const char* v = getenv("MLA_DEBUG_SYNC");
+  return v != nullptr && v[0] != 0 && strcmp(v, "0") != 0;
+}
+
+// Status of a launch that returned `e` on `stream`.
+int launched(hipError_t e, hipStream_t stream, const char* where) {
+  if (e != hipSuccess) return hip_fail(e, where);
+  if (!debug_sync()) return MLA_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e, where);
+  if (cs != hipStreamCaptureStatusNone) return MLA_OK;
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, where);
+  return MLA_OK;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -124,8 +149,7 @@ int splitkv_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
   hipError_t e = mla::launch_splitkv(a, static_cast<hipStream_t>(stream),
                                      static_cast<hipEvent_t>(start_event),
                                      static_cast<hipEvent_t>(stop_event));
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_splitkv launch");
-  return MLA_OK;
+  return launched(e, static_cast<hipStream_t>(stream), "mla_decode_splitkv launch");
 }
 
 int check_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
@@ -229,8 +253,7 @@ int mla_decode_metadata(const int32_t* seqlens_d, int batch, int s_q, int h_q, i
   const int c = mla::fixed_cost_pages(mla::rows_per_tile(s_q, h_q));
   hipError_t e = mla::launch_metadata(seqlens_d, batch, c, num_parts, tile_meta_d,
                                       split_offsets_d, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_metadata launch");
-  return MLA_OK;
+  return launched(e, static_cast<hipStream_t>(stream), "mla_decode_metadata launch");
 }
 
 int mla_decode_splitkv_timed(const void* q_d, const void* kcache_d, int64_t num_blocks,
@@ -290,8 +313,7 @@ int mla_decode_combine(const int32_t* seqlens_d, int batch, int s_q, int h_q,
   a.M = s_q * h_q;
   a.const_len = 0;
   hipError_t e = mla::launch_combine(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_combine launch");
-  return MLA_OK;
+  return launched(e, static_cast<hipStream_t>(stream), "mla_decode_combine launch");
 }
 
 int mla_decode_fwd(const void* q_d, const void* kcache_d, int64_t num_blocks,
@@ -369,8 +391,7 @@ int mla_kv_append(const void* new_kv_d, void* kcache_d, int64_t num_blocks,
                                        static_cast<uint16_t*>(kcache_d), num_blocks,
                                        block_table_d, bt_stride, seqlens_d, batch, s_q,
                                        static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mla_kv_append launch");
-  return MLA_OK;
+  return launched(e, static_cast<hipStream_t>(stream), "mla_kv_append launch");
 }
 
 int mla_kv_append_fp8(const void* new_kv_d, void* kcache_fp8_d, int64_t num_blocks,
@@ -383,8 +404,7 @@ int mla_kv_append_fp8(const void* new_kv_d, void* kcache_fp8_d, int64_t num_bloc
                                            static_cast<uint8_t*>(kcache_fp8_d), num_blocks,
                                            block_table_d, bt_stride, seqlens_d, batch, s_q,
                                            static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "mla_kv_append_fp8 launch");
-  return MLA_OK;
+  return launched(e, static_cast<hipStream_t>(stream), "mla_kv_append_fp8 launch");
 }
 
 const char* mla_status_string(int status) {
@@ -429,8 +449,7 @@ int mla_decode_sparse_metadata(int batch, int s_q, int h_q, int topk, int num_pa
   const int c = mla::fixed_cost_pages(mla::rows_per_tile(1, h_q));
   hipError_t e = mla::launch_metadata(nullptr, batch * s_q, c, num_parts, tile_meta_d,
                                       split_offsets_d, static_cast<hipStream_t>(stream), topk);
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_metadata launch");
-  return MLA_OK;
+  return launched(e, static_cast<hipStream_t>(stream), "mla_decode_sparse_metadata launch");
 }
 
 }  // extern "C"
@@ -468,7 +487,8 @@ int sparse_fwd_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
   hipError_t e = mla::launch_sparse_resolve(indices_d, block_table_d, bt_stride, seqlens_d,
                                             num_blocks, batch, s_q, topk, causal, rowids, vmask,
                                             zero_row, s);
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_fwd resolve launch");
+  st = launched(e, s, "mla_decode_sparse_fwd resolve launch");
+  if (st != MLA_OK) return st;
   const int items = batch * s_q;
   mla::DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q_d);
@@ -503,7 +523,8 @@ int sparse_fwd_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
   a.split_offsets_out = nullptr;
   e = mla::launch_splitkv(a, s, static_cast<hipEvent_t>(start_event),
                           static_cast<hipEvent_t>(stop_event));
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_fwd decode launch");
+  st = launched(e, s, "mla_decode_sparse_fwd decode launch");
+  if (st != MLA_OK) return st;
   mla::CombineArgs c;
   c.seqlens = nullptr;
   c.split_offsets = split_offsets_d;
@@ -515,8 +536,7 @@ int sparse_fwd_impl(const void* q_d, const void* kcache_d, int64_t num_blocks,
   c.M = h_q;
   c.const_len = topk;
   e = mla::launch_combine(c, s);
-  if (e != hipSuccess) return hip_fail(e, "mla_decode_sparse_fwd combine launch");
-  return MLA_OK;
+  return launched(e, s, "mla_decode_sparse_fwd combine launch");
 }
 
 }  // namespace

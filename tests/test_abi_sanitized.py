@@ -6,7 +6,8 @@ without sanitizers) with the sanitizers on the host side only, linked with a
 C driver
 (tests/asan/host_abi_driver.c) that makes the argument-validation calls of
 test_abi.py and the HIP-error path of a valid call (no device is visible, so
-the launch fails); a sanitizer report or a wrong status fails the test.
+the launch fails), once as is and once in the checked mode (MLA_DEBUG_SYNC=1);
+a sanitizer report or a wrong status fails the test.
 """
 import os
 import shutil
@@ -52,8 +53,10 @@ def driver(tmp_path_factory):
     return exe
 
 
-def test_host_abi_under_sanitizers(driver):
+@pytest.mark.parametrize("debug_sync", ["", "1"])
+def test_host_abi_under_sanitizers(driver, debug_sync):
     env = dict(os.environ)
+    env["MLA_DEBUG_SYNC"] = debug_sync      # the checked mode's host path too
     # the HIP runtime keeps allocations until exit; leaks are not what this checks
     env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=0:halt_on_error=1"
     env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
