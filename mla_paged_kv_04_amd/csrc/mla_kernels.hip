@@ -812,6 +812,11 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 // RT: 16-row tiles in the workgroup tile (1, 2 or 4: 16, 32 or 64 query
 // rows); score waves q >= RT have no rows and only keep step with the others.
+// With one tile (dense mode) the unit's two 16-key tiles are split instead:
+// score waves 0 and 1 both take the 16 rows, wave q the keys 16q .. 16q+15
+// of every unit, each with its own online softmax over its key tile, and the
+// value waves keep one accumulator per key tile; the two are merged exactly
+// (the log-sum-exp merge of two key sets) when a piece ends.
 // F8: the cache holds FP8 pages (layout above) instead of bf16 rows.
 // SP: sparse mode: items of selected entries, rows gathered one by one
 // (issue_half_load_sparse, or issue_half_load_f8_sparse over FP8 pages),
@@ -821,15 +826,20 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
   constexpr int NBUF = F8 ? kWSBufsF8 : kWSBufs;          // ring of unit buffers
   constexpr int DL = 8;   // 16-dim output tiles per value wave (128 dims)
   constexpr int UB = F8 ? (SP ? kF8SpUnitBytes : kF8UnitBytes) : kHalfBytes;   // one unit buffer
+  constexpr bool KS = RT == 1 && !SP;   // key tiles split over two score waves
+  constexpr int NR = KS ? 2 : RT;       // softmax streams: row tiles, or key tiles
 
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * UB];
-  __shared__ bf16x8 p_lds[2][RT][64];   // P^T operands: [unit parity][row tile][lane]
-  __shared__ float alpha_lds[2][16 * RT];   // per-row rescale factor of the unit
+  // P^T operands: [unit parity][row tile][lane]; with KS, score wave q fills
+  // the 8-byte half q of every lane's operand (its key tile's elements)
+  __shared__ bf16x8 p_lds[2][RT][64];
+  __shared__ float alpha_lds[2][16 * NR];   // per-row rescale factor of the unit (per stream)
   // per 16-row block q, byte q: any of its rows rescaled in the unit (one
   // dword, so the value waves test all blocks with one read; blocks without
   // rows keep the 0 written here)
   __shared__ uint32_t grow_lds[2];
-  __shared__ float lfin_lds[2][16 * RT];    // per-row sum of a piece ending at the unit
+  __shared__ float lfin_lds[2][16 * NR];    // per-row sum of a piece ending at the unit
+  __shared__ float mfin_lds[2][KS ? 32 : 1];  // KS: per-row reference of each key tile's sum
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -900,8 +910,8 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     const int q = w;
     // uniform: this wave's 16-row block exists (s_q*h_q is a multiple of 16,
     // so a block is either all real rows or all beyond the last one)
-    const bool active = q < RT && tile_row0 + 16 * q < a.M;
-    const int row_own = tile_row0 + 16 * q + i;
+    const bool active = KS ? (q < 2 && tile_row0 < a.M) : (q < RT && tile_row0 + 16 * q < a.M);
+    const int row_own = tile_row0 + (KS ? 0 : 16 * q) + i;
     const int fi = lds_swizzle(i & 7);
     const int a_off0 = i * kRowBytes + (((0 + g) ^ fi) << 4);
     const int a_off1 = a_off0 ^ 64;   // unit 4+g instead of g (row bases are multiples of 128)
@@ -951,6 +961,100 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       const uint32_t vm = SP ? static_cast<uint32_t>(ldc(reinterpret_cast<const int32_t*>(a.vmask) +
                                                          (long long)b * (a.const_len / 32) + 2 * k + h))
                              : 0xffffffffu;
+      if constexpr (KS) {
+        if (active) {
+          // ---- S^T[key][row] = K . Q^T: this wave's 16 keys x the 16 rows ----
+          f32x4 s1;
+          f32x4 sc1 = f32x4{1.f, 1.f, 1.f, 1.f};   // FP8: scales of the lane's keys 16q + 4g + v
+          if constexpr (!F8) {
+            f32x4 sp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            constexpr int D1 = 4;   // K steps read ahead of their products
+            bf16x8 ka[D1 + 1];
+            const char* kbase = ubuf + q * 16 * kRowBytes;
+#pragma unroll
+            for (int ks = 0; ks < 18 + D1; ++ks) {
+              if (ks < 18)
+                ka[ks % (D1 + 1)] = *reinterpret_cast<const bf16x8*>(
+                    kbase + ((ks & 1) ? a_off1 : a_off0) + 128 * (ks >> 1));
+              const int cs = ks - D1;
+              if (cs >= 0)
+                sp[cs & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[cs % (D1 + 1)], qreg[cs],
+                                                                     sp[cs & 1], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            s1 = sp[0] + sp[1];
+          } else {
+            // the same three-stage pipeline as below, over one key tile
+            f32x4 sp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int cq = q ? co[1] : co[0];
+            u32x4 kc[2];
+            bf16x8 kb[2][2];
+            bf16x8 ra[2];
+#pragma unroll
+            for (int ps = 0; ps < 8 + 2; ++ps) {
+              if (ps < 8) kc[ps & 1] = *reinterpret_cast<const u32x4*>(ubuf + (cq ^ (64 * ps)));
+              if (ps == 0) {
+#pragma unroll
+                for (int rs = 0; rs < 2; ++rs)
+                  ra[rs] = *reinterpret_cast<const bf16x8*>(ubuf + (ro ^ (64 * rs)) + 2048 * q);
+                sc1 = *reinterpret_cast<const f32x4*>(ubuf + kF8UnitScale + 4 * (16 * q + 4 * g));
+              }
+              const int cv = ps - 1;
+              if (cv >= 0 && cv < 8) {
+                const u32x4 wv = kc[cv & 1];
+                kb[cv & 1][0] = e4m3x8_to_bf16(wv[0], wv[1]);
+                kb[cv & 1][1] = e4m3x8_to_bf16(wv[2], wv[3]);
+              }
+              const int cp = ps - 2;
+              if (cp >= 0) {
+                sp[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[cp & 1][0], qreg[2 * cp], sp[0],
+                                                                0, 0, 0);
+                sp[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[cp & 1][1], qreg[2 * cp + 1],
+                                                                sp[1], 0, 0, 0);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int rs = 0; rs < 2; ++rs)
+              sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[rs], qreg[16 + rs], sr, 0, 0, 0);
+            s1 = sc1 * (sp[0] + sp[1]) + sr;
+          }
+
+          // ---- online softmax of row_own over this key tile ----
+          const int key0 = k * kBlock + h * kHalfRows + 16 * q + 4 * g;
+          const bool need_mask = !pvalid || k * kBlock + (h + 1) * kHalfRows > lim_min;
+          const int lim_u = pvalid ? lim : -1;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float xv = s1[v] * a.scale_log2;
+            if (need_mask && key0 + v >= lim_u) xv = -INFINITY;
+            s1[v] = xv;
+            mx = fmaxf(mx, xv);
+          }
+          mx = wave_max_4lanes(mx);
+          const float m_new = fmaxf(m_run, mx);
+          const bool grow = m_new > m_run + kRescaleSlack;
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+          if (grow) m_run = m_new;
+          l_run *= alpha;
+          const float m_use = m_run == -INFINITY ? 0.f : m_run;
+          float lsum = 0.f;
+          bf16x4 pb;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float p = __builtin_amdgcn_exp2f(s1[v] - m_use);
+            lsum += p;
+            pb[v] = (__bf16)(F8 ? p * sc1[v] : p);
+          }
+          l_run += lsum;
+          reinterpret_cast<bf16x4*>(&p_lds[t & 1][0][lane])[q] = pb;
+          if (g == 0) alpha_lds[t & 1][16 * q + i] = alpha;
+          const int any = __any(grow) ? 1 : 0;
+          if (lane == 0) reinterpret_cast<uint8_t*>(&grow_lds[t & 1])[q] = static_cast<uint8_t>(any);
+        }
+      } else {
       if (active) {
 
       // ---- S^T[key][row] = K . Q^T: 32 keys x this wave's 16 rows ----
@@ -1092,6 +1196,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
         if (lane == 0) reinterpret_cast<uint8_t*>(&grow_lds[t & 1])[q] = static_cast<uint8_t>(any);
       }
       }   // active
+      }   // !KS
 
       // ---- next unit; at a piece end publish the row sum and write the LSE ----
       unit_next(a, cb, ck, ch, cL, b1, k1);
@@ -1099,15 +1204,23 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       new_piece = !(more && cb == b);
       if (new_piece && active) {
         const float lt = wave_sum_4lanes(l_run);
-        const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
-        bool whole;
-        const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : n, n, whole);
-        if (g == 0) {
-          lfin_lds[t & 1][16 * q + i] = lt;
-          if (whole)
-            a.lse[(long long)b * a.M + row_own] = lse2 * kLn2;
-          else
-            a.part_lse[slot * a.M + row_own] = lse2;
+        if constexpr (KS) {
+          // the value waves merge the two key tiles and write the LSE
+          if (g == 0) {
+            lfin_lds[t & 1][16 * q + i] = lt;
+            mfin_lds[t & 1][16 * q + i] = m_run;
+          }
+        } else {
+          const float lse2 = lt > 0.f ? m_run + log2f(lt) : -INFINITY;
+          bool whole;
+          const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : n, n, whole);
+          if (g == 0) {
+            lfin_lds[t & 1][16 * q + i] = lt;
+            if (whole)
+              a.lse[(long long)b * a.M + row_own] = lse2 * kLn2;
+            else
+              a.part_lse[slot * a.M + row_own] = lse2;
+          }
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P, alpha, flags, sums written
@@ -1170,10 +1283,13 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
     }
 
     f32x4 o[DL][RT];
+    f32x4 o2[KS ? DL : 1];   // KS: the accumulator of key tile 1 (o holds key tile 0)
 #pragma unroll
-    for (int dl = 0; dl < DL; ++dl)
+    for (int dl = 0; dl < DL; ++dl) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) o[dl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KS) o2[dl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // issue cursor (ib, ik, ih); compute cursor (cb, ck, ch) is one unit behind
     // the score waves
@@ -1286,6 +1402,15 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       bf16x8 pB[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) pB[rt] = p_lds[par][rt][lane];
+      // KS: the two key tiles' operands, each with the other tile's keys zero
+      float al2 = 1.f;
+      bf16x8 pK0 = pB[0], pK1 = pB[0];
+      if constexpr (KS) {
+        al2 = alpha_lds[par][16 + i];
+        const u32x4 pw = __builtin_bit_cast(u32x4, pB[0]);
+        pK0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], 0u, 0u});
+        pK1 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, pw[2], pw[3]});
+      }
       i32x2 vc[DL];   // FP8: transposed code reads
       auto read_vc = [&]() {
         if constexpr (F8) {
@@ -1305,6 +1430,10 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           for (int dl = 0; dl < DL; ++dl) o[dl][rt] *= al[rt];
           __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (KS) {
+#pragma unroll
+          for (int dl = 0; dl < DL; ++dl) o2[dl] *= al2;
+        }
       }
       if constexpr (!kEarlyV) read_vc();
       {
@@ -1315,9 +1444,14 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
           for (int dl = 0; dl < DL; ++dl) {
             bf16x8 nxt = cur;
             if (dl + 1 < DL) nxt = e4m3x8_to_bf16(vc[dl + 1][0], vc[dl + 1][1]);
+            if constexpr (KS) {
+              o[dl][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pK0, o[dl][0], 0, 0, 0);
+              o2[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pK1, o2[dl], 0, 0, 0);
+            } else {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-              o[dl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pB[rt], o[dl][rt], 0, 0, 0);
+              for (int rt = 0; rt < RT; ++rt)
+                o[dl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, pB[rt], o[dl][rt], 0, 0, 0);
+            }
             cur = nxt;
           }
         } else {
@@ -1328,10 +1462,15 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
               if (hl_on) half_load_slot(hl, off[dl + 1], dl + 1);
               __builtin_amdgcn_sched_barrier(0);
             }
+            if constexpr (KS) {
+              o[dl][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pK0, o[dl][0], 0, 0, 0);
+              o2[dl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pK1, o2[dl], 0, 0, 0);
+            } else {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-              o[dl][rt] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pB[rt], o[dl][rt], 0, 0, 0);
+              for (int rt = 0; rt < RT; ++rt)
+                o[dl][rt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dl], pB[rt], o[dl][rt], 0, 0, 0);
+            }
           }
         }
       }
@@ -1342,9 +1481,33 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
       if (!(more && cb == b)) {
         bool whole;
         const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : n, n, whole);
+        // KS: merge the key tiles' sums (each relative to its own reference)
+        // into o[][0] and the row sum; value wave 0 writes the LSE
+        float l_ks = 0.f;
+        if constexpr (KS) {
+          const float l0 = lfin_lds[par][i], l1 = lfin_lds[par][16 + i];
+          const float m0 = mfin_lds[par][i], m1 = mfin_lds[par][16 + i];
+          const float mm = fmaxf(m0, m1);
+          const float e0 = l0 > 0.f ? __builtin_amdgcn_exp2f(m0 - mm) : 0.f;
+          const float e1 = l1 > 0.f ? __builtin_amdgcn_exp2f(m1 - mm) : 0.f;
+          l_ks = l0 * e0 + l1 * e1;
+#pragma unroll
+          for (int dl = 0; dl < DL; ++dl) {
+            o[dl][0] = o[dl][0] * e0 + o2[dl] * e1;
+            o2[dl] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          if (j == 0 && g == 0 && tile_row0 < a.M) {
+            const float lse2 = l_ks > 0.f ? mm + log2f(l_ks) : -INFINITY;
+            const int row = tile_row0 + i;
+            if (whole)
+              a.lse[(long long)b * a.M + row] = lse2 * kLn2;
+            else
+              a.part_lse[slot * a.M + row] = lse2;
+          }
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const float lt = lfin_lds[par][16 * rt + i];
+          const float lt = KS ? l_ks : lfin_lds[par][16 * rt + i];
           const float inv = lt > 0.f ? 1.f / lt : 0.f;
           const int row = tile_row0 + 16 * rt + i;
           if (tile_row0 + 16 * rt >= a.M) {   // rows past the last query row
