@@ -1846,11 +1846,35 @@ __device__ __forceinline__ void acc_read_i(int db, float (&e)[16]) {
   }
 }
 
-__global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const DecodeArgs a) {
+// Sparse mode of the row-wave kernel: one 1 KB slot of a half page, every
+// lane's 16 bytes from its own address (global_load_lds_dwordx4: 64-bit
+// address per lane, LDS destination M0 + 16 * lane), and the row ids of a
+// page (global_load_lds_dword: 4 bytes per lane to M0 + 4 * lane).  Same asm
+// rationale as half_load_slot: the compiler must not track these loads.
+__device__ __forceinline__ void rowwave_sparse_slot(uint32_t m0, const char* src) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a], off"
+               :
+               : [m] "s"(m0), [a] "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void rowwave_rid_load(uint32_t m0, const int32_t* src) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dword %[a], off"
+               :
+               : [m] "s"(m0), [a] "v"(src)
+               : "memory", "m0");
+}
+
+// The row-wave kernel's body.  SP: sparse mode (items of selected entries,
+// every row gathered through its resolved row id; see rowwave_sparse_slot).
+template <bool SP>
+__device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
   constexpr int NBUF = kWSBufs;
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * kHalfBytes];
   __shared__ int plan_lds[8];
   __shared__ int so_lds[kPlanMaxBatch + 1];
+  // sparse: each wave's copy of the row ids of the next two pages to issue
+  // ([wave][page parity][entry]); a wave reads only what it loaded itself
+  __shared__ int rid_lds[SP ? 4 : 1][2][kBlock];
 
   const int tid = threadIdx.x;
   const int w = uni(tid >> 6);
@@ -1869,7 +1893,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
     rtile = x % R;
   }
   int b0, k0, b1, k1, first_split;
-  const bool inplan = a.inplan;
+  const bool inplan = !SP && a.inplan;   // the sparse mode always reads its plan
   if (inplan) {
     if (w == 0) {
       plan_part_wave(a, part, plan_lds, so_lds);
@@ -1899,6 +1923,18 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
   if (!before_end(a, cb, ck, b1, k1)) return;   // uniform: empty part
   int cL = seqlen_of(a, cb);
   const int row = rtile * kRWRows + 32 * w + lr;   // < M (M is a multiple of 128)
+  // Kernel arguments read again from the kernel argument segment where they
+  // are used (through an opaque pointer; the argument block is the kernel's
+  // only parameter), so that the compiler keeps neither them nor addresses
+  // derived from them in registers across the page loop.  The sparse kernel
+  // uses it for the arguments only it needs and for the outputs, which it
+  // has no registers to spare for.
+  auto args = [&]() {
+    typedef const __attribute__((address_space(4))) DecodeArgs* KArgs;
+    KArgs p = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
+    asm volatile("" : "+s"(p));
+    return p;
+  };
   const int tok = row / a.h_q;
 
   auto piece_slot = [&](int b, int pbeg, int pend, int n, bool& whole) {
@@ -1980,12 +2016,45 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
     if (pf_on) {
       const int rows = iL - ik * kBlock;
       pf_rows = rows > kBlock ? kBlock : rows;
-      pf_page = ik < a.bt_stride ? ldc(a.block_table + (long long)ib * a.bt_stride + ik) : -1;
+
+      if constexpr (!SP)
+        pf_page = ik < a.bt_stride ? ldc(a.block_table + (long long)ib * a.bt_stride + ik) : -1;
     }
+  };
+  // sparse: the row ids of the page at the issue cursor are in rid_lds
+  // (parity issued & 1); rid_pre holds the one this lane's next slot needs,
+  // read a slot ahead so that the LDS latency stays off the issue path.
+  // (Entries past the item's end hold entry 0's id: their rows load but
+  // every key there is masked.)  The packed offsets pass through an empty
+  // Slot m's chunk offset in its row (low half-word) and row of the half
+  // (high half-word) are recomputed at each use from an opaque copy of tid,
+  // so that the compiler keeps no per-slot values in registers across the
+  // loop (the sparse kernel has no registers to spare for them).
+  int rid_pre = -1;
+  auto slot_word = [&](int m) {
+    int t2 = tid;
+    asm volatile("" : "+v"(t2));
+    const int p = 256 * (m % 9) + t2;
+    const int r = p / kChunksPerRow;
+    return (((p - r * kChunksPerRow) ^ rw_swizzle(r)) << 4) | (r << 16);
+  };
+  auto read_rid = [&](int m) {
+    const int e = (m / 9) * kHalfRows + (slot_word(m) >> 16);
+    rid_pre = rid_lds[w][(issued - 1) & 1][e];
   };
   auto issue_page = [&]() {
     hl_on = pf_on;
-    if (hl_on) {
+    if constexpr (SP) {
+      if (hl_on) {
+        hla.m0 = uni(static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((MLA_LDS char*)(smem + 2 * (issued & 1) * kHalfBytes)) +
+            w * 1024));
+        hlb.m0 = hla.m0 + kHalfBytes;
+        vring |= 1u << (issued & 1);
+        ++issued;
+        read_rid(0);
+      }
+    } else if (hl_on) {
       const bool in_pool = pf_page >= 0 && (long long)pf_page < a.num_blocks;
       const bool ok = in_pool && pf_rows > 0;
       const char* base = reinterpret_cast<const char*>(a.kcache) +
@@ -2007,7 +2076,42 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
   };
   // slot m of the page: half m / 9, slot m % 9 of that half
   auto issue_slot = [&](int m) {
-    if (hl_on) half_load_slot(m < 9 ? hla : hlb, off[m % 9], m % 9);
+    if constexpr (SP) {
+      if (hl_on) {
+        const int rid = rid_pre;
+        if (m + 1 < 18) read_rid(m + 1);
+        // the lane's 16 bytes: its chunk of its row, read from the row's
+        // cache row (the zero row for an entry that does not count)
+        const int coff = slot_word(m) & 0xffff;
+        const char* src = (rid >= 0 ? reinterpret_cast<const char*>(a.kcache) + (long long)rid * kRowBytes
+                                    : reinterpret_cast<const char*>(a.zero_row)) + coff;
+        rowwave_sparse_slot((m < 9 ? hla.m0 : hlb.m0) + (m % 9) * 0x1000, src);
+      }
+    } else {
+      if (hl_on) half_load_slot(m < 9 ? hla : hlb, off[m % 9], m % 9);
+    }
+  };
+  // sparse: the row ids of the page after the one at the issue cursor
+  // (next = true) or of that page itself, into this wave's rid_lds copy of
+  // parity par, one direct-to-LDS dword per lane; lanes past the item's end
+  // reload entry 0.  An item has ceil(const_len / 64) pages.
+  auto rid_load = [&](int par, bool next) {
+    int rb = ib, rk = ik;
+    if (next) {
+      const int npi = (a.const_len + kBlock - 1) / kBlock;
+      if (++rk == npi) {
+        ++rb;
+        rk = 0;
+      }
+    }
+    if (before_end(a, rb, rk, b1, k1)) {
+      const long long e0 = (long long)rb * a.const_len + rk * kBlock;
+      const int rows = a.const_len - rk * kBlock;
+      const int32_t* src = args()->rowids + e0 + (lane < rows ? lane : 0);
+      const uint32_t m0 = uni(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((MLA_LDS int*)(&rid_lds[w][par][0]))));
+      rowwave_rid_load(m0, src);
+    }
   };
   auto wait_page = [&](int p) {
     wait_loads_behind<2 * kHalfLoadsPerWave, 1>(issued - p - 1);
@@ -2015,6 +2119,11 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
 
   // page 0, all slots at once; page 1's id on its way
   prefetch_page(false);
+  if constexpr (SP) {
+    rid_load(0, false);   // pages 0 and 1
+    rid_load(1, true);
+    vm_wait<0>();
+  }
   issue_page();
 #pragma unroll
   for (int m = 0; m < 18; ++m) issue_slot(m);
@@ -2047,15 +2156,19 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
     bool whole;
     const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : npg, npg, whole);
     const float linv = lt > 0.f ? 1.f / lt : 0.f;
+    float* const lse_p = SP ? args()->lse : a.lse;
+    float* const plse_p = SP ? args()->part_lse : a.part_lse;
+    uint16_t* const out_p = SP ? args()->out : a.out;
+    float* const po_p = SP ? args()->part_o : a.part_o;
     if (lh == 0) {
       if (whole)
-        a.lse[(long long)b * a.M + row] = lse2 * kLn2;
+        lse_p[(long long)b * a.M + row] = lse2 * kLn2;
       else
-        a.part_lse[slot * a.M + row] = lse2;
+        plse_p[slot * a.M + row] = lse2;
     }
     acc_drain();
     if (whole) {
-      uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + 4 * lh;
+      uint16_t* op = out_p + ((long long)b * a.M + row) * kDV + 4 * lh;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         float e[16];
@@ -2068,7 +2181,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
         }
       }
     } else {
-      float* op = a.part_o + (slot * a.M + row) * kDV + 4 * lh;
+      float* op = po_p + (slot * a.M + row) * kDV + 4 * lh;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         float e[16];
@@ -2101,14 +2214,16 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
   bool resc_any = false;
   // kbase: position of the half's first key; valid: its page is in the pool;
   // restart: the half starts a piece
+  // vmh (sparse): bit e says whether entry kbase + e counts
   auto softmax_step = [&](int st, f32x16& sv, bf16x8 (&pv)[2], int kbase, bool valid,
-                          bool restart) {
+                          bool restart, uint32_t vmh) {
     if (st == 0) {
       if (restart) {
         m_run = -INFINITY;
         l_run = 0.f;
       }
-      const bool need_mask = scale_neg || !valid || kbase + kHalfRows > lim_min;
+      const bool need_mask = scale_neg || !valid || kbase + kHalfRows > lim_min ||
+                             (SP && vmh != ~0u);
       if (!need_mask) {
         float m0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
         float m1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
@@ -2130,6 +2245,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
           for (int i = 0; i < 4; ++i) {
             float xv = sv[4 * j + i] * a.scale_log2;
             if (key0 + 8 * j + i >= lim_u) xv = -INFINITY;
+            if (SP && !((vmh >> (8 * j + 4 * lh + i)) & 1u)) xv = -INFINITY;
             sv[4 * j + i] = xv;
             mx = fmaxf(mx, xv);
           }
@@ -2167,7 +2283,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
   // innermost, V read D2 products ahead; with SMX the softmax steps of
   // another half sit between its products.
   auto value_product = [&](const char* vbuf, bf16x8 (&pv)[2], bool smx, f32x16& s2,
-                           bf16x8 (&p2)[2], int kb2, bool valid2) {
+                           bf16x8 (&p2)[2], int kb2, bool valid2, uint32_t vm2) {
     constexpr int D2 = 2;
     bf16x4 vlo[D2 + 1], vhi[D2 + 1];
     auto read_v = [&](int st) {
@@ -2188,13 +2304,13 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
       acc_mfma_i(i & 15, va, pv[i >> 4]);
       // the other half's exponentials come after the products that read
       // P[0], so that its P[0] can take those registers
-      if (smx && i == 2) softmax_step(0, s2, p2, kb2, valid2, false);
-      if (smx && i == 4) softmax_step(1, s2, p2, kb2, valid2, false);
-      if (smx && i >= 16) softmax_step(i - 14, s2, p2, kb2, valid2, false);
+      if (smx && i == 2) softmax_step(0, s2, p2, kb2, valid2, false, vm2);
+      if (smx && i == 4) softmax_step(1, s2, p2, kb2, valid2, false, vm2);
+      if (smx && i >= 16) softmax_step(i - 14, s2, p2, kb2, valid2, false, vm2);
       asm volatile("" ::"v"(va));   // operand registers held past the product's issue
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (smx) softmax_step(kSmxSteps - 1, s2, p2, kb2, valid2, false);
+    if (smx) softmax_step(kSmxSteps - 1, s2, p2, kb2, valid2, false, vm2);
     // the last products may still read P: wait states before its registers
     // can be reused
     asm volatile("s_nop 7" ::"v"(pv[0]), "v"(pv[1]));
@@ -2205,7 +2321,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
   // softmax steps of another half sit between them too.
   constexpr int D1 = 3;
   auto score_chain = [&](const char* kbuf, f32x16& sacc, int slot0, bool smx, f32x16& s2,
-                         bf16x8 (&p2)[2], int kb2, bool valid2, bool restart2) {
+                         bf16x8 (&p2)[2], int kb2, bool valid2, bool restart2, uint32_t vm2) {
     constexpr int NK = D1 + 1;   // K operand ring: a slot is rewritten one step after its product
     bf16x8 ka[NK];
     auto read_k = [&](int ks) {
@@ -2234,7 +2350,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
       }
       if ((i & 3) == 1) issue_slot(slot0 + (i >> 2));
       if (smx && i >= 2 && i - 2 < kSmxSteps)
-        softmax_step(i - 2, s2, p2, kb2, valid2, restart2);
+        softmax_step(i - 2, s2, p2, kb2, valid2, restart2, vm2);
       // the product may still be reading its K operand: the register stays
       // allocated (no VALU result lands in it) until here.  (Only this step's
       // operand: naming the register of a read still in flight would make
@@ -2259,7 +2375,16 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
       load_q(cb);
       q_ready();
     }
+    // sparse: validity words of page t's halves (bit e: entry e counts)
+    uint32_t vm_a = ~0u, vm_b = ~0u;
+    if constexpr (SP) {
+      const uint32_t* vw = args()->vmask + (long long)cb * (a.const_len / 32) + 2 * ck;
+      vm_a = static_cast<uint32_t>(ldc(reinterpret_cast<const int32_t*>(vw)));
+      vm_b = (ck + 1) * kBlock > a.const_len ? 0u
+                                              : static_cast<uint32_t>(ldc(reinterpret_cast<const int32_t*>(vw + 1)));
+    }
     issue_page();   // page t + 1 into the other slot
+    if constexpr (SP) rid_load(t & 1, true);   // page t + 2: lands by this phase's end
     const char* bufa = smem + 2 * (t & 1) * kHalfBytes;
     const char* bufb = bufa + kHalfBytes;
     const int kb = ck * kBlock;
@@ -2267,12 +2392,12 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
     bf16x8 pa[2], pb[2];
     // (a page of 32 rows or fewer runs half B too: its rows were loaded as
     // zeros and all of its keys are masked)
-    score_chain(bufa, sa, 0, false, sa, pa, kb, valid, first);
-    score_chain(bufb, sb, 9, true, sa, pa, kb, valid, first);
+    score_chain(bufa, sa, 0, false, sa, pa, kb, valid, first, vm_a);
+    score_chain(bufb, sb, 9, true, sa, pa, kb, valid, first, vm_a);
     if (resc_any) acc_scale_all(alpha);
-    value_product(bufa, pa, true, sb, pb, kb + kHalfRows, valid);
+    value_product(bufa, pa, true, sb, pb, kb + kHalfRows, valid, vm_b);
     if (resc_any) acc_scale_all(alpha);
-    value_product(bufb, pb, false, sb, pb, kb + kHalfRows, valid);
+    value_product(bufb, pb, false, sb, pb, kb + kHalfRows, valid, vm_b);
 
     // the compute cursor moves to the next page; a piece ends with its request
     const int pbi = cb;
@@ -2292,6 +2417,17 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const Decode
     wg_barrier();   // page t + 1 landed in every wave's slots; page t's slot is free
     ++t;
   }
+}
+
+__global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_kernel(const DecodeArgs a) {
+  rowwave_body<false>(a);
+}
+
+// Sparse mode (bf16 cache): the item's selected entries in pages of 64, each
+// row gathered from its resolved cache row (or the zero row), entries that do
+// not count masked by their validity bits.
+__global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_sparse_kernel(const DecodeArgs a) {
+  rowwave_body<true>(a);
 }
 
 // FP8 unit of the row-wave kernel in LDS: code rows padded to 33 16-byte
@@ -2894,16 +3030,21 @@ hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, 
 hipError_t launch_splitkv(const DecodeArgs& args, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
   DecodeArgs a = args;
-  if (!a.sparse && a.M % kRWRows == 0) {
+  // 128-row tiles: the row-wave kernels (dense over either cache format,
+  // sparse over the bf16 cache)
+  if (a.M % kRWRows == 0 && !(a.sparse && a.kv_fp8)) {
     a.row_tile_rows = kRWRows;
     a.row_tiles = a.M / kRWRows;
     const dim3 grid(a.num_parts * a.row_tiles);
     const dim3 block(kRWThreads);
-    const void* kern = a.kv_fp8 ? reinterpret_cast<const void*>(&mla_rowwave_f8_kernel)
-                                : reinterpret_cast<const void*>(&mla_rowwave_kernel);
+    const void* kern = a.sparse   ? reinterpret_cast<const void*>(&mla_rowwave_sparse_kernel)
+                       : a.kv_fp8 ? reinterpret_cast<const void*>(&mla_rowwave_f8_kernel)
+                                  : reinterpret_cast<const void*>(&mla_rowwave_kernel);
     void* kargs[] = {&a};
     if (start == nullptr && stop == nullptr) {
-      if (a.kv_fp8)
+      if (a.sparse)
+        hipLaunchKernelGGL(mla_rowwave_sparse_kernel, grid, block, 0, stream, a);
+      else if (a.kv_fp8)
         hipLaunchKernelGGL(mla_rowwave_f8_kernel, grid, block, 0, stream, a);
       else
         hipLaunchKernelGGL(mla_rowwave_kernel, grid, block, 0, stream, a);
