@@ -50,106 +50,116 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "130cd4231b68ea28c5b0fbc7bd90669a65930818fc91805e5b917855e27afbf2",
-        "fetch_bytes": 306999109,
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 306999426,
         "write_bytes": 8404992,
-        "fetch_scale": 1.99986,
+        "fetch_scale": 1.99988,
         "write_scale": 1.0,
-        "mfma_util": 0.0568
+        "mfma_util": 0.0812
     },
     "ridge": {
-        "kernel_sha256": "130cd4231b68ea28c5b0fbc7bd90669a65930818fc91805e5b917855e27afbf2",
-        "fetch_bytes": 722800187,
-        "write_bytes": 93390688,
-        "fetch_scale": 1.99989,
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 722837321,
+        "write_bytes": 93418272,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3944
+        "mfma_util": 0.3881
     },
     "long": {
-        "kernel_sha256": "130cd4231b68ea28c5b0fbc7bd90669a65930818fc91805e5b917855e27afbf2",
-        "fetch_bytes": 774442583,
-        "write_bytes": 69608809,
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 774481760,
+        "write_bytes": 69610393,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4257
+        "mfma_util": 0.4166
     },
     "ragged": {
-        "kernel_sha256": "130cd4231b68ea28c5b0fbc7bd90669a65930818fc91805e5b917855e27afbf2",
-        "fetch_bytes": 528743745,
-        "write_bytes": 118483104,
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 528802622,
+        "write_bytes": 118483449,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4294
+        "mfma_util": 0.431
     },
     "draft": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 210932775,
-        "write_bytes": 58843136,
-        "fetch_scale": 1.99993,
-        "write_scale": 1.0
-    },
-    "sparse": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 171351819,
-        "write_bytes": 33619968,
-        "fetch_scale": 1.99986,
-        "write_scale": 1.0
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 228850180,
+        "write_bytes": 94557296,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0,
+        "mfma_util": 0.4278
     },
     "prefill": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 405363435,
-        "write_bytes": 92569600,
-        "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 424842417,
+        "write_bytes": 142966784,
+        "fetch_scale": 1.99993,
+        "write_scale": 1.0,
+        "mfma_util": 0.4935
+    },
+    "sparse": {
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 189843558,
+        "write_bytes": 69193635,
+        "fetch_scale": 1.9999,
+        "write_scale": 1.0,
+        "mfma_util": 0.1952
     },
     "membound/fp8": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 173871138,
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 173880421,
         "write_bytes": 8404992,
-        "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "fetch_scale": 1.99986,
+        "write_scale": 1.0,
+        "mfma_util": 0.1104
     },
     "ridge/fp8": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 410163666,
-        "write_bytes": 59894272,
-        "fetch_scale": 1.99989,
-        "write_scale": 1.0
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 428652739,
+        "write_bytes": 93378163,
+        "fetch_scale": 1.9999,
+        "write_scale": 1.0,
+        "mfma_util": 0.3059
     },
     "long/fp8": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 438015799,
-        "write_bytes": 37559808,
-        "fetch_scale": 1.99993,
-        "write_scale": 1.0
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 442130050,
+        "write_bytes": 69603843,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0,
+        "mfma_util": 0.3173
     },
     "ragged/fp8": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 310500893,
-        "write_bytes": 78838784,
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 329074510,
+        "write_bytes": 118482944,
         "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "write_scale": 1.0,
+        "mfma_util": 0.3134
     },
     "draft/fp8": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 133711684,
-        "write_bytes": 58843136,
-        "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 151877019,
+        "write_bytes": 94556265,
+        "fetch_scale": 1.99989,
+        "write_scale": 1.0,
+        "mfma_util": 0.3108
     },
     "prefill/fp8": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 264231629,
-        "write_bytes": 92569600,
-        "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 283991345,
+        "write_bytes": 142966784,
+        "fetch_scale": 1.9999,
+        "write_scale": 1.0,
+        "mfma_util": 0.3519
     },
     "sparse/fp8": {
-        "kernel_sha256": "41fa654bfc7fd6e170fafef236f00be874a6a88e8a4352dd7ab1d2c46805e3df",
-        "fetch_bytes": 114837473,
-        "write_bytes": 33619968,
+        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
+        "fetch_bytes": 134913147,
+        "write_bytes": 67239936,
         "fetch_scale": 1.99992,
-        "write_scale": 1.0
+        "write_scale": 1.0,
+        "mfma_util": 0.1505
     }
 }
 
