@@ -242,9 +242,9 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
 def splitkv_kernel_name(m_rows: int, kv: str = "bf16", sparse: bool = False) -> str:
     """HIP kernel that the decode launches for m_rows query rows per request
     (per item in the sparse mode)."""
-    if m_rows % 128 == 0 and not (sparse and kv == "fp8"):
+    if m_rows % 128 == 0:
         if sparse:
-            return "mla_rowwave_sparse_kernel"
+            return "mla_rowwave_sparse_kernel" if kv == "bf16" else "mla_rowwave_f8_sparse_kernel"
         return "mla_rowwave_kernel" if kv == "bf16" else "mla_rowwave_f8_kernel"
     rt = 1 if m_rows <= 16 else 2 if m_rows <= 32 else 4
     f = lambda x: "true" if x else "false"

@@ -1857,6 +1857,12 @@ __device__ __forceinline__ void rowwave_sparse_slot(uint32_t m0, const char* src
                : [m] "s"(m0), [a] "v"(src)
                : "memory", "m0");
 }
+__device__ __forceinline__ void rowwave_sparse_dword(uint32_t m0, const char* src) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dword %[a], off"
+               :
+               : [m] "s"(m0), [a] "v"(src)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void rowwave_rid_load(uint32_t m0, const int32_t* src) {
   asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dword %[a], off"
                :
@@ -2471,12 +2477,15 @@ __device__ __forceinline__ void f8_slot_x1(__amdgpu_buffer_rsrc_t r, uint32_t m0
 //  * values: the transposing 8-bit read hands a lane dim d of eight keys,
 //    converted to bf16; P carries the key's scale (P' = bf16(p * scale)),
 //    the row sum takes p itself.
-__global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const DecodeArgs a) {
+template <bool SP>
+__device__ __forceinline__ void rowwave_f8_body(const DecodeArgs& a) {
   constexpr int kSlots = 3;                      // page slots of the ring
   constexpr int kUnit = kF8RwUnit;               // one half page
   __shared__ __attribute__((aligned(1024))) char smem[kSlots * 2 * kUnit];
   __shared__ int plan_lds[8];
   __shared__ int so_lds[kPlanMaxBatch + 1];
+  // sparse: each wave's copy of the row ids of two pages ([wave][page parity][entry])
+  __shared__ int rid_lds[SP ? 4 : 1][2][kBlock];
 
   const int tid = threadIdx.x;
   const int w = uni(tid >> 6);
@@ -2495,7 +2504,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
     rtile = x % R;
   }
   int b0, k0, b1, k1, first_split;
-  const bool inplan = a.inplan;
+  const bool inplan = !SP && a.inplan;   // the sparse mode always reads its plan
   if (inplan) {
     if (w == 0) {
       plan_part_wave(a, part, plan_lds, so_lds);
@@ -2526,6 +2535,16 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
   int cL = seqlen_of(a, cb);
   const int row = rtile * kRWRows + 32 * w + lr;   // < M (M is a multiple of 128)
   const int tok = row / a.h_q;
+  // Kernel arguments read again from the kernel argument segment where they
+  // are used (through an opaque pointer; the argument block is the kernel's
+  // only parameter), so that the compiler keeps neither them nor addresses
+  // derived from them in registers across the page loop (sparse mode).
+  auto args = [&]() {
+    typedef const __attribute__((address_space(4))) DecodeArgs* KArgs;
+    KArgs p = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
+    asm volatile("" : "+s"(p));
+    return p;
+  };
 
   auto piece_slot = [&](int b, int pbeg, int pend, int n, bool& whole) {
     whole = pbeg == 0 && pend == n;
@@ -2558,8 +2577,22 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
   bf16x8 qreg[36];
   // qreg[2p + e] = dims 32p + 16lh + 8e .. +8 (latent), qreg[32 + s] = dims
   // 512 + 16s + 8lh .. +8 (rope)
+  // Sparse: the lane id counted afresh where it is used (an asm the
+  // compiler cannot merge with another), and the row rebuilt from it, so
+  // that neither is kept, and spilled, across the page loop.
+  auto lane_now = [&]() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+  };
+  auto row_at = [&]() {
+    if constexpr (SP)
+      return uni(rtile * kRWRows + 32 * w) + (lane_now() & 31);
+    else
+      return row;
+  };
   auto load_q = [&](int b) {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + ((long long)b * a.M + row) * kDK);
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + ((long long)b * a.M + row_at()) * kDK);
 #pragma unroll
     for (int pp = 0; pp < 16; ++pp) {
       qreg[2 * pp] = qp[4 * pp + 2 * lh];
@@ -2611,11 +2644,41 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
     return (r < kHalfRows && c < 8) ? r * 128 + 16 * c : kNoLoad;
   };
   int offc[4], offr, offx;
+  // sparse: per slot m (0..5) a 16-bit word, two slots to a register
+  // (spk[m >> 1], half m & 1): the row of the unit that the lane's bytes
+  // belong to (bits 11-15), the region (bits 9-10: 0 codes, 1 rope, 2
+  // scales, 3 nothing) and the 16-byte unit in the row (bits 0-8)
+  int spk[3];
+  if constexpr (SP) {
+    auto word = [&](int m) {
+      const bool code = m < 4 || (m == 5 && w == 0);
+      const bool rope = m == 4 || (m == 5 && w == 1);
+      int r = 0, kind = 3, c = 0;
+      if (code) {
+        const int q = 64 * (m < 4 ? 4 * m + w : 16) + lane;
+        r = q / 33;
+        c = q - 33 * r;
+        kind = (r < kHalfRows && c < 32) ? 0 : 3;
+      } else if (rope) {
+        const int q = 64 * (m == 4 ? w : 4) + lane;
+        r = q / 9;
+        c = q - 9 * r;
+        kind = (r < kHalfRows && c < 8) ? 1 : 3;
+      } else if (w == 2) {
+        r = lane;
+        kind = lane < kHalfRows ? 2 : 3;
+      }
+      return ((r < kHalfRows ? r : 0) << 11) | (kind << 9) | c;
+    };
 #pragma unroll
-  for (int k = 0; k < 4; ++k) offc[k] = code_off(64 * (4 * k + w) + lane);
-  offr = rope_off(64 * w + lane);
-  offx = w == 0 ? code_off(64 * 16 + lane) : w == 1 ? rope_off(64 * 4 + lane)
-                                             : (lane < kHalfRows ? 4 * lane : kNoLoad);
+    for (int k = 0; k < 3; ++k) spk[k] = word(2 * k) | (word(2 * k + 1) << 16);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) offc[k] = code_off(64 * (4 * k + w) + lane);
+    offr = rope_off(64 * w + lane);
+    offx = w == 0 ? code_off(64 * 16 + lane) : w == 1 ? rope_off(64 * 4 + lane)
+                                               : (lane < kHalfRows ? 4 * lane : kNoLoad);
+  }
   bool pf_on = false;       // a page is at the issue cursor
   int pf_page = -1, pf_rows = 0;
   bool hl_on = false;       // the slots of an issued page are pending
@@ -2629,12 +2692,70 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
     if (pf_on) {
       const int rows = iL - ik * kBlock;
       pf_rows = rows > kBlock ? kBlock : rows;
-      pf_page = ik < a.bt_stride ? ldc(a.block_table + (long long)ib * a.bt_stride + ik) : -1;
+      if constexpr (!SP)
+        pf_page = ik < a.bt_stride ? ldc(a.block_table + (long long)ib * a.bt_stride + ik) : -1;
+    }
+  };
+  // Sparse: a lane's part of slot m (0..5) of unit u: the entry (row of the
+  // page) it loads, and the byte offset in a cache page of its data relative
+  // to that row's own (-1 for a lane that loads nothing), unpacked from the
+  // slot's word through an empty asm so that the compiler keeps only the
+  // packed words across the loop.
+  // returns the byte offset of the lane's data in a cache page relative to
+  // its row's own (-1: nothing to load); *e receives the entry; *stride the
+  // region's row pitch
+  auto sp_lane = [&](int u, int m, int* e, int* stride) {
+    int pk = spk[m >> 1];
+    asm volatile("" : "+v"(pk));
+    // (unsigned: a row of 16 or more sets bit 31 of the upper word)
+    const int wd = static_cast<int>((m & 1) ? (static_cast<uint32_t>(pk) >> 16)
+                                            : (static_cast<uint32_t>(pk) & 0xffffu));
+    *e = u * kHalfRows + (wd >> 11);
+    const int kind = (wd >> 9) & 3, c = wd & 511;
+    *stride = kind == 0 ? kF8Latent : kind == 1 ? 128 : 4;
+    return kind == 3 ? -1 : kind == 0 ? 16 * c : kind == 1 ? kF8RopeOff + 16 * c : kF8ScaleOff;
+  };
+  // the row id of this lane's next slot, read from rid_lds a slot ahead
+  int rid_pre = -1;
+  auto read_rid = [&](int u, int m) {
+    int e, st;
+    (void)sp_lane(u, m, &e, &st);
+    rid_pre = rid_lds[w][(issued - 1) & 1][e];
+  };
+  // the row ids of the page after the one at the issue cursor (next) or of
+  // that page, into this wave's rid_lds copy of parity par, one
+  // direct-to-LDS dword per lane; lanes past the item's end reload entry 0
+  auto rid_load = [&](int par, bool next) {
+    int rb = ib, rk = ik;
+    if (next) {
+      const int npi = (a.const_len + kBlock - 1) / kBlock;
+      if (++rk == npi) {
+        ++rb;
+        rk = 0;
+      }
+    }
+    if (before_end(a, rb, rk, b1, k1)) {
+      const long long e0 = (long long)rb * a.const_len + rk * kBlock;
+      const int rows = a.const_len - rk * kBlock;
+      const int ln = lane_now();
+      const int32_t* src = args()->rowids + e0 + (ln < rows ? ln : 0);
+      const uint32_t m0 = uni(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((MLA_LDS int*)(&rid_lds[w][par][0]))));
+      rowwave_rid_load(m0, src);
     }
   };
   auto issue_page = [&]() {
     hl_on = pf_on;
-    if (hl_on) {
+    if constexpr (SP) {
+      if (hl_on) {
+        const int sl = issued % kSlots;
+        hl_m0 = uni(static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((MLA_LDS char*)(smem + 2 * sl * kUnit))));
+        vring |= 1u << sl;
+        ++issued;
+        read_rid(0, 0);
+      }
+    } else if (hl_on) {
       const bool in_pool = pf_page >= 0 && (long long)pf_page < a.num_blocks;
       const bool ok = in_pool && pf_rows > 0;
       hl_pg = reinterpret_cast<const char*>(a.kcache) + (ok ? (long long)pf_page * kF8PageBytes : 0);
@@ -2651,6 +2772,31 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
   // 4m + w (m < 4), rope slot w (m = 4), the extra one (m = 5)
   auto issue_slot = [&](int u, int m) {
     if (!hl_on || (m == 5 && w == 3)) return;
+    if constexpr (SP) {
+      const int rid = rid_pre;
+      // the next slot's row id (unit 1 follows unit 0; wave 3 has no slot 5)
+      const int last = w == 3 ? 4 : 5;
+      if (m < last)
+        read_rid(u, m + 1);
+      else if (u == 0)
+        read_rid(1, 0);
+      int e, stride;
+      const int off = sp_lane(u, m, &e, &stride);
+      const char* src = (off >= 0 && rid >= 0)
+                            ? reinterpret_cast<const char*>(a.kcache) +
+                                  (long long)(rid >> 6) * kF8PageBytes + off + (rid & 63) * stride
+                            : reinterpret_cast<const char*>(a.zero_row);
+      const uint32_t ub = hl_m0 + u * kUnit;
+      const bool code = m < 4 || (m == 5 && w == 0);
+      const bool rope = m == 4 || (m == 5 && w == 1);
+      if (code)
+        rowwave_sparse_slot(ub + (m < 4 ? 4 * m + w : 16) * 1024, src);
+      else if (rope)
+        rowwave_sparse_slot(ub + kF8RwRope + (m == 4 ? w : 4) * 1024, src);
+      else
+        rowwave_sparse_dword(ub + kF8RwScale, src);
+      return;
+    }
     int ru = hl_rows - u * kHalfRows;
     ru = ru < 0 ? 0 : (ru > kHalfRows ? kHalfRows : ru);
     const uint32_t ub = hl_m0 + u * kUnit;
@@ -2688,9 +2834,15 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
 
   // pages 0 and 1, all slots at once; page 2's id on its way
   prefetch_page(false);
+  if constexpr (SP) {
+    rid_load(0, false);   // pages 0 and 1
+    rid_load(1, true);
+    vm_wait<0>();
+  }
 #pragma unroll
   for (int pg = 0; pg < 2; ++pg) {
     issue_page();
+    if (SP && pg == 1) rid_load(0, true);   // page 2, ahead of page 1's slots
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -2708,8 +2860,8 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
   // ---- per piece (the run of the part's pages of one request) ----
   float m_run = -INFINITY, l_run = 0.f;   // running max (log2 units) and sum of the lane's row
   int pbeg = ck, npg = n_pages(cL);
-  int lim = a.causal ? cL - a.s_q + 1 + tok : cL;
-  int lim_min = a.causal ? cL - a.s_q + 1 : cL;
+  int lim = (!SP && a.causal) ? cL - a.s_q + 1 + tok : cL;
+  int lim_min = (!SP && a.causal) ? cL - a.s_q + 1 : cL;
   bool first = true;        // the phase's page starts a piece
 
   // O / l of the finished piece: bf16 to out for a whole request, fp32
@@ -2725,15 +2877,20 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
     bool whole;
     const long long slot = piece_slot(b, pbeg, (b == b1) ? k1 : npg, npg, whole);
     const float linv = lt > 0.f ? 1.f / lt : 0.f;
+    float* const lse_p = SP ? args()->lse : a.lse;
+    float* const plse_p = SP ? args()->part_lse : a.part_lse;
+    uint16_t* const out_p = SP ? args()->out : a.out;
+    float* const po_p = SP ? args()->part_o : a.part_o;
+    const int rr = row_at();
     if (lh == 0) {
       if (whole)
-        a.lse[(long long)b * a.M + row] = lse2 * kLn2;
+        lse_p[(long long)b * a.M + rr] = lse2 * kLn2;
       else
-        a.part_lse[slot * a.M + row] = lse2;
+        plse_p[slot * a.M + rr] = lse2;
     }
     acc_drain();
     if (whole) {
-      uint16_t* op = a.out + ((long long)b * a.M + row) * kDV + 4 * lh;
+      uint16_t* op = out_p + ((long long)b * a.M + rr) * kDV + 4 * lh;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         float e[16];
@@ -2746,7 +2903,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
         }
       }
     } else {
-      float* op = a.part_o + (slot * a.M + row) * kDV + 4 * lh;
+      float* op = po_p + (slot * a.M + rr) * kDV + 4 * lh;
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         float e[16];
@@ -2781,14 +2938,16 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
   // restart: the half starts a piece
   // ubuf: the half's unit (the key scales: element 4j + i is key 8j + 4lh + i)
   f32x4 ksc, ksc_n;   // scales of elements 4j .. 4j+3, and of the next group (read ahead)
+  // vmh (sparse): bit e says whether entry kbase + e counts
   auto softmax_step = [&](int st, f32x16& sv, bf16x8 (&pv)[2], int kbase, bool valid,
-                          bool restart, const char* ubuf) {
+                          bool restart, const char* ubuf, uint32_t vmh) {
     if (st == 0) {
       if (restart) {
         m_run = -INFINITY;
         l_run = 0.f;
       }
-      const bool need_mask = scale_neg || !valid || kbase + kHalfRows > lim_min;
+      const bool need_mask = scale_neg || !valid || kbase + kHalfRows > lim_min ||
+                             (SP && vmh != ~0u);
       if (!need_mask) {
         float m0 = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
         float m1 = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
@@ -2810,6 +2969,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
           for (int i = 0; i < 4; ++i) {
             float xv = sv[4 * j + i] * a.scale_log2;
             if (key0 + 8 * j + i >= lim_u) xv = -INFINITY;
+            if (SP && !((vmh >> (8 * j + 4 * lh + i)) & 1u)) xv = -INFINITY;
             sv[4 * j + i] = xv;
             mx = fmaxf(mx, xv);
           }
@@ -2828,12 +2988,20 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
       l_run *= alpha;
       neg_m = m_run == -INFINITY ? 0.f : -m_run;
       lsum = 0.f;
-      ksc_n = *reinterpret_cast<const f32x4*>(ubuf + kF8RwScale + 4 * (4 * lh));
+      if constexpr (SP)   // (sparse: no read-ahead, for the gather's registers)
+        ksc = *reinterpret_cast<const f32x4*>(ubuf + kF8RwScale + 4 * (4 * lh));
+      else
+        ksc_n = *reinterpret_cast<const f32x4*>(ubuf + kF8RwScale + 4 * (4 * lh));
     } else if (st < 18) {
       const int e = st - 2;
-      if ((e & 3) == 0) ksc = ksc_n;
-      if ((e & 3) == 1 && e < 12)   // the next group's scales, three steps ahead
-        ksc_n = *reinterpret_cast<const f32x4*>(ubuf + kF8RwScale + 4 * (2 * (e + 3) + 4 * lh));
+      if constexpr (SP) {
+        if ((e & 3) == 0 && e > 0)
+          ksc = *reinterpret_cast<const f32x4*>(ubuf + kF8RwScale + 4 * (2 * e + 4 * lh));
+      } else {
+        if ((e & 3) == 0) ksc = ksc_n;
+        if ((e & 3) == 1 && e < 12)   // the next group's scales, three steps ahead
+          ksc_n = *reinterpret_cast<const f32x4*>(ubuf + kF8RwScale + 4 * (2 * (e + 3) + 4 * lh));
+      }
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], cx, neg_m));
       lsum += p;
       // the value operand holds raw codes: P carries the key's scale
@@ -2854,8 +3022,9 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
   // D2 products ahead), converted exactly to bf16.  With SMX the softmax
   // steps of another half sit between its products.
   auto value_product = [&](const char* vbuf, bf16x8 (&pv)[2], bool smx, f32x16& s2,
-                           bf16x8 (&p2)[2], int kb2, bool valid2, const char* ubuf2) {
-    constexpr int D2 = 2;
+                           bf16x8 (&p2)[2], int kb2, bool valid2, const char* ubuf2,
+                           uint32_t vm2) {
+    constexpr int D2 = SP ? 1 : 2;   // (sparse: one read less in flight, for the gather's registers)
     i32x2 vc[D2 + 1];
     auto read_v = [&](int st) {
       const int u = st >> 4, db = st & 15;
@@ -2873,13 +3042,13 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
       acc_mfma_i(i & 15, va, pv[i >> 4]);
       // the other half's exponentials come after the products that read
       // P[0], so that its P[0] can take those registers
-      if (smx && i == 2) softmax_step(0, s2, p2, kb2, valid2, false, ubuf2);
-      if (smx && i == 4) softmax_step(1, s2, p2, kb2, valid2, false, ubuf2);
-      if (smx && i >= 16) softmax_step(i - 14, s2, p2, kb2, valid2, false, ubuf2);
+      if (smx && i == 2) softmax_step(0, s2, p2, kb2, valid2, false, ubuf2, vm2);
+      if (smx && i == 4) softmax_step(1, s2, p2, kb2, valid2, false, ubuf2, vm2);
+      if (smx && i >= 16) softmax_step(i - 14, s2, p2, kb2, valid2, false, ubuf2, vm2);
       asm volatile("" ::"v"(va));   // operand registers held past the product's issue
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (smx) softmax_step(kSmxSteps - 1, s2, p2, kb2, valid2, false, ubuf2);
+    if (smx) softmax_step(kSmxSteps - 1, s2, p2, kb2, valid2, false, ubuf2, vm2);
     // the last products may still read P: wait states before its registers
     // can be reused
     asm volatile("s_nop 7" ::"v"(pv[0]), "v"(pv[1]));
@@ -2892,7 +3061,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
   // half sit between them too.  BLK: the half's pinned accumulator block.
   auto score_chain = [&](const char* kbuf, f32x16& sacc, int U, bool smx, f32x16& s2,
                          bf16x8 (&p2)[2], int kb2, bool valid2, bool restart2,
-                         const char* ubuf2) {
+                         const char* ubuf2, uint32_t vm2) {
     u32x4 kc[2];
     auto read_c = [&](int pp) {
       kc[pp & 1] = *reinterpret_cast<const u32x4*>(kbuf + kco + 32 * pp);
@@ -2926,7 +3095,7 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
       mfma(i, kv, qreg[i]);
       if (i % 6 == 1) issue_slot(U, i / 6);
       if (smx && i >= 2 && i - 2 < kSmxSteps)
-        softmax_step(i - 2, s2, p2, kb2, valid2, restart2, ubuf2);
+        softmax_step(i - 2, s2, p2, kb2, valid2, restart2, ubuf2, vm2);
       asm volatile("" ::"v"(kv));   // the product's operand stays allocated until here
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -2962,7 +3131,16 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
       load_q(cb);
       q_ready();
     }
+    // sparse: validity words of page t's halves (bit e: entry e counts)
+    uint32_t vm_a = ~0u, vm_b = ~0u;
+    if constexpr (SP) {
+      const uint32_t* vw = args()->vmask + (long long)cb * (a.const_len / 32) + 2 * ck;
+      vm_a = static_cast<uint32_t>(ldc(reinterpret_cast<const int32_t*>(vw)));
+      vm_b = (ck + 1) * kBlock > a.const_len ? 0u
+                                              : static_cast<uint32_t>(ldc(reinterpret_cast<const int32_t*>(vw + 1)));
+    }
     issue_page();   // page t + 2 into the slot of page t - 1
+    if constexpr (SP) rid_load((t + 1) & 1, true);   // page t + 3, ahead of page t + 2's slots
     const char* bufa = smem + 2 * slot * kUnit;
     const char* bufb = bufa + kUnit;
     const int kb = ck * kBlock;
@@ -2970,12 +3148,12 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
     bf16x8 pa[2], pb[2];
     // (a page of 32 rows or fewer runs half B too: its rows were loaded as
     // zeros and all of its keys are masked)
-    score_chain(bufa, sa, 0, false, sa, pa, kb, valid, first, bufa);
-    score_chain(bufb, sb, 1, true, sa, pa, kb, valid, first, bufa);
+    score_chain(bufa, sa, 0, false, sa, pa, kb, valid, first, bufa, vm_a);
+    score_chain(bufb, sb, 1, true, sa, pa, kb, valid, first, bufa, vm_a);
     if (resc_any) acc_scale_all(alpha);
-    value_product(bufa, pa, true, sb, pb, kb + kHalfRows, valid, bufb);
+    value_product(bufa, pa, true, sb, pb, kb + kHalfRows, valid, bufb, vm_b);
     if (resc_any) acc_scale_all(alpha);
-    value_product(bufb, pb, false, sb, pb, kb + kHalfRows, valid, bufb);
+    value_product(bufb, pb, false, sb, pb, kb + kHalfRows, valid, bufb, vm_b);
 
     // the compute cursor moves to the next page; a piece ends with its request
     const int pbi = cb;
@@ -2987,8 +3165,9 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
     if (first) {
       pbeg = ck;
       npg = n_pages(cL);
-      lim = a.causal ? cL - a.s_q + 1 + tok : cL;
-      lim_min = a.causal ? cL - a.s_q + 1 : cL;
+      // (the sparse mode is never causal: its items carry their own limits)
+      lim = (!SP && a.causal) ? cL - a.s_q + 1 + tok : cL;
+      lim_min = (!SP && a.causal) ? cL - a.s_q + 1 : cL;
     }
     prefetch_page(true);   // completes while this wave waits at the barrier
     wait_page(t + 1);
@@ -2997,9 +3176,19 @@ __global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const Dec
   }
 }
 
+__global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_kernel(const DecodeArgs a) {
+  rowwave_f8_body<false>(a);
+}
+
+// Sparse mode over FP8 pages: each selected row's codes, rope and scale
+// gathered from its own page through its resolved row id (the zero row for
+// an entry that does not count), entries that do not count masked.
+__global__ __launch_bounds__(kRWThreads, 1) void mla_rowwave_f8_sparse_kernel(const DecodeArgs a) {
+  rowwave_f8_body<true>(a);
+}
+
 // Rows per workgroup tile of the split plan: 128 when s_q*h_q is a multiple
-// of 128 (mla_rowwave_kernel, mla_rowwave_f8_kernel), else the ws kernel's
-// 16, 32 or 64.
+// of 128 (the row-wave kernels), else the ws kernel's 16, 32 or 64.
 int tile_rows_for(int M) {
   if (M % kRWRows == 0) return kRWRows;
   if (M <= 16) return 16;    // mla_splitkv_ws_kernel<1>
@@ -3030,19 +3219,22 @@ hipError_t launch_ws(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, 
 hipError_t launch_splitkv(const DecodeArgs& args, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
   DecodeArgs a = args;
-  // 128-row tiles: the row-wave kernels (dense over either cache format,
-  // sparse over the bf16 cache)
-  if (a.M % kRWRows == 0 && !(a.sparse && a.kv_fp8)) {
+  // 128-row tiles: the row-wave kernels (dense or sparse, either cache format)
+  if (a.M % kRWRows == 0) {
     a.row_tile_rows = kRWRows;
     a.row_tiles = a.M / kRWRows;
     const dim3 grid(a.num_parts * a.row_tiles);
     const dim3 block(kRWThreads);
-    const void* kern = a.sparse   ? reinterpret_cast<const void*>(&mla_rowwave_sparse_kernel)
-                       : a.kv_fp8 ? reinterpret_cast<const void*>(&mla_rowwave_f8_kernel)
-                                  : reinterpret_cast<const void*>(&mla_rowwave_kernel);
+    const void* kern =
+        a.sparse ? (a.kv_fp8 ? reinterpret_cast<const void*>(&mla_rowwave_f8_sparse_kernel)
+                             : reinterpret_cast<const void*>(&mla_rowwave_sparse_kernel))
+        : a.kv_fp8 ? reinterpret_cast<const void*>(&mla_rowwave_f8_kernel)
+                   : reinterpret_cast<const void*>(&mla_rowwave_kernel);
     void* kargs[] = {&a};
     if (start == nullptr && stop == nullptr) {
-      if (a.sparse)
+      if (a.sparse && a.kv_fp8)
+        hipLaunchKernelGGL(mla_rowwave_f8_sparse_kernel, grid, block, 0, stream, a);
+      else if (a.sparse)
         hipLaunchKernelGGL(mla_rowwave_sparse_kernel, grid, block, 0, stream, a);
       else if (a.kv_fp8)
         hipLaunchKernelGGL(mla_rowwave_f8_kernel, grid, block, 0, stream, a);

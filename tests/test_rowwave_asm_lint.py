@@ -1,6 +1,7 @@
 """Static checks of the row-wave kernels' gfx950 assembly (no GPU needed):
-mla_rowwave_kernel (bf16 cache), mla_rowwave_sparse_kernel (sparse mode,
-bf16 cache) and mla_rowwave_f8_kernel (FP8 cache).
+mla_rowwave_kernel (bf16 cache), mla_rowwave_f8_kernel (FP8 cache) and
+their sparse-mode versions mla_rowwave_sparse_kernel and
+mla_rowwave_f8_sparse_kernel.
 
 The kernels keep their 512-dim output accumulators in AGPRs a0-a255 that only
 inline asm touches, and issue some matrix products as inline asm, which the
@@ -31,7 +32,8 @@ CSRC = os.path.join(ROOT, "mla_paged_kv_04_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 KERNELS = ["_ZN3mla18mla_rowwave_kernelENS_10DecodeArgsE",
            "_ZN3mla25mla_rowwave_sparse_kernelENS_10DecodeArgsE",
-           "_ZN3mla21mla_rowwave_f8_kernelENS_10DecodeArgsE"]
+           "_ZN3mla21mla_rowwave_f8_kernelENS_10DecodeArgsE",
+           "_ZN3mla28mla_rowwave_f8_sparse_kernelENS_10DecodeArgsE"]
 RESULT_WAIT_STATES = 12
 
 
