@@ -50,116 +50,116 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 306999426,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 307015432,
         "write_bytes": 8404992,
-        "fetch_scale": 1.99988,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.0812
+        "mfma_util": 0.0823
     },
     "ridge": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 722837321,
-        "write_bytes": 93418272,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 722810851,
+        "write_bytes": 93383356,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3881
+        "mfma_util": 0.3939
     },
     "long": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 774481760,
-        "write_bytes": 69610393,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 774477083,
+        "write_bytes": 69604156,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4166
+        "mfma_util": 0.4246
     },
     "ragged": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 528802622,
-        "write_bytes": 118483449,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 528788947,
+        "write_bytes": 118483603,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.431
+        "mfma_util": 0.4296
     },
     "draft": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 228850180,
-        "write_bytes": 94557296,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 228832542,
+        "write_bytes": 94556243,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4278
+        "mfma_util": 0.4194
     },
     "prefill": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 424842417,
-        "write_bytes": 142966784,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 424828169,
+        "write_bytes": 142968752,
         "fetch_scale": 1.99993,
         "write_scale": 1.0,
-        "mfma_util": 0.4935
+        "mfma_util": 0.4977
     },
     "sparse": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 189843558,
-        "write_bytes": 69193635,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 189859142,
+        "write_bytes": 69208851,
         "fetch_scale": 1.9999,
         "write_scale": 1.0,
-        "mfma_util": 0.1952
+        "mfma_util": 0.1953
     },
     "membound/fp8": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 173880421,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 173869301,
         "write_bytes": 8404992,
-        "fetch_scale": 1.99986,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.1104
+        "mfma_util": 0.1116
     },
     "ridge/fp8": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 428652739,
-        "write_bytes": 93378163,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 428755046,
+        "write_bytes": 93378054,
         "fetch_scale": 1.9999,
         "write_scale": 1.0,
-        "mfma_util": 0.3059
+        "mfma_util": 0.3068
     },
     "long/fp8": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 442130050,
-        "write_bytes": 69603843,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 442160861,
+        "write_bytes": 69603859,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3173
+        "mfma_util": 0.3215
     },
     "ragged/fp8": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 329074510,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 329160379,
         "write_bytes": 118482944,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3134
+        "mfma_util": 0.3132
     },
     "draft/fp8": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 151877019,
-        "write_bytes": 94556265,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 151882522,
+        "write_bytes": 94558147,
         "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.3108
+        "mfma_util": 0.3134
     },
     "prefill/fp8": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 283991345,
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 284025844,
         "write_bytes": 142966784,
-        "fetch_scale": 1.9999,
-        "write_scale": 1.0,
-        "mfma_util": 0.3519
-    },
-    "sparse/fp8": {
-        "kernel_sha256": "00285e161148e23799490eacc56a11849abd602424ed42f0f3d4dbd83cfa0d65",
-        "fetch_bytes": 134913147,
-        "write_bytes": 67239936,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.1505
+        "mfma_util": 0.3518
+    },
+    "sparse/fp8": {
+        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
+        "fetch_bytes": 136312262,
+        "write_bytes": 67789129,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0,
+        "mfma_util": 0.172
     }
 }
 
