@@ -75,8 +75,9 @@ extern "C" {
 /*
  * mla_decode_num_parts — host only, no HIP call.
  * Recommended number of split-KV parts (workers) for a launch: one workgroup
- * per compute unit.  A workgroup carries one row tile of query rows (up to 64
- * rows; s_q*h_q <= 32 fits one tile, larger counts use s_q*h_q/64 tiles), and
+ * per compute unit.  A workgroup carries one row tile of query rows: 128
+ * rows when s_q*h_q is a multiple of 128 (s_q*h_q/128 tiles), else up to 64
+ * (s_q*h_q <= 32 fits one tile, larger counts use ceil(s_q*h_q/64) tiles);
  * each part runs once per row tile, so parts = num_cus / row_tiles.
  *   h_q in {16,32,64,128}, 1 <= s_q <= MLA_MAX_S_Q, h_kv == 1, num_cus >= 1.
  * Returns MLA_OK and *num_parts_out >= 1, or an error status.

@@ -45,7 +45,7 @@ struct DecodeArgs {
   int causal;
   int num_parts;
   int row_tiles;
-  int row_tile_rows;          // query rows per workgroup tile (16, 32, 64, or 128 for the row-wave kernel)
+  int row_tile_rows;          // query rows per workgroup tile (16, 32, 64, or 128 for the row-wave kernels)
   float scale_log2;           // scale * log2(e)
   int kv_fp8;                 // 1: kcache holds FP8 pages
   // Sparse mode (selected keys): requests are (request, token) items of
@@ -109,7 +109,8 @@ hipError_t launch_kv_append_fp8(const uint16_t* new_kv, uint8_t* kcache, long lo
                                 const int32_t* seqlens, int batch, int s_q, hipStream_t stream);
 
 // Rows per workgroup tile for M query rows: 128 when M is a multiple of 128
-// (the row-wave kernel over a bf16 cache), else 16, 32 or 64.
+// (the row-wave kernels: dense or sparse, either cache format), else 16, 32
+// or 64 (mla_splitkv_ws_kernel).
 int tile_rows_for(int M);
 
 // Host layer helpers shared with the entry point that allocates nothing
