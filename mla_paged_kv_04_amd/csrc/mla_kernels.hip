@@ -1572,16 +1572,21 @@ constexpr int kRWRows = 128;
 
 // 16-byte unit swizzle of row r in this kernel's unit buffers: unit c is
 // stored at c ^ rw_swizzle(r), inside its aligned group of 8 (72 units per
-// row).  Both read patterns of the kernel then hit every LDS bank at most
-// once per 256 bytes: the score operand (8 consecutive rows at one unit per
-// 8 lanes: even and odd rows differ by 128 bytes, and the XOR takes four
-// distinct values on the even and on the odd rows of any 8) and the
-// transposed value operand (per 32 lanes 4 consecutive rows x 4 consecutive
-// units of an aligned group of 4: bit 2 of the XOR follows row bit 1, so
-// rows r and r + 2 land in the two halves of the group of 8).  The r & 7
-// swizzle of the ws kernel puts rows r and r + 2 of that value pattern on
-// the same banks.
-__device__ __forceinline__ int rw_swizzle(int r) { return ((r & 2) << 1) | ((r & 4) >> 1); }
+// row).  A row is 1152 = 4.5 x 256 bytes, so even and odd rows start 128
+// bytes apart in the 256 bytes the LDS serves at once.  Both read patterns
+// of the kernel then hit every bank at most once per 256 bytes: the score
+// operand (16 consecutive rows at one unit per 16 lanes: the XOR takes all
+// eight values on the even and on the odd rows of any 16, bit 2 from row bit
+// 1, bit 1 from row bit 2, bit 0 from row bit 3) and the transposed value
+// operand (per 32 lanes 4 consecutive rows x 4 consecutive units of an
+// aligned group of 4: rows r and r + 2 land in the two halves of the group
+// of 8, and row bit 3 only permutes the units inside a group of 4).  With
+// two bits (rows r and r + 8 alike) the score read measured a 2-way
+// conflict: SQ_LDS_BANK_CONFLICT 1.05e7 cycles against 3.04e7 active on the
+// 128-head ridge workload.
+__device__ __forceinline__ int rw_swizzle(int r) {
+  return ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
+}
 
 // Page validity of unit (b, k): its table slot exists and names a page of
 // the pool.  Units of invalid pages are zero-filled by the loads and their
@@ -1959,7 +1964,10 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
   // V (value A operand) of dim block db, key step u, read jj: 16-lane group G
   // reads keys 16u + 8jj + 4(G >> 1) + (i >> 2), 8 bytes at dims
   // 32db + 16(G & 1) + 4(i & 3); the transpose hands lane i the four keys of
-  // dim 32db + 16(G & 1) + i.  Offset: vo[db & 1] + (16u + 8jj) rows + 128 (db >> 1).
+  // dim 32db + 16(G & 1) + i.  Offset: vo[db & 1] + (16u + 8jj) rows + 128 (db >> 1),
+  // with vo[] ^ 16 for jj = 1: row bit 3 flips bit 0 of the swizzled unit,
+  // i.e. bit 4 of the offset (rows are multiples of 128 bytes, the 8-byte
+  // half sits below bit 4).
   int vo[2];
   {
     const int G = lane >> 4, i = lane & 15;
@@ -2145,8 +2153,8 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
   // ---- per piece (the run of the part's pages of one request) ----
   float m_run = -INFINITY, l_run = 0.f;   // running max (log2 units) and sum of the lane's row
   int pbeg = ck, npg = n_pages(cL);
-  int lim = a.causal ? cL - a.s_q + 1 + tok : cL;
-  int lim_min = a.causal ? cL - a.s_q + 1 : cL;
+  int lim = (!SP && a.causal) ? cL - a.s_q + 1 + tok : cL;   // (the sparse mode is never causal)
+  int lim_min = (!SP && a.causal) ? cL - a.s_q + 1 : cL;
   bool first = true;        // the phase's page starts a piece
 
   // O / l of the finished piece: bf16 to out for a whole request, fp32
@@ -2295,9 +2303,9 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
     auto read_v = [&](int st) {
       const int u = st >> 4, db = st & 15;
       const char* vb = vbuf + vo[db & 1] + 128 * (db >> 1) + 16 * u * kRowBytes;
+      const char* vb1 = vbuf + (vo[db & 1] ^ 16) + 128 * (db >> 1) + (16 * u + 8) * kRowBytes;
       vlo[st % (D2 + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb));
-      vhi[st % (D2 + 1)] =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb + 8 * kRowBytes));
+      vhi[st % (D2 + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(vb1));
     };
 #pragma unroll
     for (int st = 0; st < D2; ++st) read_v(st);
@@ -2415,8 +2423,8 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
     if (first) {
       pbeg = ck;
       npg = n_pages(cL);
-      lim = a.causal ? cL - a.s_q + 1 + tok : cL;
-      lim_min = a.causal ? cL - a.s_q + 1 : cL;
+      lim = (!SP && a.causal) ? cL - a.s_q + 1 + tok : cL;
+      lim_min = (!SP && a.causal) ? cL - a.s_q + 1 : cL;
     }
     prefetch_page(true);   // completes while this wave waits at the barrier
     wait_page(t + 1);
