@@ -50,116 +50,116 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 307015432,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 307011940,
         "write_bytes": 8404992,
-        "fetch_scale": 1.99989,
+        "fetch_scale": 1.99986,
         "write_scale": 1.0,
-        "mfma_util": 0.0823
+        "mfma_util": 0.083
     },
     "ridge": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 722810851,
-        "write_bytes": 93383356,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 722795338,
+        "write_bytes": 93391097,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3939
+        "mfma_util": 0.3916
     },
     "long": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 774477083,
-        "write_bytes": 69604156,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 774463768,
+        "write_bytes": 69608121,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4246
+        "mfma_util": 0.4217
     },
     "ragged": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 528788947,
-        "write_bytes": 118483603,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 528700020,
+        "write_bytes": 118483465,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4296
+        "mfma_util": 0.4268
     },
     "draft": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 228832542,
-        "write_bytes": 94556243,
-        "fetch_scale": 1.99992,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 228844138,
+        "write_bytes": 94557840,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.4194
+        "mfma_util": 0.4238
     },
     "prefill": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 424828169,
-        "write_bytes": 142968752,
-        "fetch_scale": 1.99993,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 424816645,
+        "write_bytes": 142966918,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.4977
+        "mfma_util": 0.4889
     },
     "sparse": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 189859142,
-        "write_bytes": 69208851,
-        "fetch_scale": 1.9999,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 189815318,
+        "write_bytes": 69555203,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.1953
+        "mfma_util": 0.1964
     },
     "membound/fp8": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 173869301,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 173880633,
         "write_bytes": 8404992,
         "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.1116
+        "mfma_util": 0.1096
     },
     "ridge/fp8": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 428755046,
-        "write_bytes": 93378054,
-        "fetch_scale": 1.9999,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 428727415,
+        "write_bytes": 93378048,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3068
+        "mfma_util": 0.3069
     },
     "long/fp8": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 442160861,
-        "write_bytes": 69603859,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 442157083,
+        "write_bytes": 69605574,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3215
+        "mfma_util": 0.3246
     },
     "ragged/fp8": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 329160379,
-        "write_bytes": 118482944,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 329134087,
+        "write_bytes": 118482963,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3132
+        "mfma_util": 0.3165
     },
     "draft/fp8": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 151882522,
-        "write_bytes": 94558147,
-        "fetch_scale": 1.99989,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 151900281,
+        "write_bytes": 94556236,
+        "fetch_scale": 1.9999,
         "write_scale": 1.0,
-        "mfma_util": 0.3134
+        "mfma_util": 0.3147
     },
     "prefill/fp8": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 284025844,
-        "write_bytes": 142966784,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 284074951,
+        "write_bytes": 142966822,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3518
+        "mfma_util": 0.3527
     },
     "sparse/fp8": {
-        "kernel_sha256": "98e570b30fda2358fac7177ae1002df27019a76987a0b838c957ba6390d49b3b",
-        "fetch_bytes": 136312262,
-        "write_bytes": 67789129,
+        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
+        "fetch_bytes": 136322626,
+        "write_bytes": 67941507,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.172
+        "mfma_util": 0.1748
     }
 }
 
