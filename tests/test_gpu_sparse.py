@@ -77,12 +77,13 @@ def test_sparse_small(mla, h_q, s_q, topk, parts):
     _assert_parity(out, lse, O_ref, L_ref, tag=f"sparse h{h_q} s{s_q} k{topk} P={parts}")
 
 
-def test_sparse_edge_entries(mla):
+@pytest.mark.parametrize("h_q", [32, 128])   # 64-row tiles; the 128-row (row-wave) kernel
+def test_sparse_edge_entries(mla, h_q):
     """Duplicates, padding, positions at/after the limit, future positions of
     an earlier token, an all-padding item and a zero-length request."""
-    _say("case sparse edge entries")
+    _say(f"case sparse edge entries h_q={h_q}")
     lens = [200, 0, 100, 70]
-    inp = build_inputs(lens, 2, 32, seed=1201, extra_pool=3)
+    inp = build_inputs(lens, 2, h_q, seed=1201, extra_pool=3)
     g = torch.Generator().manual_seed(12)
     ix = draw_topk_indices(lens, 2, 64, True, g)
     ix[0, 0, :4] = torch.tensor([5, 5, 5, 199], dtype=torch.int32)   # dup; 199 beyond token 0
@@ -93,15 +94,16 @@ def test_sparse_edge_entries(mla):
     O_ref, L_ref = decode_sparse(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix, inp.scale,
                                  True)
     assert np.all(L_ref[2, 0] == -np.inf) and np.all(L_ref[1] == -np.inf)
-    _assert_parity(out, lse, O_ref, L_ref, tag="sparse edges")
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"sparse edges h{h_q}")
 
 
-def test_sparse_all_visible_matches_dense(mla):
+@pytest.mark.parametrize("h_q", [64, 128])
+def test_sparse_all_visible_matches_dense(mla, h_q):
     """Selecting every visible position is the dense mode: the two GPU paths
     agree to the bar, and each agrees with its oracle."""
-    _say("case sparse = dense")
+    _say(f"case sparse = dense h_q={h_q}")
     lens = [64, 96, 160, 20]
-    inp = build_inputs(lens, 1, 64, seed=1202, extra_pool=2)
+    inp = build_inputs(lens, 1, h_q, seed=1202, extra_pool=2)
     ix = torch.full((4, 1, 160), -1, dtype=torch.int32)
     for b, L in enumerate(lens):
         ix[b, 0, :L] = torch.arange(L, dtype=torch.int32)
@@ -167,14 +169,15 @@ def test_sparse_fp8_small(mla, h_q, s_q, topk, parts):
     _assert_parity(out, lse, O_ref, L_ref, tag=f"sparse fp8 h{h_q} s{s_q} k{topk} P={parts}")
 
 
-def test_sparse_fp8_edge_entries(mla):
+@pytest.mark.parametrize("h_q", [32, 128])
+def test_sparse_fp8_edge_entries(mla, h_q):
     """Duplicates, padding, positions at/after the limit, an all-padding item
     and a zero-length request, over FP8 pages."""
     from oracle import decode_sparse_fp8
     from workloads import build_fp8_inputs
-    _say("case sparse fp8 edge entries")
+    _say(f"case sparse fp8 edge entries h_q={h_q}")
     lens = [200, 0, 100, 70]
-    inp = build_fp8_inputs(lens, 2, 32, seed=1401, extra_pool=3)
+    inp = build_fp8_inputs(lens, 2, h_q, seed=1401, extra_pool=3)
     g = torch.Generator().manual_seed(14)
     ix = draw_topk_indices(lens, 2, 64, True, g)
     ix[0, 0, :4] = torch.tensor([5, 5, 5, 199], dtype=torch.int32)
@@ -185,16 +188,17 @@ def test_sparse_fp8_edge_entries(mla):
     O_ref, L_ref = decode_sparse_fp8(inp.q, inp.kcache, inp.block_table, inp.seqlens, ix,
                                      inp.scale, True)
     assert np.all(L_ref[2, 0] == -np.inf) and np.all(L_ref[1] == -np.inf)
-    _assert_parity(out, lse, O_ref, L_ref, tag="sparse fp8 edges")
+    _assert_parity(out, lse, O_ref, L_ref, tag=f"sparse fp8 edges h{h_q}")
 
 
-def test_sparse_fp8_all_visible_matches_dense_fp8(mla):
+@pytest.mark.parametrize("h_q", [64, 128])
+def test_sparse_fp8_all_visible_matches_dense_fp8(mla, h_q):
     """Selecting every visible position is the dense FP8 mode: the two GPU
     paths agree to the bar."""
     from workloads import build_fp8_inputs
-    _say("case sparse fp8 = dense fp8")
+    _say(f"case sparse fp8 = dense fp8 h_q={h_q}")
     lens = [64, 96, 160, 20]
-    inp = build_fp8_inputs(lens, 1, 64, seed=1402, extra_pool=2)
+    inp = build_fp8_inputs(lens, 1, h_q, seed=1402, extra_pool=2)
     ix = torch.full((4, 1, 160), -1, dtype=torch.int32)
     for b, L in enumerate(lens):
         ix[b, 0, :L] = torch.arange(L, dtype=torch.int32)
