@@ -87,13 +87,16 @@ int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int num_cus,
 
 /*
  * mla_decode_workspace_bytes — host only, no HIP call.
- * Size of the fp32 split-partial workspace that mla_decode_fwd /
+ * Size of the split-partial workspace that mla_decode_fwd /
  * mla_decode_splitkv / mla_decode_combine need for `num_parts` parts:
  *   slots = 2*(num_parts-1) (an upper bound of the pieces of split requests),
- *   bytes = slots * s_q*h_q * (512 + 1) * 4, rounded up to 256.
+ *   bytes = slots * s_q*h_q * (512*2 + 4), rounded up to 256.
  * May be 0 (num_parts == 1); then the workspace pointer may be NULL.
- * Layout (M = s_q*h_q, slots as above): fp32 partial outputs
- * O_part[slots][M][512], each normalised over its own keys, followed by fp32
+ * Layout (M = s_q*h_q, slots as above): bf16 partial outputs
+ * O_part[slots][M][512], each normalised over its own keys and rounded to
+ * bf16 as a whole request's output is (fp32 accumulation before; the merge
+ * weights are at most 1 and sum to 1, so the rounding adds at most
+ * 2^-9 * max|O_part| to a merged element), followed by fp32
  * LSE_part[slots][M] in BASE-2 (log2 of the sum of exp(scale*q.k)), -inf for a
  * piece with no visible key.  Request b's pieces occupy slots
  * [split_offsets[b], split_offsets[b+1]) in key order.
@@ -137,7 +140,7 @@ int mla_decode_metadata(const int32_t* seqlens_d, int batch, int s_q, int h_q,
  * table into LDS, computes scores (bf16 MFMA, fp32 accumulate), the online
  * softmax in fp32, and probabilities times values (bf16 MFMA).  A request
  * covered by one part is written to out_d / lse_d directly; pieces of split
- * requests are written as fp32 partials into the workspace, to be merged by
+ * requests are written as bf16 partials into the workspace, to be merged by
  * mla_decode_combine.
  *   q_d           bf16 [batch, s_q, h_q, 576]
  *   kcache_d      bf16 [num_blocks, 64, h_kv=1, 576]
@@ -335,7 +338,7 @@ int mla_decode_fwd_inline_plan_fp8(const void* q_d, const void* kcache_fp8_d,
  *   entries; none counted gives O = 0, LSE = -inf.
  * Work is split over (request, token) items of topk entries each:
  *   - parts: mla_decode_num_parts(batch * s_q, 1, h_q, 1, num_cus, ...)
- *   - workspace: mla_decode_sparse_workspace_bytes (fp32 partials as for
+ *   - workspace: mla_decode_sparse_workspace_bytes (partials as for
  *     mla_decode_workspace_bytes(batch*s_q, 1, h_q, num_parts), then the
  *     resolved row ids, validity bits and a zero row)
  *   - metadata: mla_decode_sparse_metadata (device, no host sync)
@@ -390,7 +393,7 @@ int mla_decode_sparse_fwd_fp8(const void* q_d, const void* kcache_d, int64_t num
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  It runs mla_decode_metadata, mla_decode_splitkv and
  * mla_decode_combine on `stream` with the plan (tile_meta, split_offsets) and
- * the fp32 partials in one device array that the library holds for the life
+ * the split partials in one device array that the library holds for the life
  * of the process, MLA_NOALLOC_SCRATCH_BYTES per device, instead of caller
  * buffers; it allocates and frees nothing and calls no allocating routine.
  *   Arguments as mla_decode_fwd without tile_meta_d / split_offsets_d /

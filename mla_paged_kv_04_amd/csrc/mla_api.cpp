@@ -67,16 +67,16 @@ int row_tiles(int s_q, int h_q) {
 size_t workspace_need(int s_q, int h_q, int num_parts) {
   const size_t slots = num_parts > 1 ? 2 * (size_t)(num_parts - 1) : 0;
   const size_t M = (size_t)s_q * h_q;
-  size_t bytes = slots * M * (mla::kDV + 1) * sizeof(float);
+  size_t bytes = slots * M * (mla::kDV * sizeof(uint16_t) + sizeof(float));
   return (bytes + 255) / 256 * 256;
 }
 
-// Partial O lives first, partial LSE after it.
-void split_workspace(void* ws, int s_q, int h_q, int num_parts, float** po, float** plse) {
+// Partial O (bf16) lives first, partial LSE (fp32) after it.
+void split_workspace(void* ws, int s_q, int h_q, int num_parts, uint16_t** po, float** plse) {
   const size_t slots = num_parts > 1 ? 2 * (size_t)(num_parts - 1) : 0;
   const size_t M = (size_t)s_q * h_q;
-  *po = static_cast<float*>(ws);
-  *plse = ws ? static_cast<float*>(ws) + slots * M * mla::kDV : nullptr;
+  *po = static_cast<uint16_t*>(ws);
+  *plse = ws ? reinterpret_cast<float*>(static_cast<uint16_t*>(ws) + slots * M * mla::kDV) : nullptr;
 }
 
 int check_common(const void* seqlens, const void* split_offsets, int batch, int s_q, int h_q,
@@ -301,7 +301,8 @@ int mla_decode_combine(const int32_t* seqlens_d, int batch, int s_q, int h_q,
                         workspace_bytes, out_d, lse_d);
   if (st != MLA_OK) return st;
   mla::CombineArgs a;
-  float *po, *plse;
+  uint16_t* po;
+  float* plse;
   split_workspace(const_cast<void*>(workspace_d), s_q, h_q, num_parts, &po, &plse);
   a.seqlens = seqlens_d;
   a.split_offsets = split_offsets_d;

@@ -33,7 +33,7 @@ struct DecodeArgs {
   const int32_t* seqlens;     // [B]
   const int32_t* tile_meta;   // [P, 8]
   const int32_t* split_offsets;  // [B+1]
-  float* part_o;              // [slots, M, 512]
+  uint16_t* part_o;           // bf16 [slots, M, 512]
   float* part_lse;            // [slots, M]   (log2 domain)
   uint16_t* out;              // bf16 [B, s_q, h_q, 512]
   float* lse;                 // [B, s_q, h_q] (natural log)
@@ -74,7 +74,7 @@ constexpr int kPlanMaxBatch = 1024;
 struct CombineArgs {
   const int32_t* seqlens;
   const int32_t* split_offsets;
-  const float* part_o;
+  const uint16_t* part_o;     // bf16 [slots, M, 512]
   const float* part_lse;
   uint16_t* out;
   float* lse;

@@ -1519,11 +1519,14 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
               const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
               *reinterpret_cast<bf16x4*>(op + dl * 16) = bv;
             }
-          } else {
-            float* op = a.part_o + (slot * a.M + row) * kDV + j * 128 + 4 * g;
+          } else {   // the same rounding to bf16 into the partial slot
+            uint16_t* op = a.part_o + (slot * a.M + row) * kDV + j * 128 + 4 * g;
 #pragma unroll
-            for (int dl = 0; dl < DL; ++dl)
-              *reinterpret_cast<f32x4*>(op + dl * 16) = o[dl][rt] * inv;
+            for (int dl = 0; dl < DL; ++dl) {
+              const f32x4 v = o[dl][rt] * inv;
+              const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+              *reinterpret_cast<bf16x4*>(op + dl * 16) = bv;
+            }
           }
 #pragma unroll
           for (int dl = 0; dl < DL; ++dl) o[dl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1613,30 +1616,35 @@ __device__ __forceinline__ bool page_ok(const DecodeArgs& a, int b, int k) {
 // compiler may place a copy of the accumulator right after the statement
 // that produced it, and that copy must already see the result.
 // Two fixed accumulator blocks (one per half of a page).
+#ifdef MLA_NO_PRE_NOP
+#define MLA_PRE ""
+#else
+#define MLA_PRE "s_nop 1\n\t"
+#endif
 #define MLA_SACC0 "{v[236:251]}"
 #define MLA_SACC1 "{v[220:235]}"
 template <int BLK>
 __device__ __forceinline__ void score_mfma_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
   if constexpr (BLK == 0)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC0(s) : "v"(k), "v"(q));
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC0(s) : "v"(k), "v"(q));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC1(s) : "v"(k), "v"(q));
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC1(s) : "v"(k), "v"(q));
 }
 template <int BLK>
 __device__ __forceinline__ void score_mfma(f32x16& s, const bf16x8& k, const bf16x8& q) {
   if constexpr (BLK == 0)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC0(s) : "v"(k), "v"(q));
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC0(s) : "v"(k), "v"(q));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC1(s) : "v"(k), "v"(q));
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC1(s) : "v"(k), "v"(q));
 }
 template <int BLK>
 __device__ __forceinline__ void score_mfma_last(f32x16& s, const bf16x8& k, const bf16x8& q) {
   if constexpr (BLK == 0)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+" MLA_SACC0(s)
                  : "v"(k), "v"(q));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+" MLA_SACC1(s)
                  : "v"(k), "v"(q));
 }
@@ -1686,52 +1694,52 @@ __device__ __forceinline__ void score_mfma_last(f32x16& s, const bf16x8& k, cons
 template <int DB>
 __device__ __forceinline__ void acc_mfma(const bf16x8& v, const bf16x8& p) {
   if constexpr (DB == 0) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[0:15], %0, %1, a[0:15]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[0:15], %0, %1, a[0:15]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B0);
   } else if constexpr (DB == 1) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[16:31], %0, %1, a[16:31]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[16:31], %0, %1, a[16:31]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B1);
   } else if constexpr (DB == 2) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[32:47], %0, %1, a[32:47]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[32:47], %0, %1, a[32:47]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B2);
   } else if constexpr (DB == 3) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[48:63], %0, %1, a[48:63]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[48:63], %0, %1, a[48:63]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B3);
   } else if constexpr (DB == 4) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[64:79], %0, %1, a[64:79]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[64:79], %0, %1, a[64:79]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B4);
   } else if constexpr (DB == 5) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[80:95], %0, %1, a[80:95]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[80:95], %0, %1, a[80:95]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B5);
   } else if constexpr (DB == 6) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[96:111], %0, %1, a[96:111]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[96:111], %0, %1, a[96:111]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B6);
   } else if constexpr (DB == 7) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[112:127], %0, %1, a[112:127]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[112:127], %0, %1, a[112:127]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B7);
   } else if constexpr (DB == 8) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[128:143], %0, %1, a[128:143]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[128:143], %0, %1, a[128:143]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B8);
   } else if constexpr (DB == 9) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[144:159], %0, %1, a[144:159]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[144:159], %0, %1, a[144:159]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B9);
   } else if constexpr (DB == 10) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[160:175], %0, %1, a[160:175]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[160:175], %0, %1, a[160:175]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B10);
   } else if constexpr (DB == 11) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[176:191], %0, %1, a[176:191]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[176:191], %0, %1, a[176:191]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B11);
   } else if constexpr (DB == 12) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[192:207], %0, %1, a[192:207]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[192:207], %0, %1, a[192:207]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B12);
   } else if constexpr (DB == 13) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[208:223], %0, %1, a[208:223]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[208:223], %0, %1, a[208:223]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B13);
   } else if constexpr (DB == 14) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[224:239], %0, %1, a[224:239]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[224:239], %0, %1, a[224:239]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B14);
   } else if constexpr (DB == 15) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[240:255], %0, %1, a[240:255]" ::"v"(v), "v"(p)
+    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[240:255], %0, %1, a[240:255]" ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B15);
   }
 }
@@ -2173,7 +2181,7 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
     float* const lse_p = SP ? args()->lse : a.lse;
     float* const plse_p = SP ? args()->part_lse : a.part_lse;
     uint16_t* const out_p = SP ? args()->out : a.out;
-    float* const po_p = SP ? args()->part_o : a.part_o;
+    uint16_t* const po_p = SP ? args()->part_o : a.part_o;
     if (lh == 0) {
       if (whole)
         lse_p[(long long)b * a.M + row] = lse2 * kLn2;
@@ -2181,31 +2189,19 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
         plse_p[slot * a.M + row] = lse2;
     }
     acc_drain();
-    if (whole) {
-      uint16_t* op = out_p + ((long long)b * a.M + row) * kDV + 4 * lh;
+    // O / l rounded to bf16: the output row of a whole request, else the
+    // piece's partial row
+    uint16_t* const op = whole ? out_p + ((long long)b * a.M + row) * kDV + 4 * lh
+                               : po_p + (slot * a.M + row) * kDV + 4 * lh;
 #pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        float e[16];
-        acc_read_i(db, e);
+    for (int db = 0; db < 16; ++db) {
+      float e[16];
+      acc_read_i(db, e);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x4 bv = {(__bf16)(e[4 * j] * linv), (__bf16)(e[4 * j + 1] * linv),
-                             (__bf16)(e[4 * j + 2] * linv), (__bf16)(e[4 * j + 3] * linv)};
-          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j) = bv;
-        }
-      }
-    } else {
-      float* op = po_p + (slot * a.M + row) * kDV + 4 * lh;
-#pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        float e[16];
-        acc_read_i(db, e);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 v = {e[4 * j] * linv, e[4 * j + 1] * linv, e[4 * j + 2] * linv,
-                           e[4 * j + 3] * linv};
-          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * j) = v;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const bf16x4 bv = {(__bf16)(e[4 * j] * linv), (__bf16)(e[4 * j + 1] * linv),
+                           (__bf16)(e[4 * j + 2] * linv), (__bf16)(e[4 * j + 3] * linv)};
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j) = bv;
       }
     }
     acc_zero_all(zero8);
@@ -2888,7 +2884,7 @@ __device__ __forceinline__ void rowwave_f8_body(const DecodeArgs& a) {
     float* const lse_p = SP ? args()->lse : a.lse;
     float* const plse_p = SP ? args()->part_lse : a.part_lse;
     uint16_t* const out_p = SP ? args()->out : a.out;
-    float* const po_p = SP ? args()->part_o : a.part_o;
+    uint16_t* const po_p = SP ? args()->part_o : a.part_o;
     const int rr = row_at();
     if (lh == 0) {
       if (whole)
@@ -2897,31 +2893,19 @@ __device__ __forceinline__ void rowwave_f8_body(const DecodeArgs& a) {
         plse_p[slot * a.M + rr] = lse2;
     }
     acc_drain();
-    if (whole) {
-      uint16_t* op = out_p + ((long long)b * a.M + rr) * kDV + 4 * lh;
+    // O / l rounded to bf16: the output row of a whole request, else the
+    // piece's partial row
+    uint16_t* const op = whole ? out_p + ((long long)b * a.M + rr) * kDV + 4 * lh
+                               : po_p + (slot * a.M + rr) * kDV + 4 * lh;
 #pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        float e[16];
-        acc_read_i(db, e);
+    for (int db = 0; db < 16; ++db) {
+      float e[16];
+      acc_read_i(db, e);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x4 bv = {(__bf16)(e[4 * j] * linv), (__bf16)(e[4 * j + 1] * linv),
-                             (__bf16)(e[4 * j + 2] * linv), (__bf16)(e[4 * j + 3] * linv)};
-          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j) = bv;
-        }
-      }
-    } else {
-      float* op = po_p + (slot * a.M + rr) * kDV + 4 * lh;
-#pragma unroll
-      for (int db = 0; db < 16; ++db) {
-        float e[16];
-        acc_read_i(db, e);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 v = {e[4 * j] * linv, e[4 * j + 1] * linv, e[4 * j + 2] * linv,
-                           e[4 * j + 3] * linv};
-          *reinterpret_cast<f32x4*>(op + 32 * db + 8 * j) = v;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const bf16x4 bv = {(__bf16)(e[4 * j] * linv), (__bf16)(e[4 * j + 1] * linv),
+                           (__bf16)(e[4 * j + 2] * linv), (__bf16)(e[4 * j + 3] * linv)};
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j) = bv;
       }
     }
     acc_zero_all(zero8);
@@ -3279,8 +3263,8 @@ hipError_t launch_splitkv(const DecodeArgs& args, hipStream_t stream, hipEvent_t
 // --------------------------------------------------------------------------
 // LSE combine: exact merge of the split partials of each split request.
 // One workgroup per (request, 16 query rows, quarter of the 512 output dims):
-// 16 threads per row, 8 dims each (2 x float4, interleaved so that a row's
-// 16 threads read 256 contiguous bytes per step).  Splitting the dims keeps
+// 16 threads per row, 8 contiguous dims each (one 16-byte bf16 load per
+// partial, so a row's 16 threads read 256 contiguous bytes).  Splitting the dims keeps
 // a few hundred workgroups in flight even for small batches.
 // --------------------------------------------------------------------------
 constexpr int kCombineQuarters = 4;
@@ -3296,30 +3280,27 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const CombineArgs
   uint16_t* op = a.out + ((long long)b * a.M + r) * kDV + dq;
   if (ns == 0) {
     if ((a.const_len > 0 ? a.const_len : a.seqlens[b]) <= 0) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        *reinterpret_cast<uint2*>(op + (j + 16 * c) * 4) = make_uint2(0u, 0u);
+      *reinterpret_cast<uint4*>(op + 8 * j) = make_uint4(0u, 0u, 0u, 0u);
       if (j == 0 && blockIdx.z == 0) a.lse[(long long)b * a.M + r] = -INFINITY;
     }
     return;
   }
-  // Merge in groups of four partials: each group's loads (LSEs and rows) go
-  // out together, then fold into a running (max, weight sum, weighted row),
-  // the same exact log-sum-exp merge in a streaming order.
+  // Merge in groups of four partials: each group's loads (LSEs and bf16
+  // rows) go out together, then fold into a running (max, weight sum,
+  // weighted row), the same exact log-sum-exp merge in a streaming order.
+  // Lane j holds dims dq + 8j .. dq + 8j + 7 of row r.
   constexpr int G = 4;
   float mx = -INFINITY, tot = 0.f;
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < ns; s += G) {
     float ls[G];
-    f32x4 po[G][2];
+    bf16x8 po[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const bool ok = s + u < ns;
       const long long rowi = (long long)(s0 + (ok ? s + u : 0)) * a.M + r;
       ls[u] = ok ? a.part_lse[rowi] : -INFINITY;
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + rowi * kDV + dq);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) po[u][c] = src[j + 16 * c];
+      po[u] = *reinterpret_cast<const bf16x8*>(a.part_o + rowi * kDV + dq + 8 * j);
     }
     float gm = mx;
 #pragma unroll
@@ -3328,23 +3309,21 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const CombineArgs
     const float al = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - gm);
     tot *= al;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) acc[c] *= al;
+    for (int e = 0; e < 8; ++e) acc[e] *= al;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const float wgt = ls[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls[u] - gm);
       tot += wgt;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) acc[c] += wgt * po[u][c];
+      for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)po[u][e];
     }
     mx = gm;
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  bf16x8 ov;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const f32x4 v = acc[c] * inv;
-    const bf16x4 bv = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-    *reinterpret_cast<bf16x4*>(op + (j + 16 * c) * 4) = bv;
-  }
+  for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x8*>(op + 8 * j) = ov;
   if (j == 0 && blockIdx.z == 0)
     a.lse[(long long)b * a.M + r] = tot > 0.f ? (mx + log2f(tot)) * kLn2 : -INFINITY;
 }

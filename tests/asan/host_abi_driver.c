@@ -105,7 +105,7 @@ int main(void) {
   EXPECT(mla_decode_num_parts(2, 1, 16, 1, 256, NULL) == MLA_ERR_INVALID_ARG, "num_parts NULL out");
   EXPECT(mla_decode_workspace_bytes(4, 1, 16, 1, &bytes) == MLA_OK && bytes == 0, "workspace 1 part");
   EXPECT(mla_decode_workspace_bytes(4, 1, 16, 256, &bytes) == MLA_OK &&
-             bytes >= (size_t)2 * 255 * 16 * 513 * 4 && bytes % 256 == 0,
+             bytes >= (size_t)2 * 255 * 16 * (512 * 2 + 4) && bytes % 256 == 0,
          "workspace 256 parts");
   EXPECT(mla_decode_workspace_bytes(4, 1, 16, (1 << 16) + 1, &bytes) == MLA_ERR_INVALID_ARG,
          "workspace beyond the part cap");

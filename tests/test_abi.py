@@ -68,9 +68,10 @@ def test_num_parts():
 
 def test_workspace_bytes():
     assert mla.workspace_bytes(4, 1, 16, 1) == 0
+    # bf16 O_part[slots][M][512] then fp32 LSE_part[slots][M], slots = 2 (parts - 1)
     b = mla.workspace_bytes(4, 1, 16, 256)
-    assert b >= 2 * 255 * 16 * 513 * 4 and b % 256 == 0
-    assert mla.workspace_bytes(4, 2, 128, 64) >= 2 * 63 * 256 * 513 * 4
+    assert b == -(-(2 * 255 * 16 * (512 * 2 + 4)) // 256) * 256
+    assert mla.workspace_bytes(4, 2, 128, 64) >= 2 * 63 * 256 * (512 * 2 + 4)
 
 
 def test_status_strings():

@@ -209,9 +209,11 @@ def test_combine_standalone(mla, s_q, h_q):
     nbytes = mla.workspace_bytes(4, s_q, h_q, parts)
     max_slots = 2 * (parts - 1)
     assert slots <= max_slots
-    ws = torch.zeros(nbytes // 4, dtype=torch.float32)
-    po = ws[: max_slots * M * 512].view(max_slots, M, 512)
-    pl = ws[max_slots * M * 512: max_slots * M * 513].view(max_slots, M)
+    # workspace layout: bf16 O_part[max_slots][M][512], then fp32 LSE_part[max_slots][M]
+    ws = torch.zeros(nbytes, dtype=torch.uint8)
+    po_bytes = max_slots * M * 512 * 2
+    po = ws[:po_bytes].view(torch.bfloat16).view(max_slots, M, 512)
+    pl = ws[po_bytes: po_bytes + max_slots * M * 4].view(torch.float32).view(max_slots, M)
     expect_O = np.zeros((4, M, 512))
     expect_L = np.full((4, M), -np.inf)
     for b in range(4):
@@ -225,7 +227,7 @@ def test_combine_standalone(mla, s_q, h_q):
             Ob, Lb = attend_rows(qrows, K[lo:hi], inp.scale, nvis)
             parts_b.append((Ob, Lb))
             if len(c) - 1 >= 2:
-                po[split_offsets[b] + i] = torch.from_numpy(Ob).float()
+                po[split_offsets[b] + i] = torch.from_numpy(Ob).to(torch.bfloat16)
                 pl[split_offsets[b] + i] = torch.from_numpy(Lb / math.log(2)).float()
         if len(c) - 1 >= 2:
             expect_O[b], expect_L[b] = lse_merge(parts_b)
