@@ -104,6 +104,21 @@ __device__ __forceinline__ int n_pages(int L) {
   return L > 0 ? (L + kBlock - 1) / kBlock : 0;
 }
 
+// Part and row tile of workgroup x (grid = num_parts x row tiles R).
+// Workgroups are dealt to the eight XCDs in turn (x mod 8), each XCD with its
+// own L2; with R > 1 the R row tiles of a part (which read the same pages)
+// go to one XCD.  (Runs of consecutive parts on one XCD, for R = 1, were
+// measured: top-2048 sparse 2 % faster, long-context 1.6 % slower; not kept.)
+__device__ __forceinline__ void part_of_block(int x, int R, int P, int& part, int& rtile) {
+  if (P % 8 == 0 && R > 1) {
+    part = (x / (8 * R)) * 8 + (x & 7);
+    rtile = (x >> 3) % R;
+  } else {
+    part = x / R;
+    rtile = x % R;
+  }
+}
+
 // --------------------------------------------------------------------------
 // Split-KV scheduler: one workgroup.  Implements the integer balancing rule
 // documented with mla_decode_metadata (cost_b = pages + c, equal quotas).
@@ -849,15 +864,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
   const int i = lane & 15;
 
   int part, rtile;
-  const int x = blockIdx.x;
-  const int R = a.row_tiles;
-  if (R > 1 && (a.num_parts % 8) == 0) {
-    part = (x / (8 * R)) * 8 + (x & 7);
-    rtile = (x >> 3) % R;
-  } else {
-    part = x / R;
-    rtile = x % R;
-  }
+  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, part, rtile);
   __shared__ int plan_lds[8];
   __shared__ int so_lds[kPlanMaxBatch + 1];   // split offsets (in-kernel plan)
   int b0, k0, b1, k1, first_split;
@@ -1606,45 +1613,52 @@ __device__ __forceinline__ bool page_ok(const DecodeArgs& a, int b, int k) {
 // accumulator (early-clobber where it is only written: a product's result
 // must not share registers with its operands).  The compiler does not see
 // these asm statements as matrix products, so the asm carries the hazard
-// waits itself: five wait states
-// before each product (a VALU write of an operand register, e.g. a move the
-// compiler placed just before, must be that far ahead of the read);
+// waits itself: two wait states before a product whose operand registers a
+// VALU instruction may have written just before (MLA_MFMA below);
 // consecutive products on the same accumulator of the same shape need none
 // between them.  The last product of a chain, score_mfma_last, waits out
 // the wait states before a VALU instruction may read its result (a 16-pass
 // product: at most 19; 24 are inserted) inside its own asm block: the
 // compiler may place a copy of the accumulator right after the statement
 // that produced it, and that copy must already see the result.
+// A product's asm statement, with (W) or without the two wait states that a
+// VALU write of one of its operands needs when it is the instruction just
+// before: kernels whose operands come straight from LDS or global loads
+// (the bf16 cache) drop them, kernels that convert operands with VALU
+// instructions (FP8 pages) keep them; the assembly lint checks every product
+// of the built kernels for that hazard along every control-flow path.
+#define MLA_MFMA(W, INSN, ...)                     \
+  do {                                             \
+    if constexpr (W)                               \
+      asm volatile("s_nop 1\n\t" INSN __VA_ARGS__); \
+    else                                           \
+      asm volatile(INSN __VA_ARGS__);              \
+  } while (0)
 // Two fixed accumulator blocks (one per half of a page).
-#ifdef MLA_NO_PRE_NOP
-#define MLA_PRE ""
-#else
-#define MLA_PRE "s_nop 1\n\t"
-#endif
 #define MLA_SACC0 "{v[236:251]}"
 #define MLA_SACC1 "{v[220:235]}"
-template <int BLK>
+template <int BLK, bool W = true>
 __device__ __forceinline__ void score_mfma_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
   if constexpr (BLK == 0)
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC0(s) : "v"(k), "v"(q));
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0", : "=&" MLA_SACC0(s) : "v"(k), "v"(q));
   else
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&" MLA_SACC1(s) : "v"(k), "v"(q));
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0", : "=&" MLA_SACC1(s) : "v"(k), "v"(q));
 }
-template <int BLK>
+template <int BLK, bool W = true>
 __device__ __forceinline__ void score_mfma(f32x16& s, const bf16x8& k, const bf16x8& q) {
   if constexpr (BLK == 0)
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC0(s) : "v"(k), "v"(q));
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0", : "+" MLA_SACC0(s) : "v"(k), "v"(q));
   else
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+" MLA_SACC1(s) : "v"(k), "v"(q));
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0", : "+" MLA_SACC1(s) : "v"(k), "v"(q));
 }
-template <int BLK>
+template <int BLK, bool W = true>
 __device__ __forceinline__ void score_mfma_last(f32x16& s, const bf16x8& k, const bf16x8& q) {
   if constexpr (BLK == 0)
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7",
                  : "+" MLA_SACC0(s)
                  : "v"(k), "v"(q));
   else
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7",
                  : "+" MLA_SACC1(s)
                  : "v"(k), "v"(q));
 }
@@ -1691,55 +1705,55 @@ __device__ __forceinline__ void score_mfma_last(f32x16& s, const bf16x8& k, cons
 #define MLA_AGPR_CLOBBERS_B14 "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", "a234", "a235", "a236", "a237", "a238", "a239"
 #define MLA_AGPR_CLOBBERS_B15 "a240", "a241", "a242", "a243", "a244", "a245", "a246", "a247", "a248", "a249", "a250", "a251", "a252", "a253", "a254", "a255"
 
-template <int DB>
+template <int DB, bool W = true>
 __device__ __forceinline__ void acc_mfma(const bf16x8& v, const bf16x8& p) {
   if constexpr (DB == 0) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[0:15], %0, %1, a[0:15]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[0:15], %0, %1, a[0:15]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B0);
   } else if constexpr (DB == 1) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[16:31], %0, %1, a[16:31]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[16:31], %0, %1, a[16:31]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B1);
   } else if constexpr (DB == 2) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[32:47], %0, %1, a[32:47]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[32:47], %0, %1, a[32:47]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B2);
   } else if constexpr (DB == 3) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[48:63], %0, %1, a[48:63]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[48:63], %0, %1, a[48:63]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B3);
   } else if constexpr (DB == 4) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[64:79], %0, %1, a[64:79]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[64:79], %0, %1, a[64:79]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B4);
   } else if constexpr (DB == 5) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[80:95], %0, %1, a[80:95]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[80:95], %0, %1, a[80:95]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B5);
   } else if constexpr (DB == 6) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[96:111], %0, %1, a[96:111]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[96:111], %0, %1, a[96:111]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B6);
   } else if constexpr (DB == 7) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[112:127], %0, %1, a[112:127]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[112:127], %0, %1, a[112:127]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B7);
   } else if constexpr (DB == 8) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[128:143], %0, %1, a[128:143]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[128:143], %0, %1, a[128:143]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B8);
   } else if constexpr (DB == 9) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[144:159], %0, %1, a[144:159]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[144:159], %0, %1, a[144:159]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B9);
   } else if constexpr (DB == 10) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[160:175], %0, %1, a[160:175]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[160:175], %0, %1, a[160:175]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B10);
   } else if constexpr (DB == 11) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[176:191], %0, %1, a[176:191]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[176:191], %0, %1, a[176:191]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B11);
   } else if constexpr (DB == 12) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[192:207], %0, %1, a[192:207]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[192:207], %0, %1, a[192:207]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B12);
   } else if constexpr (DB == 13) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[208:223], %0, %1, a[208:223]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[208:223], %0, %1, a[208:223]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B13);
   } else if constexpr (DB == 14) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[224:239], %0, %1, a[224:239]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[224:239], %0, %1, a[224:239]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B14);
   } else if constexpr (DB == 15) {
-    asm volatile(MLA_PRE "v_mfma_f32_32x32x16_bf16 a[240:255], %0, %1, a[240:255]" ::"v"(v), "v"(p)
+    MLA_MFMA(W, "v_mfma_f32_32x32x16_bf16 a[240:255], %0, %1, a[240:255]", ::"v"(v), "v"(p)
                  : MLA_AGPR_CLOBBERS_B15);
   }
 }
@@ -1817,24 +1831,25 @@ __device__ __forceinline__ void acc_scale_all(float x) {
 // the wait states of a 16-pass product before its accumulators are read
 __device__ __forceinline__ void acc_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 
+template <bool W = true>
 __device__ __forceinline__ void acc_mfma_i(int db, const bf16x8& v, const bf16x8& p) {
   switch (db) {
-    case 0: acc_mfma<0>(v, p); break;
-    case 1: acc_mfma<1>(v, p); break;
-    case 2: acc_mfma<2>(v, p); break;
-    case 3: acc_mfma<3>(v, p); break;
-    case 4: acc_mfma<4>(v, p); break;
-    case 5: acc_mfma<5>(v, p); break;
-    case 6: acc_mfma<6>(v, p); break;
-    case 7: acc_mfma<7>(v, p); break;
-    case 8: acc_mfma<8>(v, p); break;
-    case 9: acc_mfma<9>(v, p); break;
-    case 10: acc_mfma<10>(v, p); break;
-    case 11: acc_mfma<11>(v, p); break;
-    case 12: acc_mfma<12>(v, p); break;
-    case 13: acc_mfma<13>(v, p); break;
-    case 14: acc_mfma<14>(v, p); break;
-    default: acc_mfma<15>(v, p); break;
+    case 0: acc_mfma<0, W>(v, p); break;
+    case 1: acc_mfma<1, W>(v, p); break;
+    case 2: acc_mfma<2, W>(v, p); break;
+    case 3: acc_mfma<3, W>(v, p); break;
+    case 4: acc_mfma<4, W>(v, p); break;
+    case 5: acc_mfma<5, W>(v, p); break;
+    case 6: acc_mfma<6, W>(v, p); break;
+    case 7: acc_mfma<7, W>(v, p); break;
+    case 8: acc_mfma<8, W>(v, p); break;
+    case 9: acc_mfma<9, W>(v, p); break;
+    case 10: acc_mfma<10, W>(v, p); break;
+    case 11: acc_mfma<11, W>(v, p); break;
+    case 12: acc_mfma<12, W>(v, p); break;
+    case 13: acc_mfma<13, W>(v, p); break;
+    case 14: acc_mfma<14, W>(v, p); break;
+    default: acc_mfma<15, W>(v, p); break;
   }
 }
 
@@ -1902,15 +1917,7 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
   const int lh = lane >> 5;    // lane half: keys 4lh + 8j + i of a 32-key unit
 
   int part, rtile;
-  const int x = blockIdx.x;
-  const int R = a.row_tiles;
-  if (R > 1 && (a.num_parts % 8) == 0) {
-    part = (x / (8 * R)) * 8 + (x & 7);
-    rtile = (x >> 3) % R;
-  } else {
-    part = x / R;
-    rtile = x % R;
-  }
+  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, part, rtile);
   int b0, k0, b1, k1, first_split;
   const bool inplan = !SP && a.inplan;   // the sparse mode always reads its plan
   if (inplan) {
@@ -2311,7 +2318,7 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
       if (i + D2 < 32) read_v(i + D2);
       const bf16x4 lo = vlo[i % (D2 + 1)], hi = vhi[i % (D2 + 1)];
       const bf16x8 va = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc_mfma_i(i & 15, va, pv[i >> 4]);
+      acc_mfma_i<false>(i & 15, va, pv[i >> 4]);
       // the other half's exponentials come after the products that read
       // P[0], so that its P[0] can take those registers
       if (smx && i == 2) softmax_step(0, s2, p2, kb2, valid2, false, vm2);
@@ -2345,18 +2352,18 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
       if (i + D1 < 36) read_k(i + D1);
       if (slot0 == 0) {
         if (i == 0)
-          score_mfma_first<0>(sacc, ka[0], qreg[0]);
+          score_mfma_first<0, false>(sacc, ka[0], qreg[0]);
         else if (i < 35)
-          score_mfma<0>(sacc, ka[i % NK], qreg[i]);
+          score_mfma<0, false>(sacc, ka[i % NK], qreg[i]);
         else
-          score_mfma_last<0>(sacc, ka[i % NK], qreg[i]);
+          score_mfma_last<0, false>(sacc, ka[i % NK], qreg[i]);
       } else {
         if (i == 0)
-          score_mfma_first<1>(sacc, ka[0], qreg[0]);
+          score_mfma_first<1, false>(sacc, ka[0], qreg[0]);
         else if (i < 35)
-          score_mfma<1>(sacc, ka[i % NK], qreg[i]);
+          score_mfma<1, false>(sacc, ka[i % NK], qreg[i]);
         else
-          score_mfma_last<1>(sacc, ka[i % NK], qreg[i]);
+          score_mfma_last<1, false>(sacc, ka[i % NK], qreg[i]);
       }
       if ((i & 3) == 1) issue_slot(slot0 + (i >> 2));
       if (smx && i >= 2 && i - 2 < kSmxSteps)
@@ -2498,15 +2505,7 @@ __device__ __forceinline__ void rowwave_f8_body(const DecodeArgs& a) {
   const int lh = lane >> 5;    // lane half: keys 4lh + 8j + i of a 32-key unit
 
   int part, rtile;
-  const int x = blockIdx.x;
-  const int R = a.row_tiles;
-  if (R > 1 && (a.num_parts % 8) == 0) {
-    part = (x / (8 * R)) * 8 + (x & 7);
-    rtile = (x >> 3) % R;
-  } else {
-    part = x / R;
-    rtile = x % R;
-  }
+  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, part, rtile);
   int b0, k0, b1, k1, first_split;
   const bool inplan = !SP && a.inplan;   // the sparse mode always reads its plan
   if (inplan) {

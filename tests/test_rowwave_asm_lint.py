@@ -17,8 +17,11 @@ assembly that hipcc emits for the library source:
   result of a matrix product within the wait states that a 32x32x16 bf16
   product needs before its result may be read (12 on gfx950; the compiler
   itself inserts 12);
-* every inline-asm matrix product is preceded, inside its asm block, by the
-  two wait states that a VALU write of an operand needs (s_nop 1).
+* no VALU instruction writes an operand register of a matrix product within
+  the two wait states before it, along every control-flow path (the bf16
+  kernels' products take their operands from loads and carry no wait states
+  of their own; the FP8 kernels convert operands with VALU instructions and
+  their product asm starts with s_nop 1).
 """
 import os
 import re
@@ -124,28 +127,89 @@ def test_mfma_results_not_touched_early(asm, kernel):
     assert not bad, bad[:10]
 
 
+OPERAND_WAIT_STATES = 2   # a VALU write of a matrix product's operand, then the product
+
+
+def _cfg(asm_text, kernel):
+    """The kernel's instructions and labels in order, with each label's
+    branch sources (as ('label', name) / ('ins', text) items)."""
+    items = []
+    for ln in _body(asm_text, kernel):
+        t = ln.split(";")[0].strip()
+        if not t or t.startswith("."):
+            m = re.match(r"^(\.LBB\w+):", ln.strip())
+            if m:
+                items.append(("label", m.group(1)))
+            continue
+        if t.endswith(":"):
+            continue
+        items.append(("ins", t))
+    preds = {}
+    for i, (kind, x) in enumerate(items):
+        m = re.match(r"s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", x) if kind == "ins" else None
+        if m:
+            preds.setdefault(m.group(1), []).append(i)
+    return items, preds
+
+
+def _valu_dst(ins):
+    op = ins.split()[0]
+    if not op.startswith("v_") or op.startswith("v_mfma"):
+        return set()
+    if op.startswith("v_cmp") and "_e64" not in op:
+        return set()   # VOPC writes vcc only
+    args = ins[len(op):].split(",")
+    return _regs(args[0]) if args and args[0].strip() else set()
+
+
+def _regs(tok):
+    tok = tok.strip()
+    m = re.match(r"([va])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_inline_asm_products_carry_operand_wait_states(asm, kernel):
-    lines = [l.strip() for l in _body(asm, kernel)]
-    inside = False
-    prev = None
+def test_products_wait_for_valu_written_operands(asm, kernel):
+    """No VALU instruction writes a register that a matrix product reads
+    (A, B or C operand, VGPR or AGPR) within the two wait states before it,
+    along every control-flow path into the product (branch sources and
+    fall-through alike; each instruction counts one wait state, s_nop N
+    counts N + 1)."""
+    items, preds = _cfg(asm, kernel)
     n = 0
     bad = []
-    for l in lines:
-        if l.startswith(";;#ASMSTART"):
-            inside, prev = True, None
+    for i, (kind, x) in enumerate(items):
+        if kind != "ins" or not x.startswith("v_mfma"):
             continue
-        if l.startswith(";;#ASMEND"):
-            inside = False
-            continue
-        if not inside or not l or l.startswith(";"):
-            continue
-        if l.startswith("v_mfma"):
-            n += 1
-            ok = prev is not None and (prev.startswith("v_mfma") or
-                                       re.match(r"s_nop ([1-9]|1\d)\b", prev))
-            if not ok:
-                bad.append(l)
-        prev = l
+        n += 1
+        ops = [o.strip() for o in x.split(None, 1)[1].split(",")]
+        srcs = set()
+        for o in ops[1:4]:
+            srcs |= _regs(o)
+        work, seen = [(i - 1, OPERAND_WAIT_STATES)], set()
+        while work:
+            p, rem = work.pop()
+            if rem <= 0 or (p, rem) in seen:
+                continue
+            seen.add((p, rem))
+            if p < 0:
+                continue
+            kind2, y = items[p]
+            if kind2 == "label":
+                work.extend((b, rem) for b in preds.get(y, []))
+                q = p - 1
+                while q >= 0 and items[q][0] == "label":
+                    q -= 1
+                if q >= 0 and not items[q][1].startswith(("s_branch", "s_endpgm")):
+                    work.append((p - 1, rem))
+                continue
+            if _valu_dst(y) & srcs:
+                bad.append((x, y))
+                continue
+            m = re.match(r"s_nop (\d+)", y)
+            work.append((p - 1, rem - (int(m.group(1)) + 1 if m else 1)))
     assert n > 0
     assert not bad, bad[:10]
