@@ -50,116 +50,116 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 307011940,
-        "write_bytes": 8404992,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 307010414,
+        "write_bytes": 4210688,
         "fetch_scale": 1.99986,
         "write_scale": 1.0,
-        "mfma_util": 0.083
+        "mfma_util": 0.0846
     },
     "ridge": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 722795338,
-        "write_bytes": 93391097,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 722680684,
+        "write_bytes": 47784045,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3916
+        "mfma_util": 0.4118
     },
     "long": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 774463768,
-        "write_bytes": 69608121,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 774458572,
+        "write_bytes": 34870157,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4217
+        "mfma_util": 0.4374
     },
     "ragged": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 528700020,
-        "write_bytes": 118483465,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 528498665,
+        "write_bytes": 65792000,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4268
+        "mfma_util": 0.4391
     },
     "draft": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 228844138,
-        "write_bytes": 94557840,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 228781322,
+        "write_bytes": 47370240,
         "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.4238
+        "mfma_util": 0.4271
     },
     "prefill": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 424816645,
-        "write_bytes": 142966918,
-        "fetch_scale": 1.99989,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 424543256,
+        "write_bytes": 92635136,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4889
+        "mfma_util": 0.4948
     },
     "sparse": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 189815318,
-        "write_bytes": 69555203,
-        "fetch_scale": 1.99989,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 189793468,
+        "write_bytes": 33685504,
+        "fetch_scale": 1.99986,
         "write_scale": 1.0,
-        "mfma_util": 0.1964
+        "mfma_util": 0.1982
     },
     "membound/fp8": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 173880633,
-        "write_bytes": 8404992,
-        "fetch_scale": 1.99989,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 173872915,
+        "write_bytes": 4210688,
+        "fetch_scale": 1.99986,
         "write_scale": 1.0,
-        "mfma_util": 0.1096
+        "mfma_util": 0.113
     },
     "ridge/fp8": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 428727415,
-        "write_bytes": 93378048,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 428528192,
+        "write_bytes": 47765050,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3069
+        "mfma_util": 0.3097
     },
     "long/fp8": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 442157083,
-        "write_bytes": 69605574,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 442164636,
+        "write_bytes": 34869760,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3246
+        "mfma_util": 0.3298
     },
     "ragged/fp8": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 329134087,
-        "write_bytes": 118482963,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 328742279,
+        "write_bytes": 65792000,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3165
+        "mfma_util": 0.32
     },
     "draft/fp8": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 151900281,
-        "write_bytes": 94556236,
-        "fetch_scale": 1.9999,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 151809520,
+        "write_bytes": 47370240,
+        "fetch_scale": 1.99993,
         "write_scale": 1.0,
-        "mfma_util": 0.3147
+        "mfma_util": 0.3159
     },
     "prefill/fp8": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 284074951,
-        "write_bytes": 142966822,
-        "fetch_scale": 1.99992,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 283701127,
+        "write_bytes": 92635142,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.3527
+        "mfma_util": 0.3578
     },
     "sparse/fp8": {
-        "kernel_sha256": "cca2ecae58175900f865ad83c1d4eb19cbaff34879aa8c54089205d00e2104ae",
-        "fetch_bytes": 136322626,
-        "write_bytes": 67941507,
-        "fetch_scale": 1.99992,
+        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
+        "fetch_bytes": 136305329,
+        "write_bytes": 33685504,
+        "fetch_scale": 1.99991,
         "write_scale": 1.0,
-        "mfma_util": 0.1748
+        "mfma_util": 0.1697
     }
 }
 
