@@ -96,7 +96,7 @@ int mla_decode_num_parts(int batch, int s_q, int h_q, int h_kv, int num_cus,
  * O_part[slots][M][512], each normalised over its own keys and rounded to
  * bf16 as a whole request's output is (fp32 accumulation before; the merge
  * weights are at most 1 and sum to 1, so the rounding adds at most
- * 2^-9 * max|O_part| to a merged element), followed by fp32
+ * 2^-8 * max|O_part| to a merged element), followed by fp32
  * LSE_part[slots][M] in BASE-2 (log2 of the sum of exp(scale*q.k)), -inf for a
  * piece with no visible key.  Request b's pieces occupy slots
  * [split_offsets[b], split_offsets[b+1]) in key order.

@@ -337,3 +337,28 @@ def test_append_touches_only_new_rows():
     diff = ~torch.eq(kc2.view(torch.int16), inp.kcache.view(torch.int16)).all(dim=-1).squeeze(-1)
     changed = {(int(p), int(r)) for p, r in torch.nonzero(diff).tolist()}
     assert changed <= written
+
+
+@pytest.mark.parametrize("cuts", [(64,), (100, 130), (5, 6, 190), (32, 64, 96, 128, 160, 192, 224)])
+def test_bf16_partials_error_bound(cuts):
+    """Split partials stored in bf16 (the decode's workspace format): merging
+    bf16-rounded piece outputs moves the merged output by at most
+    2^-8 * max_i |O_i| per element (bf16 keeps 8 significant bits, so
+    round-to-nearest-even has relative error <= 2^-8; the merge weights are
+    nonnegative and sum to one), and the
+    LSE not at all; the bound is what the tolerance of the parity tests must
+    absorb on top of the kernel's own rounding."""
+    inp = build_inputs([257], 1, 8, seed=31, extra_pool=1)
+    K = gather_request_kv(inp.kcache, inp.block_table, inp.seqlens, 0)
+    qrows = inp.q[0, 0].double().numpy()
+    edges = [0, *cuts, 257]
+    parts = [attend_rows(qrows, K[a:b], inp.scale, np.full(8, b - a))
+             for a, b in zip(edges[:-1], edges[1:])]
+    exact_O, exact_L = lse_merge(parts)
+    rounded = [(torch.from_numpy(O).to(torch.bfloat16).double().numpy(), L) for O, L in parts]
+    O, L = lse_merge(rounded)
+    bound = 2.0 ** -8 * np.max(np.stack([np.abs(p[0]) for p in parts]), axis=0)
+    assert np.all(np.abs(O - exact_O) <= bound + 1e-15)
+    np.testing.assert_array_equal(L, exact_L)
+    # the bound is not vacuous: the rounding does move the merged output
+    assert np.max(np.abs(O - exact_O)) > 2.0 ** -8 * np.max(np.abs(exact_O)) / 64
