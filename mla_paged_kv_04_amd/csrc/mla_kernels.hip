@@ -107,12 +107,20 @@ __device__ __forceinline__ int n_pages(int L) {
 // Part and row tile of workgroup x (grid = num_parts x row tiles R).
 // Workgroups are dealt to the eight XCDs in turn (x mod 8), each XCD with its
 // own L2; with R > 1 the R row tiles of a part (which read the same pages)
-// go to one XCD.  (Runs of consecutive parts on one XCD, for R = 1, were
-// measured: top-2048 sparse 2 % faster, long-context 1.6 % slower; not kept.)
-__device__ __forceinline__ void part_of_block(int x, int R, int P, int& part, int& rtile) {
+// go to one XCD.  In the sparse mode (CONTIG; R = 1) every item is split into
+// the same number of consecutive parts, which all read the item's Q, so each
+// XCD takes a contiguous run of num_parts / 8 parts and reads an item's Q
+// through one L2 (top-2048 sparse 2 % faster, both cache formats; the same
+// map made the dense long-context workload 1.6 % slower, so dense parts keep
+// x mod 8).
+__device__ __forceinline__ void part_of_block(int x, int R, int P, bool contig, int& part,
+                                              int& rtile) {
   if (P % 8 == 0 && R > 1) {
     part = (x / (8 * R)) * 8 + (x & 7);
     rtile = (x >> 3) % R;
+  } else if (P % 8 == 0 && contig) {
+    part = (x & 7) * (P / 8) + (x >> 3);
+    rtile = 0;
   } else {
     part = x / R;
     rtile = x % R;
@@ -864,7 +872,7 @@ __global__ __launch_bounds__(kThreadsWS, 1) void mla_splitkv_ws_kernel(const Dec
   const int i = lane & 15;
 
   int part, rtile;
-  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, part, rtile);
+  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, SP, part, rtile);
   __shared__ int plan_lds[8];
   __shared__ int so_lds[kPlanMaxBatch + 1];   // split offsets (in-kernel plan)
   int b0, k0, b1, k1, first_split;
@@ -1917,7 +1925,7 @@ __device__ __forceinline__ void rowwave_body(const DecodeArgs& a) {
   const int lh = lane >> 5;    // lane half: keys 4lh + 8j + i of a 32-key unit
 
   int part, rtile;
-  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, part, rtile);
+  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, SP, part, rtile);
   int b0, k0, b1, k1, first_split;
   const bool inplan = !SP && a.inplan;   // the sparse mode always reads its plan
   if (inplan) {
@@ -2505,7 +2513,7 @@ __device__ __forceinline__ void rowwave_f8_body(const DecodeArgs& a) {
   const int lh = lane >> 5;    // lane half: keys 4lh + 8j + i of a 32-key unit
 
   int part, rtile;
-  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, part, rtile);
+  part_of_block(blockIdx.x, a.row_tiles, a.num_parts, SP, part, rtile);
   int b0, k0, b1, k1, first_split;
   const bool inplan = !SP && a.inplan;   // the sparse mode always reads its plan
   if (inplan) {
