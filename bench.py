@@ -50,116 +50,116 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 # (sha256 of csrc/mla_kernels.hip), otherwise reported as null.
 HBM_TRAFFIC = {
     "membound": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 307010414,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 307010352,
         "write_bytes": 4210688,
         "fetch_scale": 1.99986,
         "write_scale": 1.0,
         "mfma_util": 0.0846
     },
     "ridge": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 722680684,
-        "write_bytes": 47784045,
-        "fetch_scale": 1.99992,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 722688215,
+        "write_bytes": 47804982,
+        "fetch_scale": 1.99993,
         "write_scale": 1.0,
-        "mfma_util": 0.4118
+        "mfma_util": 0.4112
     },
     "long": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 774458572,
-        "write_bytes": 34870157,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 774460937,
+        "write_bytes": 34871011,
         "fetch_scale": 1.99992,
+        "write_scale": 1.0,
+        "mfma_util": 0.4426
+    },
+    "ragged": {
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 528448095,
+        "write_bytes": 65792118,
+        "fetch_scale": 1.99992,
+        "write_scale": 1.0,
+        "mfma_util": 0.4441
+    },
+    "draft": {
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 228788065,
+        "write_bytes": 47370240,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0,
         "mfma_util": 0.4374
     },
-    "ragged": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 528498665,
-        "write_bytes": 65792000,
-        "fetch_scale": 1.99992,
-        "write_scale": 1.0,
-        "mfma_util": 0.4391
-    },
-    "draft": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 228781322,
-        "write_bytes": 47370240,
-        "fetch_scale": 1.99989,
-        "write_scale": 1.0,
-        "mfma_util": 0.4271
-    },
     "prefill": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 424543256,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 424529934,
         "write_bytes": 92635136,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.4948
+        "mfma_util": 0.5074
     },
     "sparse": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 189793468,
-        "write_bytes": 33685504,
-        "fetch_scale": 1.99986,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 161516376,
+        "write_bytes": 33686010,
+        "fetch_scale": 1.99985,
         "write_scale": 1.0,
-        "mfma_util": 0.1982
+        "mfma_util": 0.2062
     },
     "membound/fp8": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 173872915,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 173876914,
         "write_bytes": 4210688,
-        "fetch_scale": 1.99986,
+        "fetch_scale": 1.99989,
         "write_scale": 1.0,
-        "mfma_util": 0.113
+        "mfma_util": 0.1155
     },
     "ridge/fp8": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 428528192,
-        "write_bytes": 47765050,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 428502401,
+        "write_bytes": 47764992,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3097
+        "mfma_util": 0.311
     },
     "long/fp8": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 442164636,
-        "write_bytes": 34869760,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 442176301,
+        "write_bytes": 34869789,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3298
+        "mfma_util": 0.3282
     },
     "ragged/fp8": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 328742279,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 328802698,
         "write_bytes": 65792000,
         "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.32
+        "mfma_util": 0.3188
     },
     "draft/fp8": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 151809520,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 151826040,
         "write_bytes": 47370240,
         "fetch_scale": 1.99993,
         "write_scale": 1.0,
-        "mfma_util": 0.3159
+        "mfma_util": 0.3182
     },
     "prefill/fp8": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 283701127,
-        "write_bytes": 92635142,
-        "fetch_scale": 1.99989,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 283635462,
+        "write_bytes": 92635146,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.3578
+        "mfma_util": 0.3576
     },
     "sparse/fp8": {
-        "kernel_sha256": "7eef1989b66e45e30dee37f29fdd0844b736b6df85b8ac03f80a733cd3e7fa1c",
-        "fetch_bytes": 136305329,
-        "write_bytes": 33685504,
-        "fetch_scale": 1.99991,
+        "kernel_sha256": "4625f0bb5924a795928211bd350bb7683e98adda00c009bef9bca9dfb8d1325c",
+        "fetch_bytes": 102086588,
+        "write_bytes": 33685600,
+        "fetch_scale": 1.99992,
         "write_scale": 1.0,
-        "mfma_util": 0.1697
+        "mfma_util": 0.1755
     }
 }
 
